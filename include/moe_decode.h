@@ -1,0 +1,209 @@
+/*
+ * moe_decode.h -- C ABI of the small-batch NVFP4 MoE decode layer for
+ * MI355X (gfx950).
+ *
+ * What the layer computes (for each token b of a batch of at most 8):
+ *   xhat  = x                                  (or RMSNorm(x) * gamma, pre-norm layers)
+ *   l     = R xhat (+ bias)                    router GEMV over E (+S) experts
+ *   route = sigmoid top-k, renormalised        (Flint page, "A 40B MoE that activates
+ *                                               2.5B parameters": sigmoid top-6 plus a
+ *                                               shared expert)
+ *        or softmax over the E+S logits, top-k over the routed E only, weights =
+ *           selected probabilities, shared expert s weighted by its own probability
+ *                                              (Inkling page, "Model Architecture":
+ *                                               the expert sink)
+ *   h_e   = SiLU(W13_e[:I] xhat) * (W13_e[I:] xhat)     per selected/shared expert
+ *   out   = sum_e w_e W2_e h_e  (+ x for pre-norm residual layers)
+ * Only the selected experts' weights are read (Flint page, "From 1,096 kernels to
+ * 346": router and expert GEMVs that read only the selected experts' weights;
+ * routing and the expert combine fused into the neighbouring GEMV kernels).
+ *
+ * Weight formats
+ *   NVFP4: e2m1 codes, one e4m3 scale per 16 consecutive elements of a row, one fp32
+ *          scale per matrix ("Frontier MoE on consumer Blackwell (SM120)", section
+ *          "GLM-5.2": e2m1 x e4m3 block-16 x per-tensor scale_2).  Activations are
+ *          bf16 (W4A16, Flint page, "A 40B MoE ...").
+ *   BF16:  plain bf16 weights.
+ *   Canonical (unpacked) order of an NVFP4 matrix [R, K]: codes uint8 [R][K/2], element
+ *   2j of a row in the low nibble of byte j, 2j+1 in the high nibble; scales uint8
+ *   [R][K/16].  Each expert has W13 [2I][H] (rows 0..I-1 gate, I..2I-1 up) and
+ *   W2 [H][I].  The packers below move these bytes into the kernel layout without
+ *   changing any of them (repack at load time, Flint page, "A 40B MoE ...": the GGUF
+ *   blocks are repacked losslessly at load).
+ *
+ * Conventions
+ *   * Every function returns a moe_status (0 = success); no exceptions cross the ABI.
+ *   * "device" pointers are HIP device memory owned by the caller; "host" pointers are
+ *     ordinary host memory owned by the caller.  The library owns only the workspace a
+ *     layer handle allocates at creation.
+ *   * `stream` is a hipStream_t passed as void* (NULL = the default stream).  Work is
+ *     enqueued asynchronously; moe_decode_layer performs no allocation, no host
+ *     synchronisation and no copy to the host.
+ *   * Argument errors are detected on the host before anything is enqueued.  Kernel
+ *     faults surface at the caller's next synchronisation of the stream.  NaN/Inf in
+ *     inputs propagate; they are not checked.
+ *   * A handle's workspace is shared by all calls made with it: calls on one handle
+ *     must be ordered (one stream, or explicit dependencies).
+ */
+#ifndef MOE_DECODE_H
+#define MOE_DECODE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_ABI_VERSION 1
+
+/* limits of this implementation */
+#define MOE_MAX_BATCH 8      /* the low-latency decode path serves up to 8 requests  */
+#define MOE_MAX_ROUTED 512
+#define MOE_MAX_TOPK 16
+#define MOE_MAX_SHARED 4
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = -1, /* null/negative/inconsistent argument                   */
+  MOE_ERR_UNSUPPORTED = -2, /* shape, dtype or routing combination not implemented    */
+  MOE_ERR_ALIGNMENT = -3,   /* a device pointer is not 16-byte aligned                */
+  MOE_ERR_BATCH = -4,       /* batch outside [1, max_batch]                           */
+  MOE_ERR_LAUNCH = -5,      /* a kernel launch or async copy was rejected by HIP      */
+  MOE_ERR_DEVICE = -6,      /* device allocation / query failed (e.g. no GPU)         */
+  MOE_ERR_STATE = -7        /* readback before any moe_decode_layer call on a handle  */
+} moe_status;
+
+typedef enum { MOE_W_NVFP4 = 0, MOE_W_BF16 = 1 } moe_wtype;
+
+typedef enum {
+  MOE_ROUTE_SIGMOID_TOPK = 0, /* s = sigmoid(l + bias), top-k of s, w = s / sum_topk s, shared c = 1 */
+  MOE_ROUTE_SOFTMAX_SINK = 1  /* p = softmax(l[0..E+S)), top-k of p[0..E), w = p, shared c_s = p[E+s] */
+} moe_route;
+
+/* Layer description.  Shapes: hidden H, inter I, n_routed E, top_k k, n_shared S.
+ * Requirements (else MOE_ERR_UNSUPPORTED): H % 32 == 0, I % 32 == 0, H <= 8192,
+ * I <= 2048, 1 <= k <= min(E, 16), E <= 512, 0 <= S <= 4, 1 <= max_batch <= 8,
+ * plus the layout conditions moe_layer_validate checks.  The router has E rows
+ * (sigmoid) or E + S rows (sink: rows E..E+S-1 score the shared experts).          */
+typedef struct {
+  int hidden;
+  int inter;
+  int n_routed;
+  int top_k;
+  int n_shared;
+  int max_batch;
+  int routed_wtype;          /* moe_wtype                                                  */
+  int shared_wtype;          /* moe_wtype; BF16 routed with NVFP4 shared is unsupported     */
+  int route;                 /* moe_route                                                  */
+  const float* router_bias;  /* device fp32 [E] added to the routed logits, or NULL.        */
+                             /* Sigmoid routing only.  Must outlive the handle.            */
+  const void* prenorm_gamma; /* device bf16 [H], or NULL.  Non-NULL turns on the pre-norm   */
+                             /* prologue xhat = bf16(x / sqrt(mean(x^2) + eps) * gamma).     */
+  float rms_eps;             /* epsilon of the pre-norm (e.g. 1e-6)                         */
+  int add_residual;          /* non-zero: out = x + MoE(xhat)                               */
+} moe_layer_desc;
+
+typedef struct moe_layer* moe_layer_t;
+
+/* Byte layout of a set of n experts of one weight type, as the packers write it.
+ * A set lives in two regions:
+ *   code region : expert e at e * code_stride: packed W13 (w13_code_bytes) then packed
+ *                 W2.  NVFP4: the e2m1 codes.  BF16: the bf16 weights.
+ *   scale region: NVFP4 only.  Expert e at e * scale_stride: packed W13 block scales
+ *                 (w13_scale_bytes) then packed W2 block scales; then, at
+ *                 tensor_scale_offset, fp32 [n][2] = (W13 scale, W2 scale) per expert.
+ *                 BF16: empty (scale_region_bytes = 0).
+ * moe_decode_layer takes the routed set's code region as `expert_packed` and its scale
+ * region as `scales`; the shared set is one buffer `shared_w` holding its code region
+ * at offset 0 and its scale region at offset shared_scale_offset.                   */
+typedef struct {
+  size_t w13_code_bytes;
+  size_t w2_code_bytes;
+  size_t code_stride;
+  size_t code_region_bytes;
+  size_t w13_scale_bytes;
+  size_t w2_scale_bytes;
+  size_t scale_stride;
+  size_t tensor_scale_offset;
+  size_t scale_region_bytes;
+  size_t shared_scale_offset; /* where the scale region starts inside a one-buffer set */
+  size_t shared_total_bytes;  /* code region + padding + scale region                   */
+} moe_expert_layout;
+
+/* ---- host-only queries (no device access) -------------------------------------- */
+
+int moe_abi_version(void);
+const char* moe_status_str(int status);
+
+/* Checks a description (shapes, limits, dtype/routing combination) without touching
+ * the device.  Device pointers inside it are not dereferenced.                       */
+int moe_layer_validate(const moe_layer_desc* desc);
+
+/* Layout of n experts of type wtype for hidden H / inter I (see moe_expert_layout). */
+int moe_expert_layout_query(int wtype, int hidden, int inter, int n_experts,
+                            moe_expert_layout* out);
+
+/* ---- packers (host memory, lossless, load time) ----------------------------------- */
+
+/* Canonical NVFP4 matrix [rows][cols] -> kernel layout.  codes: host uint8
+ * [rows][cols/2] in, code_bytes = rows*cols/2 out; scales: host uint8 [rows][cols/16]
+ * in, rows*cols/16 out.  The output is a permutation of 16-byte code units and 2-byte
+ * scale pairs; every byte (including -0 codes and NaN/zero scale bytes) is kept.
+ * rows/cols must describe a W13 ([2I][H]) or W2 ([H][I]) matrix of a valid layer.  */
+int moe_pack_nvfp4(int rows, int cols, const uint8_t* codes, const uint8_t* scales,
+                   uint8_t* codes_out, uint8_t* scales_out);
+/* Exact inverse of moe_pack_nvfp4. */
+int moe_unpack_nvfp4(int rows, int cols, const uint8_t* codes_packed,
+                     const uint8_t* scales_packed, uint8_t* codes, uint8_t* scales);
+/* Canonical bf16 matrix [rows][cols] (uint16 bit patterns) -> kernel layout, and its
+ * inverse.  A permutation of 16-byte units.                                           */
+int moe_pack_bf16(int rows, int cols, const uint16_t* w, uint16_t* w_out);
+int moe_unpack_bf16(int rows, int cols, const uint16_t* w_packed, uint16_t* w);
+
+/* ---- layer handle ------------------------------------------------------------------ */
+
+/* Validates desc and allocates the handle's device workspace on the current device
+ * (once; no later allocation).  MOE_ERR_DEVICE if no device is usable.              */
+int moe_layer_create(const moe_layer_desc* desc, moe_layer_t* out);
+int moe_layer_destroy(moe_layer_t layer);
+
+/* One MoE decode layer for `batch` tokens (1 <= batch <= max_batch).
+ *   x             device bf16 [batch][H] (16-byte aligned)
+ *   router_w      device bf16 [E_r][H] row-major, E_r = E (sigmoid) or E + S (sink)
+ *   expert_packed device, routed set's code region (moe_expert_layout)
+ *   scales        device, routed set's scale region (NULL allowed for BF16 experts)
+ *   shared_w      device, shared set (code region, then scale region at
+ *                 shared_scale_offset); NULL allowed when n_shared == 0
+ *   out           device bf16 [batch][H]; must not overlap x
+ * Enqueues three kernels on `stream`: (1) router GEMV + last-block routing + shared
+ * experts' gate/up, (2) selected experts' gate/up with SiLU*up, (3) down GEMV of all
+ * selected and shared experts with the weighted, fixed-order combine (+ residual).
+ * Deterministic: no floating-point atomics; the result does not depend on scheduling. */
+int moe_decode_layer(moe_layer_t layer, const void* x, const void* router_w,
+                     const void* expert_packed, const void* scales, const void* shared_w,
+                     void* out, int batch, void* stream);
+
+/* Routing of the last moe_decode_layer call on this handle, copied on `stream` into
+ * device buffers: ids int32 [batch][k] and w fp32 [batch][k] in selection order
+ * (descending score, ties to the lower index); c fp32 [batch][S] shared coefficients.
+ * Any pointer may be NULL to skip it.  MOE_ERR_STATE before the first call.          */
+int moe_layer_routing(moe_layer_t layer, int32_t* ids, float* w, float* c, void* stream);
+
+/* Profiling hook for benchmarks.  events: n_events hipEvent_t handles (as void*), n_events a
+ * positive multiple of 4; the pointer array is copied, the events stay owned by the caller and
+ * must outlive the setting.  Every later moe_decode_layer call number c on this handle records
+ * events[4*(c mod n_events/4) + 0..3] on its stream: before kernel 1, after kernel 1, after
+ * kernel 2 and after kernel 3.  events = NULL (or n_events = 0) turns the hook off.  Not meant
+ * for calls under stream capture.                                                            */
+int moe_layer_set_profiling(moe_layer_t layer, void* const* events, int n_events);
+
+/* Test hook: the SiLU*up activations of the last call, bf16, gathered on `stream`
+ * into h_routed [batch][k][I] (selection order) and h_shared [batch][S][I].          */
+int moe_layer_debug_h(moe_layer_t layer, void* h_routed, void* h_shared, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_DECODE_H */

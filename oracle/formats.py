@@ -73,6 +73,9 @@ def e4m3_value(byte: int) -> float:
 _E2M1 = np.array([e2m1_value(c) for c in range(16)], dtype=np.float64)
 _E4M3 = np.array([e4m3_value(b) for b in range(256)], dtype=np.float64)
 
+# Value pair of every code byte in canonical order: (low nibble, high nibble).
+_E2M1_PAIR = np.stack([_E2M1[np.arange(256) & 15], _E2M1[np.arange(256) >> 4]], axis=1)
+
 # The magnitudes codes 0..7 take under the definition, kept only so tests can
 # compare the definition against a table typed by hand.
 E2M1_MAGNITUDES_BY_DEFINITION = tuple(float(v) for v in _E2M1[:8])
@@ -116,9 +119,9 @@ def dequant_nvfp4(codes, scales, tensor_scale: float) -> np.ndarray:
     K = 2 * half_k
     if scales.shape != (R, K // 16) or K % 16:
         raise ValueError("scale shape does not match codes")
-    vals = _E2M1[unpack_nibbles(codes)]                     # [R, K]
-    blk = np.repeat(_E4M3[scales], 16, axis=1)              # [R, K]
-    return vals * blk * float(np.float32(tensor_scale))
+    vals = _E2M1_PAIR[codes].reshape(R, K // 16, 16)        # element values, by block
+    blk = _E4M3[scales][:, :, None]                         # one scale per block
+    return (vals * blk * float(np.float32(tensor_scale))).reshape(R, K)
 
 
 def dequant_bf16(bits) -> np.ndarray:

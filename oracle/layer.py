@@ -204,27 +204,38 @@ def moe_layer(layer, x_bits, force_ids=None) -> dict:
         ids[b], w[b], c[b] = i_b, w_b, c_b
         scores.append(s_b)
 
-    routed_cache: dict = {}
-    shared_cache: dict = {}
-    out = np.zeros((B, H))
+    # Dequantise each distinct expert once, apply it to every token that uses
+    # it, and release it before the next (only selected experts are touched).
+    uses: dict = {}
+    for b in range(B):
+        for j in range(k):
+            uses.setdefault(int(ids[b, j]), []).append((b, j))
+    y_routed = np.zeros((B, k, H))
+    y_shared = np.zeros((B, S, H))
     h_pairs, y_pairs = {}, {}
+    for e in sorted(uses):
+        w13, w2 = _dequant_expert(layer.routed_expert(e), layer.routed_wtype)
+        for b, j in uses[e]:
+            h, y = expert_mlp(w13, w2, xhat[b])
+            h_pairs[(b, e)], y_pairs[(b, e)] = h, y
+            y_routed[b, j] = y
+        del w13, w2
+    for s in range(S):
+        w13, w2 = _dequant_expert(layer.shared_expert(s), layer.shared_wtype)
+        for b in range(B):
+            h, y = expert_mlp(w13, w2, xhat[b])
+            h_pairs[(b, "shared", s)], y_pairs[(b, "shared", s)] = h, y
+            y_shared[b, s] = y
+        del w13, w2
+
+    # weighted combine: routed slots in selection order, then shared experts
+    out = np.zeros((B, H))
     for b in range(B):
         acc = np.zeros(H)
         for j in range(k):
-            e = int(ids[b, j])
-            if e not in routed_cache:
-                routed_cache[e] = _dequant_expert(layer.routed_expert(e),
-                                                  layer.routed_wtype)
-            h, y = expert_mlp(*routed_cache[e], xhat[b])
-            h_pairs[(b, e)], y_pairs[(b, e)] = h, y
-            acc = acc + w[b, j] * y
+            acc = acc + w[b, j] * y_routed[b, j]
         for s in range(S):
-            if s not in shared_cache:
-                shared_cache[s] = _dequant_expert(layer.shared_expert(s),
-                                                  layer.shared_wtype)
-            h, y = expert_mlp(*shared_cache[s], xhat[b])
-            h_pairs[(b, "shared", s)], y_pairs[(b, "shared", s)] = h, y
-            acc = acc + c[b, s] * y
+            acc = acc + c[b, s] * y_shared[b, s]
         out[b] = acc + (x[b] if layer.residual else 0.0)
 
     return {

@@ -1,0 +1,207 @@
+"""ctypes binding of libmoe_decode.so (argument marshalling only).
+
+The function names mirror the C ABI in include/moe_decode.h.  Every step of
+the layer runs in the library's HIP kernels; PyTorch is used only to own
+device memory and to supply the current HIP stream.  Importing this module
+loads the library and raises if it has not been built: there is no fallback.
+"""
+
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import numpy as np
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmoe_decode.so")
+
+MOE_OK = 0
+STATUS = {0: "MOE_OK", -1: "MOE_ERR_INVALID_ARG", -2: "MOE_ERR_UNSUPPORTED", -3: "MOE_ERR_ALIGNMENT",
+          -4: "MOE_ERR_BATCH", -5: "MOE_ERR_LAUNCH", -6: "MOE_ERR_DEVICE", -7: "MOE_ERR_STATE"}
+MOE_W_NVFP4, MOE_W_BF16 = 0, 1
+MOE_ROUTE_SIGMOID_TOPK, MOE_ROUTE_SOFTMAX_SINK = 0, 1
+WTYPES = {"nvfp4": MOE_W_NVFP4, "bf16": MOE_W_BF16}
+ROUTES = {"sigmoid": MOE_ROUTE_SIGMOID_TOPK, "sink": MOE_ROUTE_SOFTMAX_SINK}
+
+EXPORTED = ("moe_abi_version", "moe_status_str", "moe_layer_validate", "moe_expert_layout_query",
+            "moe_pack_nvfp4", "moe_unpack_nvfp4", "moe_pack_bf16", "moe_unpack_bf16",
+            "moe_layer_create", "moe_layer_destroy", "moe_decode_layer", "moe_layer_routing",
+            "moe_layer_set_profiling", "moe_layer_debug_h")
+
+
+class MoeError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn} failed: {STATUS.get(status, status)} ({status})")
+        self.status = status
+
+
+class moe_layer_desc(C.Structure):
+    _fields_ = [("hidden", C.c_int), ("inter", C.c_int), ("n_routed", C.c_int), ("top_k", C.c_int),
+                ("n_shared", C.c_int), ("max_batch", C.c_int), ("routed_wtype", C.c_int),
+                ("shared_wtype", C.c_int), ("route", C.c_int), ("router_bias", C.c_void_p),
+                ("prenorm_gamma", C.c_void_p), ("rms_eps", C.c_float), ("add_residual", C.c_int)]
+
+
+class moe_expert_layout(C.Structure):
+    _fields_ = [(n, C.c_size_t) for n in (
+        "w13_code_bytes", "w2_code_bytes", "code_stride", "code_region_bytes", "w13_scale_bytes",
+        "w2_scale_bytes", "scale_stride", "tensor_scale_offset", "scale_region_bytes",
+        "shared_scale_offset", "shared_total_bytes")]
+
+    def as_dict(self) -> dict:
+        return {n: int(getattr(self, n)) for n, _ in self._fields_}
+
+
+def _load() -> C.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run `python -m quantized_expert_gemv_amd.build` "
+                          "(there is no CPU fallback)")
+    lib = C.CDLL(LIB_PATH)
+    vp, i32, sz = C.c_void_p, C.c_int, C.c_size_t
+    sig = {
+        "moe_abi_version": ([], i32),
+        "moe_status_str": ([i32], C.c_char_p),
+        "moe_layer_validate": ([C.POINTER(moe_layer_desc)], i32),
+        "moe_expert_layout_query": ([i32, i32, i32, i32, C.POINTER(moe_expert_layout)], i32),
+        "moe_pack_nvfp4": ([i32, i32, vp, vp, vp, vp], i32),
+        "moe_unpack_nvfp4": ([i32, i32, vp, vp, vp, vp], i32),
+        "moe_pack_bf16": ([i32, i32, vp, vp], i32),
+        "moe_unpack_bf16": ([i32, i32, vp, vp], i32),
+        "moe_layer_create": ([C.POINTER(moe_layer_desc), C.POINTER(vp)], i32),
+        "moe_layer_destroy": ([vp], i32),
+        "moe_decode_layer": ([vp, vp, vp, vp, vp, vp, vp, i32, vp], i32),
+        "moe_layer_routing": ([vp, vp, vp, vp, vp], i32),
+        "moe_layer_set_profiling": ([vp, vp, i32], i32),
+        "moe_layer_debug_h": ([vp, vp, vp, vp], i32),
+    }
+    for name, (args, res) in sig.items():
+        f = getattr(lib, name)
+        f.argtypes, f.restype = args, res
+    del sz
+    return lib
+
+
+lib = _load()
+
+
+def _check(fn: str, status: int) -> None:
+    if status != MOE_OK:
+        raise MoeError(fn, status)
+
+
+def _ptr(a) -> int | None:
+    """Device pointer of a torch tensor, host pointer of a numpy array, or an int."""
+    if a is None:
+        return None
+    if isinstance(a, int):
+        return a
+    if isinstance(a, np.ndarray):
+        return a.ctypes.data
+    return a.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+# ---- host-only entry points ---------------------------------------------------------
+
+def moe_abi_version() -> int:
+    return lib.moe_abi_version()
+
+
+def moe_status_str(status: int) -> str:
+    return lib.moe_status_str(status).decode()
+
+
+def make_desc(*, hidden, inter, n_routed, top_k, n_shared, max_batch, routed_wtype="nvfp4",
+              shared_wtype="nvfp4", route="sigmoid", router_bias=None, prenorm_gamma=None,
+              rms_eps=1e-6, add_residual=False) -> moe_layer_desc:
+    return moe_layer_desc(hidden, inter, n_routed, top_k, n_shared, max_batch,
+                          WTYPES.get(routed_wtype, routed_wtype), WTYPES.get(shared_wtype, shared_wtype),
+                          ROUTES.get(route, route), _ptr(router_bias), _ptr(prenorm_gamma),
+                          float(rms_eps), int(bool(add_residual)))
+
+
+def moe_layer_validate(desc: moe_layer_desc) -> int:
+    return lib.moe_layer_validate(C.byref(desc))
+
+
+def moe_expert_layout_query(wtype, hidden: int, inter: int, n_experts: int) -> dict:
+    out = moe_expert_layout()
+    _check("moe_expert_layout_query",
+           lib.moe_expert_layout_query(WTYPES.get(wtype, wtype), hidden, inter, n_experts, C.byref(out)))
+    return out.as_dict()
+
+
+def moe_pack_nvfp4(codes: np.ndarray, scales: np.ndarray, codes_out=None, scales_out=None):
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.uint8)
+    rows, half = codes.shape
+    codes_out = np.empty(codes.size, np.uint8) if codes_out is None else codes_out
+    scales_out = np.empty(scales.size, np.uint8) if scales_out is None else scales_out
+    assert codes_out.nbytes >= codes.nbytes and scales_out.nbytes >= scales.nbytes
+    _check("moe_pack_nvfp4", lib.moe_pack_nvfp4(rows, 2 * half, _ptr(codes), _ptr(scales),
+                                                _ptr(codes_out), _ptr(scales_out)))
+    return codes_out, scales_out
+
+
+def moe_unpack_nvfp4(rows: int, cols: int, codes_p: np.ndarray, scales_p: np.ndarray):
+    codes = np.empty((rows, cols // 2), np.uint8)
+    scales = np.empty((rows, cols // 16), np.uint8)
+    _check("moe_unpack_nvfp4", lib.moe_unpack_nvfp4(rows, cols, _ptr(np.ascontiguousarray(codes_p)),
+                                                    _ptr(np.ascontiguousarray(scales_p)),
+                                                    _ptr(codes), _ptr(scales)))
+    return codes, scales
+
+
+def moe_pack_bf16(w: np.ndarray, w_out=None):
+    w = np.ascontiguousarray(w, dtype=np.uint16)
+    rows, cols = w.shape
+    w_out = np.empty(w.size, np.uint16) if w_out is None else w_out
+    assert w_out.nbytes >= w.nbytes
+    _check("moe_pack_bf16", lib.moe_pack_bf16(rows, cols, _ptr(w), _ptr(w_out)))
+    return w_out
+
+
+def moe_unpack_bf16(rows: int, cols: int, w_p: np.ndarray):
+    w = np.empty((rows, cols), np.uint16)
+    _check("moe_unpack_bf16", lib.moe_unpack_bf16(rows, cols, _ptr(np.ascontiguousarray(w_p)), _ptr(w)))
+    return w
+
+
+# ---- device entry points --------------------------------------------------------------
+
+def moe_layer_create(desc: moe_layer_desc) -> int:
+    h = C.c_void_p()
+    _check("moe_layer_create", lib.moe_layer_create(C.byref(desc), C.byref(h)))
+    return h.value
+
+
+def moe_layer_destroy(handle: int) -> None:
+    _check("moe_layer_destroy", lib.moe_layer_destroy(handle))
+
+
+def moe_decode_layer(handle, x, router_w, expert_packed, scales, shared_w, out, batch, stream=None) -> None:
+    _check("moe_decode_layer", lib.moe_decode_layer(handle, _ptr(x), _ptr(router_w), _ptr(expert_packed),
+                                                    _ptr(scales), _ptr(shared_w), _ptr(out), int(batch),
+                                                    _stream(stream)))
+
+
+def moe_layer_routing(handle, ids=None, w=None, c=None, stream=None) -> None:
+    _check("moe_layer_routing", lib.moe_layer_routing(handle, _ptr(ids), _ptr(w), _ptr(c), _stream(stream)))
+
+
+def moe_layer_set_profiling(handle, events, n_events: int) -> None:
+    """events: a ctypes array of hipEvent_t pointers (or None to turn profiling off)."""
+    _check("moe_layer_set_profiling", lib.moe_layer_set_profiling(handle, events, int(n_events)))
+
+
+def moe_layer_debug_h(handle, h_routed=None, h_shared=None, stream=None) -> None:
+    _check("moe_layer_debug_h", lib.moe_layer_debug_h(handle, _ptr(h_routed), _ptr(h_shared), _stream(stream)))

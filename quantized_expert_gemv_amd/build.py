@@ -1,0 +1,52 @@
+"""Compile the HIP library (libmoe_decode.so) in-tree for gfx950.
+
+    python -m quantized_expert_gemv_amd.build
+
+Uses hipcc directly; the result sits next to this file so that it travels
+with the source tree.  All device code is compiled with packed fp32
+instructions disabled.
+"""
+
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(PKG, "csrc")
+LIB = os.path.join(PKG, "libmoe_decode.so")
+ARCH = os.environ.get("MOE_OFFLOAD_ARCH", "gfx950")
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found (set HIPCC or install ROCm)")
+
+
+def build(verbose: bool = False) -> str:
+    srcs = [os.path.join(CSRC, "api.cpp"), os.path.join(CSRC, "kernels.hip")]
+    tmp = LIB + ".tmp"
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+           "-Wall", "-Wno-unused-function",
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+           "-I", os.path.join(PKG, "..", "include"), *srcs, "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    # the host pass does not know the packed-fp32 feature; that warning is expected
+    noise = "is not a recognized feature for this target"
+    msgs = [l for l in (res.stdout + res.stderr).splitlines() if noise not in l]
+    if res.returncode != 0:
+        raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
+    if verbose and msgs:
+        print("\n".join(msgs))
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

@@ -1,0 +1,792 @@
+// HIP kernels of the small-batch MoE decode layer for MI355X (gfx950, CDNA4).
+//
+// One layer call is three kernels on one stream:
+//   k1_router_shared : router GEMV (+ pre-norm prologue) and, in the same grid,
+//                      the shared experts' gate/up GEMV with SiLU*up (they do
+//                      not depend on routing).  The last router workgroup to
+//                      finish computes the routing (top-k, weights, the union of
+//                      selected experts across the batch) into the workspace.
+//   k2_gateup        : gate/up GEMV of the selected routed experts only, SiLU*up
+//                      epilogue, h in bf16 to the workspace.
+//   k3_down          : down GEMV of every selected and shared expert with the
+//                      weighted combine fused in; each workgroup owns a tile of
+//                      output rows and sums the experts in a fixed order
+//                      (deterministic, no atomics), adds the residual, rounds
+//                      once to bf16.
+// Flint page ("From 1,096 kernels to 346"): the router and expert GEMVs read
+// only the selected experts' weights, and routing and the combine are fused
+// into the neighbouring GEMV kernels.
+//
+// GEMV core: a wavefront lane owns a 32-element chunk of a weight row per
+// step (one 128-bit load of e2m1 codes, or four of bf16) plus two e4m3 block
+// scales, converts the codes to bf16 pairs in registers
+// (v_cvt_scalef32_pk_bf16_fp4) and accumulates with v_dot2_f32_bf16 against
+// the activation chunk it holds in VGPRs; the two 16-element block partial
+// sums are scaled by their e4m3 scales (v_cvt_f32_fp8) in fp32.  Lane
+// partial sums are reduced across the lanes of a row with cross-lane
+// shuffles.  The NVFP4 value is e2m1 x e4m3 block scale x fp32 tensor scale
+// ("Frontier MoE on consumer Blackwell (SM120)", section "GLM-5.2").
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "moe_internal.h"
+
+namespace moe {
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+enum { WT_NVFP4 = 0, WT_BF16 = 1 };
+
+// ---------------------------------------------------------------------------
+// scalar helpers
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ float bf16lo(uint32_t v) { return __uint_as_float(v << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t v) { return __uint_as_float(v & 0xffff0000u); }
+
+// fp32 -> bf16 bits, round to nearest even; NaN -> canonical quiet NaN.
+__device__ __forceinline__ uint32_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                         __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+// Two e2m1 codes (byte SEL of v; low nibble = lower element) -> bf16 pair.
+template <int SEL>
+__device__ __forceinline__ uint32_t fp4pair(uint32_t v) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, 1.0f, SEL));
+}
+
+// 32 e2m1 codes in canonical order -> 16 bf16 pairs (pair i = elements 2i, 2i+1).
+__device__ __forceinline__ void decode_chunk(const uint4& c, uint32_t w[16]) {
+  w[0] = fp4pair<0>(c.x);  w[1] = fp4pair<1>(c.x);  w[2] = fp4pair<2>(c.x);  w[3] = fp4pair<3>(c.x);
+  w[4] = fp4pair<0>(c.y);  w[5] = fp4pair<1>(c.y);  w[6] = fp4pair<2>(c.y);  w[7] = fp4pair<3>(c.y);
+  w[8] = fp4pair<0>(c.z);  w[9] = fp4pair<1>(c.z);  w[10] = fp4pair<2>(c.z); w[11] = fp4pair<3>(c.z);
+  w[12] = fp4pair<0>(c.w); w[13] = fp4pair<1>(c.w); w[14] = fp4pair<2>(c.w); w[15] = fp4pair<3>(c.w);
+}
+
+// e4m3 byte SEL of v -> fp32.
+template <int SEL>
+__device__ __forceinline__ float e4m3f(uint32_t v) {
+  return __builtin_amdgcn_cvt_f32_fp8((int)v, SEL);
+}
+
+// Sum over groups of `width` consecutive lanes (butterfly; every lane of the
+// group ends with the same value).
+__device__ __forceinline__ float lane_reduce(float v, int width) {
+  for (int o = width >> 1; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+__device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+
+__device__ __forceinline__ void unpack4(const uint4& v, uint32_t* d) {
+  d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
+}
+
+// ---------------------------------------------------------------------------
+// activations
+// ---------------------------------------------------------------------------
+
+// Pre-norm: 1/sqrt(mean(x_b^2) + eps) for every token of the batch, into
+// s_rn[b].  Whole workgroup; ends with a barrier.
+__device__ void block_rms(const LayerArgs& a, float* s_rn, float* s_red) {
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int nunits = a.H / 8;
+  for (int b = 0; b < a.B; ++b) {
+    float s = 0.f;
+    for (int u = tid; u < nunits; u += kThreads) {
+      uint32_t d[4];
+      unpack4(ld16(a.x + (size_t)b * a.H + u * 8), d);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float lo = bf16lo(d[i]), hi = bf16hi(d[i]);
+        s = fmaf(lo, lo, s);
+        s = fmaf(hi, hi, s);
+      }
+    }
+    s = lane_reduce(s, 64);
+    if (lane == 0) s_red[wave * MOE_MAX_BATCH + b] = s;
+  }
+  __syncthreads();
+  if (tid < a.B) {
+    float s = 0.f;
+    for (int w = 0; w < kWaves; ++w) s += s_red[w * MOE_MAX_BATCH + tid];
+    s_rn[tid] = 1.0f / sqrtf(s / (float)a.H + a.eps);
+  }
+  __syncthreads();
+}
+
+// xhat pair = bf16(x * rn * gamma) elementwise on a packed bf16 pair.
+__device__ __forceinline__ uint32_t norm_pair(uint32_t xv, uint32_t gv, float rn) {
+  const float lo = (bf16lo(xv) * rn) * bf16lo(gv);
+  const float hi = (bf16hi(xv) * rn) * bf16hi(gv);
+  return f2bf(lo) | (f2bf(hi) << 16);
+}
+
+// The 32-element activation chunk starting at column col0 for every token in
+// `mask`, as 16 bf16 pairs per token.  rn != null applies the pre-norm.
+template <int TB>
+__device__ __forceinline__ void load_act(uint32_t (&xr)[TB][16], const uint16_t* act, int H, int col0,
+                                         unsigned mask, const float* rn, const uint16_t* gamma) {
+#pragma unroll
+  for (int b = 0; b < TB; ++b) {
+    if ((mask >> b) & 1u) {
+      const uint16_t* p = act + (size_t)b * H + col0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) unpack4(ld16(p + 8 * q), &xr[b][4 * q]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) xr[b][i] = 0u;
+    }
+  }
+  if (rn != nullptr) {
+    uint32_t gr[16];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) unpack4(ld16(gamma + col0 + 8 * q), &gr[4 * q]);
+#pragma unroll
+    for (int b = 0; b < TB; ++b) {
+      if ((mask >> b) & 1u) {
+        const float r = rn[b];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) xr[b][i] = norm_pair(xr[b][i], gr[i], r);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// gate/up GEMV with SiLU*up epilogue (shared experts in k1, routed in k2)
+// ---------------------------------------------------------------------------
+
+// One workgroup: kWaves wavefronts.  Wave w takes slice w % ns of the rows
+// and row group w / ns; each wave covers kGateSteps gate steps and the same
+// number of up steps (rows I apart).  h[b][r] = SiLU(g13 * gate) * (g13 * up)
+// rounded to bf16, written to h_out[b * I + r].
+template <int TB, int WT>
+__device__ void gateup_block(const LayerArgs& a, const uint8_t* codes, const uint8_t* scales, float g13,
+                            int item, const uint16_t* act, const float* rn, const uint16_t* gamma,
+                            unsigned mask, uint16_t* h_out, float* s_part) {
+  const MatGeom& g = a.g13;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int slice = wave % g.ns, rg = wave / g.ns, nrg = kWaves / g.ns;
+  const int ri = lane / g.lpr, j = lane % g.lpr;
+  const bool active = j < g.cw;
+  const int t0 = (item * nrg + rg) * kGateSteps;
+  const int gate_steps = a.I / g.rpw;
+  const int col0 = (slice * g.cw + j) * 32;
+
+  float acc[TB][2][kGateSteps];
+#pragma unroll
+  for (int b = 0; b < TB; ++b)
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+#pragma unroll
+      for (int st = 0; st < kGateSteps; ++st) acc[b][q][st] = 0.f;
+
+  if (active) {
+    if constexpr (WT == WT_NVFP4) {
+      // issue the weight loads first (HBM), then the activation loads (L2)
+      uint4 c[2][kGateSteps];
+      uint32_t sw[2];
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int t = t0 + q * gate_steps;
+#pragma unroll
+        for (int st = 0; st < kGateSteps; ++st) c[q][st] = ld16(codes + code_unit(g, slice, t + st, ri, j) * 16);
+        sw[q] = *reinterpret_cast<const uint32_t*>(scales + scale_word(g, slice, t, ri, j));
+      }
+      uint32_t xr[TB][16];
+      load_act<TB>(xr, act, a.H, col0, mask, rn, gamma);
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+#pragma unroll
+        for (int st = 0; st < kGateSteps; ++st) {
+          const float s0 = (st == 0) ? e4m3f<0>(sw[q]) : e4m3f<2>(sw[q]);
+          const float s1 = (st == 0) ? e4m3f<1>(sw[q]) : e4m3f<3>(sw[q]);
+          uint32_t w[16];
+          decode_chunk(c[q][st], w);
+#pragma unroll
+          for (int b = 0; b < TB; ++b) {
+            if ((mask >> b) & 1u) {
+              float p0 = 0.f, p1 = 0.f;
+#pragma unroll
+              for (int i = 0; i < 8; ++i) p0 = dot2(w[i], xr[b][i], p0);
+#pragma unroll
+              for (int i = 8; i < 16; ++i) p1 = dot2(w[i], xr[b][i], p1);
+              acc[b][q][st] = fmaf(p1, s1, p0 * s0);
+            }
+          }
+        }
+      }
+    } else {
+      uint4 c[2][kGateSteps][4];
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int t = t0 + q * gate_steps;
+#pragma unroll
+        for (int st = 0; st < kGateSteps; ++st)
+#pragma unroll
+          for (int sub = 0; sub < 4; ++sub)
+            c[q][st][sub] = ld16(codes + bf16_unit(g, slice, t + st, sub, ri, j) * 16);
+      }
+      uint32_t xr[TB][16];
+      load_act<TB>(xr, act, a.H, col0, mask, rn, gamma);
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+#pragma unroll
+        for (int st = 0; st < kGateSteps; ++st) {
+          uint32_t w[16];
+#pragma unroll
+          for (int sub = 0; sub < 4; ++sub) unpack4(c[q][st][sub], &w[4 * sub]);
+#pragma unroll
+          for (int b = 0; b < TB; ++b) {
+            if ((mask >> b) & 1u) {
+              float p = 0.f;
+#pragma unroll
+              for (int i = 0; i < 16; ++i) p = dot2(w[i], xr[b][i], p);
+              acc[b][q][st] = p;
+            }
+          }
+        }
+      }
+    }
+  }
+
+  // reduce the lanes of each row
+#pragma unroll
+  for (int b = 0; b < TB; ++b)
+    if ((mask >> b) & 1u)
+#pragma unroll
+      for (int q = 0; q < 2; ++q)
+#pragma unroll
+        for (int st = 0; st < kGateSteps; ++st) acc[b][q][st] = lane_reduce(acc[b][q][st], g.lpr);
+
+  if (g.ns > 1) {
+    // rows are split over ns waves: combine the slices in slice order
+    float* mine = s_part + wave * (TB * 2 * kGateSteps);
+    if (lane == 0) {
+#pragma unroll
+      for (int b = 0; b < TB; ++b)
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+#pragma unroll
+          for (int st = 0; st < kGateSteps; ++st) mine[(b * 2 + q) * kGateSteps + st] = acc[b][q][st];
+    }
+    __syncthreads();
+    if (slice != 0) return;
+#pragma unroll
+    for (int b = 0; b < TB; ++b)
+#pragma unroll
+      for (int q = 0; q < 2; ++q)
+#pragma unroll
+        for (int st = 0; st < kGateSteps; ++st) {
+          float v = 0.f;
+          for (int s = 0; s < g.ns; ++s)
+            v += s_part[(rg * g.ns + s) * (TB * 2 * kGateSteps) + (b * 2 + q) * kGateSteps + st];
+          acc[b][q][st] = v;
+        }
+  }
+
+  if (j == 0) {
+#pragma unroll
+    for (int b = 0; b < TB; ++b) {
+      if ((mask >> b) & 1u) {
+#pragma unroll
+        for (int st = 0; st < kGateSteps; ++st) {
+          const float gt = acc[b][0][st] * g13;
+          const float up = acc[b][1][st] * g13;
+          const float h = gt / (1.0f + __expf(-gt)) * up;
+          const int r = (t0 + st) * g.rpw + ri;
+          h_out[(size_t)b * a.I + r] = (uint16_t)f2bf(h);
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// routing (last router workgroup of k1)
+// ---------------------------------------------------------------------------
+
+struct RouteSmem {
+  unsigned mask[MOE_MAX_ROUTED];
+  float w[MOE_MAX_ROUTED * MOE_MAX_BATCH];
+  int sel[kWaves][MOE_MAX_TOPK];
+  int cnt[kWaves];
+};
+
+// Top-k per token (wave per token), routing weights, then the ascending list
+// of distinct selected experts with their token masks and combine weights.
+__device__ void route_block(const LayerArgs& a, RouteSmem& sm) {
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  for (int e = tid; e < a.E; e += kThreads) sm.mask[e] = 0u;
+  __syncthreads();
+
+  for (int b = wave; b < a.B; b += kWaves) {
+    const float* lg = a.logits + (size_t)b * a.Er;
+    float v[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int e = q * 64 + lane;
+      v[q] = (e < a.Er) ? lg[e] : -INFINITY;
+    }
+    unsigned taken = 0u;
+    for (int sel = 0; sel < a.k; ++sel) {
+      // selection key: the logit (NaN ranks lowest); ties -> lower index
+      float bv = -INFINITY;
+      int be = 0x7fffffff;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int e = q * 64 + lane;
+        if (e < a.E && !((taken >> q) & 1u)) {
+          const float key = (v[q] == v[q]) ? v[q] : -INFINITY;
+          if (key > bv || (key == bv && e < be)) { bv = key; be = e; }
+        }
+      }
+      for (int o = 32; o > 0; o >>= 1) {
+        const float ov = __shfl_xor(bv, o, 64);
+        const int oe = __shfl_xor(be, o, 64);
+        if (ov > bv || (ov == bv && oe < be)) { bv = ov; be = oe; }
+      }
+      if ((be & 63) == lane) taken |= 1u << (be >> 6);
+      if (lane == 0) sm.sel[wave][sel] = be;
+    }
+
+    float m = 0.f, z = 0.f;
+    if (a.route == MOE_ROUTE_SOFTMAX_SINK) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) mx = fmaxf(mx, v[q]);
+      for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+      float s = 0.f;
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        if (q * 64 + lane < a.Er) s += expf(v[q] - mx);
+      z = lane_reduce(s, 64);
+      m = mx;
+    }
+
+    if (lane == 0) {
+      float wv[MOE_MAX_TOPK];
+      float tot = 0.f;
+      for (int jj = 0; jj < a.k; ++jj) {
+        const int e = sm.sel[wave][jj];
+        const float l = lg[e];
+        wv[jj] = (a.route == MOE_ROUTE_SOFTMAX_SINK) ? expf(l - m) / z : 1.0f / (1.0f + expf(-l));
+        tot += wv[jj];
+      }
+      for (int jj = 0; jj < a.k; ++jj) {
+        const int e = sm.sel[wave][jj];
+        const float w = (a.route == MOE_ROUTE_SOFTMAX_SINK) ? wv[jj] : wv[jj] / tot;
+        a.topk_ids[b * a.k + jj] = e;
+        a.topk_w[b * a.k + jj] = w;
+        sm.w[e * MOE_MAX_BATCH + b] = w;
+        atomicOr(&sm.mask[e], 1u << b);
+      }
+      for (int s = 0; s < a.S; ++s)
+        a.shared_c[b * a.S + s] =
+            (a.route == MOE_ROUTE_SOFTMAX_SINK) ? expf(lg[a.E + s] - m) / z : 1.0f;
+    }
+  }
+  __syncthreads();
+
+  // compaction: distinct experts in ascending order
+  int base_pos = 0;
+  for (int base = 0; base < a.E; base += kThreads) {
+    const int e = base + tid;
+    const unsigned mk = (e < a.E) ? sm.mask[e] : 0u;
+    const bool flag = mk != 0u;
+    const unsigned long long bal = __ballot(flag);
+    const int below = __popcll(bal & ((1ull << lane) - 1ull));
+    if (lane == 0) sm.cnt[wave] = __popcll(bal);
+    __syncthreads();
+    int off = base_pos;
+    for (int w = 0; w < wave; ++w) off += sm.cnt[w];
+    int tot = 0;
+    for (int w = 0; w < kWaves; ++w) tot += sm.cnt[w];
+    if (flag) {
+      const int pos = off + below;
+      a.rt_ids[pos] = e;
+      a.rt_mask[pos] = mk;
+      for (int b = 0; b < a.maxB; ++b)
+        a.rt_wt[pos * a.maxB + b] = ((mk >> b) & 1u) ? sm.w[e * MOE_MAX_BATCH + b] : 0.f;
+    }
+    base_pos += tot;
+    __syncthreads();
+  }
+  if (tid == 0) a.rt_nd[0] = base_pos;
+}
+
+// ---------------------------------------------------------------------------
+// kernel 1: router GEMV (+ routing) and shared experts' gate/up
+// ---------------------------------------------------------------------------
+
+// Router: wave per router row; lane owns 16 B units u = pass*256 + it*64 + lane
+// of the row (8 bf16 each), so every load instruction covers 1 KB contiguous.
+template <int TB>
+__device__ void router_part(const LayerArgs& a, const float* s_rn, RouteSmem& sm, int* s_last) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int row = blockIdx.x * kWaves + wave;
+  const bool has_row = row < a.Er;
+  const int nunits = a.H / 8;
+  const bool write_xhat = a.prenorm && blockIdx.x == 0 && wave == 0;
+  float acc[TB];
+#pragma unroll
+  for (int b = 0; b < TB; ++b) acc[b] = 0.f;
+
+  for (int base = 0; base < nunits; base += 256) {
+    uint4 wv[4];
+    uint32_t xr[TB][4][4];
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const int u = base + it * 64 + lane;
+      if (has_row && u < nunits) wv[it] = ld16(a.router_w + (size_t)row * a.H + u * 8);
+      else wv[it] = make_uint4(0u, 0u, 0u, 0u);
+    }
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const int u = base + it * 64 + lane;
+      const bool ok = u < nunits;
+      uint32_t gr[4] = {0u, 0u, 0u, 0u};
+      if (ok && a.prenorm) unpack4(ld16(a.gamma + u * 8), gr);
+#pragma unroll
+      for (int b = 0; b < TB; ++b) {
+        if (ok && b < a.B) {
+          unpack4(ld16(a.x + (size_t)b * a.H + u * 8), xr[b][it]);
+          if (a.prenorm) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) xr[b][it][i] = norm_pair(xr[b][it][i], gr[i], s_rn[b]);
+            if (write_xhat)
+              *reinterpret_cast<uint4*>(a.xhat + (size_t)b * a.H + u * 8) =
+                  make_uint4(xr[b][it][0], xr[b][it][1], xr[b][it][2], xr[b][it][3]);
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) xr[b][it][i] = 0u;
+        }
+      }
+    }
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const uint32_t w4[4] = {wv[it].x, wv[it].y, wv[it].z, wv[it].w};
+#pragma unroll
+      for (int b = 0; b < TB; ++b)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[b] = dot2(w4[i], xr[b][it][i], acc[b]);
+    }
+  }
+
+  if (has_row) {
+#pragma unroll
+    for (int b = 0; b < TB; ++b) {
+      if (b < a.B) {
+        const float v = lane_reduce(acc[b], 64);
+        if (lane == 0) {
+          const float bias = (a.bias != nullptr && row < a.E) ? a.bias[row] : 0.f;
+          a.logits[(size_t)b * a.Er + row] = v + bias;
+        }
+      }
+    }
+  }
+
+  // the last router workgroup to finish computes the routing
+  __threadfence();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const unsigned prev = atomicAdd(a.counter, 1u);
+    *s_last = (prev == (unsigned)(a.n_router_blocks - 1));
+  }
+  __syncthreads();
+  if (!*s_last) return;
+  __threadfence();
+  if (threadIdx.x == 0) atomicExch(a.counter, 0u);
+  route_block(a, sm);
+}
+
+template <int TB, int WTS>
+__global__ __launch_bounds__(kThreads) void k1_router_shared(LayerArgs a) {
+  __shared__ float s_rn[MOE_MAX_BATCH];
+  __shared__ float s_red[kWaves * MOE_MAX_BATCH];
+  __shared__ float s_part[kWaves * TB * 2 * kGateSteps];
+  __shared__ RouteSmem sm;
+  __shared__ int s_last;
+  if (a.prenorm) block_rms(a, s_rn, s_red);
+  if ((int)blockIdx.x < a.n_router_blocks) {
+    router_part<TB>(a, s_rn, sm, &s_last);
+    return;
+  }
+  const int sb = blockIdx.x - a.n_router_blocks;
+  const int s = sb / a.wpe13, item = sb % a.wpe13;
+  const uint8_t* codes = a.s_codes + (size_t)s * a.s_code_stride;
+  const uint8_t* scales = (WTS == WT_NVFP4) ? a.s_scales + (size_t)s * a.s_scale_stride : nullptr;
+  const float g13 = (WTS == WT_NVFP4) ? a.s_tscale[2 * s] : 1.0f;
+  const unsigned mask = (1u << a.B) - 1u;
+  gateup_block<TB, WTS>(a, codes, scales, g13, item, a.x, a.prenorm ? s_rn : nullptr, a.gamma, mask,
+                        a.h_shared + (size_t)s * a.maxB * a.I, s_part);
+}
+
+// ---------------------------------------------------------------------------
+// kernel 2: gate/up of the selected routed experts
+// ---------------------------------------------------------------------------
+
+template <int TB, int WTR>
+__global__ __launch_bounds__(kThreads) void k2_gateup(LayerArgs a) {
+  __shared__ float s_part[kWaves * TB * 2 * kGateSteps];
+  const int d = blockIdx.x / a.wpe13, item = blockIdx.x % a.wpe13;
+  if (d >= a.rt_nd[0]) return;  // fewer distinct experts than the grid allows for
+  const int e = a.rt_ids[d];
+  if (e < 0 || e >= a.E) return;
+  const unsigned mask = a.rt_mask[d];
+  const uint8_t* codes = a.r_codes + (size_t)e * a.r_code_stride;
+  const uint8_t* scales = (WTR == WT_NVFP4) ? a.r_scales + (size_t)e * a.r_scale_stride : nullptr;
+  const float g13 = (WTR == WT_NVFP4) ? a.r_tscale[2 * e] : 1.0f;
+  const uint16_t* act = a.prenorm ? a.xhat : a.x;
+  gateup_block<TB, WTR>(a, codes, scales, g13, item, act, nullptr, nullptr, mask,
+                        a.h_routed + (size_t)d * a.maxB * a.I, s_part);
+}
+
+// ---------------------------------------------------------------------------
+// kernel 3: down GEMV + weighted combine (+ residual)
+// ---------------------------------------------------------------------------
+
+// One expert's contribution to the workgroup's S3 output steps:
+// acc[b][st] += wf[b] * (W2 h_b)[rows of step t0+st] (lane partial sums).
+template <int TB, int WT, int S3>
+__device__ __forceinline__ void down_item(const uint8_t* codes, const uint8_t* scales, const MatGeom& g,
+                                          int t0, int ri, int j, const uint16_t* h_base, int I, int maxB,
+                                          unsigned mask, const float (&wf)[TB], float (&acc)[TB][S3]) {
+  if constexpr (WT == WT_NVFP4) {
+    uint4 c[S3];
+    uint32_t sw[S3 / 2];
+#pragma unroll
+    for (int st = 0; st < S3; ++st) c[st] = ld16(codes + code_unit(g, 0, t0 + st, ri, j) * 16);
+#pragma unroll
+    for (int p = 0; p < S3 / 2; ++p)
+      sw[p] = *reinterpret_cast<const uint32_t*>(scales + scale_word(g, 0, t0 + 2 * p, ri, j));
+    uint32_t hr[TB][16];
+#pragma unroll
+    for (int b = 0; b < TB; ++b)
+      if ((mask >> b) & 1u) {
+        const uint16_t* p = h_base + (size_t)b * I + j * 32;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) unpack4(ld16(p + 8 * q), &hr[b][4 * q]);
+      }
+#pragma unroll
+    for (int st = 0; st < S3; ++st) {
+      const float s0 = (st & 1) ? e4m3f<2>(sw[st / 2]) : e4m3f<0>(sw[st / 2]);
+      const float s1 = (st & 1) ? e4m3f<3>(sw[st / 2]) : e4m3f<1>(sw[st / 2]);
+      uint32_t w[16];
+      decode_chunk(c[st], w);
+#pragma unroll
+      for (int b = 0; b < TB; ++b) {
+        if ((mask >> b) & 1u) {
+          float p0 = 0.f, p1 = 0.f;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) p0 = dot2(w[i], hr[b][i], p0);
+#pragma unroll
+          for (int i = 8; i < 16; ++i) p1 = dot2(w[i], hr[b][i], p1);
+          acc[b][st] = fmaf(fmaf(p1, s1, p0 * s0), wf[b], acc[b][st]);
+        }
+      }
+    }
+  } else {
+    uint4 c[S3][4];
+#pragma unroll
+    for (int st = 0; st < S3; ++st)
+#pragma unroll
+      for (int sub = 0; sub < 4; ++sub) c[st][sub] = ld16(codes + bf16_unit(g, 0, t0 + st, sub, ri, j) * 16);
+    uint32_t hr[TB][16];
+#pragma unroll
+    for (int b = 0; b < TB; ++b)
+      if ((mask >> b) & 1u) {
+        const uint16_t* p = h_base + (size_t)b * I + j * 32;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) unpack4(ld16(p + 8 * q), &hr[b][4 * q]);
+      }
+#pragma unroll
+    for (int st = 0; st < S3; ++st) {
+      uint32_t w[16];
+#pragma unroll
+      for (int sub = 0; sub < 4; ++sub) unpack4(c[st][sub], &w[4 * sub]);
+#pragma unroll
+      for (int b = 0; b < TB; ++b) {
+        if ((mask >> b) & 1u) {
+          float p = 0.f;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) p = dot2(w[i], hr[b][i], p);
+          acc[b][st] = fmaf(p, wf[b], acc[b][st]);
+        }
+      }
+    }
+  }
+}
+
+template <int TB, int WTR, int WTS, int S3>
+__global__ __launch_bounds__(kThreads) void k3_down(LayerArgs a) {
+  __shared__ float s_red[kWaves * 1024];
+  const MatGeom& g = a.g2;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int ri = lane / g.lpr, j = lane % g.lpr;
+  const bool active = j < g.cw;
+  const int t0 = blockIdx.x * S3;
+  const int nd = a.rt_nd[0];
+  const int nitems = nd + a.S;
+
+  float acc[TB][S3];
+#pragma unroll
+  for (int b = 0; b < TB; ++b)
+#pragma unroll
+    for (int st = 0; st < S3; ++st) acc[b][st] = 0.f;
+
+  if (active) {
+    // wave w takes items w, w+4, ...: routed slots first, then shared experts
+    for (int it = wave; it < nitems; it += kWaves) {
+      float wf[TB];
+      if (it < nd) {
+        const int e = a.rt_ids[it];
+        if (e < 0 || e >= a.E) continue;
+        const unsigned mask = a.rt_mask[it];
+        const float g2 = (WTR == WT_NVFP4) ? a.r_tscale[2 * e + 1] : 1.0f;
+#pragma unroll
+        for (int b = 0; b < TB; ++b) wf[b] = ((mask >> b) & 1u) ? a.rt_wt[it * a.maxB + b] * g2 : 0.f;
+        const uint8_t* codes = a.r_codes + (size_t)e * a.r_code_stride + a.r_w13_code;
+        const uint8_t* scales =
+            (WTR == WT_NVFP4) ? a.r_scales + (size_t)e * a.r_scale_stride + a.r_w13_scale : nullptr;
+        down_item<TB, WTR, S3>(codes, scales, g, t0, ri, j, a.h_routed + (size_t)it * a.maxB * a.I, a.I,
+                               a.maxB, mask, wf, acc);
+      } else {
+        const int s = it - nd;
+        const unsigned mask = (1u << a.B) - 1u;
+        const float g2 = (WTS == WT_NVFP4) ? a.s_tscale[2 * s + 1] : 1.0f;
+#pragma unroll
+        for (int b = 0; b < TB; ++b) wf[b] = (b < a.B) ? a.shared_c[b * a.S + s] * g2 : 0.f;
+        const uint8_t* codes = a.s_codes + (size_t)s * a.s_code_stride + a.s_w13_code;
+        const uint8_t* scales =
+            (WTS == WT_NVFP4) ? a.s_scales + (size_t)s * a.s_scale_stride + a.s_w13_scale : nullptr;
+        down_item<TB, WTS, S3>(codes, scales, g, t0, ri, j, a.h_shared + (size_t)s * a.maxB * a.I, a.I,
+                               a.maxB, mask, wf, acc);
+      }
+    }
+  }
+
+  const int rpw = g.rpw;
+#pragma unroll
+  for (int b = 0; b < TB; ++b) {
+    if (b < a.B) {
+#pragma unroll
+      for (int st = 0; st < S3; ++st) {
+        const float v = lane_reduce(acc[b][st], g.lpr);
+        if (j == 0) s_red[((wave * TB + b) * S3 + st) * rpw + ri] = v;
+      }
+    }
+  }
+  __syncthreads();
+  const int nout = a.B * S3 * rpw;
+  for (int idx = threadIdx.x; idx < nout; idx += kThreads) {
+    const int b = idx / (S3 * rpw), rem = idx % (S3 * rpw);
+    const int st = rem / rpw, r_in = rem % rpw;
+    float v = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) v += s_red[((w * TB + b) * S3 + st) * rpw + r_in];
+    const int row = (t0 + st) * rpw + r_in;
+    if (a.residual) v += bf16lo(a.x[(size_t)b * a.H + row]);
+    a.out[(size_t)b * a.H + row] = (uint16_t)f2bf(v);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// test hook: gather h of the last call in selection order
+// ---------------------------------------------------------------------------
+
+__global__ __launch_bounds__(kThreads) void k_debug_h(LayerArgs a, uint16_t* h_r, uint16_t* h_s) {
+  const int pair = blockIdx.x;
+  const uint16_t* src = nullptr;
+  uint16_t* dst = nullptr;
+  if (pair < a.B * a.k) {
+    const int b = pair / a.k;
+    const int e = a.topk_ids[pair];
+    const int nd = a.rt_nd[0];
+    int d = -1;
+    for (int i = 0; i < nd; ++i)
+      if (a.rt_ids[i] == e) d = i;
+    if (d < 0 || h_r == nullptr) return;
+    src = a.h_routed + ((size_t)d * a.maxB + b) * a.I;
+    dst = h_r + (size_t)pair * a.I;
+  } else {
+    const int p = pair - a.B * a.k;
+    const int b = p / a.S, s = p % a.S;
+    if (h_s == nullptr) return;
+    src = a.h_shared + ((size_t)s * a.maxB + b) * a.I;
+    dst = h_s + (size_t)p * a.I;
+  }
+  for (int i = threadIdx.x; i < a.I; i += kThreads) dst[i] = src[i];
+}
+
+// ---------------------------------------------------------------------------
+// launch
+// ---------------------------------------------------------------------------
+
+static inline void mark(void* const* ev, int i, hipStream_t st) {
+  if (ev != nullptr) (void)hipEventRecord(reinterpret_cast<hipEvent_t>(ev[i]), st);
+}
+
+template <int TB, int WTR, int WTS, int S3>
+static int launch_impl(const LayerArgs& a, hipStream_t st, void* const* ev) {
+  const int g1 = a.n_router_blocks + a.S * a.wpe13;
+  const int nd_max = (a.B * a.k < a.E) ? a.B * a.k : a.E;
+  const int g2 = nd_max * a.wpe13;
+  const int g3 = a.g2.nsteps / S3;
+  mark(ev, 0, st);
+  hipLaunchKernelGGL((k1_router_shared<TB, WTS>), dim3(g1), dim3(kThreads), 0, st, a);
+  mark(ev, 1, st);
+  hipLaunchKernelGGL((k2_gateup<TB, WTR>), dim3(g2), dim3(kThreads), 0, st, a);
+  mark(ev, 2, st);
+  hipLaunchKernelGGL((k3_down<TB, WTR, WTS, S3>), dim3(g3), dim3(kThreads), 0, st, a);
+  mark(ev, 3, st);
+  return (int)hipGetLastError();
+}
+
+template <int TB, int WTR, int WTS>
+static int launch_s3(const LayerArgs& a, hipStream_t st, void* const* ev) {
+  if (a.s3 == 8) return launch_impl<TB, WTR, WTS, 8>(a, st, ev);
+  return launch_impl<TB, WTR, WTS, 2>(a, st, ev);
+}
+
+template <int TB>
+static int launch_wt(const LayerArgs& a, int rwt, int swt, hipStream_t st, void* const* ev) {
+  if (rwt == WT_NVFP4 && swt == WT_NVFP4) return launch_s3<TB, WT_NVFP4, WT_NVFP4>(a, st, ev);
+  if (rwt == WT_BF16 && swt == WT_BF16) return launch_s3<TB, WT_BF16, WT_BF16>(a, st, ev);
+  if (rwt == WT_NVFP4 && swt == WT_BF16) return launch_s3<TB, WT_NVFP4, WT_BF16>(a, st, ev);
+  return (int)hipErrorInvalidValue;
+}
+
+int launch_layer(const LayerArgs& a, int tb, int rwt, int swt, void* stream, void* const* ev4) {
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  (void)hipGetLastError();  // clear a stale error so it is not reported as ours
+  switch (tb) {
+    case 1: return launch_wt<1>(a, rwt, swt, st, ev4);
+    case 2: return launch_wt<2>(a, rwt, swt, st, ev4);
+    case 4: return launch_wt<4>(a, rwt, swt, st, ev4);
+    case 8: return launch_wt<8>(a, rwt, swt, st, ev4);
+    default: return (int)hipErrorInvalidValue;
+  }
+}
+
+int launch_debug_h(const LayerArgs& a, uint16_t* h_r, uint16_t* h_s, void* stream) {
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  const int n = a.B * a.k + a.B * a.S;
+  hipLaunchKernelGGL(k_debug_h, dim3(n), dim3(kThreads), 0, st, a, h_r, h_s);
+  return (int)hipGetLastError();
+}
+
+}  // namespace moe

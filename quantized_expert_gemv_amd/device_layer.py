@@ -1,0 +1,121 @@
+"""Load a layer's canonical bytes onto the GPU and call it through the C ABI.
+
+``DeviceLayer(layer, max_batch)`` takes any object with the canonical-layer
+attributes (see ``synth.SynthLayer`` / ``synth.ArrayLayer``), repacks every
+expert with the library's lossless packers on the host, copies the packed
+buffers to device memory owned by torch tensors, and creates a layer handle.
+Calling it runs ``moe_decode_layer`` on the current torch stream.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from . import binding as B
+
+
+def bits_to_bf16_tensor(bits: np.ndarray, device) -> torch.Tensor:
+    t = torch.from_numpy(np.ascontiguousarray(bits, dtype=np.uint16).view(np.int16))
+    return t.view(torch.bfloat16).to(device)
+
+
+def bf16_tensor_to_bits(t: torch.Tensor) -> np.ndarray:
+    return t.detach().to("cpu").contiguous().view(torch.int16).numpy().view(np.uint16).copy()
+
+
+def pack_expert_set(get_expert, n: int, wtype: str, H: int, I: int):
+    """Host-side packing of n experts into (code region, scale region) bytes."""
+    lay = B.moe_expert_layout_query(wtype, H, I, n)
+    codes = np.zeros(max(lay["code_region_bytes"], 16), np.uint8)
+    scales = np.zeros(max(lay["scale_region_bytes"], 16), np.uint8)
+    for e in range(n):
+        ex = get_expert(e)
+        c0 = e * lay["code_stride"]
+        c1 = c0 + lay["w13_code_bytes"]
+        c2 = c1 + lay["w2_code_bytes"]
+        if wtype == "nvfp4":
+            s0 = e * lay["scale_stride"]
+            s1 = s0 + lay["w13_scale_bytes"]
+            s2 = s1 + lay["w2_scale_bytes"]
+            B.moe_pack_nvfp4(ex["codes13"], ex["scales13"], codes[c0:c1], scales[s0:s1])
+            B.moe_pack_nvfp4(ex["codes2"], ex["scales2"], codes[c1:c2], scales[s1:s2])
+            ts = lay["tensor_scale_offset"] + 8 * e
+            scales[ts:ts + 8].view(np.float32)[:] = [np.float32(ex["g13"]), np.float32(ex["g2"])]
+        else:
+            B.moe_pack_bf16(ex["w13"], codes[c0:c1].view(np.uint16))
+            B.moe_pack_bf16(ex["w2"], codes[c1:c2].view(np.uint16))
+    return codes, scales, lay
+
+
+class DeviceLayer:
+    def __init__(self, layer, max_batch: int, device="cuda"):
+        self.layer = layer
+        self.device = torch.device(device)
+        H, I, E, S = layer.hidden, layer.inter, layer.n_routed, layer.n_shared
+        self.H, self.I, self.E, self.S, self.k = H, I, E, S, layer.top_k
+        self.max_batch = max_batch
+
+        codes, scales, self.layout_r = pack_expert_set(layer.routed_expert, E, layer.routed_wtype, H, I)
+        self.expert_packed = torch.from_numpy(codes).to(self.device)
+        self.scales = torch.from_numpy(scales).to(self.device) if layer.routed_wtype == "nvfp4" else None
+        del codes, scales
+        if S > 0:
+            s_codes, s_scales, self.layout_s = pack_expert_set(layer.shared_expert, S, layer.shared_wtype, H, I)
+            blob = np.zeros(max(self.layout_s["shared_total_bytes"], 16), np.uint8)
+            blob[:self.layout_s["code_region_bytes"]] = s_codes[:self.layout_s["code_region_bytes"]]
+            if layer.shared_wtype == "nvfp4":
+                o = self.layout_s["shared_scale_offset"]
+                blob[o:o + self.layout_s["scale_region_bytes"]] = s_scales[:self.layout_s["scale_region_bytes"]]
+            self.shared_w = torch.from_numpy(blob).to(self.device)
+        else:
+            self.layout_s, self.shared_w = None, None
+
+        self.router_w = bits_to_bf16_tensor(layer.router_w, self.device)
+        self.router_bias = (torch.from_numpy(np.asarray(layer.router_bias, np.float32)).to(self.device)
+                            if layer.router_bias is not None else None)
+        self.gamma = bits_to_bf16_tensor(layer.gamma, self.device) if layer.gamma is not None else None
+        self.desc = B.make_desc(hidden=H, inter=I, n_routed=E, top_k=layer.top_k, n_shared=S,
+                                max_batch=max_batch, routed_wtype=layer.routed_wtype,
+                                shared_wtype=layer.shared_wtype, route=layer.route,
+                                router_bias=self.router_bias, prenorm_gamma=self.gamma,
+                                rms_eps=layer.eps, add_residual=layer.residual)
+        self.handle = B.moe_layer_create(self.desc)
+
+    # buffers of this layer as the C ABI takes them (may be swapped for copies)
+    def buffers(self) -> dict:
+        return {"router_w": self.router_w, "expert_packed": self.expert_packed,
+                "scales": self.scales, "shared_w": self.shared_w}
+
+    def __call__(self, x: torch.Tensor, out: torch.Tensor | None = None, stream=None, bufs: dict | None = None):
+        b = bufs or self.buffers()
+        batch = x.shape[0]
+        if out is None:
+            out = torch.empty((batch, self.H), dtype=torch.bfloat16, device=self.device)
+        B.moe_decode_layer(self.handle, x, b["router_w"], b["expert_packed"], b["scales"], b["shared_w"],
+                           out, batch, stream)
+        return out
+
+    def routing(self, batch: int):
+        ids = torch.empty((batch, self.k), dtype=torch.int32, device=self.device)
+        w = torch.empty((batch, self.k), dtype=torch.float32, device=self.device)
+        c = torch.empty((batch, max(self.S, 1)), dtype=torch.float32, device=self.device)
+        B.moe_layer_routing(self.handle, ids, w, c)
+        return ids, w, c[:, :self.S]
+
+    def debug_h(self, batch: int):
+        hr = torch.empty((batch, self.k, self.I), dtype=torch.bfloat16, device=self.device)
+        hs = torch.empty((batch, max(self.S, 1), self.I), dtype=torch.bfloat16, device=self.device)
+        B.moe_layer_debug_h(self.handle, hr, hs)
+        return hr, hs[:, :self.S]
+
+    def close(self):
+        if getattr(self, "handle", None):
+            B.moe_layer_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -156,7 +156,8 @@ class SynthLayer:
         w = wl.wid
 
         def scales(tid, shape):
-            a = np.abs(_rng(w, self.slot, tid, index).standard_normal(size=shape)) * wl.scale_mult
+            a = np.abs(_rng(w, self.slot, tid, index).standard_normal(size=shape, dtype=np.float32))
+            a *= np.float32(wl.scale_mult)
             return to_e4m3_bytes(a)
 
         return {
@@ -175,8 +176,8 @@ class SynthLayer:
         r13 = _rng(wl.wid, self.slot, _T_BF13, index)
         r2 = _rng(wl.wid, self.slot, _T_BF2, index)
         return {
-            "w13": to_bf16_bits(r13.normal(0.0, wl.bf16_std, size=(2 * I, H))),
-            "w2": to_bf16_bits(r2.normal(0.0, wl.bf16_std, size=(H, I))),
+            "w13": to_bf16_bits(r13.standard_normal(size=(2 * I, H), dtype=np.float32) * np.float32(wl.bf16_std)),
+            "w2": to_bf16_bits(r2.standard_normal(size=(H, I), dtype=np.float32) * np.float32(wl.bf16_std)),
         }
 
     def routed_expert(self, e: int) -> dict:
