@@ -54,6 +54,11 @@ class moe_expert_layout(C.Structure):
 
 
 def _load() -> C.CDLL:
+    # torch ships its own HIP runtime whose SONAME equals the system one's.
+    # Importing torch first makes the library's libamdhip64.so.7 dependency
+    # resolve to that already-loaded runtime, so the process has a single HIP
+    # runtime and torch's allocations and streams are valid in our calls.
+    import torch  # noqa: F401
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is not built; run `python -m quantized_expert_gemv_amd.build` "
                           "(there is no CPU fallback)")
