@@ -22,7 +22,6 @@ Prints one JSON line.
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -67,14 +66,6 @@ def algorithmic_bytes(wl, d_routed: float, batch: int) -> dict:
     k3 = d_routed * r["w2"] + wl.n_shared * s["w2"] + x_io
     total = router + d_routed * (r["w13"] + r["w2"]) + wl.n_shared * (s["w13"] + s["w2"]) + 2 * x_io
     return {"k1": k1, "k2": k2, "k3": k3, "total": total}
-
-
-def src_digest() -> str:
-    h = hashlib.sha256()
-    for f in ("kernels.hip", "api.cpp", "moe_internal.h"):
-        with open(os.path.join(ROOT, "quantized_expert_gemv_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
-    return h.hexdigest()[:16]
 
 
 def cpu_baseline(layer, xs, budget_s: float, algo_total: float) -> dict:
@@ -235,8 +226,9 @@ def main():
         if os.path.exists(tf):
             with open(tf) as fh:
                 t = json.load(fh)
+            from quantized_expert_gemv_amd.profiling import src_digest
             if t.get("src_digest") == src_digest():
-                traffic = t.get("k2_bytes_per_launch")
+                traffic = t.get("dominant_bytes_per_launch")
         roof = {"bound": "hbm", "kernel": "k2_gateup", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                 "algorithmic_bytes_per_launch": int(round(algo["k2"]))}

@@ -3,11 +3,12 @@
 // One layer call is three kernels on one stream:
 //   k1_router_shared : router GEMV (+ pre-norm prologue) and, in the same grid,
 //                      the shared experts' gate/up GEMV with SiLU*up (they do
-//                      not depend on routing).  The last router workgroup to
-//                      finish computes the routing (top-k, weights, the union of
-//                      selected experts across the batch) into the workspace.
-//   k2_gateup        : gate/up GEMV of the selected routed experts only, SiLU*up
-//                      epilogue, h in bf16 to the workspace.
+//                      not depend on routing).
+//   k2_gateup        : every workgroup first computes the routing from the
+//                      logits (top-k, weights, the union of the selected
+//                      experts across the batch; workgroup 0 also stores it for
+//                      kernel 3), then the gate/up GEMV of its selected routed
+//                      expert, SiLU*up epilogue, h in bf16 to the workspace.
 //   k3_down          : down GEMV of every selected and shared expert with the
 //                      weighted combine fused in; each workgroup owns a tile of
 //                      output rows and sums the experts in a fixed order
@@ -79,11 +80,68 @@ __device__ __forceinline__ float e4m3f(uint32_t v) {
   return __builtin_amdgcn_cvt_f32_fp8((int)v, SEL);
 }
 
-// Sum over groups of `width` consecutive lanes (butterfly; every lane of the
-// group ends with the same value).
+// DPP lane permutes (gfx9 encodings): quad_perm [1,0,3,2], quad_perm [2,3,0,1],
+// row_half_mirror (lane i <- 7-i within 8), row_mirror (lane i <- 15-i within 16).
+#define MOE_DPP_XOR1 0xB1
+#define MOE_DPP_XOR2 0x4E
+#define MOE_DPP_HALF_MIRROR 0x141
+#define MOE_DPP_MIRROR 0x140
+
+__device__ __forceinline__ float dpp_f(float v, int ctrl_sel) {
+  switch (ctrl_sel) {
+    case 0: return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), MOE_DPP_XOR1, 0xF, 0xF, false));
+    case 1: return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), MOE_DPP_XOR2, 0xF, 0xF, false));
+    case 2: return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), MOE_DPP_HALF_MIRROR, 0xF, 0xF, false));
+    default: return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), MOE_DPP_MIRROR, 0xF, 0xF, false));
+  }
+}
+
+// Sum over groups of `width` consecutive lanes (width a power of two <= 64).
+// Each step adds the value of a partner lane from the other half of the
+// group, so every lane of a group ends with the same, order-fixed sum.
 __device__ __forceinline__ float lane_reduce(float v, int width) {
-  for (int o = width >> 1; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  if (width >= 2) v += dpp_f(v, 0);
+  if (width >= 4) v += dpp_f(v, 1);
+  if (width >= 8) v += dpp_f(v, 2);
+  if (width >= 16) v += dpp_f(v, 3);
+  if (width >= 32) v += __shfl_xor(v, 16, 64);
+  if (width >= 64) v += __shfl_xor(v, 32, 64);
   return v;
+}
+
+// Max of a 32-bit unsigned key over the wavefront, returned uniform.
+__device__ __forceinline__ unsigned wave_umax(unsigned v) {
+  v = max(v, (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, MOE_DPP_XOR1, 0xF, 0xF, false));
+  v = max(v, (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, MOE_DPP_XOR2, 0xF, 0xF, false));
+  v = max(v, (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, MOE_DPP_HALF_MIRROR, 0xF, 0xF, false));
+  v = max(v, (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, MOE_DPP_MIRROR, 0xF, 0xF, false));
+  const unsigned a = (unsigned)__builtin_amdgcn_readlane((int)v, 0);
+  const unsigned b = (unsigned)__builtin_amdgcn_readlane((int)v, 16);
+  const unsigned c = (unsigned)__builtin_amdgcn_readlane((int)v, 32);
+  const unsigned d = (unsigned)__builtin_amdgcn_readlane((int)v, 48);
+  return max(max(a, b), max(c, d));
+}
+
+// Sum over the wavefront, returned uniform (fixed order: rows of 16 by DPP,
+// then the four row sums in lane order).
+__device__ __forceinline__ float wave_fsum(float v) {
+  v = lane_reduce(v, 16);
+  const float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float b = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float d = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return (a + b) + (c + d);
+}
+
+// Order-preserving map of fp32 to uint32 (larger float -> larger key);
+// both zeros map to the same key and NaN maps to 0, below every number.
+__device__ __forceinline__ unsigned fkey(float f) {
+  if (f != f) return 0u;
+  const unsigned u = (f == 0.0f) ? 0u : __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float unkey(unsigned k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
 }
 
 __device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
@@ -137,17 +195,21 @@ __device__ __forceinline__ uint32_t norm_pair(uint32_t xv, uint32_t gv, float rn
 template <int TB>
 __device__ __forceinline__ void load_act(uint32_t (&xr)[TB][16], const uint16_t* act, int H, int col0,
                                          unsigned mask, const float* rn, const uint16_t* gamma) {
+  // every load is issued before any is used: rows of tokens outside `mask`
+  // are redirected to the first token of the mask and zeroed afterwards
+  const int b0 = __builtin_ctz(mask | 0x80000000u);
 #pragma unroll
   for (int b = 0; b < TB; ++b) {
-    if ((mask >> b) & 1u) {
-      const uint16_t* p = act + (size_t)b * H + col0;
+    const int bb = ((mask >> b) & 1u) ? b : b0;
+    const uint16_t* p = act + (size_t)bb * H + col0;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) unpack4(ld16(p + 8 * q), &xr[b][4 * q]);
-    } else {
+    for (int q = 0; q < 4; ++q) unpack4(ld16(p + 8 * q), &xr[b][4 * q]);
+  }
+#pragma unroll
+  for (int b = 0; b < TB; ++b)
+    if (!((mask >> b) & 1u))
 #pragma unroll
       for (int i = 0; i < 16; ++i) xr[b][i] = 0u;
-    }
-  }
   if (rn != nullptr) {
     uint32_t gr[16];
 #pragma unroll
@@ -167,14 +229,22 @@ __device__ __forceinline__ void load_act(uint32_t (&xr)[TB][16], const uint16_t*
 // gate/up GEMV with SiLU*up epilogue (shared experts in k1, routed in k2)
 // ---------------------------------------------------------------------------
 
+// First activation column of this lane's chunk in the gate/up GEMV.
+__device__ __forceinline__ int gateup_col0(const MatGeom& g) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int j = lane % g.lpr;
+  const int jj = (j < g.cw) ? j : 0;      // idle lanes read a valid chunk
+  return ((wave % g.ns) * g.cw + jj) * 32;
+}
+
 // One workgroup: kWaves wavefronts.  Wave w takes slice w % ns of the rows
 // and row group w / ns; each wave covers kGateSteps gate steps and the same
 // number of up steps (rows I apart).  h[b][r] = SiLU(g13 * gate) * (g13 * up)
 // rounded to bf16, written to h_out[b * I + r].
 template <int TB, int WT>
 __device__ void gateup_block(const LayerArgs& a, const uint8_t* codes, const uint8_t* scales, float g13,
-                            int item, const uint16_t* act, const float* rn, const uint16_t* gamma,
-                            unsigned mask, uint16_t* h_out, float* s_part) {
+                            int item, const uint32_t (&xr)[TB][16], unsigned mask, uint16_t* h_out,
+                            float* s_part) {
   const MatGeom& g = a.g13;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int slice = wave % g.ns, rg = wave / g.ns, nrg = kWaves / g.ns;
@@ -182,7 +252,6 @@ __device__ void gateup_block(const LayerArgs& a, const uint8_t* codes, const uin
   const bool active = j < g.cw;
   const int t0 = (item * nrg + rg) * kGateSteps;
   const int gate_steps = a.I / g.rpw;
-  const int col0 = (slice * g.cw + j) * 32;
 
   float acc[TB][2][kGateSteps];
 #pragma unroll
@@ -204,8 +273,6 @@ __device__ void gateup_block(const LayerArgs& a, const uint8_t* codes, const uin
         for (int st = 0; st < kGateSteps; ++st) c[q][st] = ld16(codes + code_unit(g, slice, t + st, ri, j) * 16);
         sw[q] = *reinterpret_cast<const uint32_t*>(scales + scale_word(g, slice, t, ri, j));
       }
-      uint32_t xr[TB][16];
-      load_act<TB>(xr, act, a.H, col0, mask, rn, gamma);
 #pragma unroll
       for (int q = 0; q < 2; ++q) {
 #pragma unroll
@@ -238,8 +305,6 @@ __device__ void gateup_block(const LayerArgs& a, const uint8_t* codes, const uin
           for (int sub = 0; sub < 4; ++sub)
             c[q][st][sub] = ld16(codes + bf16_unit(g, slice, t + st, sub, ri, j) * 16);
       }
-      uint32_t xr[TB][16];
-      load_act<TB>(xr, act, a.H, col0, mask, rn, gamma);
 #pragma unroll
       for (int q = 0; q < 2; ++q) {
 #pragma unroll
@@ -314,18 +379,38 @@ __device__ void gateup_block(const LayerArgs& a, const uint8_t* codes, const uin
 }
 
 // ---------------------------------------------------------------------------
-// routing (last router workgroup of k1)
+// routing, recomputed by every workgroup of k2 from the router logits
 // ---------------------------------------------------------------------------
 
 struct RouteSmem {
-  unsigned mask[MOE_MAX_ROUTED];
-  float w[MOE_MAX_ROUTED * MOE_MAX_BATCH];
-  int sel[kWaves][MOE_MAX_TOPK];
+  unsigned mask[MOE_MAX_ROUTED];                 // token mask per expert
+  int sel[MOE_MAX_BATCH][MOE_MAX_TOPK];          // selected experts, selection order
+  float selw[MOE_MAX_BATCH][MOE_MAX_TOPK];       // their combine weights
+  float shc[MOE_MAX_BATCH][MOE_MAX_SHARED];      // shared-expert coefficients
+  int ids[MOE_MAX_BATCH * MOE_MAX_TOPK];         // distinct experts, ascending
+  unsigned dmask[MOE_MAX_BATCH * MOE_MAX_TOPK];
   int cnt[kWaves];
+  int nd;
 };
 
-// Top-k per token (wave per token), routing weights, then the ascending list
-// of distinct selected experts with their token masks and combine weights.
+// Compare-exchange for a descending sort that keeps equal keys in index order.
+__device__ __forceinline__ void cx(unsigned& ka, int& ea, unsigned& kb, int& eb) {
+  if (kb > ka) {
+    const unsigned tk = ka; ka = kb; kb = tk;
+    const int te = ea; ea = eb; eb = te;
+  }
+}
+
+// Top-k per token (one wavefront per token).  Lane l holds the router logits
+// of experts 8l .. 8l+7 (as order-preserving integer keys; experts past E and
+// NaN logits get key 0) sorted descending within the lane, equal keys in
+// index order.  Each of the k rounds takes the largest lane head over the
+// wavefront; among equal heads the lowest lane wins, which is the lowest
+// expert index because lanes hold consecutive experts; the winning lane pops
+// its head.  Lanes 0..k-1 then hold the selection in order and compute the
+// routing weights in parallel.  Finally the ascending list of distinct
+// selected experts with their token masks.  Whole workgroup; ends with a
+// barrier.
 __device__ void route_block(const LayerArgs& a, RouteSmem& sm) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   for (int e = tid; e < a.E; e += kThreads) sm.mask[e] = 0u;
@@ -333,69 +418,70 @@ __device__ void route_block(const LayerArgs& a, RouteSmem& sm) {
 
   for (int b = wave; b < a.B; b += kWaves) {
     const float* lg = a.logits + (size_t)b * a.Er;
-    float v[8];
+    // per = experts per lane (E <= 512 -> at most 8)
+    float lv[8];
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const int e = q * 64 + lane;
-      v[q] = (e < a.Er) ? lg[e] : -INFINITY;
-    }
-    unsigned taken = 0u;
-    for (int sel = 0; sel < a.k; ++sel) {
-      // selection key: the logit (NaN ranks lowest); ties -> lower index
-      float bv = -INFINITY;
-      int be = 0x7fffffff;
+    for (int q = 0; q < 8; ++q) lv[q] = lg[min(lane * 8 + q, a.Er - 1)];
+    unsigned k0, k1, k2, k3, k4, k5, k6, k7;
+    int e0 = lane * 8, e1 = e0 + 1, e2 = e0 + 2, e3 = e0 + 3, e4 = e0 + 4, e5 = e0 + 5, e6 = e0 + 6, e7 = e0 + 7;
+    k0 = (e0 < a.E) ? fkey(lv[0]) : 0u;
+    k1 = (e1 < a.E) ? fkey(lv[1]) : 0u;
+    k2 = (e2 < a.E) ? fkey(lv[2]) : 0u;
+    k3 = (e3 < a.E) ? fkey(lv[3]) : 0u;
+    k4 = (e4 < a.E) ? fkey(lv[4]) : 0u;
+    k5 = (e5 < a.E) ? fkey(lv[5]) : 0u;
+    k6 = (e6 < a.E) ? fkey(lv[6]) : 0u;
+    k7 = (e7 < a.E) ? fkey(lv[7]) : 0u;
+    // stable descending sort of 8 (odd-even transposition: 8 passes)
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const int e = q * 64 + lane;
-        if (e < a.E && !((taken >> q) & 1u)) {
-          const float key = (v[q] == v[q]) ? v[q] : -INFINITY;
-          if (key > bv || (key == bv && e < be)) { bv = key; be = e; }
-        }
-      }
-      for (int o = 32; o > 0; o >>= 1) {
-        const float ov = __shfl_xor(bv, o, 64);
-        const int oe = __shfl_xor(be, o, 64);
-        if (ov > bv || (ov == bv && oe < be)) { bv = ov; be = oe; }
-      }
-      if ((be & 63) == lane) taken |= 1u << (be >> 6);
-      if (lane == 0) sm.sel[wave][sel] = be;
+    for (int pass = 0; pass < 4; ++pass) {
+      cx(k0, e0, k1, e1); cx(k2, e2, k3, e3); cx(k4, e4, k5, e5); cx(k6, e6, k7, e7);
+      cx(k1, e1, k2, e2); cx(k3, e3, k4, e4); cx(k5, e5, k6, e6);
     }
+    // experts past E sort behind every real expert of the lane: a real key
+    // beats key 0, and a real NaN (key 0) has the lower index
 
-    float m = 0.f, z = 0.f;
+    int my_e = 0;
+    float my_l = 0.f;
+    for (int r = 0; r < a.k; ++r) {
+      const unsigned m = wave_umax(k0);
+      const unsigned long long bal = __ballot(k0 == m);
+      const int win = __builtin_ctzll(bal);
+      const int e_sel = __builtin_amdgcn_readlane(e0, win);
+      if (lane == r) { my_e = e_sel; my_l = unkey(m); }
+      if (lane == win) {
+        k0 = k1; e0 = e1; k1 = k2; e1 = e2; k2 = k3; e2 = e3; k3 = k4; e3 = e4;
+        k4 = k5; e4 = e5; k5 = k6; e5 = e6; k6 = k7; e6 = e7; k7 = 0u; e7 = 0x7fffffff;
+      }
+    }
+    my_e = min(max(my_e, 0), a.E - 1);    // in range whatever the inputs
+
+    float mx = 0.f, z = 1.f;
     if (a.route == MOE_ROUTE_SOFTMAX_SINK) {
-      float mx = -INFINITY;
+      unsigned km = 0u;
 #pragma unroll
-      for (int q = 0; q < 8; ++q) mx = fmaxf(mx, v[q]);
-      for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+      for (int q = 0; q < 8; ++q)
+        if (lane * 8 + q < a.Er) km = max(km, fkey(lv[q]));
+      mx = unkey(wave_umax(km));
       float s = 0.f;
 #pragma unroll
       for (int q = 0; q < 8; ++q)
-        if (q * 64 + lane < a.Er) s += expf(v[q] - mx);
-      z = lane_reduce(s, 64);
-      m = mx;
+        if (lane * 8 + q < a.Er) s += expf(lv[q] - mx);
+      z = wave_fsum(s);
     }
-
-    if (lane == 0) {
-      float wv[MOE_MAX_TOPK];
-      float tot = 0.f;
-      for (int jj = 0; jj < a.k; ++jj) {
-        const int e = sm.sel[wave][jj];
-        const float l = lg[e];
-        wv[jj] = (a.route == MOE_ROUTE_SOFTMAX_SINK) ? expf(l - m) / z : 1.0f / (1.0f + expf(-l));
-        tot += wv[jj];
-      }
-      for (int jj = 0; jj < a.k; ++jj) {
-        const int e = sm.sel[wave][jj];
-        const float w = (a.route == MOE_ROUTE_SOFTMAX_SINK) ? wv[jj] : wv[jj] / tot;
-        a.topk_ids[b * a.k + jj] = e;
-        a.topk_w[b * a.k + jj] = w;
-        sm.w[e * MOE_MAX_BATCH + b] = w;
-        atomicOr(&sm.mask[e], 1u << b);
-      }
-      for (int s = 0; s < a.S; ++s)
-        a.shared_c[b * a.S + s] =
-            (a.route == MOE_ROUTE_SOFTMAX_SINK) ? expf(lg[a.E + s] - m) / z : 1.0f;
+    const bool sel = lane < a.k;
+    float v = 0.f;
+    if (sel)
+      v = (a.route == MOE_ROUTE_SOFTMAX_SINK) ? expf(my_l - mx) / z : 1.0f / (1.0f + expf(-my_l));
+    float w = v;
+    if (a.route != MOE_ROUTE_SOFTMAX_SINK) w = v / wave_fsum(v);
+    if (sel) {
+      sm.sel[b][lane] = my_e;
+      sm.selw[b][lane] = w;
+      atomicOr(&sm.mask[my_e], 1u << b);
     }
+    if (lane < a.S)
+      sm.shc[b][lane] = (a.route == MOE_ROUTE_SOFTMAX_SINK) ? expf(lg[a.E + lane] - mx) / z : 1.0f;
   }
   __syncthreads();
 
@@ -414,16 +500,42 @@ __device__ void route_block(const LayerArgs& a, RouteSmem& sm) {
     int tot = 0;
     for (int w = 0; w < kWaves; ++w) tot += sm.cnt[w];
     if (flag) {
-      const int pos = off + below;
-      a.rt_ids[pos] = e;
-      a.rt_mask[pos] = mk;
-      for (int b = 0; b < a.maxB; ++b)
-        a.rt_wt[pos * a.maxB + b] = ((mk >> b) & 1u) ? sm.w[e * MOE_MAX_BATCH + b] : 0.f;
+      sm.ids[off + below] = e;
+      sm.dmask[off + below] = mk;
     }
     base_pos += tot;
     __syncthreads();
   }
-  if (tid == 0) a.rt_nd[0] = base_pos;
+  if (tid == 0) sm.nd = base_pos;
+  __syncthreads();
+}
+
+// The routing of this call, for the down kernel and the readback hooks.
+// rt_wt holds each (slot, token) combine weight already multiplied by the
+// expert's W2 tensor scale.
+template <int WTR>
+__device__ void write_route_table(const LayerArgs& a, const RouteSmem& sm) {
+  const int tid = threadIdx.x;
+  if (tid == 0) a.rt_nd[0] = sm.nd;
+  for (int d = tid; d < sm.nd; d += kThreads) {
+    const int e = sm.ids[d];
+    const unsigned mk = sm.dmask[d];
+    const float g2 = (WTR == WT_NVFP4) ? a.r_tscale[2 * e + 1] : 1.0f;
+    a.rt_ids[d] = e;
+    a.rt_mask[d] = mk;
+    for (int b = 0; b < a.maxB; ++b) {
+      float w = 0.f;
+      if (b < a.B && ((mk >> b) & 1u))
+        for (int r = 0; r < a.k; ++r)
+          if (sm.sel[b][r] == e) w = sm.selw[b][r];
+      a.rt_wt[d * a.maxB + b] = w * g2;
+    }
+  }
+  for (int i = tid; i < a.B * a.k; i += kThreads) {
+    a.topk_ids[i] = sm.sel[i / a.k][i % a.k];
+    a.topk_w[i] = sm.selw[i / a.k][i % a.k];
+  }
+  for (int i = tid; i < a.B * a.S; i += kThreads) a.shared_c[i] = sm.shc[i / a.S][i % a.S];
 }
 
 // ---------------------------------------------------------------------------
@@ -433,7 +545,7 @@ __device__ void route_block(const LayerArgs& a, RouteSmem& sm) {
 // Router: wave per router row; lane owns 16 B units u = pass*256 + it*64 + lane
 // of the row (8 bf16 each), so every load instruction covers 1 KB contiguous.
 template <int TB>
-__device__ void router_part(const LayerArgs& a, const float* s_rn, RouteSmem& sm, int* s_last) {
+__device__ void router_part(const LayerArgs& a, const float* s_rn) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int row = blockIdx.x * kWaves + wave;
   const bool has_row = row < a.Er;
@@ -498,18 +610,6 @@ __device__ void router_part(const LayerArgs& a, const float* s_rn, RouteSmem& sm
     }
   }
 
-  // the last router workgroup to finish computes the routing
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const unsigned prev = atomicAdd(a.counter, 1u);
-    *s_last = (prev == (unsigned)(a.n_router_blocks - 1));
-  }
-  __syncthreads();
-  if (!*s_last) return;
-  __threadfence();
-  if (threadIdx.x == 0) atomicExch(a.counter, 0u);
-  route_block(a, sm);
 }
 
 template <int TB, int WTS>
@@ -517,11 +617,9 @@ __global__ __launch_bounds__(kThreads) void k1_router_shared(LayerArgs a) {
   __shared__ float s_rn[MOE_MAX_BATCH];
   __shared__ float s_red[kWaves * MOE_MAX_BATCH];
   __shared__ float s_part[kWaves * TB * 2 * kGateSteps];
-  __shared__ RouteSmem sm;
-  __shared__ int s_last;
   if (a.prenorm) block_rms(a, s_rn, s_red);
   if ((int)blockIdx.x < a.n_router_blocks) {
-    router_part<TB>(a, s_rn, sm, &s_last);
+    router_part<TB>(a, s_rn);
     return;
   }
   const int sb = blockIdx.x - a.n_router_blocks;
@@ -530,8 +628,9 @@ __global__ __launch_bounds__(kThreads) void k1_router_shared(LayerArgs a) {
   const uint8_t* scales = (WTS == WT_NVFP4) ? a.s_scales + (size_t)s * a.s_scale_stride : nullptr;
   const float g13 = (WTS == WT_NVFP4) ? a.s_tscale[2 * s] : 1.0f;
   const unsigned mask = (1u << a.B) - 1u;
-  gateup_block<TB, WTS>(a, codes, scales, g13, item, a.x, a.prenorm ? s_rn : nullptr, a.gamma, mask,
-                        a.h_shared + (size_t)s * a.maxB * a.I, s_part);
+  uint32_t xr[TB][16];
+  load_act<TB>(xr, a.x, a.H, gateup_col0(a.g13), mask, a.prenorm ? s_rn : nullptr, a.gamma);
+  gateup_block<TB, WTS>(a, codes, scales, g13, item, xr, mask, a.h_shared + (size_t)s * a.maxB * a.I, s_part);
 }
 
 // ---------------------------------------------------------------------------
@@ -541,105 +640,165 @@ __global__ __launch_bounds__(kThreads) void k1_router_shared(LayerArgs a) {
 template <int TB, int WTR>
 __global__ __launch_bounds__(kThreads) void k2_gateup(LayerArgs a) {
   __shared__ float s_part[kWaves * TB * 2 * kGateSteps];
+  __shared__ RouteSmem sm;
+  // activations of every token: issued together with the logits loads
+  uint32_t xr[TB][16];
+  load_act<TB>(xr, a.prenorm ? a.xhat : a.x, a.H, gateup_col0(a.g13), (1u << a.B) - 1u, nullptr, nullptr);
+  route_block(a, sm);
+  if (blockIdx.x == 0) write_route_table<WTR>(a, sm);
   const int d = blockIdx.x / a.wpe13, item = blockIdx.x % a.wpe13;
-  if (d >= a.rt_nd[0]) return;  // fewer distinct experts than the grid allows for
-  const int e = a.rt_ids[d];
+  if (d >= sm.nd) return;  // fewer distinct experts than the grid allows for
+  const int e = sm.ids[d];
   if (e < 0 || e >= a.E) return;
-  const unsigned mask = a.rt_mask[d];
+  const unsigned mask = sm.dmask[d];
+#pragma unroll
+  for (int b = 0; b < TB; ++b)
+    if (!((mask >> b) & 1u))
+#pragma unroll
+      for (int i = 0; i < 16; ++i) xr[b][i] = 0u;
   const uint8_t* codes = a.r_codes + (size_t)e * a.r_code_stride;
   const uint8_t* scales = (WTR == WT_NVFP4) ? a.r_scales + (size_t)e * a.r_scale_stride : nullptr;
   const float g13 = (WTR == WT_NVFP4) ? a.r_tscale[2 * e] : 1.0f;
-  const uint16_t* act = a.prenorm ? a.xhat : a.x;
-  gateup_block<TB, WTR>(a, codes, scales, g13, item, act, nullptr, nullptr, mask,
-                        a.h_routed + (size_t)d * a.maxB * a.I, s_part);
+  gateup_block<TB, WTR>(a, codes, scales, g13, item, xr, mask, a.h_routed + (size_t)d * a.maxB * a.I, s_part);
 }
 
 // ---------------------------------------------------------------------------
 // kernel 3: down GEMV + weighted combine (+ residual)
 // ---------------------------------------------------------------------------
 
-// One expert's contribution to the workgroup's S3 output steps:
-// acc[b][st] += wf[b] * (W2 h_b)[rows of step t0+st] (lane partial sums).
+// Weight and activation registers of one down-GEMV item.
 template <int TB, int WT, int S3>
-__device__ __forceinline__ void down_item(const uint8_t* codes, const uint8_t* scales, const MatGeom& g,
-                                          int t0, int ri, int j, const uint16_t* h_base, int I, int maxB,
-                                          unsigned mask, const float (&wf)[TB], float (&acc)[TB][S3]) {
+struct DownRegs {
+  uint4 c[WT == WT_NVFP4 ? S3 : 4 * S3];
+  uint32_t sw[S3 / 2];
+  uint32_t hr[TB][16];
+};
+
+template <int TB, int WT, int S3, typename Item>
+__device__ __forceinline__ void down_load(DownRegs<TB, WT, S3>& r, const Item& d, const MatGeom& g, int t0,
+                                          int ri, int j, int I) {
   if constexpr (WT == WT_NVFP4) {
-    uint4 c[S3];
-    uint32_t sw[S3 / 2];
 #pragma unroll
-    for (int st = 0; st < S3; ++st) c[st] = ld16(codes + code_unit(g, 0, t0 + st, ri, j) * 16);
+    for (int st = 0; st < S3; ++st) r.c[st] = ld16(d.codes + code_unit(g, 0, t0 + st, ri, j) * 16);
 #pragma unroll
     for (int p = 0; p < S3 / 2; ++p)
-      sw[p] = *reinterpret_cast<const uint32_t*>(scales + scale_word(g, 0, t0 + 2 * p, ri, j));
-    uint32_t hr[TB][16];
-#pragma unroll
-    for (int b = 0; b < TB; ++b)
-      if ((mask >> b) & 1u) {
-        const uint16_t* p = h_base + (size_t)b * I + j * 32;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) unpack4(ld16(p + 8 * q), &hr[b][4 * q]);
-      }
-#pragma unroll
-    for (int st = 0; st < S3; ++st) {
-      const float s0 = (st & 1) ? e4m3f<2>(sw[st / 2]) : e4m3f<0>(sw[st / 2]);
-      const float s1 = (st & 1) ? e4m3f<3>(sw[st / 2]) : e4m3f<1>(sw[st / 2]);
-      uint32_t w[16];
-      decode_chunk(c[st], w);
-#pragma unroll
-      for (int b = 0; b < TB; ++b) {
-        if ((mask >> b) & 1u) {
-          float p0 = 0.f, p1 = 0.f;
-#pragma unroll
-          for (int i = 0; i < 8; ++i) p0 = dot2(w[i], hr[b][i], p0);
-#pragma unroll
-          for (int i = 8; i < 16; ++i) p1 = dot2(w[i], hr[b][i], p1);
-          acc[b][st] = fmaf(fmaf(p1, s1, p0 * s0), wf[b], acc[b][st]);
-        }
-      }
-    }
+      r.sw[p] = *reinterpret_cast<const uint32_t*>(d.scales + scale_word(g, 0, t0 + 2 * p, ri, j));
   } else {
-    uint4 c[S3][4];
 #pragma unroll
     for (int st = 0; st < S3; ++st)
 #pragma unroll
-      for (int sub = 0; sub < 4; ++sub) c[st][sub] = ld16(codes + bf16_unit(g, 0, t0 + st, sub, ri, j) * 16);
-    uint32_t hr[TB][16];
+      for (int sub = 0; sub < 4; ++sub) r.c[4 * st + sub] = ld16(d.codes + bf16_unit(g, 0, t0 + st, sub, ri, j) * 16);
+  }
+  const int b0 = __builtin_ctz(d.mask | 0x80000000u);
 #pragma unroll
-    for (int b = 0; b < TB; ++b)
+  for (int b = 0; b < TB; ++b) {
+    const int bb = ((d.mask >> b) & 1u) ? b : b0;
+    const uint16_t* p = d.h + (size_t)bb * I + j * 32;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) unpack4(ld16(p + 8 * q), &r.hr[b][4 * q]);
+  }
+}
+
+// acc[b][st] += wf[b] * (W2 h_b)[rows of step t0+st]   (lane partial sums)
+template <int TB, int WT, int S3>
+__device__ __forceinline__ void down_compute(const DownRegs<TB, WT, S3>& r, unsigned mask, const float (&wf)[TB],
+                                             float (&acc)[TB][S3]) {
+#pragma unroll
+  for (int st = 0; st < S3; ++st) {
+    uint32_t w[16];
+    float s0 = 1.f, s1 = 1.f;
+    if constexpr (WT == WT_NVFP4) {
+      s0 = (st & 1) ? e4m3f<2>(r.sw[st / 2]) : e4m3f<0>(r.sw[st / 2]);
+      s1 = (st & 1) ? e4m3f<3>(r.sw[st / 2]) : e4m3f<1>(r.sw[st / 2]);
+      decode_chunk(r.c[st], w);
+    } else {
+#pragma unroll
+      for (int sub = 0; sub < 4; ++sub) unpack4(r.c[4 * st + sub], &w[4 * sub]);
+    }
+#pragma unroll
+    for (int b = 0; b < TB; ++b) {
       if ((mask >> b) & 1u) {
-        const uint16_t* p = h_base + (size_t)b * I + j * 32;
+        float v;
+        if constexpr (WT == WT_NVFP4) {
+          float p0 = 0.f, p1 = 0.f;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) unpack4(ld16(p + 8 * q), &hr[b][4 * q]);
-      }
+          for (int i = 0; i < 8; ++i) p0 = dot2(w[i], r.hr[b][i], p0);
 #pragma unroll
-    for (int st = 0; st < S3; ++st) {
-      uint32_t w[16];
-#pragma unroll
-      for (int sub = 0; sub < 4; ++sub) unpack4(c[st][sub], &w[4 * sub]);
-#pragma unroll
-      for (int b = 0; b < TB; ++b) {
-        if ((mask >> b) & 1u) {
+          for (int i = 8; i < 16; ++i) p1 = dot2(w[i], r.hr[b][i], p1);
+          v = fmaf(p1, s1, p0 * s0);
+        } else {
           float p = 0.f;
 #pragma unroll
-          for (int i = 0; i < 16; ++i) p = dot2(w[i], hr[b][i], p);
-          acc[b][st] = fmaf(p, wf[b], acc[b][st]);
+          for (int i = 0; i < 16; ++i) p = dot2(w[i], r.hr[b][i], p);
+          v = p;
         }
+        acc[b][st] = fmaf(v, wf[b], acc[b][st]);
       }
     }
   }
 }
 
+template <int TB, int WT, int S3, typename Item>
+__device__ __forceinline__ void down_one(const Item& d, const MatGeom& g, int t0, int ri, int j, int I,
+                                         const float (&wf)[TB], float (&acc)[TB][S3]) {
+  DownRegs<TB, WT, S3> r;
+  down_load<TB, WT, S3>(r, d, g, t0, ri, j, I);
+  down_compute<TB, WT, S3>(r, d.mask, wf, acc);
+}
+
+// Two items with all their loads issued before either is computed.
+template <int TB, int WT1, int WT2, int S3, typename Item>
+__device__ __forceinline__ void down_pair(const Item& d1, const Item& d2, const MatGeom& g, int t0, int ri, int j,
+                                          int I, const float (&wf1)[TB], const float (&wf2)[TB],
+                                          float (&acc)[TB][S3]) {
+  DownRegs<TB, WT1, S3> r1;
+  DownRegs<TB, WT2, S3> r2;
+  down_load<TB, WT1, S3>(r1, d1, g, t0, ri, j, I);
+  down_load<TB, WT2, S3>(r2, d2, g, t0, ri, j, I);
+  down_compute<TB, WT1, S3>(r1, d1.mask, wf1, acc);
+  down_compute<TB, WT2, S3>(r2, d2.mask, wf2, acc);
+}
+
+// One item of the down kernel: an expert (shared experts first, then the
+// routed slots in ascending expert order) with its token mask, per-token
+// combine weights (times the W2 tensor scale) and activations.
+struct DownItem {
+  const uint8_t* codes;
+  const uint8_t* scales;
+  const uint16_t* h;
+  unsigned mask;
+  int slot;       // index into the per-slot weight table (shared: -1 - s)
+};
+
 template <int TB, int WTR, int WTS, int S3>
 __global__ __launch_bounds__(kThreads) void k3_down(LayerArgs a) {
   __shared__ float s_red[kWaves * 1024];
+  __shared__ int s_ids[MOE_MAX_BATCH * MOE_MAX_TOPK];
+  __shared__ unsigned s_mask[MOE_MAX_BATCH * MOE_MAX_TOPK];
+  __shared__ float s_wf[MOE_MAX_BATCH * MOE_MAX_TOPK * MOE_MAX_BATCH];
+  __shared__ float s_cf[MOE_MAX_SHARED * MOE_MAX_BATCH];
+  __shared__ int s_nd;
   const MatGeom& g = a.g2;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int ri = lane / g.lpr, j = lane % g.lpr;
   const bool active = j < g.cw;
   const int t0 = blockIdx.x * S3;
-  const int nd = a.rt_nd[0];
-  const int nitems = nd + a.S;
+
+  // the routing table in one round trip
+  if (tid == 0) s_nd = a.rt_nd[0];
+  for (int d = tid; d < a.maxd; d += kThreads) {
+    s_ids[d] = a.rt_ids[d];
+    s_mask[d] = a.rt_mask[d];
+  }
+  for (int i = tid; i < a.maxd * a.maxB; i += kThreads) s_wf[i] = a.rt_wt[i];
+  for (int i = tid; i < a.S * a.B; i += kThreads) {
+    const int s = i / a.B, b = i % a.B;
+    const float g2 = (WTS == WT_NVFP4) ? a.s_tscale[2 * s + 1] : 1.0f;
+    s_cf[s * MOE_MAX_BATCH + b] = a.shared_c[b * a.S + s] * g2;
+  }
+  __syncthreads();
+  const int nd = s_nd;
+  const int nitems = a.S + nd;
 
   float acc[TB][S3];
 #pragma unroll
@@ -647,34 +806,54 @@ __global__ __launch_bounds__(kThreads) void k3_down(LayerArgs a) {
 #pragma unroll
     for (int st = 0; st < S3; ++st) acc[b][st] = 0.f;
 
+  auto item_of = [&](int it) {
+    DownItem d;
+    if (it < a.S) {
+      d.codes = a.s_codes + (size_t)it * a.s_code_stride + a.s_w13_code;
+      d.scales = (WTS == WT_NVFP4) ? a.s_scales + (size_t)it * a.s_scale_stride + a.s_w13_scale : nullptr;
+      d.h = a.h_shared + (size_t)it * a.maxB * a.I;
+      d.mask = (1u << a.B) - 1u;
+      d.slot = -1 - it;
+    } else {
+      const int sl = it - a.S;
+      const int e = min(max(s_ids[sl], 0), a.E - 1);
+      d.codes = a.r_codes + (size_t)e * a.r_code_stride + a.r_w13_code;
+      d.scales = (WTR == WT_NVFP4) ? a.r_scales + (size_t)e * a.r_scale_stride + a.r_w13_scale : nullptr;
+      d.h = a.h_routed + (size_t)sl * a.maxB * a.I;
+      d.mask = s_mask[sl];
+      d.slot = sl;
+    }
+    return d;
+  };
+  auto weights_of = [&](const DownItem& d, float (&wf)[TB]) {
+#pragma unroll
+    for (int b = 0; b < TB; ++b) {
+      const bool on = (d.mask >> b) & 1u;
+      wf[b] = !on ? 0.f : (d.slot >= 0 ? s_wf[d.slot * a.maxB + b] : s_cf[(-1 - d.slot) * MOE_MAX_BATCH + b]);
+    }
+  };
+
   if (active) {
-    // wave w takes items w, w+4, ...: routed slots first, then shared experts
-    for (int it = wave; it < nitems; it += kWaves) {
-      float wf[TB];
-      if (it < nd) {
-        const int e = a.rt_ids[it];
-        if (e < 0 || e >= a.E) continue;
-        const unsigned mask = a.rt_mask[it];
-        const float g2 = (WTR == WT_NVFP4) ? a.r_tscale[2 * e + 1] : 1.0f;
-#pragma unroll
-        for (int b = 0; b < TB; ++b) wf[b] = ((mask >> b) & 1u) ? a.rt_wt[it * a.maxB + b] * g2 : 0.f;
-        const uint8_t* codes = a.r_codes + (size_t)e * a.r_code_stride + a.r_w13_code;
-        const uint8_t* scales =
-            (WTR == WT_NVFP4) ? a.r_scales + (size_t)e * a.r_scale_stride + a.r_w13_scale : nullptr;
-        down_item<TB, WTR, S3>(codes, scales, g, t0, ri, j, a.h_routed + (size_t)it * a.maxB * a.I, a.I,
-                               a.maxB, mask, wf, acc);
-      } else {
-        const int s = it - nd;
-        const unsigned mask = (1u << a.B) - 1u;
-        const float g2 = (WTS == WT_NVFP4) ? a.s_tscale[2 * s + 1] : 1.0f;
-#pragma unroll
-        for (int b = 0; b < TB; ++b) wf[b] = (b < a.B) ? a.shared_c[b * a.S + s] * g2 : 0.f;
-        const uint8_t* codes = a.s_codes + (size_t)s * a.s_code_stride + a.s_w13_code;
-        const uint8_t* scales =
-            (WTS == WT_NVFP4) ? a.s_scales + (size_t)s * a.s_scale_stride + a.s_w13_scale : nullptr;
-        down_item<TB, WTS, S3>(codes, scales, g, t0, ri, j, a.h_shared + (size_t)s * a.maxB * a.I, a.I,
-                               a.maxB, mask, wf, acc);
+    // wave w takes items w, w+4, w+8, ...; at small batch two items are in
+    // flight at a time (their loads issued before either is computed), at
+    // larger batch the activation registers allow one
+    constexpr int kInFlight = (TB <= 2 && (S3 == 2 || (WTR == WT_NVFP4 && WTS == WT_NVFP4))) ? 2 : 1;
+    for (int it = wave; it < nitems; it += kInFlight * kWaves) {
+      const int it2 = it + kWaves;
+      const DownItem d1 = item_of(it);
+      float wf1[TB];
+      weights_of(d1, wf1);
+      if (kInFlight == 1 || it2 >= nitems) {
+        if (it < a.S) down_one<TB, WTS, S3>(d1, g, t0, ri, j, a.I, wf1, acc);
+        else down_one<TB, WTR, S3>(d1, g, t0, ri, j, a.I, wf1, acc);
+        continue;
       }
+      const DownItem d2 = item_of(it2);
+      float wf2[TB];
+      weights_of(d2, wf2);
+      if (it2 < a.S) down_pair<TB, WTS, WTS, S3>(d1, d2, g, t0, ri, j, a.I, wf1, wf2, acc);
+      else if (it < a.S) down_pair<TB, WTS, WTR, S3>(d1, d2, g, t0, ri, j, a.I, wf1, wf2, acc);
+      else down_pair<TB, WTR, WTR, S3>(d1, d2, g, t0, ri, j, a.I, wf1, wf2, acc);
     }
   }
 
@@ -691,7 +870,7 @@ __global__ __launch_bounds__(kThreads) void k3_down(LayerArgs a) {
   }
   __syncthreads();
   const int nout = a.B * S3 * rpw;
-  for (int idx = threadIdx.x; idx < nout; idx += kThreads) {
+  for (int idx = tid; idx < nout; idx += kThreads) {
     const int b = idx / (S3 * rpw), rem = idx % (S3 * rpw);
     const int st = rem / rpw, r_in = rem % rpw;
     float v = 0.f;
