@@ -60,6 +60,21 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
                                          __builtin_bit_cast(bf16x2_t, b), c, false);
 }
 
+// sum_i w[i] . x[i] over the 8 bf16 pairs [OFF, OFF+8), as two independent
+// 4-long dot2 chains added at the end (shorter dependency chains).
+template <int OFF>
+__device__ __forceinline__ float dot8(const uint32_t* w, const uint32_t* x) {
+  float pa = dot2(w[OFF + 0], x[OFF + 0], 0.f);
+  float pb = dot2(w[OFF + 1], x[OFF + 1], 0.f);
+  pa = dot2(w[OFF + 2], x[OFF + 2], pa);
+  pb = dot2(w[OFF + 3], x[OFF + 3], pb);
+  pa = dot2(w[OFF + 4], x[OFF + 4], pa);
+  pb = dot2(w[OFF + 5], x[OFF + 5], pb);
+  pa = dot2(w[OFF + 6], x[OFF + 6], pa);
+  pb = dot2(w[OFF + 7], x[OFF + 7], pb);
+  return pa + pb;
+}
+
 // Two e2m1 codes (byte SEL of v; low nibble = lower element) -> bf16 pair.
 template <int SEL>
 __device__ __forceinline__ uint32_t fp4pair(uint32_t v) {
@@ -96,6 +111,27 @@ __device__ __forceinline__ float dpp_f(float v, int ctrl_sel) {
   }
 }
 
+// Value of lane i ^ 16 / lane i ^ 32 (gfx950 v_permlane16_swap / v_permlane32_swap
+// with both operands equal: the two results hold the lane's own value and
+// its partner's, in an order that depends on the half, so their sum / max
+// combines a lane with its partner in every lane).
+__device__ __forceinline__ float add_x16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float add_x32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ unsigned max_x16(unsigned v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  return max((unsigned)r[0], (unsigned)r[1]);
+}
+__device__ __forceinline__ unsigned max_x32(unsigned v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return max((unsigned)r[0], (unsigned)r[1]);
+}
+
 // Sum over groups of `width` consecutive lanes (width a power of two <= 64).
 // Each step adds the value of a partner lane from the other half of the
 // group, so every lane of a group ends with the same, order-fixed sum.
@@ -104,8 +140,8 @@ __device__ __forceinline__ float lane_reduce(float v, int width) {
   if (width >= 4) v += dpp_f(v, 1);
   if (width >= 8) v += dpp_f(v, 2);
   if (width >= 16) v += dpp_f(v, 3);
-  if (width >= 32) v += __shfl_xor(v, 16, 64);
-  if (width >= 64) v += __shfl_xor(v, 32, 64);
+  if (width >= 32) v = add_x16(v);
+  if (width >= 64) v = add_x32(v);
   return v;
 }
 
@@ -115,22 +151,14 @@ __device__ __forceinline__ unsigned wave_umax(unsigned v) {
   v = max(v, (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, MOE_DPP_XOR2, 0xF, 0xF, false));
   v = max(v, (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, MOE_DPP_HALF_MIRROR, 0xF, 0xF, false));
   v = max(v, (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, MOE_DPP_MIRROR, 0xF, 0xF, false));
-  const unsigned a = (unsigned)__builtin_amdgcn_readlane((int)v, 0);
-  const unsigned b = (unsigned)__builtin_amdgcn_readlane((int)v, 16);
-  const unsigned c = (unsigned)__builtin_amdgcn_readlane((int)v, 32);
-  const unsigned d = (unsigned)__builtin_amdgcn_readlane((int)v, 48);
-  return max(max(a, b), max(c, d));
+  v = max_x32(max_x16(v));
+  return (unsigned)__builtin_amdgcn_readfirstlane((int)v);
 }
 
-// Sum over the wavefront, returned uniform (fixed order: rows of 16 by DPP,
-// then the four row sums in lane order).
+// Sum over the wavefront, returned uniform (fixed order).
 __device__ __forceinline__ float wave_fsum(float v) {
-  v = lane_reduce(v, 16);
-  const float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
-  const float b = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
-  const float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
-  const float d = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
-  return (a + b) + (c + d);
+  v = lane_reduce(v, 64);
+  return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(v)));
 }
 
 // Order-preserving map of fp32 to uint32 (larger float -> larger key);
@@ -261,65 +289,49 @@ __device__ void gateup_block(const LayerArgs& a, const uint8_t* codes, const uin
 #pragma unroll
       for (int st = 0; st < kGateSteps; ++st) acc[b][q][st] = 0.f;
 
+  // 1. this wave's weight loads (HBM)
+  uint4 cq[2][kGateSteps];        // nvfp4 codes
+  uint32_t sw[2];                 // nvfp4 scale words
+  uint4 cb[2][kGateSteps][4];     // bf16 weights
   if (active) {
-    if constexpr (WT == WT_NVFP4) {
-      // issue the weight loads first (HBM), then the activation loads (L2)
-      uint4 c[2][kGateSteps];
-      uint32_t sw[2];
 #pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        const int t = t0 + q * gate_steps;
+    for (int q = 0; q < 2; ++q) {
+      const int t = t0 + q * gate_steps;
+      if constexpr (WT == WT_NVFP4) {
 #pragma unroll
-        for (int st = 0; st < kGateSteps; ++st) c[q][st] = ld16(codes + code_unit(g, slice, t + st, ri, j) * 16);
+        for (int st = 0; st < kGateSteps; ++st) cq[q][st] = ld16(codes + code_unit(g, slice, t + st, ri, j) * 16);
         sw[q] = *reinterpret_cast<const uint32_t*>(scales + scale_word(g, slice, t, ri, j));
-      }
-#pragma unroll
-      for (int q = 0; q < 2; ++q) {
-#pragma unroll
-        for (int st = 0; st < kGateSteps; ++st) {
-          const float s0 = (st == 0) ? e4m3f<0>(sw[q]) : e4m3f<2>(sw[q]);
-          const float s1 = (st == 0) ? e4m3f<1>(sw[q]) : e4m3f<3>(sw[q]);
-          uint32_t w[16];
-          decode_chunk(c[q][st], w);
-#pragma unroll
-          for (int b = 0; b < TB; ++b) {
-            if ((mask >> b) & 1u) {
-              float p0 = 0.f, p1 = 0.f;
-#pragma unroll
-              for (int i = 0; i < 8; ++i) p0 = dot2(w[i], xr[b][i], p0);
-#pragma unroll
-              for (int i = 8; i < 16; ++i) p1 = dot2(w[i], xr[b][i], p1);
-              acc[b][q][st] = fmaf(p1, s1, p0 * s0);
-            }
-          }
-        }
-      }
-    } else {
-      uint4 c[2][kGateSteps][4];
-#pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        const int t = t0 + q * gate_steps;
+      } else {
 #pragma unroll
         for (int st = 0; st < kGateSteps; ++st)
 #pragma unroll
           for (int sub = 0; sub < 4; ++sub)
-            c[q][st][sub] = ld16(codes + bf16_unit(g, slice, t + st, sub, ri, j) * 16);
+            cb[q][st][sub] = ld16(codes + bf16_unit(g, slice, t + st, sub, ri, j) * 16);
       }
+    }
+  }
+  // 2. compute
+  if (active) {
 #pragma unroll
-      for (int q = 0; q < 2; ++q) {
+    for (int q = 0; q < 2; ++q) {
 #pragma unroll
-        for (int st = 0; st < kGateSteps; ++st) {
-          uint32_t w[16];
+      for (int st = 0; st < kGateSteps; ++st) {
+        uint32_t w[16];
+        float s0 = 1.f, s1 = 1.f;
+        if constexpr (WT == WT_NVFP4) {
+          s0 = (st == 0) ? e4m3f<0>(sw[q]) : e4m3f<2>(sw[q]);
+          s1 = (st == 0) ? e4m3f<1>(sw[q]) : e4m3f<3>(sw[q]);
+          decode_chunk(cq[q][st], w);
+        } else {
 #pragma unroll
-          for (int sub = 0; sub < 4; ++sub) unpack4(c[q][st][sub], &w[4 * sub]);
+          for (int sub = 0; sub < 4; ++sub) unpack4(cb[q][st][sub], &w[4 * sub]);
+        }
 #pragma unroll
-          for (int b = 0; b < TB; ++b) {
-            if ((mask >> b) & 1u) {
-              float p = 0.f;
-#pragma unroll
-              for (int i = 0; i < 16; ++i) p = dot2(w[i], xr[b][i], p);
-              acc[b][q][st] = p;
-            }
+        for (int b = 0; b < TB; ++b) {
+          if ((mask >> b) & 1u) {
+            const float p0 = dot8<0>(w, xr[b]);
+            const float p1 = dot8<8>(w, xr[b]);
+            acc[b][q][st] = (WT == WT_NVFP4) ? fmaf(p1, s1, p0 * s0) : p0 + p1;
           }
         }
       }
@@ -383,105 +395,112 @@ __device__ void gateup_block(const LayerArgs& a, const uint8_t* codes, const uin
 // ---------------------------------------------------------------------------
 
 struct RouteSmem {
-  unsigned mask[MOE_MAX_ROUTED];                 // token mask per expert
-  int sel[MOE_MAX_BATCH][MOE_MAX_TOPK];          // selected experts, selection order
-  float selw[MOE_MAX_BATCH][MOE_MAX_TOPK];       // their combine weights
-  float shc[MOE_MAX_BATCH][MOE_MAX_SHARED];      // shared-expert coefficients
-  int ids[MOE_MAX_BATCH * MOE_MAX_TOPK];         // distinct experts, ascending
+  unsigned mask[MOE_MAX_ROUTED];                       // token mask per expert
+  unsigned ckey[MOE_MAX_BATCH][kWaves * MOE_MAX_TOPK]; // per-wave candidates (keys), wave-major
+  int cexp[MOE_MAX_BATCH][kWaves * MOE_MAX_TOPK];      // and their experts
+  float wmax[MOE_MAX_BATCH][kWaves];                   // sink: per-wave max logit
+  float wsum[MOE_MAX_BATCH][kWaves];                   //       and sum of exp(l - max)
+  int sel[MOE_MAX_BATCH][MOE_MAX_TOPK];                // selected experts, selection order
+  float selw[MOE_MAX_BATCH][MOE_MAX_TOPK];             // their combine weights
+  float shc[MOE_MAX_BATCH][MOE_MAX_SHARED];            // shared-expert coefficients
+  int ids[MOE_MAX_BATCH * MOE_MAX_TOPK];               // distinct experts, ascending
   unsigned dmask[MOE_MAX_BATCH * MOE_MAX_TOPK];
   int cnt[kWaves];
   int nd;
 };
 
-// Compare-exchange for a descending sort that keeps equal keys in index order.
-__device__ __forceinline__ void cx(unsigned& ka, int& ea, unsigned& kb, int& eb) {
-  if (kb > ka) {
-    const unsigned tk = ka; ka = kb; kb = tk;
-    const int te = ea; ea = eb; eb = te;
-  }
-}
-
-// Top-k per token (one wavefront per token).  Lane l holds the router logits
-// of experts 8l .. 8l+7 (as order-preserving integer keys; experts past E and
-// NaN logits get key 0) sorted descending within the lane, equal keys in
-// index order.  Each of the k rounds takes the largest lane head over the
-// wavefront; among equal heads the lowest lane wins, which is the lowest
-// expert index because lanes hold consecutive experts; the winning lane pops
-// its head.  Lanes 0..k-1 then hold the selection in order and compute the
-// routing weights in parallel.  Finally the ascending list of distinct
-// selected experts with their token masks.  Whole workgroup; ends with a
-// barrier.
+// Routing from the router logits, computed by a whole workgroup.
+//
+// Top-k per token in two stages.  (1) Wave w holds experts
+// [64 w p, 64 (w+1) p) (p = 1 or 2 per lane, consecutive), keys = order-
+// preserving integers of the fp32 logits (experts past E and NaN logits get
+// key 0), and picks its local top-k in k rounds: the largest lane head over
+// the wave, ties to the lowest lane, which is the lowest expert because
+// lanes hold consecutive experts.  (2) One wave ranks the 4k candidates:
+// a candidate's rank counts the candidates with a larger key, plus those
+// with an equal key that come earlier (lower wave, or earlier pick of the
+// same wave, i.e. lower expert index).  Ranks below k are the selection, in
+// order.  Then the routing weights, and the ascending list of distinct
+// selected experts with their token masks.  Ends with a barrier.
 __device__ void route_block(const LayerArgs& a, RouteSmem& sm) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int p = (a.Er > 256) ? 2 : 1;
+  const int e0i = (wave * 64 + lane) * p;
   for (int e = tid; e < a.E; e += kThreads) sm.mask[e] = 0u;
-  __syncthreads();
+  // all logits of all tokens issued before any is used (clamped addresses)
+  float lv[MOE_MAX_BATCH][2];
+#pragma unroll
+  for (int b = 0; b < MOE_MAX_BATCH; ++b) {
+    const float* lg = a.logits + (size_t)min(b, a.B - 1) * a.Er;
+    lv[b][0] = lg[min(e0i, a.Er - 1)];
+    lv[b][1] = lg[min(e0i + 1, a.Er - 1)];
+  }
 
-  for (int b = wave; b < a.B; b += kWaves) {
-    const float* lg = a.logits + (size_t)b * a.Er;
-    // per = experts per lane (E <= 512 -> at most 8)
-    float lv[8];
 #pragma unroll
-    for (int q = 0; q < 8; ++q) lv[q] = lg[min(lane * 8 + q, a.Er - 1)];
-    unsigned k0, k1, k2, k3, k4, k5, k6, k7;
-    int e0 = lane * 8, e1 = e0 + 1, e2 = e0 + 2, e3 = e0 + 3, e4 = e0 + 4, e5 = e0 + 5, e6 = e0 + 6, e7 = e0 + 7;
-    k0 = (e0 < a.E) ? fkey(lv[0]) : 0u;
-    k1 = (e1 < a.E) ? fkey(lv[1]) : 0u;
-    k2 = (e2 < a.E) ? fkey(lv[2]) : 0u;
-    k3 = (e3 < a.E) ? fkey(lv[3]) : 0u;
-    k4 = (e4 < a.E) ? fkey(lv[4]) : 0u;
-    k5 = (e5 < a.E) ? fkey(lv[5]) : 0u;
-    k6 = (e6 < a.E) ? fkey(lv[6]) : 0u;
-    k7 = (e7 < a.E) ? fkey(lv[7]) : 0u;
-    // stable descending sort of 8 (odd-even transposition: 8 passes)
-#pragma unroll
-    for (int pass = 0; pass < 4; ++pass) {
-      cx(k0, e0, k1, e1); cx(k2, e2, k3, e3); cx(k4, e4, k5, e5); cx(k6, e6, k7, e7);
-      cx(k1, e1, k2, e2); cx(k3, e3, k4, e4); cx(k5, e5, k6, e6);
+  for (int b = 0; b < MOE_MAX_BATCH; ++b) {
+    if (b >= a.B) break;
+    unsigned k0 = (e0i < a.E) ? fkey(lv[b][0]) : 0u;
+    unsigned k1 = (p == 2 && e0i + 1 < a.E) ? fkey(lv[b][1]) : 0u;
+    int x0 = e0i, x1 = e0i + 1;
+    if (k1 > k0) {
+      const unsigned tk = k0; k0 = k1; k1 = tk;
+      const int te = x0; x0 = x1; x1 = te;
     }
-    // experts past E sort behind every real expert of the lane: a real key
-    // beats key 0, and a real NaN (key 0) has the lower index
-
-    int my_e = 0;
-    float my_l = 0.f;
+    if (p == 1) { k1 = 0u; x1 = 0x7fffffff; }
     for (int r = 0; r < a.k; ++r) {
       const unsigned m = wave_umax(k0);
-      const unsigned long long bal = __ballot(k0 == m);
-      const int win = __builtin_ctzll(bal);
-      const int e_sel = __builtin_amdgcn_readlane(e0, win);
-      if (lane == r) { my_e = e_sel; my_l = unkey(m); }
-      if (lane == win) {
-        k0 = k1; e0 = e1; k1 = k2; e1 = e2; k2 = k3; e2 = e3; k3 = k4; e3 = e4;
-        k4 = k5; e4 = e5; k5 = k6; e5 = e6; k6 = k7; e6 = e7; k7 = 0u; e7 = 0x7fffffff;
+      const int win = __builtin_ctzll(__ballot(k0 == m));
+      const int e_sel = __builtin_amdgcn_readlane(x0, win);
+      if (lane == 0) {
+        sm.ckey[b][wave * a.k + r] = m;
+        sm.cexp[b][wave * a.k + r] = e_sel;
+      }
+      if (lane == win) { k0 = k1; x0 = x1; k1 = 0u; x1 = 0x7fffffff; }
+    }
+    if (a.route == MOE_ROUTE_SOFTMAX_SINK) {
+      const bool v0 = e0i < a.Er, v1 = (p == 2) && (e0i + 1 < a.Er);
+      float mx = fmaxf(v0 ? lv[b][0] : -INFINITY, v1 ? lv[b][1] : -INFINITY);
+      mx = unkey(wave_umax(fkey(mx)));
+      float sv = (v0 ? expf(lv[b][0] - mx) : 0.f) + (v1 ? expf(lv[b][1] - mx) : 0.f);
+      sv = wave_fsum(sv);
+      if (lane == 0) {
+        sm.wmax[b][wave] = mx;
+        sm.wsum[b][wave] = sv;
       }
     }
-    my_e = min(max(my_e, 0), a.E - 1);    // in range whatever the inputs
+  }
+  __syncthreads();
 
+  const int nc = kWaves * a.k;
+  for (int b = wave; b < a.B; b += kWaves) {
+    const unsigned ki = (lane < nc) ? sm.ckey[b][lane] : 0u;
+    int ei = (lane < nc) ? sm.cexp[b][lane] : 0;
+    int rank = 0;
+    for (int jc = 0; jc < nc; ++jc) {
+      const unsigned kj = (unsigned)__builtin_amdgcn_readlane((int)ki, jc);
+      rank += (kj > ki || (kj == ki && jc < lane)) ? 1 : 0;
+    }
+    const bool sel = lane < nc && rank < a.k;
+    ei = min(max(ei, 0), a.E - 1);          // in range whatever the inputs
     float mx = 0.f, z = 1.f;
     if (a.route == MOE_ROUTE_SOFTMAX_SINK) {
-      unsigned km = 0u;
-#pragma unroll
-      for (int q = 0; q < 8; ++q)
-        if (lane * 8 + q < a.Er) km = max(km, fkey(lv[q]));
-      mx = unkey(wave_umax(km));
-      float s = 0.f;
-#pragma unroll
-      for (int q = 0; q < 8; ++q)
-        if (lane * 8 + q < a.Er) s += expf(lv[q] - mx);
-      z = wave_fsum(s);
+      mx = fmaxf(fmaxf(sm.wmax[b][0], sm.wmax[b][1]), fmaxf(sm.wmax[b][2], sm.wmax[b][3]));
+      z = 0.f;
+      for (int w = 0; w < kWaves; ++w) z += sm.wsum[b][w] * expf(sm.wmax[b][w] - mx);
     }
-    const bool sel = lane < a.k;
+    const float l = unkey(ki);
     float v = 0.f;
-    if (sel)
-      v = (a.route == MOE_ROUTE_SOFTMAX_SINK) ? expf(my_l - mx) / z : 1.0f / (1.0f + expf(-my_l));
+    if (sel) v = (a.route == MOE_ROUTE_SOFTMAX_SINK) ? expf(l - mx) / z : 1.0f / (1.0f + expf(-l));
     float w = v;
     if (a.route != MOE_ROUTE_SOFTMAX_SINK) w = v / wave_fsum(v);
     if (sel) {
-      sm.sel[b][lane] = my_e;
-      sm.selw[b][lane] = w;
-      atomicOr(&sm.mask[my_e], 1u << b);
+      sm.sel[b][rank] = ei;
+      sm.selw[b][rank] = w;
+      atomicOr(&sm.mask[ei], 1u << b);
     }
     if (lane < a.S)
-      sm.shc[b][lane] = (a.route == MOE_ROUTE_SOFTMAX_SINK) ? expf(lg[a.E + lane] - mx) / z : 1.0f;
+      sm.shc[b][lane] = (a.route == MOE_ROUTE_SOFTMAX_SINK)
+                            ? expf(a.logits[(size_t)b * a.Er + a.E + lane] - mx) / z : 1.0f;
   }
   __syncthreads();
 
@@ -720,17 +739,9 @@ __device__ __forceinline__ void down_compute(const DownRegs<TB, WT, S3>& r, unsi
       if ((mask >> b) & 1u) {
         float v;
         if constexpr (WT == WT_NVFP4) {
-          float p0 = 0.f, p1 = 0.f;
-#pragma unroll
-          for (int i = 0; i < 8; ++i) p0 = dot2(w[i], r.hr[b][i], p0);
-#pragma unroll
-          for (int i = 8; i < 16; ++i) p1 = dot2(w[i], r.hr[b][i], p1);
-          v = fmaf(p1, s1, p0 * s0);
+          v = fmaf(dot8<8>(w, r.hr[b]), s1, dot8<0>(w, r.hr[b]) * s0);
         } else {
-          float p = 0.f;
-#pragma unroll
-          for (int i = 0; i < 16; ++i) p = dot2(w[i], r.hr[b][i], p);
-          v = p;
+          v = dot8<0>(w, r.hr[b]) + dot8<8>(w, r.hr[b]);
         }
         acc[b][st] = fmaf(v, wf[b], acc[b][st]);
       }
