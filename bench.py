@@ -3,8 +3,8 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload flint_b1]
 
 A step is one MoE layer call (router GEMV + routing, gate/up GEMV with
-SiLU*up, down GEMV with weighted combine) over one batch of seeded synthetic
-tokens.  Weights stay cold: the layer is copied into L distinct device slots
+SiLU*up, down GEMV with weighted combine, all in one kernel launch) over one
+batch of seeded synthetic tokens.  Weights stay cold: the layer is copied into L distinct device slots
 (47 by default, one per MoE layer of the Flint model) and step i uses slot
 i % L with its own input, so the touched bytes of a cycle (~631 MB at batch
 1) exceed the 256 MB Infinity Cache plus the 32 MB of L2.
@@ -13,8 +13,8 @@ The timed region replays a HIP graph of the K steps (captured once, after W
 eager warm-up steps and one untimed replay), bracketed by
 torch.cuda.synchronize() and HIP events on the stream the kernels run on.
 A second timed region runs the same K steps eagerly with the library's
-profiling events between its three kernels; it gives each kernel's average
-duration, from which the roofline figure of the dominant kernel is computed.
+profiling events around its one kernel; it gives the kernel's average
+duration, from which the roofline figure is computed.
 
 Prints one JSON line.
 """
@@ -185,27 +185,27 @@ def main():
     print(f"[bench] timed {K} steps ({mode}): {us_step:.2f} us/step", file=sys.stderr, flush=True)
 
     # second timed region: eager, with events between the three kernels
-    n_ev = 4 * K
+    n_ev = 2 * K
     evs = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
-    kern = None
-    if True:
-        for e in evs:
-            e.record(stream)            # materialise the underlying HIP events
-        torch.cuda.synchronize()
-        ev_ptrs = (B.C.c_void_p * n_ev)(*[e.cuda_event for e in evs])
-        B.moe_layer_set_profiling(dev.handle, ev_ptrs, n_ev)
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for i in range(K):
-            step(W + i)
-        torch.cuda.synchronize()
-        eager_wall = time.perf_counter() - t0
-        B.moe_layer_set_profiling(dev.handle, None, 0)
-        d = np.array([[evs[4 * i + j].elapsed_time(evs[4 * i + j + 1]) for j in range(3)] for i in range(K)])
-        kern = {"k1_router_shared_us": float(d[:, 0].mean() * 1e3), "k2_gateup_us": float(d[:, 1].mean() * 1e3),
-                "k3_down_us": float(d[:, 2].mean() * 1e3),
-                "eager_us_per_step": eager_wall * 1e6 / K}
-        print(f"[bench] per-kernel (eager, events): {kern}", file=sys.stderr, flush=True)
+    for e in evs:
+        e.record(stream)                # materialise the underlying HIP events
+    torch.cuda.synchronize()
+    ev_ptrs = (B.C.c_void_p * n_ev)(*[e.cuda_event for e in evs])
+    B.moe_layer_set_profiling(dev.handle, ev_ptrs, n_ev)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        step(W + i)
+    torch.cuda.synchronize()
+    eager_wall = time.perf_counter() - t0
+    B.moe_layer_set_profiling(dev.handle, None, 0)
+    d = np.array([evs[2 * i].elapsed_time(evs[2 * i + 1]) for i in range(K)])
+    kern = {"layer_kernel_us": float(d.mean() * 1e3), "layer_kernel_us_p50": float(np.median(d) * 1e3),
+            "eager_us_per_step": eager_wall * 1e6 / K}
+    print(f"[bench] layer kernel (eager, events): {kern}", file=sys.stderr, flush=True)
+    flags = dev.error()
+    if flags:
+        raise SystemExit(f"[bench] the layer kernel reported error bits {flags:#x}")
 
     # plain copy of known size, for HBM counter calibration under rocprofv3 --pmc
     if args.calib_copy_mb > 0:
@@ -219,8 +219,8 @@ def main():
     gbs = algo["total"] / (us_step * 1e-6) / 1e9
     roof = None
     if kern is not None:
-        k2_us = kern["k2_gateup_us"]
-        achieved = algo["k2"] / (k2_us * 1e-6) / 1e9
+        k_us = kern["layer_kernel_us"]
+        achieved = algo["total"] / (k_us * 1e-6) / 1e9
         traffic = None
         tf = os.path.join(ROOT, "profiles", f"traffic_{args.workload}.json")
         if os.path.exists(tf):
@@ -229,9 +229,9 @@ def main():
             from quantized_expert_gemv_amd.profiling import src_digest
             if t.get("src_digest") == src_digest():
                 traffic = t.get("dominant_bytes_per_launch")
-        roof = {"bound": "hbm", "kernel": "k2_gateup", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+        roof = {"bound": "hbm", "kernel": "k_fused_layer", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "algorithmic_bytes_per_launch": int(round(algo["k2"]))}
+                "algorithmic_bytes_per_launch": int(round(algo["total"]))}
 
     cpu = None
     if not args.no_cpu:

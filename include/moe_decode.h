@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 1
+#define MOE_ABI_VERSION 2
 
 /* limits of this implementation */
 #define MOE_MAX_BATCH 8      /* the low-latency decode path serves up to 8 requests  */
@@ -176,10 +176,18 @@ int moe_layer_destroy(moe_layer_t layer);
  *   shared_w      device, shared set (code region, then scale region at
  *                 shared_scale_offset); NULL allowed when n_shared == 0
  *   out           device bf16 [batch][H]; must not overlap x
- * Enqueues three kernels on `stream`: (1) router GEMV + last-block routing + shared
- * experts' gate/up, (2) selected experts' gate/up with SiLU*up, (3) down GEMV of all
- * selected and shared experts with the weighted, fixed-order combine (+ residual).
- * Deterministic: no floating-point atomics; the result does not depend on scheduling. */
+ * Enqueues ONE kernel on `stream` whose workgroups (moe_layer_grid) are all resident at
+ * once and hand data to each other in device memory: router GEMV, routing (every
+ * workgroup computes the same top-k from the gathered logits), the shared and the
+ * selected experts' gate/up GEMV with SiLU*up, and the down GEMV of every selected and
+ * shared expert with the weighted, fixed-order combine (+ residual).  The Flint page
+ * ("From 1,096 kernels to 346") fuses routing and the combine into the neighbouring
+ * GEMVs and reads only the selected experts' weights; this call does the same in one
+ * launch.  Deterministic: no floating-point atomics; the result does not depend on
+ * scheduling.  Every cross-workgroup wait is bounded (0.2 s): if the grid cannot be
+ * resident at once (for example another such call of a different handle runs
+ * concurrently on another stream), the kernel still ends, sets an error bit
+ * (moe_layer_error) and its output is undefined.  Calls on one handle must be ordered.*/
 int moe_decode_layer(moe_layer_t layer, const void* x, const void* router_w,
                      const void* expert_packed, const void* scales, const void* shared_w,
                      void* out, int batch, void* stream);
@@ -191,16 +199,31 @@ int moe_decode_layer(moe_layer_t layer, const void* x, const void* router_w,
 int moe_layer_routing(moe_layer_t layer, int32_t* ids, float* w, float* c, void* stream);
 
 /* Profiling hook for benchmarks.  events: n_events hipEvent_t handles (as void*), n_events a
- * positive multiple of 4; the pointer array is copied, the events stay owned by the caller and
+ * positive multiple of 2; the pointer array is copied, the events stay owned by the caller and
  * must outlive the setting.  Every later moe_decode_layer call number c on this handle records
- * events[4*(c mod n_events/4) + 0..3] on its stream: before kernel 1, after kernel 1, after
- * kernel 2 and after kernel 3.  events = NULL (or n_events = 0) turns the hook off.  Not meant
- * for calls under stream capture.                                                            */
+ * events[2*(c mod n_events/2) + 0] before its kernel and events[... + 1] after it, on its
+ * stream.  events = NULL (or n_events = 0) turns the hook off.  Not meant for calls under
+ * stream capture.                                                                            */
 int moe_layer_set_profiling(moe_layer_t layer, void* const* events, int n_events);
 
 /* Test hook: the SiLU*up activations of the last call, bf16, gathered on `stream`
- * into h_routed [batch][k][I] (selection order) and h_shared [batch][S][I].          */
+ * into h_routed [batch][k][I] (selection order) and h_shared [batch][S][I].  Either
+ * pointer may be NULL.                                                               */
 int moe_layer_debug_h(moe_layer_t layer, void* h_routed, void* h_shared, void* stream);
+
+/* Sticky error bits of the handle's calls so far, read synchronously (waits for the
+ * device): 1 = a workgroup gave up waiting for router logits, 2 = for activations (the
+ * grid was not resident at once).  clear != 0 resets them.  After a non-zero result the
+ * handle's later outputs are undefined until moe_layer_reset.                        */
+int moe_layer_error(moe_layer_t layer, unsigned* flags, int clear);
+
+/* Waits for the device and returns the handle's workspace to its state after
+ * moe_layer_create (call counter 0, no error bits, no last call).                   */
+int moe_layer_reset(moe_layer_t layer);
+
+/* Launch plan of the handle: workgroups of its kernel (all resident at once) and the
+ * shared-memory bytes each uses at max_batch.  Either pointer may be NULL.           */
+int moe_layer_grid(moe_layer_t layer, int* workgroups, int* lds_bytes);
 
 #ifdef __cplusplus
 }

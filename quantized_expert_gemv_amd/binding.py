@@ -27,7 +27,8 @@ ROUTES = {"sigmoid": MOE_ROUTE_SIGMOID_TOPK, "sink": MOE_ROUTE_SOFTMAX_SINK}
 EXPORTED = ("moe_abi_version", "moe_status_str", "moe_layer_validate", "moe_expert_layout_query",
             "moe_pack_nvfp4", "moe_unpack_nvfp4", "moe_pack_bf16", "moe_unpack_bf16",
             "moe_layer_create", "moe_layer_destroy", "moe_decode_layer", "moe_layer_routing",
-            "moe_layer_set_profiling", "moe_layer_debug_h")
+            "moe_layer_set_profiling", "moe_layer_debug_h", "moe_layer_error", "moe_layer_reset",
+            "moe_layer_grid")
 
 
 class MoeError(RuntimeError):
@@ -79,6 +80,9 @@ def _load() -> C.CDLL:
         "moe_layer_routing": ([vp, vp, vp, vp, vp], i32),
         "moe_layer_set_profiling": ([vp, vp, i32], i32),
         "moe_layer_debug_h": ([vp, vp, vp, vp], i32),
+        "moe_layer_error": ([vp, C.POINTER(C.c_uint), i32], i32),
+        "moe_layer_reset": ([vp], i32),
+        "moe_layer_grid": ([vp, C.POINTER(i32), C.POINTER(i32)], i32),
     }
     for name, (args, res) in sig.items():
         f = getattr(lib, name)
@@ -210,3 +214,21 @@ def moe_layer_set_profiling(handle, events, n_events: int) -> None:
 
 def moe_layer_debug_h(handle, h_routed=None, h_shared=None, stream=None) -> None:
     _check("moe_layer_debug_h", lib.moe_layer_debug_h(handle, _ptr(h_routed), _ptr(h_shared), _stream(stream)))
+
+
+def moe_layer_error(handle, clear: bool = False) -> int:
+    """Sticky error bits of the handle (waits for the device)."""
+    flags = C.c_uint(0)
+    _check("moe_layer_error", lib.moe_layer_error(handle, C.byref(flags), int(bool(clear))))
+    return int(flags.value)
+
+
+def moe_layer_reset(handle) -> None:
+    _check("moe_layer_reset", lib.moe_layer_reset(handle))
+
+
+def moe_layer_grid(handle) -> tuple[int, int]:
+    """(workgroups of the layer kernel, shared-memory bytes per workgroup at max_batch)."""
+    g, l = C.c_int(0), C.c_int(0)
+    _check("moe_layer_grid", lib.moe_layer_grid(handle, C.byref(g), C.byref(l)))
+    return int(g.value), int(l.value)

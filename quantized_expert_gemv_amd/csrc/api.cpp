@@ -1,6 +1,7 @@
-// Host side of the MoE decode C ABI: descriptor validation, layouts, the
-// lossless NVFP4 / bf16 packers, the layer handle and its workspace, and the
-// launch sequence of one layer call.  Declarations: include/moe_decode.h.
+// Host side of the MoE decode C ABI: descriptor validation and the launch
+// plan, expert layouts, the lossless NVFP4 / bf16 packers, the layer handle
+// and its workspace, and the single launch of one layer call.
+// Declarations: include/moe_decode.h.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -16,16 +17,22 @@ using moe::MatGeom;
 namespace {
 
 constexpr size_t kAlign = 256;
+constexpr unsigned long long kWaitTicks = 20000000ull;   // 0.2 s of the 100 MHz clock
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+inline int tb_of(int batch) { return batch <= 1 ? 1 : batch <= 2 ? 2 : batch <= 4 ? 4 : 8; }
+inline int tb_index(int tb) { return tb == 1 ? 0 : tb == 2 ? 1 : tb == 4 ? 2 : 3; }
 
 struct Plan {
   MatGeom g13, g2;
-  int Er, maxd, n_router_blocks, wpe13, s3;
+  int Er, maxd, tbmax;
+  int spg_max;                 // most down steps a workgroup owns (given G)
+  int G;                       // workgroups (0 until the device is known)
+  int lds_act[4], lds_acc[4];  // per token bucket 1, 2, 4, 8
 };
 
-// Full check of a description; fills the kernel plan on success.
-int plan_layer(const moe_layer_desc* d, Plan* p) {
+// Shape checks that need no device.  Fills the geometry part of the plan.
+int plan_shapes(const moe_layer_desc* d, Plan* p) {
   if (d == nullptr) return MOE_ERR_INVALID_ARG;
   const int H = d->hidden, I = d->inter, E = d->n_routed, k = d->top_k, S = d->n_shared;
   if (H <= 0 || I <= 0 || E <= 0 || k <= 0 || S < 0 || d->max_batch <= 0) return MOE_ERR_INVALID_ARG;
@@ -46,18 +53,38 @@ int plan_layer(const moe_layer_desc* d, Plan* p) {
 
   if (moe::make_geom(2 * I, H, &p->g13) || moe::make_geom(H, I, &p->g2)) return MOE_ERR_UNSUPPORTED;
   if (p->g2.ns != 1) return MOE_ERR_UNSUPPORTED;
-  if (I % p->g13.rpw) return MOE_ERR_UNSUPPORTED;
-  const int gate_steps = I / p->g13.rpw;
-  const int nrg = moe::kWaves / p->g13.ns;
-  if (gate_steps % (moe::kGateSteps * nrg)) return MOE_ERR_UNSUPPORTED;
-  p->wpe13 = gate_steps / (moe::kGateSteps * nrg);
-  // down kernel: steps per workgroup; its LDS tile holds 8 * s3 * rpw floats per wave
-  p->s3 = (p->g2.nsteps % 8 == 0 && p->g2.nsteps / 8 >= 512 && 8 * 8 * p->g2.rpw <= 1024) ? 8 : 2;
-  if (8 * p->s3 * p->g2.rpw > 1024) return MOE_ERR_UNSUPPORTED;
+  if (I % (2 * p->g13.rpw)) return MOE_ERR_UNSUPPORTED;                 // whole gate step pairs
+  if (p->g13.ns > 1 && (p->g13.rpw != 1 || moe::kFusedWaves % p->g13.ns)) return MOE_ERR_UNSUPPORTED;
+  p->tbmax = tb_of(d->max_batch);
+  const int qx = p->tbmax >= 8 ? 1 : 4;                                 // router units per thread
+  if (H / 8 > moe::kFusedThreads * qx) return MOE_ERR_UNSUPPORTED;
   p->Er = Er;
   p->maxd = (d->max_batch * k < E) ? d->max_batch * k : E;
-  p->n_router_blocks = (Er + moe::kWaves - 1) / moe::kWaves;
+  p->G = 0;
   return MOE_OK;
+}
+
+// Grid and shared-memory plan for G workgroups.
+void plan_grid(const moe_layer_desc* d, Plan* p, int G) {
+  p->G = G;
+  const int nsteps2 = p->g2.nsteps;
+  p->spg_max = (nsteps2 + G - 1) / G;
+  const int gs2 = d->inter / p->g13.rpw / 2;
+  const int ns = p->g13.ns;
+  for (int ti = 0; ti < 4; ++ti) {
+    const int tb = 1 << ti;
+    size_t part = 0;
+    if (ns > 1) {
+      const int n1 = d->n_shared * gs2, n2 = p->maxd * gs2;
+      const int per = ((n1 > n2 ? n1 : n2) + G - 1) / G;
+      part = (size_t)per * tb * 4 * ns * sizeof(float);
+    }
+    const size_t xbytes = (size_t)tb * d->hidden * 2 + part;
+    const int nb = d->max_batch < tb ? d->max_batch : tb;
+    const size_t hbytes = (size_t)nb * (d->top_k + d->n_shared) * d->inter * 2;
+    p->lds_act[ti] = (int)align_up(xbytes > hbytes ? xbytes : hbytes, 16);
+    p->lds_acc[ti] = moe::kFusedWaves * tb * p->spg_max * p->g2.rpw * (int)sizeof(float);
+  }
 }
 
 int layout(int wtype, int H, int I, int n, moe_expert_layout* o) {
@@ -87,6 +114,7 @@ int layout(int wtype, int H, int I, int n, moe_expert_layout* o) {
   return MOE_OK;
 }
 
+
 // Matrices the packers accept: a geometry must exist for them.
 int pack_geom(int rows, int cols, MatGeom* g) {
   if (rows <= 0 || cols <= 0) return MOE_ERR_INVALID_ARG;
@@ -103,20 +131,15 @@ struct moe_layer {
   int device;
   void* ws;
   size_t ws_bytes;
-  unsigned* counter;
-  float* logits;
-  int* rt_nd;
-  int* rt_ids;
-  unsigned* rt_mask;
-  float* rt_wt;
+  unsigned* epoch;
+  unsigned* err;
+  unsigned long long* xlog;
+  unsigned long long* xh;
   int* topk_ids;
   float* topk_w;
   float* shared_c;
-  uint16_t* xhat;
-  uint16_t* h_routed;
-  uint16_t* h_shared;
+  int* pair_of;
   int last_batch;
-  const void* last_x;
   std::vector<void*> prof;       // profiling events (caller-owned)
   unsigned long long prof_call;
 };
@@ -141,7 +164,7 @@ const char* moe_status_str(int s) {
 
 int moe_layer_validate(const moe_layer_desc* desc) {
   Plan p;
-  return plan_layer(desc, &p);
+  return plan_shapes(desc, &p);
 }
 
 int moe_expert_layout_query(int wtype, int hidden, int inter, int n_experts, moe_expert_layout* out) {
@@ -216,61 +239,76 @@ int moe_layer_create(const moe_layer_desc* desc, moe_layer_t* out) {
   if (out == nullptr) return MOE_ERR_INVALID_ARG;
   *out = nullptr;
   Plan p;
-  if (int st = plan_layer(desc, &p)) return st;
+  if (int st = plan_shapes(desc, &p)) return st;
+  int device = 0, cus = 0;
+  if (hipGetDevice(&device) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess || cus <= 0) {
+    (void)hipGetLastError();
+    return MOE_ERR_DEVICE;
+  }
+  // One workgroup per router row at most (each publishes a logit, which is how
+  // workgroup 0 knows every workgroup has read the call counter), at most two
+  // rows each, and never more workgroups than can be resident together.
+  int G = p.Er < cus ? p.Er : cus;
+  plan_grid(desc, &p, G);
+  const int rwt = desc->routed_wtype, swt = desc->shared_wtype;
+  for (int tb = 1; tb <= p.tbmax; tb *= 2) {
+    int occ = 0;
+    const int ti = tb_index(tb);
+    if (moe::fused_occupancy(tb, rwt, swt, p.lds_act[ti] + p.lds_acc[ti], &occ) != 0 || occ < 1) {
+      (void)hipGetLastError();
+      return MOE_ERR_UNSUPPORTED;
+    }
+    if (G > occ * cus) G = occ * cus;
+  }
+  if (2 * G < p.Er) return MOE_ERR_UNSUPPORTED;
+  plan_grid(desc, &p, G);
+
   moe_layer* L = new (std::nothrow) moe_layer();
   if (L == nullptr) return MOE_ERR_DEVICE;
   L->d = *desc;
   L->p = p;
+  L->device = device;
   layout(desc->routed_wtype, desc->hidden, desc->inter, desc->n_routed, &L->lr);
   layout(desc->shared_wtype, desc->hidden, desc->inter, desc->n_shared, &L->ls);
-  if (hipGetDevice(&L->device) != hipSuccess) {
-    delete L;
-    return MOE_ERR_DEVICE;
-  }
-  const size_t maxB = desc->max_batch, H = desc->hidden, I = desc->inter, k = desc->top_k;
-  const size_t S1 = desc->n_shared > 0 ? desc->n_shared : 1, maxd = p.maxd;
+  const size_t maxB = desc->max_batch, k = desc->top_k;
+  const size_t S1 = desc->n_shared > 0 ? desc->n_shared : 1;
+  const size_t npairs = maxB * (k + desc->n_shared);
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t o = off;
     off = align_up(off + bytes, kAlign);
     return o;
   };
-  const size_t o_counter = take(sizeof(unsigned));
-  const size_t o_logits = take(maxB * p.Er * sizeof(float));
-  const size_t o_nd = take(sizeof(int));
-  const size_t o_ids = take(maxd * sizeof(int));
-  const size_t o_mask = take(maxd * sizeof(unsigned));
-  const size_t o_wt = take(maxd * maxB * sizeof(float));
+  const size_t o_epoch = take(sizeof(unsigned));
+  const size_t o_err = take(sizeof(unsigned));
+  const size_t o_xlog = take((size_t)p.Er * moe::kLogitLine * 8);
+  const size_t o_xh = take(npairs * (desc->inter / 2) * 8);
   const size_t o_tid = take(maxB * k * sizeof(int));
   const size_t o_tw = take(maxB * k * sizeof(float));
   const size_t o_c = take(maxB * S1 * sizeof(float));
-  const size_t o_xhat = take(desc->prenorm_gamma ? maxB * H * 2 : 16);
-  const size_t o_hr = take(maxd * maxB * I * 2);
-  const size_t o_hs = take(S1 * maxB * I * 2);
+  const size_t o_po = take(maxB * k * sizeof(int));
   L->ws_bytes = off;
   if (hipMalloc(&L->ws, L->ws_bytes) != hipSuccess) {
     (void)hipGetLastError();
     delete L;
     return MOE_ERR_DEVICE;
   }
-  if (hipMemset(L->ws, 0, L->ws_bytes) != hipSuccess) {
+  // zero words carry tag 0, which no call uses (tags start at 1)
+  if (hipMemset(L->ws, 0, L->ws_bytes) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
     (void)hipFree(L->ws);
     delete L;
     return MOE_ERR_DEVICE;
   }
   char* w = static_cast<char*>(L->ws);
-  L->counter = reinterpret_cast<unsigned*>(w + o_counter);
-  L->logits = reinterpret_cast<float*>(w + o_logits);
-  L->rt_nd = reinterpret_cast<int*>(w + o_nd);
-  L->rt_ids = reinterpret_cast<int*>(w + o_ids);
-  L->rt_mask = reinterpret_cast<unsigned*>(w + o_mask);
-  L->rt_wt = reinterpret_cast<float*>(w + o_wt);
+  L->epoch = reinterpret_cast<unsigned*>(w + o_epoch);
+  L->err = reinterpret_cast<unsigned*>(w + o_err);
+  L->xlog = reinterpret_cast<unsigned long long*>(w + o_xlog);
+  L->xh = reinterpret_cast<unsigned long long*>(w + o_xh);
   L->topk_ids = reinterpret_cast<int*>(w + o_tid);
   L->topk_w = reinterpret_cast<float*>(w + o_tw);
   L->shared_c = reinterpret_cast<float*>(w + o_c);
-  L->xhat = reinterpret_cast<uint16_t*>(w + o_xhat);
-  L->h_routed = reinterpret_cast<uint16_t*>(w + o_hr);
-  L->h_shared = reinterpret_cast<uint16_t*>(w + o_hs);
+  L->pair_of = reinterpret_cast<int*>(w + o_po);
   *out = L;
   return MOE_OK;
 }
@@ -287,9 +325,9 @@ int moe_layer_destroy(moe_layer_t L) {
 
 namespace {
 
-moe::LayerArgs make_args(const moe_layer* L, const void* x, const void* router_w, const void* expert_packed,
+moe::FusedArgs make_args(const moe_layer* L, const void* x, const void* router_w, const void* expert_packed,
                          const void* scales, const void* shared_w, void* out, int batch) {
-  moe::LayerArgs a;
+  moe::FusedArgs a;
   memset(&a, 0, sizeof(a));
   const moe_layer_desc& d = L->d;
   a.x = static_cast<const uint16_t*>(x);
@@ -307,27 +345,21 @@ moe::LayerArgs make_args(const moe_layer* L, const void* x, const void* router_w
                    ? reinterpret_cast<const float*>(a.s_scales + L->ls.tensor_scale_offset)
                    : nullptr;
   a.out = static_cast<uint16_t*>(out);
-  a.counter = L->counter;
-  a.logits = L->logits;
-  a.rt_nd = L->rt_nd;
-  a.rt_ids = L->rt_ids;
-  a.rt_mask = L->rt_mask;
-  a.rt_wt = L->rt_wt;
+  a.epoch = L->epoch;
+  a.err = L->err;
+  a.xlog = L->xlog;
+  a.xh = L->xh;
   a.topk_ids = L->topk_ids;
   a.topk_w = L->topk_w;
   a.shared_c = L->shared_c;
-  a.xhat = L->xhat;
-  a.h_routed = L->h_routed;
-  a.h_shared = L->h_shared;
+  a.pair_of = L->pair_of;
   a.B = batch;
-  a.maxB = d.max_batch;
   a.H = d.hidden;
   a.I = d.inter;
   a.E = d.n_routed;
   a.k = d.top_k;
   a.S = d.n_shared;
   a.Er = L->p.Er;
-  a.maxd = L->p.maxd;
   a.route = d.route;
   a.prenorm = d.prenorm_gamma != nullptr;
   a.residual = d.add_residual != 0;
@@ -342,9 +374,12 @@ moe::LayerArgs make_args(const moe_layer* L, const void* x, const void* router_w
   a.s_w13_code = L->ls.w13_code_bytes;
   a.s_scale_stride = L->ls.scale_stride;
   a.s_w13_scale = L->ls.w13_scale_bytes;
-  a.n_router_blocks = L->p.n_router_blocks;
-  a.wpe13 = L->p.wpe13;
-  a.s3 = L->p.s3;
+  a.G = L->p.G;
+  const int ti = tb_index(tb_of(batch));
+  a.lds_act = L->p.lds_act[ti];
+  a.lds_acc = L->p.lds_acc[ti];
+  a.spg_max = L->p.spg_max;
+  a.wait_ticks = kWaitTicks;
   return a;
 }
 
@@ -364,16 +399,19 @@ int moe_decode_layer(moe_layer_t L, const void* x, const void* router_w, const v
   if (!aligned16(x) || !aligned16(router_w) || !aligned16(expert_packed) || !aligned16(out) ||
       (scales && !aligned16(scales)) || (shared_w && !aligned16(shared_w)))
     return MOE_ERR_ALIGNMENT;
-  const moe::LayerArgs a = make_args(L, x, router_w, expert_packed, scales, shared_w, out, batch);
-  const int tb = batch <= 1 ? 1 : batch <= 2 ? 2 : batch <= 4 ? 4 : 8;
-  void* const* ev = nullptr;
+  const moe::FusedArgs a = make_args(L, x, router_w, expert_packed, scales, shared_w, out, batch);
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   if (!L->prof.empty()) {
-    ev = L->prof.data() + 4 * (L->prof_call % (L->prof.size() / 4));
+    void* const* ev = L->prof.data() + 2 * (L->prof_call % (L->prof.size() / 2));
     ++L->prof_call;
+    (void)hipEventRecord(reinterpret_cast<hipEvent_t>(ev[0]), st);
+    const int r = moe::launch_fused(a, tb_of(batch), d.routed_wtype, d.shared_wtype, stream);
+    (void)hipEventRecord(reinterpret_cast<hipEvent_t>(ev[1]), st);
+    if (r != 0) return MOE_ERR_LAUNCH;
+  } else if (moe::launch_fused(a, tb_of(batch), d.routed_wtype, d.shared_wtype, stream) != 0) {
+    return MOE_ERR_LAUNCH;
   }
-  if (moe::launch_layer(a, tb, d.routed_wtype, d.shared_wtype, stream, ev) != 0) return MOE_ERR_LAUNCH;
   L->last_batch = batch;
-  L->last_x = x;
   return MOE_OK;
 }
 
@@ -397,7 +435,7 @@ int moe_layer_set_profiling(moe_layer_t L, void* const* events, int n_events) {
     L->prof.clear();
     return MOE_OK;
   }
-  if (n_events < 4 || n_events % 4) return MOE_ERR_INVALID_ARG;
+  if (n_events < 2 || n_events % 2) return MOE_ERR_INVALID_ARG;
   for (int i = 0; i < n_events; ++i)
     if (events[i] == nullptr) return MOE_ERR_INVALID_ARG;
   L->prof.assign(events, events + n_events);
@@ -408,9 +446,42 @@ int moe_layer_set_profiling(moe_layer_t L, void* const* events, int n_events) {
 int moe_layer_debug_h(moe_layer_t L, void* h_routed, void* h_shared, void* stream) {
   if (L == nullptr) return MOE_ERR_INVALID_ARG;
   if (L->last_batch == 0) return MOE_ERR_STATE;
-  const moe::LayerArgs a = make_args(L, L->last_x, nullptr, nullptr, nullptr, nullptr, nullptr, L->last_batch);
-  if (moe::launch_debug_h(a, static_cast<uint16_t*>(h_routed), static_cast<uint16_t*>(h_shared), stream) != 0)
+  const moe::FusedArgs a = make_args(L, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, L->last_batch);
+  if (moe::launch_fused_debug_h(a, L->pair_of, static_cast<uint16_t*>(h_routed), static_cast<uint16_t*>(h_shared),
+                                stream) != 0)
     return MOE_ERR_LAUNCH;
+  return MOE_OK;
+}
+
+int moe_layer_error(moe_layer_t L, unsigned* flags, int clear) {
+  if (L == nullptr || flags == nullptr) return MOE_ERR_INVALID_ARG;
+  if (hipMemcpy(flags, L->err, sizeof(unsigned), hipMemcpyDeviceToHost) != hipSuccess) {
+    (void)hipGetLastError();
+    return MOE_ERR_DEVICE;
+  }
+  if (clear && *flags != 0u && hipMemset(L->err, 0, sizeof(unsigned)) != hipSuccess) {
+    (void)hipGetLastError();
+    return MOE_ERR_DEVICE;
+  }
+  return MOE_OK;
+}
+
+int moe_layer_reset(moe_layer_t L) {
+  if (L == nullptr) return MOE_ERR_INVALID_ARG;
+  if (hipDeviceSynchronize() != hipSuccess || hipMemset(L->ws, 0, L->ws_bytes) != hipSuccess ||
+      hipDeviceSynchronize() != hipSuccess) {
+    (void)hipGetLastError();
+    return MOE_ERR_DEVICE;
+  }
+  L->last_batch = 0;
+  return MOE_OK;
+}
+
+int moe_layer_grid(moe_layer_t L, int* workgroups, int* lds_bytes) {
+  if (L == nullptr) return MOE_ERR_INVALID_ARG;
+  const int ti = tb_index(L->p.tbmax);
+  if (workgroups) *workgroups = L->p.G;
+  if (lds_bytes) *lds_bytes = L->p.lds_act[ti] + L->p.lds_acc[ti];
   return MOE_OK;
 }
 

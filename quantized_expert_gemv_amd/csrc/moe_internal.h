@@ -1,5 +1,5 @@
-// Internal definitions shared by the host side (api.cpp) and the kernels
-// (kernels.hip) of the MoE decode library.  Not part of the public ABI.
+// Internal definitions shared by the host side (api.cpp) and the kernel
+// (layer.hip) of the MoE decode library.  Not part of the public ABI.
 #pragma once
 
 #include <stddef.h>
@@ -20,7 +20,7 @@ namespace moe {
 // A row is cut into chunks of 32 consecutive elements; a lane owns one chunk
 // per "wave step" (16 B of e2m1 codes, or 4 x 16 B of bf16, plus 2 e4m3 block
 // scales).  Rows longer than 64 chunks are split into `ns` slices of `cw`
-// chunks each, handled by different wavefronts of a workgroup.  A slice of
+// chunks each.  A slice of
 // `cw` chunks occupies `lpr` (power of two >= cw) lanes, so one wave step
 // covers `rpw` = 64 / lpr rows.  Steps run over rows: step t covers rows
 // t*rpw .. t*rpw + rpw - 1.  `su` is the number of 16 B units one wave step
@@ -73,54 +73,67 @@ MOE_HD inline size_t bf16_unit(const MatGeom& g, int s, int t, int sub, int ri, 
   return (((size_t)s * g.nsteps + t) * 4 + sub) * g.su + (size_t)ri * g.cw + j;
 }
 
-constexpr int kWaves = 4;          // wavefronts per workgroup
-constexpr int kThreads = 64 * kWaves;
-constexpr int kGateSteps = 2;      // gate (and up) steps per wavefront in gate/up kernels
+// ---------------------------------------------------------------------------
+// single-launch layer kernel
+// ---------------------------------------------------------------------------
 
-// Everything the three kernels of one layer call need, passed by value.
-struct LayerArgs {
-  // inputs
+constexpr int kFusedWaves = 4;                    // wavefronts per workgroup
+constexpr int kFusedThreads = 64 * kFusedWaves;
+constexpr int kLogitLine = 16;                    // 8-byte words per router row (one 128-B line)
+constexpr int kMaxPairs = MOE_MAX_BATCH * (MOE_MAX_TOPK + MOE_MAX_SHARED);
+
+// Everything one launch of the single-launch layer kernel needs, by value.
+//
+// Cross-workgroup data (router logits, SiLU*up activations) moves through
+// tagged 8-byte words: the low half holds the value, the high half the call's
+// tag (the handle's call counter + 1).  A reader polls a word until its tag
+// matches, so no flag, fence or barrier is needed: each word carries its own
+// validity, and a word of an older call never matches.
+struct FusedArgs {
+  // inputs (caller-owned device memory)
   const uint16_t* x;         // bf16 [B][H]
   const uint16_t* router_w;  // bf16 [Er][H]
   const float* bias;         // fp32 [E] or null
   const uint16_t* gamma;     // bf16 [H] or null
   const uint8_t* r_codes;    // routed code region
-  const uint8_t* r_scales;   // routed scale region base
+  const uint8_t* r_scales;   // routed scale region
   const float* r_tscale;     // routed tensor scales [E][2]
   const uint8_t* s_codes;    // shared code region
-  const uint8_t* s_scales;   // shared scale region base
+  const uint8_t* s_scales;   // shared scale region
   const float* s_tscale;     // shared tensor scales [S][2]
   uint16_t* out;             // bf16 [B][H]
-  // workspace
-  unsigned* counter;         // last-block counter (kept at 0 between calls)
-  float* logits;             // [maxB][Er]
-  int* rt_nd;                // [1] number of distinct routed experts
-  int* rt_ids;               // [maxd] distinct experts, ascending
-  unsigned* rt_mask;         // [maxd] token masks
-  float* rt_wt;              // [maxd][maxB] combine weight per (slot, token)
-  int* topk_ids;             // [maxB][k]
-  float* topk_w;             // [maxB][k]
-  float* shared_c;           // [maxB][S]
-  uint16_t* xhat;            // bf16 [maxB][H] (pre-norm only)
-  uint16_t* h_routed;        // bf16 [maxd][maxB][I]
-  uint16_t* h_shared;        // bf16 [S][maxB][I]
+  // workspace (handle-owned)
+  unsigned* epoch;                 // [1] number of completed calls
+  unsigned* err;                   // [1] sticky error bits (kErr*)
+  unsigned long long* xlog;        // [Er][kLogitLine] logit words
+  unsigned long long* xh;          // [maxP][I/2] activation words
+  int* topk_ids;                   // [maxB][k] readback
+  float* topk_w;                   // [maxB][k]
+  float* shared_c;                 // [maxB][S]
+  int* pair_of;                    // [maxB][k] activation pair of each selection
   // shapes
-  int B, maxB, H, I, E, k, S, Er, maxd;
+  int B, H, I, E, k, S, Er;
   int route, prenorm, residual;
   float eps;
   MatGeom g13, g2;
-  // expert set strides (bytes)
   size_t r_code_stride, r_w13_code, r_scale_stride, r_w13_scale;
   size_t s_code_stride, s_w13_code, s_scale_stride, s_w13_scale;
-  // grid bookkeeping
-  int n_router_blocks;       // kernel 1: router blocks come first
-  int wpe13;                 // workgroups per expert in the gate/up kernels
-  int s3;                    // steps per workgroup in the down kernel
+  // plan
+  int G;                           // workgroups; all must be resident at once
+  int lds_act;                     // bytes of the activation region (x, then h)
+  int lds_acc;                     // bytes of the down-GEMV accumulators
+  int spg_max;                     // most down-GEMV steps a workgroup owns
+  unsigned long long wait_ticks;   // bound of every wait, in 100 MHz ticks
 };
 
-// Launchers (kernels.hip).  Return a hipError_t as int.
-// ev4: null, or 4 hipEvent_t recorded around the three kernels.
-int launch_layer(const LayerArgs& a, int tb, int rwt, int swt, void* stream, void* const* ev4);
-int launch_debug_h(const LayerArgs& a, uint16_t* h_r, uint16_t* h_s, void* stream);
+enum : unsigned { kErrLogitWait = 1u, kErrActWait = 2u };
+
+// Dynamic LDS bytes of the kernel for a plan.
+MOE_HD inline int fused_lds_bytes(const FusedArgs& a) { return a.lds_act + a.lds_acc; }
+
+int launch_fused(const FusedArgs& a, int tb, int rwt, int swt, void* stream);
+int launch_fused_debug_h(const FusedArgs& a, const int* pair_of_sel, uint16_t* h_r, uint16_t* h_s,
+                         void* stream);
+int fused_occupancy(int tb, int rwt, int swt, int lds_bytes, int* blocks_per_cu);
 
 }  // namespace moe

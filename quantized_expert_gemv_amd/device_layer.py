@@ -109,6 +109,12 @@ class DeviceLayer:
         B.moe_layer_debug_h(self.handle, hr, hs)
         return hr, hs[:, :self.S]
 
+    def error(self, clear: bool = False) -> int:
+        return B.moe_layer_error(self.handle, clear)
+
+    def grid(self) -> tuple[int, int]:
+        return B.moe_layer_grid(self.handle)
+
     def close(self):
         if getattr(self, "handle", None):
             B.moe_layer_destroy(self.handle)

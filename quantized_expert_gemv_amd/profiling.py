@@ -26,7 +26,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 
 def src_digest() -> str:
     h = hashlib.sha256()
-    for f in ("kernels.hip", "api.cpp", "moe_internal.h"):
+    for f in ("layer.hip", "device_util.h", "api.cpp", "moe_internal.h"):
         with open(os.path.join(_PKG, "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -83,7 +83,7 @@ def main():
     t.add_argument("write_csv")
     t.add_argument("--copy-bytes", type=int, required=True)
     t.add_argument("--workload", required=True)
-    t.add_argument("--dominant", default="moe::k2_gateup")
+    t.add_argument("--dominant", default="k_fused_layer")
     t.add_argument("--out")
     a = p.parse_args()
     if a.cmd == "stats":
@@ -93,7 +93,7 @@ def main():
                   f"{r['max_us']:.2f} | {r['pct']:.1f} |")
     else:
         t = traffic(a.fetch_csv, a.write_csv, a.copy_bytes)
-        dom = next((v for k, v in t["kernels"].items() if k.startswith(a.dominant)), None)
+        dom = next((v for k, v in t["kernels"].items() if a.dominant in k), None)
         t.update({"workload": a.workload, "src_digest": src_digest(),
                   "dominant_kernel": a.dominant,
                   "dominant_bytes_per_launch": None if dom is None else dom["bytes_per_launch"]})

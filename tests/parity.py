@@ -38,6 +38,8 @@ def compare_layer(dev, layer, x_bits: np.ndarray, tokens=None, tol: float = OUT_
     out = dev(x)
     ids, w, c = dev.routing(B)
     torch.cuda.synchronize()
+    flags = dev.error()
+    assert flags == 0, f"layer kernel reported error bits {flags:#x} (a wait for another workgroup timed out)"
     out_f = bf16_bits_f64(bf16_tensor_to_bits(out))
     ids_g, w_g, c_g = ids.cpu().numpy(), w.cpu().numpy(), c.cpu().numpy()
 

@@ -29,7 +29,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_abi_version_and_status_strings():
-    assert B.moe_abi_version() == 1
+    assert B.moe_abi_version() == 2
     for code in B.STATUS:
         assert B.moe_status_str(code)
     assert B.moe_status_str(0) == "ok"

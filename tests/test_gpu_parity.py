@@ -311,3 +311,59 @@ def test_error_paths_on_device():
         assert B.lib.moe_layer_routing(fresh, None, None, None, None) == -7
     finally:
         B.moe_layer_destroy(fresh)
+
+
+def test_grid_plan_one_workgroup_per_cu():
+    from quantized_expert_gemv_amd import binding as B
+    layer, dev = dev_layer("flint_b1")
+    G, lds = dev.grid()
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    _note(f"[grid] flint_b1: {G} workgroups, {lds} B shared memory; device has {cus} CUs")
+    assert G == min(cus, layer.n_routed)
+    assert B.moe_layer_error(dev.handle) == 0
+
+
+def test_graph_replays_match_eager_calls():
+    """The call counter that tags cross-workgroup words lives on the device, so
+    replaying a captured sequence of calls must give the eager results every time."""
+    layer, dev = dev_layer("flint_b8")
+    from quantized_expert_gemv_amd.device_layer import bits_to_bf16_tensor
+    xs = [bits_to_bf16_tensor(layer.x(40 + i, batch=n), dev.device) for i, n in enumerate((8, 3, 1))]
+    eager = [dev(x).clone() for x in xs]
+    torch.cuda.synchronize()
+    outs = [torch.empty_like(e) for e in eager]
+    g = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cap):
+        with torch.cuda.graph(g, stream=cap):
+            for x, o in zip(xs, outs):
+                dev(x, out=o)
+    torch.cuda.current_stream().wait_stream(cap)
+    for rep in range(3):
+        for o in outs:
+            o.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        for e, o in zip(eager, outs):
+            assert torch.equal(e.view(torch.int16), o.view(torch.int16)), rep
+        # eager work between replays
+        again = dev(xs[1])
+        torch.cuda.synchronize()
+        assert torch.equal(again.view(torch.int16), eager[1].view(torch.int16))
+    assert dev.error() == 0
+
+
+def test_many_calls_alternating_batches():
+    layer, dev = dev_layer("flint_b8")
+    from quantized_expert_gemv_amd.device_layer import bits_to_bf16_tensor
+    ref = {}
+    for rep in range(3):
+        for n in (8, 1, 5):
+            x = bits_to_bf16_tensor(layer.x(60 + n, batch=n), dev.device)
+            o = dev(x).clone()
+            if n in ref:
+                assert torch.equal(o.view(torch.int16), ref[n].view(torch.int16)), (rep, n)
+            ref[n] = o
+    torch.cuda.synchronize()
+    assert dev.error() == 0
