@@ -56,8 +56,8 @@ int plan_shapes(const moe_layer_desc* d, Plan* p) {
   if (I % (2 * p->g13.rpw)) return MOE_ERR_UNSUPPORTED;                 // whole gate step pairs
   if (p->g13.ns > 1 && (p->g13.rpw != 1 || moe::kFusedWaves % p->g13.ns)) return MOE_ERR_UNSUPPORTED;
   p->tbmax = tb_of(d->max_batch);
-  const int qx = p->tbmax >= 8 ? 1 : 4;                                 // router units per thread
-  if (H / 8 > moe::kFusedThreads * qx) return MOE_ERR_UNSUPPORTED;
+  const int qx = moe::fused_qx(H);                                      // router units per thread
+  if (qx == 0 || (p->tbmax >= 8 && qx != 1)) return MOE_ERR_UNSUPPORTED;
   p->Er = Er;
   p->maxd = (d->max_batch * k < E) ? d->max_batch * k : E;
   p->G = 0;
@@ -83,7 +83,7 @@ void plan_grid(const moe_layer_desc* d, Plan* p, int G) {
     const int nb = d->max_batch < tb ? d->max_batch : tb;
     const size_t hbytes = (size_t)nb * (d->top_k + d->n_shared) * d->inter * 2;
     p->lds_act[ti] = (int)align_up(xbytes > hbytes ? xbytes : hbytes, 16);
-    p->lds_acc[ti] = moe::kFusedWaves * tb * p->spg_max * p->g2.rpw * (int)sizeof(float);
+    p->lds_acc[ti] = moe::kFusedWaves * tb * p->spg_max * p->g2.rpw * (int)sizeof(float);   // nsub <= waves
   }
 }
 
@@ -138,7 +138,6 @@ struct moe_layer {
   int* topk_ids;
   float* topk_w;
   float* shared_c;
-  int* pair_of;
   int last_batch;
   std::vector<void*> prof;       // profiling events (caller-owned)
   unsigned long long prof_call;
@@ -255,7 +254,8 @@ int moe_layer_create(const moe_layer_desc* desc, moe_layer_t* out) {
   for (int tb = 1; tb <= p.tbmax; tb *= 2) {
     int occ = 0;
     const int ti = tb_index(tb);
-    if (moe::fused_occupancy(tb, rwt, swt, p.lds_act[ti] + p.lds_acc[ti], &occ) != 0 || occ < 1) {
+    if (moe::fused_occupancy(tb, moe::fused_qx(desc->hidden), rwt, swt, p.lds_act[ti] + p.lds_acc[ti], &occ) != 0 ||
+        occ < 1) {
       (void)hipGetLastError();
       return MOE_ERR_UNSUPPORTED;
     }
@@ -287,7 +287,6 @@ int moe_layer_create(const moe_layer_desc* desc, moe_layer_t* out) {
   const size_t o_tid = take(maxB * k * sizeof(int));
   const size_t o_tw = take(maxB * k * sizeof(float));
   const size_t o_c = take(maxB * S1 * sizeof(float));
-  const size_t o_po = take(maxB * k * sizeof(int));
   L->ws_bytes = off;
   if (hipMalloc(&L->ws, L->ws_bytes) != hipSuccess) {
     (void)hipGetLastError();
@@ -308,7 +307,6 @@ int moe_layer_create(const moe_layer_desc* desc, moe_layer_t* out) {
   L->topk_ids = reinterpret_cast<int*>(w + o_tid);
   L->topk_w = reinterpret_cast<float*>(w + o_tw);
   L->shared_c = reinterpret_cast<float*>(w + o_c);
-  L->pair_of = reinterpret_cast<int*>(w + o_po);
   *out = L;
   return MOE_OK;
 }
@@ -352,7 +350,6 @@ moe::FusedArgs make_args(const moe_layer* L, const void* x, const void* router_w
   a.topk_ids = L->topk_ids;
   a.topk_w = L->topk_w;
   a.shared_c = L->shared_c;
-  a.pair_of = L->pair_of;
   a.B = batch;
   a.H = d.hidden;
   a.I = d.inter;
@@ -447,8 +444,7 @@ int moe_layer_debug_h(moe_layer_t L, void* h_routed, void* h_shared, void* strea
   if (L == nullptr) return MOE_ERR_INVALID_ARG;
   if (L->last_batch == 0) return MOE_ERR_STATE;
   const moe::FusedArgs a = make_args(L, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, L->last_batch);
-  if (moe::launch_fused_debug_h(a, L->pair_of, static_cast<uint16_t*>(h_routed), static_cast<uint16_t*>(h_shared),
-                                stream) != 0)
+  if (moe::launch_fused_debug_h(a, static_cast<uint16_t*>(h_routed), static_cast<uint16_t*>(h_shared), stream) != 0)
     return MOE_ERR_LAUNCH;
   return MOE_OK;
 }

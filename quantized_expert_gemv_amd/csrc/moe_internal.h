@@ -110,7 +110,6 @@ struct FusedArgs {
   int* topk_ids;                   // [maxB][k] readback
   float* topk_w;                   // [maxB][k]
   float* shared_c;                 // [maxB][S]
-  int* pair_of;                    // [maxB][k] activation pair of each selection
   // shapes
   int B, H, I, E, k, S, Er;
   int route, prenorm, residual;
@@ -121,7 +120,7 @@ struct FusedArgs {
   // plan
   int G;                           // workgroups; all must be resident at once
   int lds_act;                     // bytes of the activation region (x, then h)
-  int lds_acc;                     // bytes of the down-GEMV accumulators
+  int lds_acc;                     // bytes of the down-GEMV partial sums
   int spg_max;                     // most down-GEMV steps a workgroup owns
   unsigned long long wait_ticks;   // bound of every wait, in 100 MHz ticks
 };
@@ -132,8 +131,9 @@ enum : unsigned { kErrLogitWait = 1u, kErrActWait = 2u };
 MOE_HD inline int fused_lds_bytes(const FusedArgs& a) { return a.lds_act + a.lds_acc; }
 
 int launch_fused(const FusedArgs& a, int tb, int rwt, int swt, void* stream);
-int launch_fused_debug_h(const FusedArgs& a, const int* pair_of_sel, uint16_t* h_r, uint16_t* h_s,
-                         void* stream);
-int fused_occupancy(int tb, int rwt, int swt, int lds_bytes, int* blocks_per_cu);
+int launch_fused_debug_h(const FusedArgs& a, uint16_t* h_r, uint16_t* h_s, void* stream);
+int fused_occupancy(int tb, int qx, int rwt, int swt, int lds_bytes, int* blocks_per_cu);
+// Router units per thread the kernel is built for at this hidden size (0: none).
+int fused_qx(int hidden);
 
 }  // namespace moe
