@@ -26,6 +26,7 @@ inline int tb_index(int tb) { return tb == 1 ? 0 : tb == 2 ? 1 : tb == 4 ? 2 : 3
 struct Plan {
   MatGeom g13, g2;
   int Er, maxd, tbmax;
+  moe::FastDiv dv_gs2;
   int spg_max;                 // most down steps a workgroup owns (given G)
   int G;                       // workgroups (0 until the device is known)
   int lds_act[4], lds_acc[4];  // per token bucket 1, 2, 4, 8
@@ -245,12 +246,15 @@ int moe_layer_create(const moe_layer_desc* desc, moe_layer_t* out) {
     (void)hipGetLastError();
     return MOE_ERR_DEVICE;
   }
-  // One workgroup per router row at most (each publishes a logit, which is how
-  // workgroup 0 knows every workgroup has read the call counter), at most two
-  // rows each, and never more workgroups than can be resident together.
-  int G = p.Er < cus ? p.Er : cus;
-  plan_grid(desc, &p, G);
+  // A power of two of workgroups (work splits by shifts), at most one per
+  // router row (each publishes a logit, which is how workgroup 0 knows every
+  // workgroup has read the call counter), at most two rows each, and never
+  // more than can be resident together.
+  int cap = p.Er < cus ? p.Er : cus;
   const int rwt = desc->routed_wtype, swt = desc->shared_wtype;
+  int G = 1;
+  while (2 * G <= cap) G *= 2;
+  plan_grid(desc, &p, G);
   for (int tb = 1; tb <= p.tbmax; tb *= 2) {
     int occ = 0;
     const int ti = tb_index(tb);
@@ -259,10 +263,17 @@ int moe_layer_create(const moe_layer_desc* desc, moe_layer_t* out) {
       (void)hipGetLastError();
       return MOE_ERR_UNSUPPORTED;
     }
-    if (G > occ * cus) G = occ * cus;
+    while (G > occ * cus) G /= 2;
   }
   if (2 * G < p.Er) return MOE_ERR_UNSUPPORTED;
   plan_grid(desc, &p, G);
+  // gate/up items: divisor of the step pairs, checked over every item count
+  const int gs2 = desc->inter / p.g13.rpw / 2;
+  if (moe::kFusedWaves / p.g13.ns > gs2) return MOE_ERR_UNSUPPORTED;
+  const moe::FastDiv dv = moe::make_fastdiv((uint32_t)gs2);
+  for (uint32_t n = 0; n < (1u << 22); ++n)
+    if (moe::fastdiv(n, dv) != n / (uint32_t)gs2) return MOE_ERR_UNSUPPORTED;
+  p.dv_gs2 = dv;
 
   moe_layer* L = new (std::nothrow) moe_layer();
   if (L == nullptr) return MOE_ERR_DEVICE;
@@ -372,6 +383,9 @@ moe::FusedArgs make_args(const moe_layer* L, const void* x, const void* router_w
   a.s_scale_stride = L->ls.scale_stride;
   a.s_w13_scale = L->ls.w13_scale_bytes;
   a.G = L->p.G;
+  a.log2G = 0;
+  while ((1 << a.log2G) < a.G) ++a.log2G;
+  a.dv_gs2 = L->p.dv_gs2;
   const int ti = tb_index(tb_of(batch));
   a.lds_act = L->p.lds_act[ti];
   a.lds_acc = L->p.lds_acc[ti];

@@ -1,5 +1,5 @@
-// Device helpers shared by the MoE decode kernels (gfx950): bf16 and e2m1/e4m3
-// conversions, dot products, DPP / permlane cross-lane reductions, sortable keys.
+// Device helpers of the MoE decode kernel (gfx950): bf16 and e2m1/e4m3
+// conversions, dot products, DPP lane-permute encodings, sortable keys.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -74,65 +74,6 @@ __device__ __forceinline__ float e4m3f(uint32_t v) {
 #define MOE_DPP_HALF_MIRROR 0x141
 #define MOE_DPP_MIRROR 0x140
 
-__device__ __forceinline__ float dpp_f(float v, int ctrl_sel) {
-  switch (ctrl_sel) {
-    case 0: return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), MOE_DPP_XOR1, 0xF, 0xF, false));
-    case 1: return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), MOE_DPP_XOR2, 0xF, 0xF, false));
-    case 2: return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), MOE_DPP_HALF_MIRROR, 0xF, 0xF, false));
-    default: return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), MOE_DPP_MIRROR, 0xF, 0xF, false));
-  }
-}
-
-// Value of lane i ^ 16 / lane i ^ 32 (gfx950 v_permlane16_swap / v_permlane32_swap
-// with both operands equal: the two results hold the lane's own value and
-// its partner's, in an order that depends on the half, so their sum / max
-// combines a lane with its partner in every lane).
-__device__ __forceinline__ float add_x16(float v) {
-  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-__device__ __forceinline__ float add_x32(float v) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-__device__ __forceinline__ unsigned max_x16(unsigned v) {
-  const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
-  return max((unsigned)r[0], (unsigned)r[1]);
-}
-__device__ __forceinline__ unsigned max_x32(unsigned v) {
-  const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
-  return max((unsigned)r[0], (unsigned)r[1]);
-}
-
-// Sum over groups of `width` consecutive lanes (width a power of two <= 64).
-// Each step adds the value of a partner lane from the other half of the
-// group, so every lane of a group ends with the same, order-fixed sum.
-__device__ __forceinline__ float lane_reduce(float v, int width) {
-  if (width >= 2) v += dpp_f(v, 0);
-  if (width >= 4) v += dpp_f(v, 1);
-  if (width >= 8) v += dpp_f(v, 2);
-  if (width >= 16) v += dpp_f(v, 3);
-  if (width >= 32) v = add_x16(v);
-  if (width >= 64) v = add_x32(v);
-  return v;
-}
-
-// Max of a 32-bit unsigned key over the wavefront, returned uniform.
-__device__ __forceinline__ unsigned wave_umax(unsigned v) {
-  v = max(v, (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, MOE_DPP_XOR1, 0xF, 0xF, false));
-  v = max(v, (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, MOE_DPP_XOR2, 0xF, 0xF, false));
-  v = max(v, (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, MOE_DPP_HALF_MIRROR, 0xF, 0xF, false));
-  v = max(v, (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, MOE_DPP_MIRROR, 0xF, 0xF, false));
-  v = max_x32(max_x16(v));
-  return (unsigned)__builtin_amdgcn_readfirstlane((int)v);
-}
-
-// Sum over the wavefront, returned uniform (fixed order).
-__device__ __forceinline__ float wave_fsum(float v) {
-  v = lane_reduce(v, 64);
-  return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(v)));
-}
-
 // Order-preserving map of fp32 to uint32 (larger float -> larger key);
 // both zeros map to the same key and NaN maps to 0, below every number.
 __device__ __forceinline__ unsigned fkey(float f) {
@@ -149,7 +90,6 @@ __device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<
 __device__ __forceinline__ void unpack4(const uint4& v, uint32_t* d) {
   d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
 }
-
 
 // xhat pair = bf16(x * rn * gamma) elementwise on a packed bf16 pair.
 __device__ __forceinline__ uint32_t norm_pair(uint32_t xv, uint32_t gv, float rn) {

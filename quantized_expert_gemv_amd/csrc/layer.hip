@@ -131,6 +131,52 @@ __device__ __forceinline__ void gather_all(int n, uint32_t tag, u64 deadline, un
 }
 
 // ---------------------------------------------------------------------------
+// cross-lane reductions
+// ---------------------------------------------------------------------------
+
+// Reductions inside rows of 16 lanes use DPP butterflies (every lane of a
+// group gets the group's result); across rows, DPP row broadcasts carry lane
+// 15 of each row into the next row and lane 31 into rows 2 and 3, so lane 63
+// ends with the result of all 64 lanes (lanes 31 and 63 with those of their
+// 32-lane halves).  No permlane or LDS traffic; the order of the operations
+// is fixed, so sums are deterministic.
+#define MOE_DPP_ROW_BCAST15 0x142
+#define MOE_DPP_ROW_BCAST31 0x143
+
+template <int CTRL>
+__device__ __forceinline__ float add_dpp(float v) {
+  return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over groups of `width` consecutive lanes (a power of two <= 64); the
+// result is valid in lane width - 1 of each group (in every lane when width <= 16).
+__device__ __forceinline__ float group_sum(float v, int width) {
+  if (width >= 2) v = add_dpp<MOE_DPP_XOR1>(v);
+  if (width >= 4) v = add_dpp<MOE_DPP_XOR2>(v);
+  if (width >= 8) v = add_dpp<MOE_DPP_HALF_MIRROR>(v);
+  if (width >= 16) v = add_dpp<MOE_DPP_MIRROR>(v);
+  if (width >= 32)
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), MOE_DPP_ROW_BCAST15, 0xA, 0xF, false));
+  if (width >= 64)
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), MOE_DPP_ROW_BCAST31, 0xC, 0xF, false));
+  return v;
+}
+
+// Wave-wide max of an unsigned key and sum of a float, uniform results.
+__device__ __forceinline__ unsigned wave_max_u32(unsigned v) {
+  v = max(v, (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, MOE_DPP_XOR1, 0xF, 0xF, false));
+  v = max(v, (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, MOE_DPP_XOR2, 0xF, 0xF, false));
+  v = max(v, (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, MOE_DPP_HALF_MIRROR, 0xF, 0xF, false));
+  v = max(v, (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, MOE_DPP_MIRROR, 0xF, 0xF, false));
+  v = max(v, (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, MOE_DPP_ROW_BCAST15, 0xA, 0xF, false));
+  v = max(v, (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, MOE_DPP_ROW_BCAST31, 0xC, 0xF, false));
+  return (unsigned)__builtin_amdgcn_readlane((int)v, 63);
+}
+__device__ __forceinline__ float wave_sum(float v) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(group_sum(v, 64)), 63));
+}
+
+// ---------------------------------------------------------------------------
 // shared-memory state
 // ---------------------------------------------------------------------------
 
@@ -142,9 +188,10 @@ struct Smem {
   int sel[MOE_MAX_BATCH][MOE_MAX_TOPK];       // per token, selection order
   float selw[MOE_MAX_BATCH][MOE_MAX_TOPK];    // routing weights
   float shc[MOE_MAX_BATCH][MOE_MAX_SHARED];   // shared-expert coefficients
-  int ids[kMaxD];                             // distinct selected experts (slot order)
-  unsigned dmask[kMaxD];                      // their token masks
-  unsigned char pr[kMaxD][MOE_MAX_BATCH];     // selection rank r of token b for slot d
+  int ids[kMaxD];                             // expert in slot d
+  float xg[kMaxD];                            // its W13 tensor scale
+  unsigned dmask[kMaxD];                      // its token mask
+  uint32_t pr[kMaxD][2];                      // selection rank r of token b for slot d, byte b
   float pw[kMaxPairs];                        // combine weight x W2 tensor scale, per pair
   float red[NW][2][MOE_MAX_BATCH];            // router / norm partial sums
   float rn[MOE_MAX_BATCH];                    // 1/rms per token
@@ -155,14 +202,86 @@ struct Smem {
 // Activation pairs: routed pair of token b's r-th selection = b k + r;
 // shared expert s of token b = B k + s B + b.
 
+// The routing's tables, spread over the lanes of every wave (entry i in lane
+// i % 64 of register i / 64) and read with v_readlane: a uniform index then
+// costs a few cycles instead of a shared-memory round trip.
+struct SlotTab {
+  uint32_t id[2], mask[2], g13[2], prlo[2], prhi[2];   // per slot
+  uint32_t pw[3];                                      // per pair
+  __device__ __forceinline__ void load(const Smem& s, int lane) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int d = lane + 64 * h;
+      id[h] = (uint32_t)s.ids[d];
+      mask[h] = s.dmask[d];
+      g13[h] = __float_as_uint(s.xg[d]);
+      prlo[h] = s.pr[d][0];
+      prhi[h] = s.pr[d][1];
+    }
+#pragma unroll
+    for (int h = 0; h < 3; ++h) pw[h] = __float_as_uint(s.pw[min(lane + 64 * h, kMaxPairs - 1)]);
+  }
+  // Lookups read other lanes, so they run only in wave-uniform control flow
+  // (all lanes active): inside lane-conditional code the inactive lanes of a
+  // register, or of the compiler's copy of it, hold no defined value.  Each
+  // register is read at lane i % 64 and the scalars are selected afterwards;
+  // a conditional on the array itself would become an indexed access, which
+  // puts the table in scratch memory.
+  __device__ __forceinline__ static uint32_t rl(uint32_t v, int i) {
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, i & 63);
+  }
+  __device__ __forceinline__ static uint32_t pick2(const uint32_t (&v)[2], int i) {
+    const uint32_t a0 = rl(v[0], i), a1 = rl(v[1], i);
+    return i >= 64 ? a1 : a0;
+  }
+  __device__ __forceinline__ int expert(int d, int E) const { return min(max((int)pick2(id, d), 0), E - 1); }
+  __device__ __forceinline__ unsigned tokens(int d) const { return pick2(mask, d); }
+  __device__ __forceinline__ float w13(int d) const { return __uint_as_float(pick2(g13, d)); }
+  __device__ __forceinline__ int rank(int d, int b) const {
+    const uint32_t wd = (b < 4) ? pick2(prlo, d) : pick2(prhi, d);
+    return (int)((wd >> (8 * (b & 3))) & 0xffu);
+  }
+  __device__ __forceinline__ float weight(int pr) const {
+    const uint32_t a0 = rl(pw[0], pr), a1 = rl(pw[1], pr), a2 = rl(pw[2], pr);
+    return __uint_as_float(pr >= 128 ? a2 : (pr >= 64 ? a1 : a0));
+  }
+};
+
 // ---------------------------------------------------------------------------
 // weight tiles
 // ---------------------------------------------------------------------------
 
-// One lane's share of one wave step of a packed matrix.
-template <int WT> struct Tile;
-template <> struct Tile<WT_NVFP4> { uint4 c; uint32_t sw; };
-template <> struct Tile<WT_BF16> { uint4 c[4]; };
+// This lane's place in one wave step of a packed matrix: byte offsets of its
+// 16-byte code unit and 4-byte scale word inside a step, and the step strides.
+struct LaneGeo {
+  uint32_t su16, su4;   // bytes of one step's code units / scale words (per scale pair)
+  int nsteps;
+  uint32_t c_off, s_off;
+  int ri, jj, jc;
+  bool active;
+};
+
+// ns == 1: a step covers rpw rows of lpr lanes; ns > 1: one row, lane = chunk.
+__device__ __forceinline__ LaneGeo lane_geo(const MatGeom& g, int lane) {
+  LaneGeo L;
+  L.su16 = (uint32_t)g.su * 16u;
+  L.su4 = (uint32_t)g.su * 4u;
+  L.nsteps = g.nsteps;
+  if (g.ns == 1) {
+    L.ri = lane / g.lpr;
+    L.jj = lane % g.lpr;
+    L.active = L.jj < g.cw;
+  } else {
+    L.ri = 0;
+    L.jj = lane;
+    L.active = lane < g.cw;
+  }
+  L.jc = L.active ? L.jj : 0;
+  const uint32_t u = (uint32_t)(L.ri * g.cw + L.jc);
+  L.c_off = u * 16u;
+  L.s_off = u * 4u;
+  return L;
+}
 
 // `dummy` when dm, else `real`, computed without a branch (a branch would
 // duplicate the load that uses it and make the loads in flight depend on
@@ -172,26 +291,44 @@ __device__ __forceinline__ const uint8_t* pick(bool dm, const uint8_t* real, con
   return reinterpret_cast<const uint8_t*>((uintptr_t)real ^ (((uintptr_t)real ^ (uintptr_t)dummy) & m));
 }
 
-// Loads the lane's chunk of (slice s, step t) of a packed matrix.  A dummy
-// load reads the first bytes of `dummy` instead (same instructions, so the
-// number of loads in flight never depends on data; the value is unused).
+__device__ __forceinline__ uint32_t ld32(const uint8_t* p) { return *reinterpret_cast<const uint32_t*>(p); }
+
+// NVFP4 byte offsets of (slice sl, step t): code unit, and the scale word
+// shared by steps t & ~1 and t | 1.
+__device__ __forceinline__ uint32_t code_off(const LaneGeo& L, int sl, int t) {
+  return (uint32_t)(sl * L.nsteps + t) * L.su16 + L.c_off;
+}
+__device__ __forceinline__ uint32_t scale_off(const LaneGeo& L, int sl, int t) {
+  return (uint32_t)(sl * (L.nsteps >> 1) + (t >> 1)) * L.su4 + L.s_off;
+}
+// BF16 unit `sub` (elements 8 sub .. 8 sub + 7 of the lane's chunk) of (sl, t).
+__device__ __forceinline__ uint32_t bf16_off(const LaneGeo& L, int sl, int t, int sub) {
+  return (uint32_t)((sl * L.nsteps + t) * 4 + sub) * L.su16 + L.c_off;
+}
+
+// One lane's share of one wave step of a packed matrix.
+template <int WT> struct Tile;
+template <> struct Tile<WT_NVFP4> { uint4 c; uint32_t sw; };
+template <> struct Tile<WT_BF16> { uint4 c[4]; };
+
+// Loads the lane's chunk of (slice sl, step t).  A dummy load reads the first
+// bytes of `dummy` instead (same instructions, so the number of loads in flight
+// never depends on data; the value is unused).
 template <int WT>
 __device__ __forceinline__ void tile_load(Tile<WT>& tl, const uint8_t* codes, const uint8_t* scales,
-                                          const MatGeom& g, int s, int t, int ri, int j, bool dm,
-                                          const uint8_t* dummy) {
+                                          const LaneGeo& L, int sl, int t, bool dm, const uint8_t* dummy) {
   if constexpr (WT == WT_NVFP4) {
-    tl.c = ld16(pick(dm, codes + code_unit(g, s, t, ri, j) * 16, dummy));
-    tl.sw = *reinterpret_cast<const uint32_t*>(pick(dm, scales + scale_word(g, s, t, ri, j), dummy));
+    tl.c = ld16(pick(dm, codes + code_off(L, sl, t), dummy));
+    tl.sw = ld32(pick(dm, scales + scale_off(L, sl, t), dummy));
   } else {
 #pragma unroll
-    for (int sub = 0; sub < 4; ++sub) tl.c[sub] = ld16(pick(dm, codes + bf16_unit(g, s, t, sub, ri, j) * 16, dummy));
+    for (int sub = 0; sub < 4; ++sub) tl.c[sub] = ld16(pick(dm, codes + bf16_off(L, sl, t, sub), dummy));
   }
 }
 
 // sum of the lane's 32 weights times act (16 bf16 pairs).  NVFP4: the two
 // block scales are bytes 0, 1 of sp.
-template <int WT>
-__device__ __forceinline__ float chunk_dot(const uint4& c, uint32_t sp, const uint32_t (&act)[16]) {
+__device__ __forceinline__ float chunk_dot_fp4(const uint4& c, uint32_t sp, const uint32_t (&act)[16]) {
   uint32_t w[16];
   decode_chunk(c, w);
   return fmaf(dot8<8>(w, act), e4m3f<1>(sp), dot8<0>(w, act) * e4m3f<0>(sp));
@@ -204,7 +341,7 @@ __device__ __forceinline__ float chunk_dot_bf16(const uint4 (&c)[4], const uint3
 }
 template <int WT>
 __device__ __forceinline__ float tile_dot(const Tile<WT>& tl, int t, const uint32_t (&act)[16]) {
-  if constexpr (WT == WT_NVFP4) return chunk_dot<WT>(tl.c, (t & 1) ? (tl.sw >> 16) : tl.sw, act);
+  if constexpr (WT == WT_NVFP4) return chunk_dot_fp4(tl.c, (t & 1) ? (tl.sw >> 16) : tl.sw, act);
   else return chunk_dot_bf16(tl.c, act);
 }
 
@@ -215,22 +352,21 @@ template <> struct Quad<WT_NVFP4> { uint4 c[4]; uint32_t sw[2]; };
 template <> struct Quad<WT_BF16> { uint4 c[4][4]; };
 
 template <int WT>
-__device__ __forceinline__ void quad_load(Quad<WT>& q, const uint8_t* codes, const uint8_t* scales, const MatGeom& g,
-                                          int sl, int gate_steps, int t2, int ri, int j, bool dm,
-                                          const uint8_t* dummy) {
+__device__ __forceinline__ void quad_load(Quad<WT>& q, const uint8_t* codes, const uint8_t* scales, const LaneGeo& L,
+                                          int sl, int gate_steps, int t2, bool dm, const uint8_t* dummy) {
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
     const int t = u * gate_steps + 2 * t2;
     if constexpr (WT == WT_NVFP4) {
-      q.c[2 * u] = ld16(pick(dm, codes + code_unit(g, sl, t, ri, j) * 16, dummy));
-      q.c[2 * u + 1] = ld16(pick(dm, codes + code_unit(g, sl, t + 1, ri, j) * 16, dummy));
-      q.sw[u] = *reinterpret_cast<const uint32_t*>(pick(dm, scales + scale_word(g, sl, t, ri, j), dummy));
+      const uint32_t co = code_off(L, sl, t);
+      q.c[2 * u] = ld16(pick(dm, codes + co, dummy));
+      q.c[2 * u + 1] = ld16(pick(dm, codes + co + L.su16, dummy));
+      q.sw[u] = ld32(pick(dm, scales + scale_off(L, sl, t), dummy));
     } else {
 #pragma unroll
       for (int st = 0; st < 2; ++st)
 #pragma unroll
-        for (int sub = 0; sub < 4; ++sub)
-          q.c[2 * u + st][sub] = ld16(pick(dm, codes + bf16_unit(g, sl, t + st, sub, ri, j) * 16, dummy));
+        for (int sub = 0; sub < 4; ++sub) q.c[2 * u + st][sub] = ld16(pick(dm, codes + bf16_off(L, sl, t + st, sub), dummy));
     }
   }
 }
@@ -240,7 +376,7 @@ template <int WT>
 __device__ __forceinline__ void quad_dot(const Quad<WT>& q, const uint32_t (&x)[16], float (&v)[4]) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    if constexpr (WT == WT_NVFP4) v[i] = chunk_dot<WT>(q.c[i], (i & 1) ? (q.sw[i >> 1] >> 16) : q.sw[i >> 1], x);
+    if constexpr (WT == WT_NVFP4) v[i] = chunk_dot_fp4(q.c[i], (i & 1) ? (q.sw[i >> 1] >> 16) : q.sw[i >> 1], x);
     else v[i] = chunk_dot_bf16(q.c[i], x);
   }
 }
@@ -258,127 +394,100 @@ __device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f +
 // gate/up phases
 // ---------------------------------------------------------------------------
 
-// Expert of a gate/up slot: shared expert `slot`, or the slot-th distinct
-// selected routed expert.
-struct Expert {
-  const uint8_t* codes;
-  const uint8_t* scales;
-  float g13;
-  unsigned mask;
-};
-
-template <int WT>
-__device__ __forceinline__ Expert expert_of(const FusedArgs& a, const Smem& s, int shared, int slot) {
-  Expert x;
-  if (shared) {
-    // a layer without shared experts has no shared buffer: x stands in (its
-    // items are all dummies, whose loads read x anyway)
-    const uint8_t* sc = a.s_codes ? a.s_codes : reinterpret_cast<const uint8_t*>(a.x);
-    const uint8_t* ss = a.s_scales ? a.s_scales : reinterpret_cast<const uint8_t*>(a.x);
-    slot = min(slot, MOE_MAX_SHARED - 1);
-    x.codes = sc + (size_t)slot * a.s_code_stride;
-    x.scales = (WT == WT_NVFP4) ? ss + (size_t)slot * a.s_scale_stride : nullptr;
-    x.g13 = (WT == WT_NVFP4) ? s.tss[slot][0] : 1.0f;
-    x.mask = (1u << a.B) - 1u;
-  } else {
-    slot = min(slot, kMaxD - 1);
-    const int e = min(max(s.ids[slot], 0), a.E - 1);
-    x.codes = a.r_codes + (size_t)e * a.r_code_stride;
-    x.scales = (WT == WT_NVFP4) ? a.r_scales + (size_t)e * a.r_scale_stride : nullptr;
-    x.g13 = (WT == WT_NVFP4) ? s.tsr[e][0] : 1.0f;
-    x.mask = s.dmask[slot];
-  }
-  return x;
-}
-
-__device__ __forceinline__ int gu_pair(const FusedArgs& a, const Smem& s, int shared, int slot, int b) {
-  return shared ? a.B * a.k + slot * a.B + b : b * a.k + s.pr[slot][b];
-}
-
 // Gate/up items of one workgroup: item j = (slot j / gs2, step pair j % gs2),
-// block [lo, hi).  With one wave step per row (ns = 1) each wave takes items
-// lo + wave, lo + wave + NW, ... on its own and publishes their SiLU*up
-// words; with ns > 1 the ns waves of a group share items, wave w % ns taking
-// slice w % ns, and after one barrier the workgroup combines the slices in
-// order.  PI items are loading at a time.
+// block [lo, hi) of the phase's n items.  With one wave step per row (ns = 1)
+// each wave takes items lo + wave, lo + wave + NW, ... on its own and
+// publishes their SiLU*up words; with ns > 1 the ns waves of a group share
+// items, wave w taking slice w % ns, and after one barrier the workgroup
+// combines the slices in order.  PI items are loading at a time.
 template <int TB, int WT, int PI>
 struct GateUp {
   Quad<WT> q[PI];
   int qslot[PI], qt2[PI];
   int shared, lo, hi, gs2, gate_steps;
-  int ns, grp, ngr, sl;
+  int ns, grp, ngr, lg_ngr, sl;
   int nmine, nloaded, cslot, ct2;   // this wave's item count, items loaded, next item
-  int ri, jj, jc;
-  bool active;
+  LaneGeo L;
 
-  __device__ __forceinline__ void setup(const FusedArgs& a, int shared_, int n, int w, int G) {
-    const MatGeom& g = a.g13;
-    const int wave = wave_id(), lane = threadIdx.x & 63;
+  // Everything that does not depend on the routing.
+  __device__ __forceinline__ void init(const FusedArgs& a, const LaneGeo& lg13, int shared_) {
+    const int wave = wave_id();
+    L = lg13;
     shared = shared_;
-    gate_steps = a.I / g.rpw;
-    gs2 = gate_steps / 2;
-    lo = (int)((long long)n * w / G);
-    hi = (int)((long long)n * (w + 1) / G);
-    ns = g.ns;
+    gate_steps = a.I / a.g13.rpw;
+    gs2 = gate_steps >> 1;
+    ns = a.g13.ns;
     ngr = NW / ns;
+    lg_ngr = (ngr == 4) ? 2 : (ngr == 2) ? 1 : 0;
     grp = wave / ns;
-    sl = wave % ns;
-    if (ns == 1) {
-      ri = lane / g.lpr;
-      jj = lane % g.lpr;
-      active = jj < g.cw;
-    } else {
-      ri = 0;
-      jj = lane;
-      active = lane < g.cw;
-    }
-    jc = active ? jj : 0;
+    sl = wave - grp * ns;
+  }
+  // The phase's item count n (items of the block are contiguous).
+  __device__ __forceinline__ void set_items(const FusedArgs& a, int n) {
+    const uint32_t w = blockIdx.x;
+    lo = (int)(((uint32_t)n * w) >> a.log2G);
+    hi = (int)(((uint32_t)n * (w + 1)) >> a.log2G);
     const int first = lo + grp;
-    nmine = (hi > first) ? (hi - first + ngr - 1) / ngr : 0;
+    nmine = (hi > first) ? (hi - first + ngr - 1) >> lg_ngr : 0;
     nloaded = 0;
-    cslot = first / gs2;
-    ct2 = first % gs2;
+    cslot = (int)fastdiv((uint32_t)first, a.dv_gs2);
+    ct2 = first - cslot * gs2;
+  }
+  __device__ __forceinline__ void bases(const FusedArgs& a, const SlotTab& tb, int slot, const uint8_t*& c,
+                                        const uint8_t*& sc) const {
+    if (shared) {
+      // a layer without shared experts has no shared buffer: x stands in (its
+      // items are all dummies, whose loads read x anyway)
+      const int sh = min(slot, MOE_MAX_SHARED - 1);
+      c = (a.s_codes ? a.s_codes : reinterpret_cast<const uint8_t*>(a.x)) + (size_t)sh * a.s_code_stride;
+      sc = (a.s_scales ? a.s_scales : reinterpret_cast<const uint8_t*>(a.x)) + (size_t)sh * a.s_scale_stride;
+    } else {
+      const int e = tb.expert(min(slot, kMaxD - 1), a.E);
+      c = a.r_codes + (size_t)e * a.r_code_stride;
+      sc = (WT == WT_NVFP4) ? a.r_scales + (size_t)e * a.r_scale_stride : reinterpret_cast<const uint8_t*>(a.x);
+    }
   }
   // Loads the next item of this wave, or a dummy once they are all loaded.
-  __device__ __forceinline__ void load_next(const FusedArgs& a, const Smem& s, int p) {
+  __device__ __forceinline__ void load_next(const FusedArgs& a, const SlotTab& tb, int p) {
     const bool dm = nloaded >= nmine;
-    const Expert x = expert_of<WT>(a, s, shared, cslot);
-    quad_load<WT>(q[p], x.codes, x.scales, a.g13, sl, gate_steps, ct2, ri, jc, dm,
-                  reinterpret_cast<const uint8_t*>(a.x));
+    const uint8_t *c, *sc;
+    bases(a, tb, cslot, c, sc);
+    quad_load<WT>(q[p], c, sc, L, sl, gate_steps, ct2, dm, reinterpret_cast<const uint8_t*>(a.x));
     qslot[p] = cslot;
     qt2[p] = ct2;
     if (!dm) {
       ++nloaded;
       ct2 += ngr;
-      while (ct2 >= gs2) {
+      if (ct2 >= gs2) {   // ngr <= gs2 (the plan checks it)
         ct2 -= gs2;
         ++cslot;
       }
     }
   }
-  __device__ __forceinline__ void prime(const FusedArgs& a, const Smem& s) {
+  __device__ __forceinline__ void prime(const FusedArgs& a, const SlotTab& tb) {
 #pragma unroll
-    for (int p = 0; p < PI; ++p) load_next(a, s, p);
+    for (int p = 0; p < PI; ++p) load_next(a, tb, p);
   }
   // part: TB * 4 * ns floats per item of the block (ns > 1 only).
-  __device__ __forceinline__ void run(const FusedArgs& a, const Smem& s, const uint32_t (&xr)[TB][16], float* part,
-                                      uint32_t tag) {
+  __device__ __forceinline__ void run(const FusedArgs& a, const Smem& s, const SlotTab& tb, const uint32_t (&xr)[TB][16],
+                                      float* part, uint32_t tag) {
     const int I2 = a.I / 2;
     const int lpr = a.g13.lpr;
+    const bool lead = L.jj == ((ns == 1) ? lpr - 1 : 63);
     for (int base = 0; base < nmine; base += PI) {
 #pragma unroll
       for (int p = 0; p < PI; ++p) {
         const int i = base + p;
         const bool live = i < nmine;   // uniform
         const int slot = qslot[p], t2 = qt2[p];
-        const Expert x = expert_of<WT>(a, s, shared, slot);
+        const unsigned mask = shared ? (1u << a.B) - 1u : tb.tokens(min(slot, kMaxD - 1));
         float v[TB][4];
         if (live) {
 #pragma unroll
           for (int b = 0; b < TB; ++b) {
-            if ((x.mask >> b) & 1u) {
+            if ((mask >> b) & 1u) {
               quad_dot<WT>(q[p], xr[b], v[b]);
-              if (!active) v[b][0] = v[b][1] = v[b][2] = v[b][3] = 0.f;
+              if (!L.active) v[b][0] = v[b][1] = v[b][2] = v[b][3] = 0.f;
             }
           }
         }
@@ -387,26 +496,30 @@ struct GateUp {
         // reload would make the compiler copy registers and wait for every
         // load in flight.
         __asm__ volatile("" ::: "memory");
-        load_next(a, s, p);
+        load_next(a, tb, p);
         if (live) {
+          const float g13 = shared ? ((WT == WT_NVFP4) ? s.tss[min(slot, MOE_MAX_SHARED - 1)][0] : 1.0f)
+                                   : tb.w13(min(slot, kMaxD - 1));
 #pragma unroll
           for (int b = 0; b < TB; ++b) {
-            if (!((x.mask >> b) & 1u)) continue;
+            if (!((mask >> b) & 1u)) continue;
             if (ns == 1) {
+              // the table lookup is a cross-lane read: it stays out of the
+              // lane-conditional code below, where other lanes are inactive
+              const int pr = shared ? a.B * a.k + slot * a.B + b : b * a.k + tb.rank(slot, b);
 #pragma unroll
-              for (int c = 0; c < 4; ++c) v[b][c] = lane_reduce(v[b][c], lpr);
-              if (jj == 0) {
-                const float h0 = silu_mul(v[b][0] * x.g13, v[b][2] * x.g13);
-                const float h1 = silu_mul(v[b][1] * x.g13, v[b][3] * x.g13);
-                publish(a.xh + (size_t)gu_pair(a, s, shared, slot, b) * I2 + t2 * a.g13.rpw + ri,
-                        f2bf(h0) | (f2bf(h1) << 16), tag);
+              for (int c = 0; c < 4; ++c) v[b][c] = group_sum(v[b][c], lpr);
+              if (lead) {
+                const float h0 = silu_mul(v[b][0] * g13, v[b][2] * g13);
+                const float h1 = silu_mul(v[b][1] * g13, v[b][3] * g13);
+                publish(a.xh + (size_t)pr * I2 + t2 * a.g13.rpw + L.ri, f2bf(h0) | (f2bf(h1) << 16), tag);
               }
             } else {
               const int il = slot * gs2 + t2 - lo;
 #pragma unroll
               for (int c = 0; c < 4; ++c) {
-                const float sum = lane_reduce(v[b][c], 64);
-                if (jj == 0) part[((il * TB + b) * 4 + c) * ns + sl] = sum;
+                const float sum = group_sum(v[b][c], 64);
+                if (lead) part[((il * TB + b) * 4 + c) * ns + sl] = sum;
               }
             }
           }
@@ -416,10 +529,12 @@ struct GateUp {
     if (ns > 1) {
       __syncthreads();
       for (int idx = threadIdx.x; idx < (hi - lo) * TB; idx += NT) {
-        const int il = idx / TB, b = idx % TB;
-        const int j = lo + il, slot = j / gs2, t2 = j % gs2;
-        const Expert x = expert_of<WT>(a, s, shared, slot);
-        if (!((x.mask >> b) & 1u)) continue;
+        const int il = idx / TB, b = idx - il * TB;
+        const int j = lo + il, slot = (int)fastdiv((uint32_t)j, a.dv_gs2), t2 = j - slot * gs2;
+        const unsigned mask = shared ? (1u << a.B) - 1u : s.dmask[min(slot, kMaxD - 1)];
+        if (!((mask >> b) & 1u)) continue;
+        const float g13 = shared ? ((WT == WT_NVFP4) ? s.tss[min(slot, MOE_MAX_SHARED - 1)][0] : 1.0f)
+                                 : s.xg[min(slot, kMaxD - 1)];
         float v[4];
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
@@ -427,9 +542,11 @@ struct GateUp {
           for (int u = 0; u < ns; ++u) acc += part[((il * TB + b) * 4 + c) * ns + u];
           v[c] = acc;
         }
-        const float h0 = silu_mul(v[0] * x.g13, v[2] * x.g13);
-        const float h1 = silu_mul(v[1] * x.g13, v[3] * x.g13);
-        publish(a.xh + (size_t)gu_pair(a, s, shared, slot, b) * I2 + t2, f2bf(h0) | (f2bf(h1) << 16), tag);
+        const float h0 = silu_mul(v[0] * g13, v[2] * g13);
+        const float h1 = silu_mul(v[1] * g13, v[3] * g13);
+        const int pr = shared ? a.B * a.k + slot * a.B + b
+                              : b * a.k + (int)((s.pr[slot][b >> 2] >> (8 * (b & 3))) & 0xffu);
+        publish(a.xh + (size_t)pr * I2 + t2, f2bf(h0) | (f2bf(h1) << 16), tag);
       }
     }
   }
@@ -437,16 +554,9 @@ struct GateUp {
 
 // This lane's activation chunk(s) from the x region of shared memory.
 template <int TB>
-__device__ __forceinline__ void load_xr(const FusedArgs& a, const uint16_t* xs, uint32_t (&xr)[TB][16]) {
-  const MatGeom& g = a.g13;
-  const int wave = wave_id(), lane = threadIdx.x & 63;
-  int col;
-  if (g.ns == 1) {
-    const int jj = lane % g.lpr;
-    col = (jj < g.cw ? jj : 0) * 32;
-  } else {
-    col = ((wave % g.ns) * g.cw + (lane < g.cw ? lane : 0)) * 32;
-  }
+__device__ __forceinline__ void load_xr(const FusedArgs& a, const LaneGeo& L, const uint16_t* xs,
+                                        uint32_t (&xr)[TB][16]) {
+  const int col = ((a.g13.ns == 1) ? L.jc : (wave_id() % a.g13.ns) * a.g13.cw + L.jc) * 32;
 #pragma unroll
   for (int b = 0; b < TB; ++b) lds_chunk(xs + (size_t)min(b, a.B - 1) * a.H + col, xr[b]);
 }
@@ -456,125 +566,179 @@ __device__ __forceinline__ void load_xr(const FusedArgs& a, const uint16_t* xs, 
 // ---------------------------------------------------------------------------
 
 // Key for selection: order-preserving integer of the logit; NaN ranks below
-// every number (key 1) and a taken expert gets key 0.
+// every number (key 1) and a taken or absent expert has key 0.
 __device__ __forceinline__ unsigned sel_key(float f) {
   const unsigned k = fkey(f);
   return k == 0u ? 1u : k;
 }
 
-// Top-k per token (wave b % NW takes token b; lane l holds experts
-// [l m, l m + m) and keeps its best untaken one; each round the wave's best
-// key wins, ties to the lowest lane, i.e. the lowest expert index), routing
-// weights and shared coefficients.  Then wave 0 numbers the distinct
-// selected experts by first appearance in (token, rank) order and fills the
-// combine weight of every pair.  Ends with a barrier.
-template <int WTR, int WTS>
-__device__ __forceinline__ void route(const FusedArgs& a, Smem& s, const float* lg /* [B][Er] */) {
-  const int tid = threadIdx.x, wave = wave_id(), lane = tid & 63;
-  for (int e = tid; e < a.E; e += NT) s.emask[e] = 0u;
-  __syncthreads();
-  const int m = (a.E + 63) / 64;   // <= 8
-  for (int b = wave; b < a.B; b += NW) {
+// Compare-exchange for a descending order by key, ties to the lower expert.
+__device__ __forceinline__ void cas(unsigned& ka, int& ia, unsigned& kb, int& ib) {
+  const bool sw = kb > ka || (kb == ka && ib < ia);
+  const unsigned k0 = sw ? kb : ka, k1 = sw ? ka : kb;
+  const int i0 = sw ? ib : ia, i1 = sw ? ia : ib;
+  ka = k0; kb = k1; ia = i0; ib = i1;
+}
+
+// Top-k of TPW tokens at once (token wave + t NW): lane l holds experts
+// [l MK, l MK + MK), sorted by key.  Each round the wave's largest head key
+// wins (ties to the lowest lane, i.e. the lowest expert), the winning lane
+// shifts its list; the lanes' chains for the TPW tokens are independent.
+// Lane r ends with the r-th selection: expert my_e, logit my_l.
+template <int MK, int TPW>
+__device__ __forceinline__ void topk(const FusedArgs& a, const float* lg, int lane, int (&my_e)[TPW],
+                                     float (&my_l)[TPW]) {
+  const int wave = wave_id();
+  unsigned key[TPW][MK];
+  int idx[TPW][MK];
+#pragma unroll
+  for (int t = 0; t < TPW; ++t) {
+    const int b = min(wave + t * NW, a.B - 1);
     const float* l = lg + (size_t)b * a.Er;
-    unsigned key[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int e = lane * m + i;
-      key[i] = (i < m && e < a.E) ? sel_key(l[e]) : 0u;
+    for (int i = 0; i < MK; ++i) {
+      const int e = lane * MK + i;
+      idx[t][i] = e;
+      key[t][i] = (e < a.E) ? sel_key(l[e]) : 0u;
     }
-    unsigned bk = key[0];
-    int bi = 0;
+    if constexpr (MK == 2) {
+      cas(key[t][0], idx[t][0], key[t][1], idx[t][1]);
+    } else if constexpr (MK == 4) {
+      cas(key[t][0], idx[t][0], key[t][1], idx[t][1]);
+      cas(key[t][2], idx[t][2], key[t][3], idx[t][3]);
+      cas(key[t][0], idx[t][0], key[t][2], idx[t][2]);
+      cas(key[t][1], idx[t][1], key[t][3], idx[t][3]);
+      cas(key[t][1], idx[t][1], key[t][2], idx[t][2]);
+    } else if constexpr (MK == 8) {
+      constexpr int net[19][2] = {{0, 1}, {2, 3}, {4, 5}, {6, 7}, {0, 2}, {1, 3}, {4, 6}, {5, 7}, {1, 2}, {5, 6},
+                                  {0, 4}, {1, 5}, {2, 6}, {3, 7}, {2, 4}, {3, 5}, {1, 2}, {3, 4}, {5, 6}};
 #pragma unroll
-    for (int i = 1; i < 8; ++i)
-      if (key[i] > bk) { bk = key[i]; bi = i; }
-    int my_e = 0;
-    float my_l = 0.f;
-    for (int r = 0; r < a.k; ++r) {
-      const unsigned M = wave_umax(bk);
-      const int win = __builtin_ctzll(__ballot(bk == M));
-      const int wi = __builtin_amdgcn_readlane(bi, win);
-      if (lane == r) {
-        my_e = min(win * m + wi, a.E - 1);
-        my_l = unkey(M);
-      }
-      if (lane == win) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-          if (i == wi) key[i] = 0u;
-        bk = key[0];
-        bi = 0;
-#pragma unroll
-        for (int i = 1; i < 8; ++i)
-          if (key[i] > bk) { bk = key[i]; bi = i; }
-      }
+      for (int c = 0; c < 19; ++c) cas(key[t][net[c][0]], idx[t][net[c][0]], key[t][net[c][1]], idx[t][net[c][1]]);
     }
+    my_e[t] = 0;
+    my_l[t] = 0.f;
+  }
+  for (int r = 0; r < a.k; ++r) {
+    unsigned M[TPW];
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) M[t] = wave_max_u32(key[t][0]);
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) {
+      const int win = __builtin_ctzll(__ballot(key[t][0] == M[t]));
+      const int e_sel = __builtin_amdgcn_readlane(idx[t][0], win);
+      const bool mine = lane == r, me = lane == win;
+      my_e[t] = mine ? e_sel : my_e[t];
+      my_l[t] = mine ? unkey(M[t]) : my_l[t];
+#pragma unroll
+      for (int i = 0; i + 1 < MK; ++i) {
+        key[t][i] = me ? key[t][i + 1] : key[t][i];
+        idx[t][i] = me ? idx[t][i + 1] : idx[t][i];
+      }
+      key[t][MK - 1] = me ? 0u : key[t][MK - 1];
+    }
+  }
+}
+
+// Routing weights and shared coefficients of the TPW tokens (wave + t NW),
+// into shared memory, with the token masks of the selected experts.
+template <int TPW>
+__device__ __forceinline__ void route_weights(const FusedArgs& a, Smem& s, const float* lg, int lane,
+                                              const int (&my_e)[TPW], const float (&my_l)[TPW]) {
+  const int wave = wave_id();
+#pragma unroll
+  for (int t = 0; t < TPW; ++t) {
+    const int b = wave + t * NW;
+    if (b >= a.B) continue;
+    const float* l = lg + (size_t)b * a.Er;
     float wv;
     if (a.route == MOE_ROUTE_SOFTMAX_SINK) {
-      float mx = -INFINITY;
-      for (int e = lane; e < a.Er; e += 64) mx = fmaxf(mx, l[e]);
-      mx = unkey(wave_umax(fkey(mx)));
+      unsigned mk = 0u;
+      for (int e = lane; e < a.Er; e += 64) mk = max(mk, fkey(l[e]));
+      const float mx = unkey(wave_max_u32(mk));
       float z = 0.f;
       for (int e = lane; e < a.Er; e += 64) z += __expf(l[e] - mx);
-      z = wave_fsum(z);
-      wv = __expf(my_l - mx) / z;
+      z = wave_sum(z);
+      wv = __expf(my_l[t] - mx) / z;
       if (lane < a.S) s.shc[b][lane] = __expf(l[a.E + lane] - mx) / z;
     } else {
-      const float sg = (lane < a.k) ? 1.0f / (1.0f + __expf(-my_l)) : 0.f;
-      wv = sg / wave_fsum(sg);
+      const float sg = (lane < a.k) ? 1.0f / (1.0f + __expf(-my_l[t])) : 0.f;
+      wv = sg / wave_sum(sg);
       if (lane < a.S) s.shc[b][lane] = 1.0f;
     }
     if (lane < a.k) {
-      s.sel[b][lane] = my_e;
+      s.sel[b][lane] = my_e[t];
       s.selw[b][lane] = wv;
-      atomicOr(&s.emask[my_e], 1u << b);
+      atomicOr(&s.emask[my_e[t]], 1u << b);
     }
+  }
+}
+
+// Wave 0: the distinct selected experts, numbered by first appearance in
+// (token, rank) order, with their token masks, expert bases and W13 tensor
+// scales; the rank of every (slot, token); the combine weight of every pair.
+// eb/er: this lane's two (token, rank) entries (lane and lane + 64).
+template <int WTR, int WTS>
+__device__ __forceinline__ void number_slots(const FusedArgs& a, Smem& s, int lane, const int (&eb)[2],
+                                             const int (&er)[2]) {
+  const int nk = a.B * a.k;
+  int nd = 0;
+  int eh[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int i = lane + 64 * h;
+    const bool valid = i < nk;
+    const int b = eb[h], r = er[h];
+    const int e = valid ? s.sel[b][r] : 0;
+    const unsigned mk = valid ? s.emask[e] : 0u;
+    const bool rep = valid && b == __builtin_ctz(mk | 0x80000000u);
+    const unsigned long long bal = __ballot(rep);
+    const int slot = nd + __popcll(bal & ((1ull << lane) - 1ull));
+    if (rep) {
+      s.ids[slot] = e;
+      s.dmask[slot] = mk;
+      s.slotmap[e] = slot;
+      s.xg[slot] = (WTR == WT_NVFP4) ? s.tsr[e][0] : 1.0f;
+      s.pr[slot][0] = 0u;
+      s.pr[slot][1] = 0u;
+    }
+    nd += __popcll(bal);
+    eh[h] = e;
+  }
+  __builtin_amdgcn_wave_barrier();
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int i = lane + 64 * h;
+    if (i < nk) {
+      atomicOr(&s.pr[s.slotmap[eh[h]]][eb[h] >> 2], (uint32_t)er[h] << (8 * (eb[h] & 3)));
+      const float g2 = (WTR == WT_NVFP4) ? s.tsr[eh[h]][1] : 1.0f;
+      s.pw[i] = s.selw[eb[h]][er[h]] * g2;
+    }
+  }
+  for (int i = lane; i < a.B * a.S; i += 64) {
+    const int sh = i / a.B, b = i - sh * a.B;
+    const float g2 = (WTS == WT_NVFP4) ? s.tss[sh][1] : 1.0f;
+    s.pw[nk + i] = s.shc[b][sh] * g2;
+  }
+  if (lane == 0) s.nd = nd;
+}
+
+template <int MK, int TPW, int WTR, int WTS>
+__device__ __forceinline__ void route(const FusedArgs& a, Smem& s, const float* lg, const int (&eb)[2],
+                                      const int (&er)[2]) {
+  const int tid = threadIdx.x, wave = wave_id(), lane = tid & 63;
+  if (wave < a.B) {
+    int my_e[TPW];
+    float my_l[TPW];
+    topk<MK, TPW>(a, lg, lane, my_e, my_l);
+    route_weights<TPW>(a, s, lg, lane, my_e, my_l);
   }
   __syncthreads();
-  if (wave == 0) {
-    const int nk = a.B * a.k;
-    int nd = 0;
-    int eh[2], bh[2], rh[2];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int i = lane + 64 * h;
-      const bool valid = i < nk;
-      const int b = valid ? i / a.k : 0, r = valid ? i - b * a.k : 0;
-      const int e = valid ? s.sel[b][r] : 0;
-      const unsigned mk = valid ? s.emask[e] : 0u;
-      const bool rep = valid && b == __builtin_ctz(mk | 0x80000000u);
-      const unsigned long long bal = __ballot(rep);
-      const int slot = nd + __popcll(bal & ((1ull << lane) - 1ull));
-      if (rep) {
-        s.ids[slot] = e;
-        s.dmask[slot] = mk;
-        s.slotmap[e] = slot;
-      }
-      nd += __popcll(bal);
-      eh[h] = e;
-      bh[h] = b;
-      rh[h] = r;
-    }
-    __builtin_amdgcn_wave_barrier();
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int i = lane + 64 * h;
-      if (i < nk) {
-        s.pr[s.slotmap[eh[h]]][bh[h]] = (unsigned char)rh[h];
-        const float g2 = (WTR == WT_NVFP4) ? s.tsr[eh[h]][1] : 1.0f;
-        s.pw[i] = s.selw[bh[h]][rh[h]] * g2;
-      }
-    }
-    for (int i = lane; i < a.B * a.S; i += 64) {
-      const int sh = i / a.B, b = i - sh * a.B;
-      const float g2 = (WTS == WT_NVFP4) ? s.tss[sh][1] : 1.0f;
-      s.pw[nk + i] = s.shc[b][sh] * g2;
-    }
-    if (lane == 0) s.nd = nd;
-  }
+  if (wave == 0) number_slots<WTR, WTS>(a, s, lane, eb, er);
   if (blockIdx.x == 0) {
     for (int i = tid; i < a.B * a.k; i += NT) {
-      a.topk_ids[i] = s.sel[i / a.k][i % a.k];
-      a.topk_w[i] = s.selw[i / a.k][i % a.k];
+      const int b = i / a.k, r = i - b * a.k;
+      a.topk_ids[i] = s.sel[b][r];
+      a.topk_w[i] = s.selw[b][r];
     }
     for (int i = tid; i < a.B * a.S; i += NT) a.shared_c[i] = s.shc[i / a.S][i % a.S];
   }
@@ -596,53 +760,53 @@ template <int TB, int WTR, int WTS, int P>
 struct Down {
   Tile<WTR> br[P];
   Tile<WTS> bs[(WTR == WTS) ? 1 : P];   // same types: shared tiles use br
-  int t_lo, spg, nsub, sub, nex, nj, ntiles;
+  int t_lo, spg, nsub, lg_nsub, sub, nex, nj, ntiles;
   int cj, cx, nloaded;                 // next tile to load: step index, expert index (mine)
   int qj[P], qx[P];
-  int ri, jj, jc;
-  bool active;
+  LaneGeo L;
 
-  __device__ __forceinline__ void setup(const FusedArgs& a, const Smem& s, int t_lo_, int spg_) {
-    const int wave = wave_id(), lane = threadIdx.x & 63;
-    t_lo = t_lo_;
-    spg = spg_;
-    ri = lane / a.g2.lpr;
-    jj = lane % a.g2.lpr;
-    active = jj < a.g2.cw;
-    jc = active ? jj : 0;
-    const int nexp = a.S + s.nd;
+  // Everything that does not depend on the routing.
+  __device__ __forceinline__ void init(const FusedArgs& a, const LaneGeo& l2) {
+    const int wave = wave_id();
+    const uint32_t w = blockIdx.x;
+    L = l2;
+    t_lo = (int)(((uint32_t)a.g2.nsteps * w) >> a.log2G);
+    spg = (int)(((uint32_t)a.g2.nsteps * (w + 1)) >> a.log2G) - t_lo;
     if (spg >= NW || spg == 0) {
       nsub = 1;
       sub = 0;
       nj = (spg > wave) ? (spg - wave + NW - 1) / NW : 0;
       cj = wave;
     } else {
-      nsub = NW / spg;
+      nsub = (spg == 1) ? 4 : (spg == 2) ? 2 : 1;
       sub = wave / spg;
       nj = (sub < nsub) ? 1 : 0;
       cj = wave % spg;
     }
-    nex = (nexp > sub) ? (nexp - sub + nsub - 1) / nsub : 0;
+    lg_nsub = (nsub == 4) ? 2 : (nsub == 2) ? 1 : 0;
+  }
+  __device__ __forceinline__ void set_experts(int nexp) {
+    nex = (nexp > sub) ? (nexp - sub + nsub - 1) >> lg_nsub : 0;
     ntiles = nj * nex;
     cx = 0;
     nloaded = 0;
   }
   __device__ __forceinline__ int ex_of(int xi) const { return sub + xi * nsub; }
   // Loads the next tile of this wave, or a dummy once they are all loaded.
-  __device__ __forceinline__ void load_next(const FusedArgs& a, const Smem& s, int p) {
+  __device__ __forceinline__ void load_next(const FusedArgs& a, const SlotTab& tb, int p) {
     const bool dm = nloaded >= ntiles;
     const int ex = dm ? 0 : ex_of(cx), t = dm ? t_lo : t_lo + cj;
     const uint8_t* dummy = reinterpret_cast<const uint8_t*>(a.x);
     if (ex < a.S) {
       const uint8_t* c = a.s_codes + (size_t)ex * a.s_code_stride + a.s_w13_code;
-      const uint8_t* sc = (WTS == WT_NVFP4) ? a.s_scales + (size_t)ex * a.s_scale_stride + a.s_w13_scale : nullptr;
-      if constexpr (WTR == WTS) tile_load<WTR>(br[p], c, sc, a.g2, 0, t, ri, jc, dm, dummy);
-      else tile_load<WTS>(bs[p], c, sc, a.g2, 0, t, ri, jc, dm, dummy);
+      const uint8_t* sc = (WTS == WT_NVFP4) ? a.s_scales + (size_t)ex * a.s_scale_stride + a.s_w13_scale : dummy;
+      if constexpr (WTR == WTS) tile_load<WTR>(br[p], c, sc, L, 0, t, dm, dummy);
+      else tile_load<WTS>(bs[p], c, sc, L, 0, t, dm, dummy);
     } else {
-      const int e = min(max(s.ids[min(ex - a.S, kMaxD - 1)], 0), a.E - 1);
+      const int e = tb.expert(min(ex - a.S, kMaxD - 1), a.E);
       const uint8_t* c = a.r_codes + (size_t)e * a.r_code_stride + a.r_w13_code;
-      const uint8_t* sc = (WTR == WT_NVFP4) ? a.r_scales + (size_t)e * a.r_scale_stride + a.r_w13_scale : nullptr;
-      tile_load<WTR>(br[p], c, sc, a.g2, 0, t, ri, jc, dm, dummy);
+      const uint8_t* sc = (WTR == WT_NVFP4) ? a.r_scales + (size_t)e * a.r_scale_stride + a.r_w13_scale : dummy;
+      tile_load<WTR>(br[p], c, sc, L, 0, t, dm, dummy);
     }
     qj[p] = cj;
     qx[p] = cx;
@@ -654,17 +818,18 @@ struct Down {
       }
     }
   }
-  __device__ __forceinline__ void prime(const FusedArgs& a, const Smem& s) {
+  __device__ __forceinline__ void prime(const FusedArgs& a, const SlotTab& tb) {
 #pragma unroll
-    for (int p = 0; p < P; ++p) load_next(a, s, p);
+    for (int p = 0; p < P; ++p) load_next(a, tb, p);
   }
   // hs: activations [pairs][I] bf16 (shared memory).  Results: nsub == 1 ->
   // out directly; else partial sums into red2 [nsub][TB][spg * rpw].
-  __device__ __forceinline__ void run(const FusedArgs& a, const Smem& s, const uint16_t* hs, float* red2) {
+  __device__ __forceinline__ void run(const FusedArgs& a, const SlotTab& tb, const uint16_t* hs, float* red2) {
     float acc[TB];
 #pragma unroll
     for (int b = 0; b < TB; ++b) acc[b] = 0.f;
     const int rpw = a.g2.rpw, lpr = a.g2.lpr;
+    const bool lead = L.jj == lpr - 1;
     for (int base = 0; base < ntiles; base += P) {
 #pragma unroll
       for (int p = 0; p < P; ++p) {
@@ -673,33 +838,33 @@ struct Down {
         const int j = qj[p], xi = qx[p], ex = ex_of(xi), t = t_lo + j;
         if (live) {
           const bool sh = ex < a.S;
-          const int slot = ex - a.S;
-          const unsigned mask = sh ? (1u << a.B) - 1u : s.dmask[slot];
+          const int slot = min(ex - a.S, kMaxD - 1);
+          const unsigned mask = sh ? (1u << a.B) - 1u : tb.tokens(slot);
 #pragma unroll
           for (int b = 0; b < TB; ++b) {
             if ((mask >> b) & 1u) {
-              const int pr = sh ? a.B * a.k + ex * a.B + b : b * a.k + s.pr[slot][b];
+              const int pr = sh ? a.B * a.k + ex * a.B + b : b * a.k + tb.rank(slot, b);
               uint32_t hv[16];
-              lds_chunk(hs + (size_t)pr * a.I + jc * 32, hv);
+              lds_chunk(hs + (size_t)pr * a.I + L.jc * 32, hv);
               float v;
               if constexpr (WTR == WTS) v = tile_dot<WTR>(br[p], t, hv);
               else v = sh ? tile_dot<WTS>(bs[p], t, hv) : tile_dot<WTR>(br[p], t, hv);
-              acc[b] = fmaf(active ? v : 0.f, s.pw[pr], acc[b]);
+              acc[b] = fmaf(L.active ? v : 0.f, tb.weight(pr), acc[b]);
             }
           }
         }
         __asm__ volatile("" ::: "memory");
-        load_next(a, s, p);   // unconditional, see GateUp::run
+        load_next(a, tb, p);   // unconditional, see GateUp::run
         if (live && xi == nex - 1) {
           // step complete: reduce each token's row sums over the row's lanes
 #pragma unroll
           for (int b = 0; b < TB; ++b) {
             if (b < a.B) {
-              const float v = lane_reduce(acc[b], lpr);
-              if (jj == 0) {
-                const int rl = j * rpw + ri;
+              const float v = group_sum(acc[b], lpr);
+              if (lead) {
+                const int rl = j * rpw + L.ri;
                 if (nsub == 1) {
-                  const int row = t * rpw + ri;
+                  const int row = t * rpw + L.ri;
                   float o = v;
                   if (a.residual) o += bf16lo(a.x[(size_t)b * a.H + row]);
                   a.out[(size_t)b * a.H + row] = (uint16_t)f2bf(o);
@@ -741,7 +906,7 @@ __global__ __launch_bounds__(NT) void k_fused_layer(FusedArgs a) {
   float* part = reinterpret_cast<float*>(dyn + (size_t)TB * a.H * 2); // gate/up partials (ns > 1)
   float* red2 = reinterpret_cast<float*>(dyn + a.lds_act);            // down partial sums (nsub > 1)
 
-  // ---- loads that need nothing: call counter, router rows, x, gamma, tensor scales, shared tiles
+  // ---- loads that need nothing: call counter, router rows, x, gamma, bias, tensor scales
   const uint32_t epoch = __hip_atomic_load(a.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   const int U = a.H / 8;                       // 16-byte units per row
   const int nrr = (w + G < a.Er) ? 2 : 1;      // router rows of this workgroup
@@ -763,7 +928,6 @@ __global__ __launch_bounds__(NT) void k_fused_layer(FusedArgs a) {
 #pragma unroll
     for (int q = 0; q < QX; ++q) gv[q] = ld16(gsrc + (size_t)min(tid + q * NT, U - 1) * 8);
   }
-  // router bias of this workgroup's rows (unconditional: clamped row, x as a stand-in)
   float biasv[2];
   {
     const float* bsrc = a.bias != nullptr ? a.bias : reinterpret_cast<const float*>(a.x);
@@ -771,20 +935,35 @@ __global__ __launch_bounds__(NT) void k_fused_layer(FusedArgs a) {
     for (int rr = 0; rr < 2; ++rr) biasv[rr] = bsrc[a.bias != nullptr ? min(w + rr * G, a.E - 1) : 0];
   }
   // tensor scales for the shared-memory tables (loaded unconditionally from
-  // clamped addresses so that no load depends on a condition)
+  // clamped addresses so that no load depends on a condition; a layer
+  // without shared experts has no shared buffer: x stands in)
   const int nts = (WTR == WT_NVFP4 && a.r_tscale != nullptr) ? 2 * a.E : 0;
   const float* tsr_src = (WTR == WT_NVFP4 && a.r_tscale != nullptr) ? a.r_tscale : reinterpret_cast<const float*>(a.x);
-  // (a layer without shared experts has no shared buffer: x stands in)
   const float* tss_src = (WTS == WT_NVFP4 && a.S > 0 && a.s_tscale != nullptr)
                              ? a.s_tscale : reinterpret_cast<const float*>(a.x);
   float tsv[2];
 #pragma unroll
   for (int h = 0; h < 2; ++h) tsv[h] = tsr_src[min(tid + h * NT, max(nts, 1) - 1)];
   const float tss = tss_src[min(tid, max(2 * a.S, 1) - 1)];
+
+  // ---- set-up that needs no data (overlaps the loads above) -------------------
+  const LaneGeo L13 = lane_geo(a.g13, lane), L2 = lane_geo(a.g2, lane);
+  int eb[2], er[2];   // (token, rank) of this lane's routing entries lane, lane + 64
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int i = lane + 64 * h;
+    eb[h] = min(i / a.k, MOE_MAX_BATCH - 1);
+    er[h] = i - (i / a.k) * a.k;
+  }
+  Down<TB, WTR, WTS, down_depth<TB, WTR, WTS>()> down;
+  down.init(a, L2);
   const int gs2 = a.I / a.g13.rpw / 2;
+  SlotTab tab = {};   // filled after routing
+  // the shared experts' tiles need no routing: they load from the start
   GateUp<TB, WTS, gu_depth<WTS>()> gus;
-  gus.setup(a, 1, a.S * gs2, w, G);
-  gus.prime(a, s);     // shared experts' tiles (their addresses need no shared-memory table)
+  gus.init(a, L13, 1);
+  gus.set_items(a, a.S * gs2);
+  gus.prime(a, tab);
 
   // ---- pre-norm: xhat = bf16(x / rms(x) * gamma) -----------------------------
   if (a.prenorm) {
@@ -803,7 +982,7 @@ __global__ __launch_bounds__(NT) void k_fused_layer(FusedArgs a) {
           }
         }
       }
-      ss = lane_reduce(ss, 64);
+      ss = wave_sum(ss);
       if (lane == 0) s.red[wave][0][b] = ss;
     }
     __syncthreads();
@@ -818,13 +997,11 @@ __global__ __launch_bounds__(NT) void k_fused_layer(FusedArgs a) {
       const float rn = s.rn[b];
 #pragma unroll
       for (int q = 0; q < QX; ++q) {
-        {
-          uint4& v = xv[b][q];
-          v.x = norm_pair(v.x, gv[q].x, rn);
-          v.y = norm_pair(v.y, gv[q].y, rn);
-          v.z = norm_pair(v.z, gv[q].z, rn);
-          v.w = norm_pair(v.w, gv[q].w, rn);
-        }
+        uint4& v = xv[b][q];
+        v.x = norm_pair(v.x, gv[q].x, rn);
+        v.y = norm_pair(v.y, gv[q].y, rn);
+        v.z = norm_pair(v.z, gv[q].z, rn);
+        v.w = norm_pair(v.w, gv[q].w, rn);
       }
     }
   }
@@ -856,9 +1033,9 @@ __global__ __launch_bounds__(NT) void k_fused_layer(FusedArgs a) {
             }
           }
         }
-        racc[rr][b] = (rr < nrr) ? lane_reduce(v, 64) : 0.f;
+        racc[rr][b] = (rr < nrr) ? group_sum(v, 64) : 0.f;
       }
-    if (lane == 0)
+    if (lane == 63)
 #pragma unroll
       for (int rr = 0; rr < 2; ++rr)
 #pragma unroll
@@ -870,6 +1047,7 @@ __global__ __launch_bounds__(NT) void k_fused_layer(FusedArgs a) {
     if (i < nts) (&s.tsr[0][0])[i] = tsv[h];
   }
   if (WTS == WT_NVFP4 && tid < 2 * a.S) (&s.tss[0][0])[tid] = tss;
+  for (int e = tid; e < a.E; e += NT) s.emask[e] = 0u;
   if (tid == 0) s.tag = epoch + 1u;
   __syncthreads();
   const uint32_t tag = s.tag;
@@ -882,33 +1060,35 @@ __global__ __launch_bounds__(NT) void k_fused_layer(FusedArgs a) {
     publish(a.xlog + (size_t)row * kLogitLine + b, __float_as_uint(v), tag);
   }
 
-  // ---- first poll of the logits, shared experts' gate/up, rest of the logits ----
+  // ---- shared experts' gate/up while the logits travel -------------------------
   uint32_t xr[TB][16];
-  load_xr<TB>(a, act, xr);
+  load_xr<TB>(a, L13, act, xr);
   auto laddr = [&](int i) { return a.xlog + (size_t)(i / a.B) * kLogitLine + (i % a.B); };
   Gather<2 * TB> lgat;
   lgat.issue(0, a.Er * a.B, laddr);
-  gus.run(a, s, xr, part, tag);
+  gus.run(a, s, tab, xr, part, tag);
   lgat.finish(tag, deadline, a.err, kErrLogitWait, laddr,
               [&](int i, uint32_t v) { lg[(i % a.B) * a.Er + i / a.B] = __uint_as_float(v); });
   __syncthreads();
   if (w == 0 && tid == 0) __hip_atomic_store(a.epoch, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
   // ---- routing ---------------------------------------------------------------------
-  route<WTR, WTS>(a, s, lg);
+  constexpr int TPW = (TB > NW) ? 2 : 1;
+  if (a.E <= 64) route<1, TPW, WTR, WTS>(a, s, lg, eb, er);
+  else if (a.E <= 256) route<4, TPW, WTR, WTS>(a, s, lg, eb, er);
+  else route<8, TPW, WTR, WTS>(a, s, lg, eb, er);
 
   // ---- phase 2: selected experts' gate/up; the down weights start loading ------------
-  const int nsteps2 = a.g2.nsteps;
-  const int t_lo = (int)((long long)nsteps2 * w / G);
-  const int t_hi = (int)((long long)nsteps2 * (w + 1) / G);
-  Down<TB, WTR, WTS, down_depth<TB, WTR, WTS>()> down;
-  down.setup(a, s, t_lo, t_hi - t_lo);
+  tab.load(s, lane);
+  const int nd = s.nd;
+  down.set_experts(a.S + nd);
   {
     GateUp<TB, WTR, gu_depth<WTR>()> gur;
-    gur.setup(a, 0, s.nd * gs2, w, G);
-    gur.prime(a, s);
-    down.prime(a, s);
-    gur.run(a, s, xr, part, tag);
+    gur.init(a, L13, 0);
+    gur.set_items(a, nd * gs2);
+    gur.prime(a, tab);
+    down.prime(a, tab);
+    gur.run(a, s, tab, xr, part, tag);
   }
 
   // ---- phase 3: gather activations, down GEMV + combine ---------------------------------
@@ -935,16 +1115,16 @@ __global__ __launch_bounds__(NT) void k_fused_layer(FusedArgs a) {
         });
   }
   __syncthreads();
-  down.run(a, s, act, red2);
+  down.run(a, tab, act, red2);
   if (down.nsub > 1) {
     __syncthreads();
-    const int rows = (t_hi - t_lo) * a.g2.rpw;
+    const int rows = down.spg * a.g2.rpw;
     const int nsub = down.nsub;
     for (int i = tid; i < a.B * rows; i += NT) {
       const int b = i / rows, r = i - b * rows;
       float v = 0.f;
       for (int u = 0; u < nsub; ++u) v += red2[(u * TB + b) * rows + r];
-      const int row = t_lo * a.g2.rpw + r;
+      const int row = down.t_lo * a.g2.rpw + r;
       if (a.residual) v += bf16lo(a.x[(size_t)b * a.H + row]);
       a.out[(size_t)b * a.H + row] = (uint16_t)f2bf(v);
     }

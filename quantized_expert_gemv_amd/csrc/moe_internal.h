@@ -73,6 +73,31 @@ MOE_HD inline size_t bf16_unit(const MatGeom& g, int s, int t, int sub, int ri, 
   return (((size_t)s * g.nsteps + t) * 4 + sub) * g.su + (size_t)ri * g.cw + j;
 }
 
+// Unsigned division by a divisor fixed per layer, as a multiply-high, an add
+// and a shift (round-up method of Granlund and Montgomery):
+// q = (mulhi(n, m) + n) >> s with s = ceil(log2 d), m = floor(2^32 (2^s - d) / d) + 1.
+// Exact for n < 2^31 (the add stays in 32 bits); moe_layer_create checks
+// every divisor it sets up over all n < 2^22.
+struct FastDiv {
+  uint32_t m, s;
+};
+MOE_HD inline FastDiv make_fastdiv(uint32_t d) {
+  uint32_t s = 0;
+  while ((1ull << s) < d) ++s;
+  FastDiv f;
+  f.m = (uint32_t)(((((unsigned long long)1 << s) - d) << 32) / d + 1);
+  f.s = s;
+  return f;
+}
+MOE_HD inline uint32_t fastdiv(uint32_t n, FastDiv f) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  const uint32_t t = __umulhi(n, f.m);
+#else
+  const uint32_t t = (uint32_t)(((unsigned long long)n * f.m) >> 32);
+#endif
+  return (t + n) >> f.s;
+}
+
 // ---------------------------------------------------------------------------
 // single-launch layer kernel
 // ---------------------------------------------------------------------------
@@ -118,7 +143,9 @@ struct FusedArgs {
   size_t r_code_stride, r_w13_code, r_scale_stride, r_w13_scale;
   size_t s_code_stride, s_w13_code, s_scale_stride, s_w13_scale;
   // plan
-  int G;                           // workgroups; all must be resident at once
+  int G;                           // workgroups (a power of two); all must be resident at once
+  int log2G;
+  FastDiv dv_gs2;                  // division by the gate/up step pairs of a matrix
   int lds_act;                     // bytes of the activation region (x, then h)
   int lds_acc;                     // bytes of the down-GEMV partial sums
   int spg_max;                     // most down-GEMV steps a workgroup owns
