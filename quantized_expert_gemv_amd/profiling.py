@@ -33,7 +33,9 @@ def src_digest() -> str:
 
 
 def short_name(kernel: str) -> str:
-    k = kernel.split("(")[0]
+    """Demangled kernel name without return type, argument list and anonymous namespace."""
+    k = kernel.replace("(anonymous namespace)::", "")
+    k = k.split("(")[0]
     return k.replace("void ", "").strip()
 
 
