@@ -258,7 +258,8 @@ int moe_layer_create(const moe_layer_desc* desc, moe_layer_t* out) {
   for (int tb = 1; tb <= p.tbmax; tb *= 2) {
     int occ = 0;
     const int ti = tb_index(tb);
-    if (moe::fused_occupancy(tb, moe::fused_qx(desc->hidden), rwt, swt, p.lds_act[ti] + p.lds_acc[ti], &occ) != 0 ||
+    const int shape = moe::fixed_shape_of(desc->hidden, desc->inter, desc->n_routed, desc->top_k, desc->n_shared, p.Er);
+    if (moe::fused_occupancy(shape, tb, moe::fused_qx(desc->hidden), rwt, swt, p.lds_act[ti] + p.lds_acc[ti], &occ) != 0 ||
         occ < 1) {
       (void)hipGetLastError();
       return MOE_ERR_UNSUPPORTED;

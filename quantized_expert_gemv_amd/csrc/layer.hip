@@ -262,7 +262,7 @@ struct LaneGeo {
 };
 
 // ns == 1: a step covers rpw rows of lpr lanes; ns > 1: one row, lane = chunk.
-__device__ __forceinline__ LaneGeo lane_geo(const MatGeom& g, int lane) {
+__device__ __forceinline__ LaneGeo lane_geo(const MatGeom g, int lane) {
   LaneGeo L;
   L.su16 = (uint32_t)g.su * 16u;
   L.su4 = (uint32_t)g.su * 4u;
@@ -410,7 +410,8 @@ struct GateUp {
   LaneGeo L;
 
   // Everything that does not depend on the routing.
-  __device__ __forceinline__ void init(const FusedArgs& a, const LaneGeo& lg13, int shared_) {
+  template <class A>
+  __device__ __forceinline__ void init(const A& a, const LaneGeo& lg13, int shared_) {
     const int wave = wave_id();
     L = lg13;
     shared = shared_;
@@ -423,7 +424,8 @@ struct GateUp {
     sl = wave - grp * ns;
   }
   // The phase's item count n (items of the block are contiguous).
-  __device__ __forceinline__ void set_items(const FusedArgs& a, int n) {
+  template <class A>
+  __device__ __forceinline__ void set_items(const A& a, int n) {
     const uint32_t w = blockIdx.x;
     lo = (int)(((uint32_t)n * w) >> a.log2G);
     hi = (int)(((uint32_t)n * (w + 1)) >> a.log2G);
@@ -433,7 +435,8 @@ struct GateUp {
     cslot = (int)fastdiv((uint32_t)first, a.dv_gs2);
     ct2 = first - cslot * gs2;
   }
-  __device__ __forceinline__ void bases(const FusedArgs& a, const SlotTab& tb, int slot, const uint8_t*& c,
+  template <class A>
+  __device__ __forceinline__ void bases(const A& a, const SlotTab& tb, int slot, const uint8_t*& c,
                                         const uint8_t*& sc) const {
     if (shared) {
       // a layer without shared experts has no shared buffer: x stands in (its
@@ -448,7 +451,8 @@ struct GateUp {
     }
   }
   // Loads the next item of this wave, or a dummy once they are all loaded.
-  __device__ __forceinline__ void load_next(const FusedArgs& a, const SlotTab& tb, int p) {
+  template <class A>
+  __device__ __forceinline__ void load_next(const A& a, const SlotTab& tb, int p) {
     const bool dm = nloaded >= nmine;
     const uint8_t *c, *sc;
     bases(a, tb, cslot, c, sc);
@@ -464,16 +468,47 @@ struct GateUp {
       }
     }
   }
-  __device__ __forceinline__ void prime(const FusedArgs& a, const SlotTab& tb) {
+  template <class A>
+  __device__ __forceinline__ void prime(const A& a, const SlotTab& tb) {
 #pragma unroll
     for (int p = 0; p < PI; ++p) load_next(a, tb, p);
   }
-  // part: TB * 4 * ns floats per item of the block (ns > 1 only).
-  __device__ __forceinline__ void run(const FusedArgs& a, const Smem& s, const SlotTab& tb, const uint32_t (&xr)[TB][16],
-                                      float* part, uint32_t tag) {
-    const int I2 = a.I / 2;
-    const int lpr = a.g13.lpr;
-    const bool lead = L.jj == ((ns == 1) ? lpr - 1 : 63);
+  // One token's share of an item: dot products, lane reduction, then the
+  // SiLU*up word (ns == 1) or the slice partials (ns > 1).  v holds the four
+  // lane partials (gate t, gate t+1, up t, up t+1).
+  template <class A>
+  __device__ __forceinline__ void finish_token(const A& a, const SlotTab& tb, float (&v)[4], int slot, int t2,
+                                               int b, float g13, bool lead, float* part, uint32_t tag) const {
+    if (!L.active) v[0] = v[1] = v[2] = v[3] = 0.f;
+    if (ns == 1) {
+      // the table lookup is a cross-lane read: it stays out of the
+      // lane-conditional code below, where other lanes are inactive
+      const int pr = shared ? a.B * a.k + slot * a.B + b : b * a.k + tb.rank(slot, b);
+      const int lpr = a.g13.lpr;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) v[c] = group_sum(v[c], lpr);
+      if (lead) {
+        const float h0 = silu_mul(v[0] * g13, v[2] * g13);
+        const float h1 = silu_mul(v[1] * g13, v[3] * g13);
+        publish(a.xh + (size_t)pr * (a.I / 2) + t2 * a.g13.rpw + L.ri, f2bf(h0) | (f2bf(h1) << 16), tag);
+      }
+    } else {
+      const int il = slot * gs2 + t2 - lo;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const float sum = group_sum(v[c], 64);
+        if (lead) part[((il * TB + b) * 4 + c) * ns + sl] = sum;
+      }
+    }
+  }
+  // xr: the tokens' activation chunks in registers (TB <= 2); otherwise each
+  // token's chunk is read from shared memory (xs + b H + xcol) per item, which
+  // leaves registers for more items in flight.  part: TB * 4 * ns floats per
+  // item of the block (ns > 1 only).
+  template <int XR, class A>
+  __device__ __forceinline__ void run(const A& a, const Smem& s, const SlotTab& tb, const uint32_t (&xr)[XR][16],
+                                      const uint16_t* xs, int xcol, float* part, uint32_t tag) {
+    const bool lead = L.jj == ((ns == 1) ? a.g13.lpr - 1 : 63);
     for (int base = 0; base < nmine; base += PI) {
 #pragma unroll
       for (int p = 0; p < PI; ++p) {
@@ -481,48 +516,39 @@ struct GateUp {
         const bool live = i < nmine;   // uniform
         const int slot = qslot[p], t2 = qt2[p];
         const unsigned mask = shared ? (1u << a.B) - 1u : tb.tokens(min(slot, kMaxD - 1));
-        float v[TB][4];
-        if (live) {
+        const float g13 = shared ? ((WT == WT_NVFP4) ? s.tss[min(slot, MOE_MAX_SHARED - 1)][0] : 1.0f)
+                                 : tb.w13(min(slot, kMaxD - 1));
+        if constexpr (XR == TB) {
+          float v[TB][4];
+          if (live) {
 #pragma unroll
-          for (int b = 0; b < TB; ++b) {
-            if ((mask >> b) & 1u) {
-              quad_dot<WT>(q[p], xr[b], v[b]);
-              if (!L.active) v[b][0] = v[b][1] = v[b][2] = v[b][3] = 0.f;
+            for (int b = 0; b < TB; ++b)
+              if ((mask >> b) & 1u) quad_dot<WT>(q[p], xr[b], v[b]);
+          }
+          // The buffer is free only now.  Its reload is unconditional (a dummy
+          // past the end) and kept below the reads: a conditional or hoisted
+          // reload would make the compiler copy registers and wait for every
+          // load in flight.
+          __asm__ volatile("" ::: "memory");
+          load_next(a, tb, p);
+          if (live) {
+#pragma unroll
+            for (int b = 0; b < TB; ++b)
+              if ((mask >> b) & 1u) finish_token(a, tb, v[b], slot, t2, b, g13, lead, part, tag);
+          }
+        } else {
+          if (live) {
+            for (unsigned m = mask; m != 0u; m &= m - 1u) {   // uniform loop over the item's tokens
+              const int b = __builtin_ctz(m);
+              uint32_t xb[16];
+              lds_chunk(xs + (size_t)b * a.H + xcol, xb);
+              float v[4];
+              quad_dot<WT>(q[p], xb, v);
+              finish_token(a, tb, v, slot, t2, b, g13, lead, part, tag);
             }
           }
-        }
-        // The buffer is free only now.  Its reload is unconditional (a dummy
-        // past the end) and kept below the reads: a conditional or hoisted
-        // reload would make the compiler copy registers and wait for every
-        // load in flight.
-        __asm__ volatile("" ::: "memory");
-        load_next(a, tb, p);
-        if (live) {
-          const float g13 = shared ? ((WT == WT_NVFP4) ? s.tss[min(slot, MOE_MAX_SHARED - 1)][0] : 1.0f)
-                                   : tb.w13(min(slot, kMaxD - 1));
-#pragma unroll
-          for (int b = 0; b < TB; ++b) {
-            if (!((mask >> b) & 1u)) continue;
-            if (ns == 1) {
-              // the table lookup is a cross-lane read: it stays out of the
-              // lane-conditional code below, where other lanes are inactive
-              const int pr = shared ? a.B * a.k + slot * a.B + b : b * a.k + tb.rank(slot, b);
-#pragma unroll
-              for (int c = 0; c < 4; ++c) v[b][c] = group_sum(v[b][c], lpr);
-              if (lead) {
-                const float h0 = silu_mul(v[b][0] * g13, v[b][2] * g13);
-                const float h1 = silu_mul(v[b][1] * g13, v[b][3] * g13);
-                publish(a.xh + (size_t)pr * I2 + t2 * a.g13.rpw + L.ri, f2bf(h0) | (f2bf(h1) << 16), tag);
-              }
-            } else {
-              const int il = slot * gs2 + t2 - lo;
-#pragma unroll
-              for (int c = 0; c < 4; ++c) {
-                const float sum = group_sum(v[b][c], 64);
-                if (lead) part[((il * TB + b) * 4 + c) * ns + sl] = sum;
-              }
-            }
-          }
+          __asm__ volatile("" ::: "memory");
+          load_next(a, tb, p);
         }
       }
     }
@@ -546,19 +572,22 @@ struct GateUp {
         const float h1 = silu_mul(v[1] * g13, v[3] * g13);
         const int pr = shared ? a.B * a.k + slot * a.B + b
                               : b * a.k + (int)((s.pr[slot][b >> 2] >> (8 * (b & 3))) & 0xffu);
-        publish(a.xh + (size_t)pr * I2 + t2, f2bf(h0) | (f2bf(h1) << 16), tag);
+        publish(a.xh + (size_t)pr * (a.I / 2) + t2, f2bf(h0) | (f2bf(h1) << 16), tag);
       }
     }
   }
 };
 
-// This lane's activation chunk(s) from the x region of shared memory.
-template <int TB>
-__device__ __forceinline__ void load_xr(const FusedArgs& a, const LaneGeo& L, const uint16_t* xs,
-                                        uint32_t (&xr)[TB][16]) {
-  const int col = ((a.g13.ns == 1) ? L.jc : (wave_id() % a.g13.ns) * a.g13.cw + L.jc) * 32;
+// This lane's column (element offset) of the activation row for the gate/up
+// tiles, and the chunks of the first XR tokens from the x region of shared memory.
+template <class A>
+__device__ __forceinline__ int x_col(const A& a, const LaneGeo& L) {
+  return ((a.g13.ns == 1) ? L.jc : (wave_id() % a.g13.ns) * a.g13.cw + L.jc) * 32;
+}
+template <int XR, class A>
+__device__ __forceinline__ void load_xr(const A& a, int col, const uint16_t* xs, uint32_t (&xr)[XR][16]) {
 #pragma unroll
-  for (int b = 0; b < TB; ++b) lds_chunk(xs + (size_t)min(b, a.B - 1) * a.H + col, xr[b]);
+  for (int b = 0; b < XR; ++b) lds_chunk(xs + (size_t)min(b, a.B - 1) * a.H + col, xr[b]);
 }
 
 // ---------------------------------------------------------------------------
@@ -585,8 +614,8 @@ __device__ __forceinline__ void cas(unsigned& ka, int& ia, unsigned& kb, int& ib
 // wins (ties to the lowest lane, i.e. the lowest expert), the winning lane
 // shifts its list; the lanes' chains for the TPW tokens are independent.
 // Lane r ends with the r-th selection: expert my_e, logit my_l.
-template <int MK, int TPW>
-__device__ __forceinline__ void topk(const FusedArgs& a, const float* lg, int lane, int (&my_e)[TPW],
+template <int MK, int TPW, class A>
+__device__ __forceinline__ void topk(const A& a, const float* lg, int lane, int (&my_e)[TPW],
                                      float (&my_l)[TPW]) {
   const int wave = wave_id();
   unsigned key[TPW][MK];
@@ -641,8 +670,8 @@ __device__ __forceinline__ void topk(const FusedArgs& a, const float* lg, int la
 
 // Routing weights and shared coefficients of the TPW tokens (wave + t NW),
 // into shared memory, with the token masks of the selected experts.
-template <int TPW>
-__device__ __forceinline__ void route_weights(const FusedArgs& a, Smem& s, const float* lg, int lane,
+template <int TPW, class A>
+__device__ __forceinline__ void route_weights(const A& a, Smem& s, const float* lg, int lane,
                                               const int (&my_e)[TPW], const float (&my_l)[TPW]) {
   const int wave = wave_id();
 #pragma unroll
@@ -677,8 +706,8 @@ __device__ __forceinline__ void route_weights(const FusedArgs& a, Smem& s, const
 // (token, rank) order, with their token masks, expert bases and W13 tensor
 // scales; the rank of every (slot, token); the combine weight of every pair.
 // eb/er: this lane's two (token, rank) entries (lane and lane + 64).
-template <int WTR, int WTS>
-__device__ __forceinline__ void number_slots(const FusedArgs& a, Smem& s, int lane, const int (&eb)[2],
+template <int WTR, int WTS, class A>
+__device__ __forceinline__ void number_slots(const A& a, Smem& s, int lane, const int (&eb)[2],
                                              const int (&er)[2]) {
   const int nk = a.B * a.k;
   int nd = 0;
@@ -722,8 +751,8 @@ __device__ __forceinline__ void number_slots(const FusedArgs& a, Smem& s, int la
   if (lane == 0) s.nd = nd;
 }
 
-template <int MK, int TPW, int WTR, int WTS>
-__device__ __forceinline__ void route(const FusedArgs& a, Smem& s, const float* lg, const int (&eb)[2],
+template <int MK, int TPW, int WTR, int WTS, class A>
+__device__ __forceinline__ void route(const A& a, Smem& s, const float* lg, const int (&eb)[2],
                                       const int (&er)[2]) {
   const int tid = threadIdx.x, wave = wave_id(), lane = tid & 63;
   if (wave < a.B) {
@@ -766,7 +795,8 @@ struct Down {
   LaneGeo L;
 
   // Everything that does not depend on the routing.
-  __device__ __forceinline__ void init(const FusedArgs& a, const LaneGeo& l2) {
+  template <class A>
+  __device__ __forceinline__ void init(const A& a, const LaneGeo& l2) {
     const int wave = wave_id();
     const uint32_t w = blockIdx.x;
     L = l2;
@@ -793,7 +823,8 @@ struct Down {
   }
   __device__ __forceinline__ int ex_of(int xi) const { return sub + xi * nsub; }
   // Loads the next tile of this wave, or a dummy once they are all loaded.
-  __device__ __forceinline__ void load_next(const FusedArgs& a, const SlotTab& tb, int p) {
+  template <class A>
+  __device__ __forceinline__ void load_next(const A& a, const SlotTab& tb, int p) {
     const bool dm = nloaded >= ntiles;
     const int ex = dm ? 0 : ex_of(cx), t = dm ? t_lo : t_lo + cj;
     const uint8_t* dummy = reinterpret_cast<const uint8_t*>(a.x);
@@ -818,13 +849,15 @@ struct Down {
       }
     }
   }
-  __device__ __forceinline__ void prime(const FusedArgs& a, const SlotTab& tb) {
+  template <class A>
+  __device__ __forceinline__ void prime(const A& a, const SlotTab& tb) {
 #pragma unroll
     for (int p = 0; p < P; ++p) load_next(a, tb, p);
   }
   // hs: activations [pairs][I] bf16 (shared memory).  Results: nsub == 1 ->
   // out directly; else partial sums into red2 [nsub][TB][spg * rpw].
-  __device__ __forceinline__ void run(const FusedArgs& a, const SlotTab& tb, const uint16_t* hs, float* red2) {
+  template <class A>
+  __device__ __forceinline__ void run(const A& a, const SlotTab& tb, const uint16_t* hs, float* red2) {
     float acc[TB];
 #pragma unroll
     for (int b = 0; b < TB; ++b) acc[b] = 0.f;
@@ -886,22 +919,21 @@ struct Down {
 // ---------------------------------------------------------------------------
 
 // Items (gate/up) and tiles (down) in flight per wave.
-template <int WT> constexpr int gu_depth() { return WT == WT_NVFP4 ? 2 : 1; }
+template <int TB, int WT> constexpr int gu_depth() { return WT == WT_NVFP4 ? (TB <= 2 ? 2 : 4) : (TB <= 2 ? 1 : 2); }
 template <int TB, int WTR, int WTS> constexpr int down_depth() {
   return (WTR == WT_NVFP4 && WTS == WT_NVFP4) ? (TB >= 8 ? 4 : 6) : 3;
 }
 
 // QX: 16-byte units of a router row per thread (H <= QX * NT * 8); the host
 // picks the smallest that fits, so every one of them is a real load.
-template <int TB, int QX, int WTR, int WTS>
-__global__ __launch_bounds__(NT) void k_fused_layer(FusedArgs a) {
+template <int TB, int QX, int WTR, int WTS, class A>
+__global__ __launch_bounds__(NT) void k_fused_layer(A a) {
   extern __shared__ __align__(16) unsigned char dyn[];
   __shared__ Smem s;
   __shared__ float lg[TB * MOE_MAX_ROUTED];
 
   const int tid = threadIdx.x, wave = wave_id(), lane = tid & 63;
   const int w = blockIdx.x, G = a.G;
-  const u64 deadline = clock100() + a.wait_ticks;
   uint16_t* act = reinterpret_cast<uint16_t*>(dyn);                  // x (phases 1-2), h (phase 3)
   float* part = reinterpret_cast<float*>(dyn + (size_t)TB * a.H * 2); // gate/up partials (ns > 1)
   float* red2 = reinterpret_cast<float*>(dyn + a.lds_act);            // down partial sums (nsub > 1)
@@ -960,7 +992,7 @@ __global__ __launch_bounds__(NT) void k_fused_layer(FusedArgs a) {
   const int gs2 = a.I / a.g13.rpw / 2;
   SlotTab tab = {};   // filled after routing
   // the shared experts' tiles need no routing: they load from the start
-  GateUp<TB, WTS, gu_depth<WTS>()> gus;
+  GateUp<TB, WTS, gu_depth<TB, WTS>()> gus;
   gus.init(a, L13, 1);
   gus.set_items(a, a.S * gs2);
   gus.prime(a, tab);
@@ -1048,7 +1080,7 @@ __global__ __launch_bounds__(NT) void k_fused_layer(FusedArgs a) {
   }
   if (WTS == WT_NVFP4 && tid < 2 * a.S) (&s.tss[0][0])[tid] = tss;
   for (int e = tid; e < a.E; e += NT) s.emask[e] = 0u;
-  if (tid == 0) s.tag = epoch + 1u;
+  if (tid == 0) s.tag = (epoch + 1u == 0u) ? 1u : epoch + 1u;   // tag 0 marks never-written words
   __syncthreads();
   const uint32_t tag = s.tag;
   if (tid < nrr * a.B) {
@@ -1061,12 +1093,17 @@ __global__ __launch_bounds__(NT) void k_fused_layer(FusedArgs a) {
   }
 
   // ---- shared experts' gate/up while the logits travel -------------------------
-  uint32_t xr[TB][16];
-  load_xr<TB>(a, L13, act, xr);
+  constexpr int XR = (TB <= 2) ? TB : 1;   // activation chunks held in registers
+  const int xcol = x_col(a, L13);
+  uint32_t xr[XR][16];
+  load_xr<XR>(a, xcol, act, xr);
   auto laddr = [&](int i) { return a.xlog + (size_t)(i / a.B) * kLogitLine + (i % a.B); };
   Gather<2 * TB> lgat;
   lgat.issue(0, a.Er * a.B, laddr);
-  gus.run(a, s, tab, xr, part, tag);
+  gus.run(a, s, tab, xr, act, xcol, part, tag);
+  // every wait ends by this time (measured from here, not from the start:
+  // the bound is not needed before the first wait)
+  const u64 deadline = clock100() + a.wait_ticks;
   lgat.finish(tag, deadline, a.err, kErrLogitWait, laddr,
               [&](int i, uint32_t v) { lg[(i % a.B) * a.Er + i / a.B] = __uint_as_float(v); });
   __syncthreads();
@@ -1083,12 +1120,12 @@ __global__ __launch_bounds__(NT) void k_fused_layer(FusedArgs a) {
   const int nd = s.nd;
   down.set_experts(a.S + nd);
   {
-    GateUp<TB, WTR, gu_depth<WTR>()> gur;
+    GateUp<TB, WTR, gu_depth<TB, WTR>()> gur;
     gur.init(a, L13, 0);
     gur.set_items(a, nd * gs2);
     gur.prime(a, tab);
     down.prime(a, tab);
-    gur.run(a, s, tab, xr, part, tag);
+    gur.run(a, s, tab, xr, act, xcol, part, tag);
   }
 
   // ---- phase 3: gather activations, down GEMV + combine ---------------------------------
@@ -1161,60 +1198,85 @@ __global__ __launch_bounds__(NT) void k_fused_debug_h(FusedArgs a, uint16_t* h_r
 // launch
 // ---------------------------------------------------------------------------
 
-template <int TB, int QX, int WTR, int WTS>
-static const void* fused_fn() {
-  return reinterpret_cast<const void*>(&k_fused_layer<TB, QX, WTR, WTS>);
+// One compiled variant of the layer kernel: layer shape (fixed or read from
+// the arguments), batch bucket, router units per thread, weight types.
+template <class SH, int TB, int QX, int WTR, int WTS>
+struct Variant {
+  static constexpr int BF = (TB <= 2) ? TB : 0;   // buckets 1 and 2 hold exactly TB tokens
+  using Args = KArgs<SH, BF>;
+  static const void* fn() { return reinterpret_cast<const void*>(&k_fused_layer<TB, QX, WTR, WTS, Args>); }
+  static int launch(const FusedArgs& f, hipStream_t st) {
+    Args k = kargs_of<SH, BF>(f);
+    void* args[] = {&k};
+    return (int)hipLaunchKernel(fn(), dim3(f.G), dim3(NT), args, (size_t)fused_lds_bytes(f), st);
+  }
+};
+template <class T> struct Tag { using type = T; };
+constexpr int kNoVariant = (int)hipErrorInvalidValue;
+
+template <class SH, int TB, int QX, class F>
+static int by_wtype(int rwt, int swt, F&& f) {
+  if (rwt == WT_NVFP4 && swt == WT_NVFP4) return f(Tag<Variant<SH, TB, QX, WT_NVFP4, WT_NVFP4>>{});
+  if (rwt == WT_BF16 && swt == WT_BF16) return f(Tag<Variant<SH, TB, QX, WT_BF16, WT_BF16>>{});
+  if constexpr (std::is_same<SH, DynShape>::value)
+    if (rwt == WT_NVFP4 && swt == WT_BF16) return f(Tag<Variant<SH, TB, QX, WT_NVFP4, WT_BF16>>{});
+  return kNoVariant;
 }
 
-template <int TB, int QX>
-static const void* fused_fn_wt(int rwt, int swt) {
-  if (rwt == WT_NVFP4 && swt == WT_NVFP4) return fused_fn<TB, QX, WT_NVFP4, WT_NVFP4>();
-  if (rwt == WT_BF16 && swt == WT_BF16) return fused_fn<TB, QX, WT_BF16, WT_BF16>();
-  if (rwt == WT_NVFP4 && swt == WT_BF16) return fused_fn<TB, QX, WT_NVFP4, WT_BF16>();
-  return nullptr;
-}
-
-// qx 1 covers H <= 2048, qx 4 H <= 8192 (batch buckets 1, 2, 4 only).
-static const void* fused_kernel(int tb, int qx, int rwt, int swt) {
+// Calls f(Tag<Variant>) for the variant of (shape, bucket, qx, weight types).
+// qx 1 covers H <= 2048, qx 4 H <= 8192 (batch buckets 1, 2, 4 only); the
+// Flint shape has its own variants.
+template <class F>
+static int with_variant(int shape, int tb, int qx, int rwt, int swt, F&& f) {
+  if (shape == 1) {
+    if (qx != 1) return kNoVariant;
+    switch (tb) {
+      case 1: return by_wtype<FlintShape, 1, 1>(rwt, swt, f);
+      case 2: return by_wtype<FlintShape, 2, 1>(rwt, swt, f);
+      case 4: return by_wtype<FlintShape, 4, 1>(rwt, swt, f);
+      case 8: return by_wtype<FlintShape, 8, 1>(rwt, swt, f);
+      default: return kNoVariant;
+    }
+  }
   if (qx == 1) {
     switch (tb) {
-      case 1: return fused_fn_wt<1, 1>(rwt, swt);
-      case 2: return fused_fn_wt<2, 1>(rwt, swt);
-      case 4: return fused_fn_wt<4, 1>(rwt, swt);
-      case 8: return fused_fn_wt<8, 1>(rwt, swt);
-      default: return nullptr;
+      case 1: return by_wtype<DynShape, 1, 1>(rwt, swt, f);
+      case 2: return by_wtype<DynShape, 2, 1>(rwt, swt, f);
+      case 4: return by_wtype<DynShape, 4, 1>(rwt, swt, f);
+      case 8: return by_wtype<DynShape, 8, 1>(rwt, swt, f);
+      default: return kNoVariant;
     }
   }
   if (qx == 4) {
     switch (tb) {
-      case 1: return fused_fn_wt<1, 4>(rwt, swt);
-      case 2: return fused_fn_wt<2, 4>(rwt, swt);
-      case 4: return fused_fn_wt<4, 4>(rwt, swt);
-      default: return nullptr;
+      case 1: return by_wtype<DynShape, 1, 4>(rwt, swt, f);
+      case 2: return by_wtype<DynShape, 2, 4>(rwt, swt, f);
+      case 4: return by_wtype<DynShape, 4, 4>(rwt, swt, f);
+      default: return kNoVariant;
     }
   }
-  return nullptr;
+  return kNoVariant;
 }
 
 int fused_qx(int hidden) { return hidden / 8 <= NT ? 1 : (hidden / 8 <= 4 * NT ? 4 : 0); }
 
-int fused_occupancy(int tb, int qx, int rwt, int swt, int lds_bytes, int* blocks_per_cu) {
-  const void* f = fused_kernel(tb, qx, rwt, swt);
-  if (f == nullptr) return (int)hipErrorInvalidValue;
-  if (lds_bytes > 64 * 1024) {
-    const hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
-    if (e != hipSuccess) return (int)e;
-  }
-  return (int)hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, f, NT, lds_bytes);
+int fused_occupancy(int shape, int tb, int qx, int rwt, int swt, int lds_bytes, int* blocks_per_cu) {
+  return with_variant(shape, tb, qx, rwt, swt, [&](auto t) -> int {
+    const void* f = decltype(t)::type::fn();
+    if (lds_bytes > 64 * 1024) {
+      const hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
+      if (e != hipSuccess) return (int)e;
+    }
+    return (int)hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, f, NT, lds_bytes);
+  });
 }
 
 int launch_fused(const FusedArgs& a, int tb, int rwt, int swt, void* stream) {
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  const void* f = fused_kernel(tb, fused_qx(a.H), rwt, swt);
-  if (f == nullptr) return (int)hipErrorInvalidValue;
   (void)hipGetLastError();  // clear a stale error so it is not reported as ours
-  void* args[] = {const_cast<FusedArgs*>(&a)};
-  return (int)hipLaunchKernel(f, dim3(a.G), dim3(NT), args, (size_t)fused_lds_bytes(a), st);
+  const int shape = fixed_shape_of(a.H, a.I, a.E, a.k, a.S, a.Er);
+  return with_variant(shape, tb, fused_qx(a.H), rwt, swt,
+                      [&](auto t) -> int { return decltype(t)::type::launch(a, st); });
 }
 
 int launch_fused_debug_h(const FusedArgs& a, uint16_t* h_r, uint16_t* h_s, void* stream) {

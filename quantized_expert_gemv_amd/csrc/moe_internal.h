@@ -5,6 +5,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "../../include/moe_decode.h"
 
 #if defined(__HIPCC__)
@@ -36,24 +38,33 @@ struct MatGeom {
   int su;      // 16 B units per step per slice = rpw * cw
 };
 
+// The geometry of a [rows][cols] matrix (rows % rpw == 0 and nsteps even
+// are checked by make_geom; ns = 0 marks a row too long for four slices).
+MOE_HD constexpr MatGeom geom_of(int rows, int cols) {
+  MatGeom g{};
+  g.rows = rows;
+  g.cols = cols;
+  g.C = cols / 32;
+  int ns = 1;
+  while (ns <= 4 && (g.C / ns > 64 || g.C % ns)) ns *= 2;
+  if (ns > 4) return g;
+  g.ns = ns;
+  g.cw = g.C / ns;
+  int lpr = 1;
+  while (lpr < g.cw) lpr *= 2;
+  g.lpr = lpr;
+  g.rpw = 64 / lpr;
+  g.nsteps = rows / g.rpw;
+  g.su = g.rpw * g.cw;
+  return g;
+}
+
 // Returns 0 and fills g, or -1 when the shape has no supported geometry.
 MOE_HD inline int make_geom(int rows, int cols, MatGeom* g) {
   if (rows <= 0 || cols <= 0 || cols % 32) return -1;
-  const int C = cols / 32;
-  int ns = 1;
-  while (C / ns > 64 || C % ns) {
-    ns *= 2;
-    if (ns > 4) return -1;
-  }
-  const int cw = C / ns;
-  int lpr = 1;
-  while (lpr < cw) lpr *= 2;
-  const int rpw = 64 / lpr;
-  if (rows % rpw) return -1;
-  const int nsteps = rows / rpw;
-  if (nsteps % 2) return -1;
-  g->rows = rows; g->cols = cols; g->C = C; g->ns = ns; g->cw = cw;
-  g->lpr = lpr; g->rpw = rpw; g->nsteps = nsteps; g->su = rpw * cw;
+  const MatGeom m = geom_of(rows, cols);
+  if (m.ns == 0 || rows % m.rpw || m.nsteps % 2) return -1;
+  *g = m;
   return 0;
 }
 
@@ -114,7 +125,8 @@ constexpr int kMaxPairs = MOE_MAX_BATCH * (MOE_MAX_TOPK + MOE_MAX_SHARED);
 // tag (the handle's call counter + 1).  A reader polls a word until its tag
 // matches, so no flag, fence or barrier is needed: each word carries its own
 // validity, and a word of an older call never matches.
-struct FusedArgs {
+// The per-layer and per-call values that are never compile-time constants.
+struct KCommon {
   // inputs (caller-owned device memory)
   const uint16_t* x;         // bf16 [B][H]
   const uint16_t* router_w;  // bf16 [Er][H]
@@ -135,11 +147,8 @@ struct FusedArgs {
   int* topk_ids;                   // [maxB][k] readback
   float* topk_w;                   // [maxB][k]
   float* shared_c;                 // [maxB][S]
-  // shapes
-  int B, H, I, E, k, S, Er;
   int route, prenorm, residual;
   float eps;
-  MatGeom g13, g2;
   size_t r_code_stride, r_w13_code, r_scale_stride, r_w13_scale;
   size_t s_code_stride, s_w13_code, s_scale_stride, s_w13_scale;
   // plan
@@ -152,14 +161,67 @@ struct FusedArgs {
   unsigned long long wait_ticks;   // bound of every wait, in 100 MHz ticks
 };
 
+// Layer shape read from the arguments ...
+struct DynShape {
+  int H, I, E, k, S, Er;
+  MatGeom g13, g2;
+};
+// ... or fixed at compile time (the kernel then folds every shape-derived
+// index, stride and branch; the host launches it only for a matching layer).
+template <int H_, int I_, int E_, int K_, int S_, int ER_>
+struct FixedShape {
+  static constexpr int H = H_, I = I_, E = E_, k = K_, S = S_, Er = ER_;
+  static constexpr MatGeom g13 = geom_of(2 * I_, H_), g2 = geom_of(H_, I_);
+};
+// Flint's MoE layer: H = 2048, I = 512, 256 routed experts, top-6, one shared
+// expert, sigmoid router over the 256 routed experts.
+using FlintShape = FixedShape<2048, 512, 256, 6, 1, 256>;
+
+// Batch size of the call: read from the arguments, or fixed (buckets 1 and 2
+// hold exactly that many tokens).
+template <int BF> struct BatchField { static constexpr int B = BF; };
+template <> struct BatchField<0> { int B; };
+
+// Kernel arguments.  Fields of a fixed shape or batch are static members, so
+// the kernel reads a.H, a.B, a.g13.lpr ... the same way in every variant.
+template <class SH, int BF>
+struct KArgs : KCommon, SH, BatchField<BF> {};
+
+// Everything one launch of the single-launch layer kernel needs, by value
+// (host side; the launcher turns it into the variant's KArgs).
+//
+// Cross-workgroup data (router logits, SiLU*up activations) moves through
+// tagged 8-byte words: the low half holds the value, the high half the call's
+// tag (the handle's call counter + 1).  A reader polls a word until its tag
+// matches, so no flag, fence or barrier is needed: each word carries its own
+// validity, and a word of an older call never matches.
+struct FusedArgs : KCommon, DynShape {
+  int B;
+};
+
+template <class SH, int BF>
+inline KArgs<SH, BF> kargs_of(const FusedArgs& f) {
+  KArgs<SH, BF> k{};
+  static_cast<KCommon&>(k) = f;
+  if constexpr (std::is_same<SH, DynShape>::value) static_cast<DynShape&>(k) = f;
+  if constexpr (BF == 0) k.B = f.B;
+  return k;
+}
+
+// Shape variant a layer runs with: 1 = FlintShape, 0 = read from the arguments.
+inline int fixed_shape_of(int H, int I, int E, int k, int S, int Er) {
+  using F = FlintShape;
+  return (H == F::H && I == F::I && E == F::E && k == F::k && S == F::S && Er == F::Er) ? 1 : 0;
+}
+
 enum : unsigned { kErrLogitWait = 1u, kErrActWait = 2u };
 
 // Dynamic LDS bytes of the kernel for a plan.
-MOE_HD inline int fused_lds_bytes(const FusedArgs& a) { return a.lds_act + a.lds_acc; }
+MOE_HD inline int fused_lds_bytes(const KCommon& a) { return a.lds_act + a.lds_acc; }
 
 int launch_fused(const FusedArgs& a, int tb, int rwt, int swt, void* stream);
 int launch_fused_debug_h(const FusedArgs& a, uint16_t* h_r, uint16_t* h_s, void* stream);
-int fused_occupancy(int tb, int qx, int rwt, int swt, int lds_bytes, int* blocks_per_cu);
+int fused_occupancy(int shape, int tb, int qx, int rwt, int swt, int lds_bytes, int* blocks_per_cu);
 // Router units per thread the kernel is built for at this hidden size (0: none).
 int fused_qx(int hidden);
 
