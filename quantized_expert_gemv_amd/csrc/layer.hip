@@ -8,13 +8,13 @@
 // data to each other through tagged words in device memory:
 //
 //   phase 1  every workgroup: its router row(s) -> publish logits; the shared
-//            experts' gate/up rows (they do not depend on routing) -> publish
-//            their SiLU*up activations
+//            experts' gate/up tiles (they do not depend on routing) start
+//            loading
 //   routing  every workgroup gathers all logits and computes the same top-k,
 //            routing weights and the union of the batch's selected experts
-//   phase 2  every workgroup: its slice of the selected experts' gate/up rows
-//            -> publish SiLU*up activations; the down-GEMV weights this
-//            workgroup needs later are already loading
+//   phase 2  every workgroup: its slice of the shared and the selected
+//            experts' gate/up rows -> publish SiLU*up activations; the
+//            down-GEMV weights this workgroup needs later are already loading
 //   phase 3  every workgroup gathers all activations and computes its output
 //            rows: down GEMV of every selected and shared expert, summed in a
 //            fixed order with the combine weights (+ residual), one bf16
@@ -422,6 +422,9 @@ struct GateUp {
     lg_ngr = (ngr == 4) ? 2 : (ngr == 2) ? 1 : 0;
     grp = wave / ns;
     sl = wave - grp * ns;
+    // shared items (at most a few per workgroup) go to the last groups, which
+    // never hold more routed items than the first ones
+    if (shared) grp = ngr - 1 - grp;
   }
   // The phase's item count n (items of the block are contiguous).
   template <class A>
@@ -574,6 +577,8 @@ struct GateUp {
                               : b * a.k + (int)((s.pr[slot][b >> 2] >> (8 * (b & 3))) & 0xffu);
         publish(a.xh + (size_t)pr * (a.I / 2) + t2, f2bf(h0) | (f2bf(h1) << 16), tag);
       }
+      // the partials are read: a following pass may overwrite them
+      __syncthreads();
     }
   }
 };
@@ -921,7 +926,7 @@ struct Down {
 // Items (gate/up) and tiles (down) in flight per wave.
 template <int TB, int WT> constexpr int gu_depth() { return WT == WT_NVFP4 ? (TB <= 2 ? 2 : 4) : (TB <= 2 ? 1 : 2); }
 template <int TB, int WTR, int WTS> constexpr int down_depth() {
-  return (WTR == WT_NVFP4 && WTS == WT_NVFP4) ? (TB >= 8 ? 4 : 6) : 3;
+  return (WTR == WT_NVFP4 && WTS == WT_NVFP4) ? (TB == 1 ? 4 : (TB >= 8 ? 4 : 6)) : 3;
 }
 
 // QX: 16-byte units of a router row per thread (H <= QX * NT * 8); the host
@@ -1092,7 +1097,7 @@ __global__ __launch_bounds__(NT) void k_fused_layer(A a) {
     publish(a.xlog + (size_t)row * kLogitLine + b, __float_as_uint(v), tag);
   }
 
-  // ---- shared experts' gate/up while the logits travel -------------------------
+  // ---- activation chunks; every workgroup gathers all logits ---------------------
   constexpr int XR = (TB <= 2) ? TB : 1;   // activation chunks held in registers
   const int xcol = x_col(a, L13);
   uint32_t xr[XR][16];
@@ -1100,7 +1105,6 @@ __global__ __launch_bounds__(NT) void k_fused_layer(A a) {
   auto laddr = [&](int i) { return a.xlog + (size_t)(i / a.B) * kLogitLine + (i % a.B); };
   Gather<2 * TB> lgat;
   lgat.issue(0, a.Er * a.B, laddr);
-  gus.run(a, s, tab, xr, act, xcol, part, tag);
   // every wait ends by this time (measured from here, not from the start:
   // the bound is not needed before the first wait)
   const u64 deadline = clock100() + a.wait_ticks;
@@ -1125,6 +1129,9 @@ __global__ __launch_bounds__(NT) void k_fused_layer(A a) {
     gur.set_items(a, nd * gs2);
     gur.prime(a, tab);
     down.prime(a, tab);
+    // the shared experts' tiles were loaded at the start: their gate/up runs
+    // while the selected experts' first tiles are in flight
+    gus.run(a, s, tab, xr, act, xcol, part, tag);
     gur.run(a, s, tab, xr, act, xcol, part, tag);
   }
 
