@@ -71,45 +71,52 @@ __device__ __forceinline__ u64 peek(const u64* p) {
 }
 
 // Polls a set of tagged words until their tags equal `tag`.  Each thread
-// owns words i = tid + NT*q, q < NB.  issue() sends the first loads (they can
-// fly while the thread does other work); finish() waits for the stragglers,
-// then hands (i, value) to sink.  Past the deadline the error bit is set and
+// owns words i = base + tid + NT*q, q < NB.  issue() sends the first poll (it
+// can fly while the thread does other work); finish() polls again until every
+// word has matched, then hands (i, value) to sink.  Every poll reads all NB
+// words (a word that already matched reads the same value again), so the
+// number of loads in flight never depends on data.  (A second poll in flight
+// did not shorten the hand-off: its time is the stores' way to the memory
+// side, not the polling rate.)  Past the deadline the error bit is set and
 // the words are taken as they are.
 template <int NB>
 struct Gather {
   u64 v[NB];
-  unsigned pend;
   int base, n;
 
+  template <typename Addr>
+  __device__ __forceinline__ void poll(u64 (&d)[NB], Addr&& addr) const {
+#pragma unroll
+    for (int q = 0; q < NB; ++q) {
+      const int i = base + q * NT + (int)threadIdx.x;
+      d[q] = peek(addr(i < n ? i : 0));
+    }
+  }
+  // true when every word of the thread in d carries the tag
+  __device__ __forceinline__ bool done(const u64 (&d)[NB], uint32_t tag) const {
+    bool ok = true;
+#pragma unroll
+    for (int q = 0; q < NB; ++q) {
+      const int i = base + q * NT + (int)threadIdx.x;
+      ok = ok && (i >= n || (uint32_t)(d[q] >> 32) == tag);
+    }
+    return ok;
+  }
   template <typename Addr>
   __device__ __forceinline__ void issue(int base_, int n_, Addr&& addr) {
     base = base_;
     n = n_;
-    pend = 0u;
-#pragma unroll
-    for (int q = 0; q < NB; ++q) {
-      const int i = base + q * NT + (int)threadIdx.x;
-      v[q] = peek(addr(i < n ? i : 0));
-      if (i < n) pend |= 1u << q;
-    }
+    poll(v, addr);
   }
   template <typename Addr, typename Sink>
   __device__ __forceinline__ void finish(uint32_t tag, u64 deadline, unsigned* err, unsigned bit, Addr&& addr,
                                          Sink&& sink) {
-#pragma unroll
-    for (int q = 0; q < NB; ++q)
-      if (((pend >> q) & 1u) && (uint32_t)(v[q] >> 32) == tag) pend &= ~(1u << q);
-    while (pend != 0u) {
+    while (!done(v, tag)) {
       if (clock100() > deadline) {
         __hip_atomic_fetch_or(err, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         break;
       }
-#pragma unroll
-      for (int q = 0; q < NB; ++q)
-        if ((pend >> q) & 1u) v[q] = peek(addr(base + q * NT + (int)threadIdx.x));
-#pragma unroll
-      for (int q = 0; q < NB; ++q)
-        if (((pend >> q) & 1u) && (uint32_t)(v[q] >> 32) == tag) pend &= ~(1u << q);
+      poll(v, addr);
     }
 #pragma unroll
     for (int q = 0; q < NB; ++q) {
@@ -400,6 +407,9 @@ __device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f +
 // publishes their SiLU*up words; with ns > 1 the ns waves of a group share
 // items, wave w taking slice w % ns, and after one barrier the workgroup
 // combines the slices in order.  PI items are loading at a time.
+template <int TB, int WT>
+constexpr bool kSkipRefills = TB <= 2 && WT == WT_NVFP4;
+
 template <int TB, int WT, int PI>
 struct GateUp {
   Quad<WT> q[PI];
@@ -508,51 +518,67 @@ struct GateUp {
   // token's chunk is read from shared memory (xs + b H + xcol) per item, which
   // leaves registers for more items in flight.  part: TB * 4 * ns floats per
   // item of the block (ns > 1 only).
+  // Item in buffer p (live: a real item of this wave).  RELOAD: refill the
+  // buffer with the wave's next item (a dummy past the end) once it is read.
+  template <bool RELOAD, int XR, class A>
+  __device__ __forceinline__ void step(const A& a, const Smem& s, const SlotTab& tb, const uint32_t (&xr)[XR][16],
+                                       const uint16_t* xs, int xcol, float* part, uint32_t tag, int p, bool live,
+                                       bool lead) {
+    const int slot = qslot[p], t2 = qt2[p];
+    const unsigned mask = shared ? (1u << a.B) - 1u : tb.tokens(min(slot, kMaxD - 1));
+    const float g13 = shared ? ((WT == WT_NVFP4) ? s.tss[min(slot, MOE_MAX_SHARED - 1)][0] : 1.0f)
+                             : tb.w13(min(slot, kMaxD - 1));
+    if constexpr (XR == TB) {
+      float v[TB][4];
+      if (live) {
+#pragma unroll
+        for (int b = 0; b < TB; ++b)
+          if ((mask >> b) & 1u) quad_dot<WT>(q[p], xr[b], v[b]);
+      }
+      // The buffer is free only now.  Its reload is unconditional (a dummy
+      // past the end) and kept below the reads: a conditional or hoisted
+      // reload would make the compiler copy registers and wait for every
+      // load in flight.
+      __asm__ volatile("" ::: "memory");   // also keeps items from being interleaved
+      if constexpr (RELOAD) load_next(a, tb, p);
+      if (live) {
+#pragma unroll
+        for (int b = 0; b < TB; ++b)
+          if ((mask >> b) & 1u) finish_token(a, tb, v[b], slot, t2, b, g13, lead, part, tag);
+      }
+    } else {
+      if (live) {
+        for (unsigned m = mask; m != 0u; m &= m - 1u) {   // uniform loop over the item's tokens
+          const int b = __builtin_ctz(m);
+          uint32_t xb[16];
+          lds_chunk(xs + (size_t)b * a.H + xcol, xb);
+          float v[4];
+          quad_dot<WT>(q[p], xb, v);
+          finish_token(a, tb, v, slot, t2, b, g13, lead, part, tag);
+        }
+      }
+      __asm__ volatile("" ::: "memory");
+      if constexpr (RELOAD) load_next(a, tb, p);
+    }
+  }
+  // xr: the tokens' activation chunks in registers (TB <= 2); otherwise each
+  // token's chunk is read from shared memory (xs + b H + xcol) per item, which
+  // leaves registers for more items in flight.  part: TB * 4 * ns floats per
+  // item of the block (ns > 1 only).
   template <int XR, class A>
   __device__ __forceinline__ void run(const A& a, const Smem& s, const SlotTab& tb, const uint32_t (&xr)[XR][16],
                                       const uint16_t* xs, int xcol, float* part, uint32_t tag) {
     const bool lead = L.jj == ((ns == 1) ? a.g13.lpr - 1 : 63);
-    for (int base = 0; base < nmine; base += PI) {
+    // Small batches: when every item of the wave is already loading, skip the
+    // refills (a second copy of the loop; larger batches keep one copy, which
+    // the register allocator handles better there).
+    if (kSkipRefills<TB, WT> && nmine <= PI) {
 #pragma unroll
-      for (int p = 0; p < PI; ++p) {
-        const int i = base + p;
-        const bool live = i < nmine;   // uniform
-        const int slot = qslot[p], t2 = qt2[p];
-        const unsigned mask = shared ? (1u << a.B) - 1u : tb.tokens(min(slot, kMaxD - 1));
-        const float g13 = shared ? ((WT == WT_NVFP4) ? s.tss[min(slot, MOE_MAX_SHARED - 1)][0] : 1.0f)
-                                 : tb.w13(min(slot, kMaxD - 1));
-        if constexpr (XR == TB) {
-          float v[TB][4];
-          if (live) {
+      for (int p = 0; p < PI; ++p) step<false>(a, s, tb, xr, xs, xcol, part, tag, p, p < nmine, lead);
+    } else {
+      for (int base = 0; base < nmine; base += PI) {
 #pragma unroll
-            for (int b = 0; b < TB; ++b)
-              if ((mask >> b) & 1u) quad_dot<WT>(q[p], xr[b], v[b]);
-          }
-          // The buffer is free only now.  Its reload is unconditional (a dummy
-          // past the end) and kept below the reads: a conditional or hoisted
-          // reload would make the compiler copy registers and wait for every
-          // load in flight.
-          __asm__ volatile("" ::: "memory");
-          load_next(a, tb, p);
-          if (live) {
-#pragma unroll
-            for (int b = 0; b < TB; ++b)
-              if ((mask >> b) & 1u) finish_token(a, tb, v[b], slot, t2, b, g13, lead, part, tag);
-          }
-        } else {
-          if (live) {
-            for (unsigned m = mask; m != 0u; m &= m - 1u) {   // uniform loop over the item's tokens
-              const int b = __builtin_ctz(m);
-              uint32_t xb[16];
-              lds_chunk(xs + (size_t)b * a.H + xcol, xb);
-              float v[4];
-              quad_dot<WT>(q[p], xb, v);
-              finish_token(a, tb, v, slot, t2, b, g13, lead, part, tag);
-            }
-          }
-          __asm__ volatile("" ::: "memory");
-          load_next(a, tb, p);
-        }
+        for (int p = 0; p < PI; ++p) step<true>(a, s, tb, xr, xs, xcol, part, tag, p, base + p < nmine, lead);
       }
     }
     if (ns > 1) {
@@ -673,6 +699,27 @@ __device__ __forceinline__ void topk(const A& a, const float* lg, int lane, int 
   }
 }
 
+// One token's routing weight in lane r < k (its r-th selection, logit
+// my_l) and shared coefficient in lane s < S, from its logits l.
+template <class A>
+__device__ __forceinline__ void token_weights(const A& a, const float* l, int lane, float my_l, float& wv,
+                                              float& shc) {
+  if (a.route == MOE_ROUTE_SOFTMAX_SINK) {
+    unsigned mk = 0u;
+    for (int e = lane; e < a.Er; e += 64) mk = max(mk, fkey(l[e]));
+    const float mx = unkey(wave_max_u32(mk));
+    float z = 0.f;
+    for (int e = lane; e < a.Er; e += 64) z += __expf(l[e] - mx);
+    z = wave_sum(z);
+    wv = __expf(my_l - mx) / z;
+    shc = (lane < a.S) ? __expf(l[a.E + min(lane, a.S - 1)] - mx) / z : 0.f;
+  } else {
+    const float sg = (lane < a.k) ? 1.0f / (1.0f + __expf(-my_l)) : 0.f;
+    wv = sg / wave_sum(sg);
+    shc = 1.0f;
+  }
+}
+
 // Routing weights and shared coefficients of the TPW tokens (wave + t NW),
 // into shared memory, with the token masks of the selected experts.
 template <int TPW, class A>
@@ -683,22 +730,9 @@ __device__ __forceinline__ void route_weights(const A& a, Smem& s, const float* 
   for (int t = 0; t < TPW; ++t) {
     const int b = wave + t * NW;
     if (b >= a.B) continue;
-    const float* l = lg + (size_t)b * a.Er;
-    float wv;
-    if (a.route == MOE_ROUTE_SOFTMAX_SINK) {
-      unsigned mk = 0u;
-      for (int e = lane; e < a.Er; e += 64) mk = max(mk, fkey(l[e]));
-      const float mx = unkey(wave_max_u32(mk));
-      float z = 0.f;
-      for (int e = lane; e < a.Er; e += 64) z += __expf(l[e] - mx);
-      z = wave_sum(z);
-      wv = __expf(my_l[t] - mx) / z;
-      if (lane < a.S) s.shc[b][lane] = __expf(l[a.E + lane] - mx) / z;
-    } else {
-      const float sg = (lane < a.k) ? 1.0f / (1.0f + __expf(-my_l[t])) : 0.f;
-      wv = sg / wave_sum(sg);
-      if (lane < a.S) s.shc[b][lane] = 1.0f;
-    }
+    float wv, shc;
+    token_weights(a, lg + (size_t)b * a.Er, lane, my_l[t], wv, shc);
+    if (lane < a.S) s.shc[b][lane] = shc;
     if (lane < a.k) {
       s.sel[b][lane] = my_e[t];
       s.selw[b][lane] = wv;
@@ -756,10 +790,41 @@ __device__ __forceinline__ void number_slots(const A& a, Smem& s, int lane, cons
   if (lane == 0) s.nd = nd;
 }
 
-template <int MK, int TPW, int WTR, int WTS, class A>
+template <int MK, int TPW, int TB, int WTR, int WTS, class A>
 __device__ __forceinline__ void route(const A& a, Smem& s, const float* lg, const int (&eb)[2],
                                       const int (&er)[2]) {
   const int tid = threadIdx.x, wave = wave_id(), lane = tid & 63;
+  if constexpr (TB == 1) {
+    // One token: its k selections are the distinct experts, slot r = rank r,
+    // so wave 0 fills the tables from its registers.
+    if (wave == 0) {
+      int my_e[1];
+      float my_l[1];
+      topk<MK, 1>(a, lg, lane, my_e, my_l);
+      float wv, shc;
+      token_weights(a, lg, lane, my_l[0], wv, shc);
+      if (lane < a.k) {
+        const int e = my_e[0];
+        s.ids[lane] = e;
+        s.dmask[lane] = 1u;
+        s.xg[lane] = (WTR == WT_NVFP4) ? s.tsr[e][0] : 1.0f;
+        s.pr[lane][0] = (uint32_t)lane;
+        s.pr[lane][1] = 0u;
+        s.pw[lane] = wv * ((WTR == WT_NVFP4) ? s.tsr[e][1] : 1.0f);
+        if (blockIdx.x == 0) {
+          a.topk_ids[lane] = e;
+          a.topk_w[lane] = wv;
+        }
+      }
+      if (lane < a.S) {
+        s.pw[a.k + lane] = shc * ((WTS == WT_NVFP4) ? s.tss[lane][1] : 1.0f);
+        if (blockIdx.x == 0) a.shared_c[lane] = shc;
+      }
+      if (lane == 0) s.nd = a.k;
+    }
+    __syncthreads();
+    return;
+  }
   if (wave < a.B) {
     int my_e[TPW];
     float my_l[TPW];
@@ -861,59 +926,70 @@ struct Down {
   }
   // hs: activations [pairs][I] bf16 (shared memory).  Results: nsub == 1 ->
   // out directly; else partial sums into red2 [nsub][TB][spg * rpw].
+  // Tile in buffer p (live: a real tile of this wave); acc: this lane's row
+  // sums of the current step, per token.  RELOAD: refill the buffer with the
+  // wave's next tile (a dummy past the end) once it is read.
+  template <bool RELOAD, class A>
+  __device__ __forceinline__ void step(const A& a, const SlotTab& tb, const uint16_t* hs, float* red2,
+                                       float (&acc)[TB], int p, bool live, bool lead) {
+    const int rpw = a.g2.rpw, lpr = a.g2.lpr;
+    const int j = qj[p], xi = qx[p], ex = ex_of(xi), t = t_lo + j;
+    if (live) {
+      const bool sh = ex < a.S;
+      const int slot = min(ex - a.S, kMaxD - 1);
+      const unsigned mask = sh ? (1u << a.B) - 1u : tb.tokens(slot);
+#pragma unroll
+      for (int b = 0; b < TB; ++b) {
+        if ((mask >> b) & 1u) {
+          const int pr = sh ? a.B * a.k + ex * a.B + b : b * a.k + tb.rank(slot, b);
+          uint32_t hv[16];
+          lds_chunk(hs + (size_t)pr * a.I + L.jc * 32, hv);
+          float v;
+          if constexpr (WTR == WTS) v = tile_dot<WTR>(br[p], t, hv);
+          else v = sh ? tile_dot<WTS>(bs[p], t, hv) : tile_dot<WTR>(br[p], t, hv);
+          acc[b] = fmaf(L.active ? v : 0.f, tb.weight(pr), acc[b]);
+        }
+      }
+    }
+    __asm__ volatile("" ::: "memory");       // also keeps tiles from being interleaved
+    if constexpr (RELOAD) load_next(a, tb, p);   // unconditional, see GateUp::step
+    if (live && xi == nex - 1) {
+      // step complete: reduce each token's row sums over the row's lanes
+#pragma unroll
+      for (int b = 0; b < TB; ++b) {
+        if (b < a.B) {
+          const float v = group_sum(acc[b], lpr);
+          if (lead) {
+            const int rl = j * rpw + L.ri;
+            if (nsub == 1) {
+              const int row = t * rpw + L.ri;
+              float o = v;
+              if (a.residual) o += bf16lo(a.x[(size_t)b * a.H + row]);
+              a.out[(size_t)b * a.H + row] = (uint16_t)f2bf(o);
+            } else {
+              red2[(sub * TB + b) * (spg * rpw) + rl] = v;
+            }
+          }
+        }
+        acc[b] = 0.f;
+      }
+    }
+  }
+  // hs: activations [pairs][I] bf16 (shared memory).  Results: nsub == 1 ->
+  // out directly; else partial sums into red2 [nsub][TB][spg * rpw].
   template <class A>
   __device__ __forceinline__ void run(const A& a, const SlotTab& tb, const uint16_t* hs, float* red2) {
     float acc[TB];
 #pragma unroll
     for (int b = 0; b < TB; ++b) acc[b] = 0.f;
-    const int rpw = a.g2.rpw, lpr = a.g2.lpr;
-    const bool lead = L.jj == lpr - 1;
-    for (int base = 0; base < ntiles; base += P) {
+    const bool lead = L.jj == a.g2.lpr - 1;
+    if (kSkipRefills<TB, WTR> && kSkipRefills<TB, WTS> && ntiles <= P) {   // see GateUp::run
 #pragma unroll
-      for (int p = 0; p < P; ++p) {
-        const int tau = base + p;
-        const bool live = tau < ntiles;   // uniform
-        const int j = qj[p], xi = qx[p], ex = ex_of(xi), t = t_lo + j;
-        if (live) {
-          const bool sh = ex < a.S;
-          const int slot = min(ex - a.S, kMaxD - 1);
-          const unsigned mask = sh ? (1u << a.B) - 1u : tb.tokens(slot);
+      for (int p = 0; p < P; ++p) step<false>(a, tb, hs, red2, acc, p, p < ntiles, lead);
+    } else {
+      for (int base = 0; base < ntiles; base += P) {
 #pragma unroll
-          for (int b = 0; b < TB; ++b) {
-            if ((mask >> b) & 1u) {
-              const int pr = sh ? a.B * a.k + ex * a.B + b : b * a.k + tb.rank(slot, b);
-              uint32_t hv[16];
-              lds_chunk(hs + (size_t)pr * a.I + L.jc * 32, hv);
-              float v;
-              if constexpr (WTR == WTS) v = tile_dot<WTR>(br[p], t, hv);
-              else v = sh ? tile_dot<WTS>(bs[p], t, hv) : tile_dot<WTR>(br[p], t, hv);
-              acc[b] = fmaf(L.active ? v : 0.f, tb.weight(pr), acc[b]);
-            }
-          }
-        }
-        __asm__ volatile("" ::: "memory");
-        load_next(a, tb, p);   // unconditional, see GateUp::run
-        if (live && xi == nex - 1) {
-          // step complete: reduce each token's row sums over the row's lanes
-#pragma unroll
-          for (int b = 0; b < TB; ++b) {
-            if (b < a.B) {
-              const float v = group_sum(acc[b], lpr);
-              if (lead) {
-                const int rl = j * rpw + L.ri;
-                if (nsub == 1) {
-                  const int row = t * rpw + L.ri;
-                  float o = v;
-                  if (a.residual) o += bf16lo(a.x[(size_t)b * a.H + row]);
-                  a.out[(size_t)b * a.H + row] = (uint16_t)f2bf(o);
-                } else {
-                  red2[(sub * TB + b) * (spg * rpw) + rl] = v;
-                }
-              }
-            }
-            acc[b] = 0.f;
-          }
-        }
+        for (int p = 0; p < P; ++p) step<true>(a, tb, hs, red2, acc, p, base + p < ntiles, lead);
       }
     }
   }
@@ -924,10 +1000,17 @@ struct Down {
 // ---------------------------------------------------------------------------
 
 // Items (gate/up) and tiles (down) in flight per wave.
-template <int TB, int WT> constexpr int gu_depth() { return WT == WT_NVFP4 ? (TB <= 2 ? 2 : 4) : (TB <= 2 ? 1 : 2); }
+template <int TB, int WT> constexpr int gu_depth() { return WT == WT_NVFP4 ? (TB <= 2 ? 2 : 4) : 1; }
 template <int TB, int WTR, int WTS> constexpr int down_depth() {
   return (WTR == WT_NVFP4 && WTS == WT_NVFP4) ? (TB == 1 ? 4 : (TB >= 8 ? 4 : 6)) : 3;
 }
+
+// Logit words each thread gathers: exact for a fixed shape, else enough for
+// up to 512 router rows.
+template <class A, int TB, bool DYN = std::is_base_of<DynShape, A>::value>
+struct LogitWords { static constexpr int value = 2 * TB; };
+template <class A, int TB>
+struct LogitWords<A, TB, false> { static constexpr int value = (A::Er * TB + NT - 1) / NT; };
 
 // QX: 16-byte units of a router row per thread (H <= QX * NT * 8); the host
 // picks the smallest that fits, so every one of them is a real load.
@@ -997,7 +1080,7 @@ __global__ __launch_bounds__(NT) void k_fused_layer(A a) {
   const int gs2 = a.I / a.g13.rpw / 2;
   SlotTab tab = {};   // filled after routing
   // the shared experts' tiles need no routing: they load from the start
-  GateUp<TB, WTS, gu_depth<TB, WTS>()> gus;
+  GateUp<TB, WTS, 1> gus;   // one item in flight: its tiles stay in registers until after routing
   gus.init(a, L13, 1);
   gus.set_items(a, a.S * gs2);
   gus.prime(a, tab);
@@ -1103,7 +1186,7 @@ __global__ __launch_bounds__(NT) void k_fused_layer(A a) {
   uint32_t xr[XR][16];
   load_xr<XR>(a, xcol, act, xr);
   auto laddr = [&](int i) { return a.xlog + (size_t)(i / a.B) * kLogitLine + (i % a.B); };
-  Gather<2 * TB> lgat;
+  Gather<LogitWords<A, TB>::value> lgat;
   lgat.issue(0, a.Er * a.B, laddr);
   // every wait ends by this time (measured from here, not from the start:
   // the bound is not needed before the first wait)
@@ -1115,9 +1198,9 @@ __global__ __launch_bounds__(NT) void k_fused_layer(A a) {
 
   // ---- routing ---------------------------------------------------------------------
   constexpr int TPW = (TB > NW) ? 2 : 1;
-  if (a.E <= 64) route<1, TPW, WTR, WTS>(a, s, lg, eb, er);
-  else if (a.E <= 256) route<4, TPW, WTR, WTS>(a, s, lg, eb, er);
-  else route<8, TPW, WTR, WTS>(a, s, lg, eb, er);
+  if (a.E <= 64) route<1, TPW, TB, WTR, WTS>(a, s, lg, eb, er);
+  else if (a.E <= 256) route<4, TPW, TB, WTR, WTS>(a, s, lg, eb, er);
+  else route<8, TPW, TB, WTR, WTS>(a, s, lg, eb, er);
 
   // ---- phase 2: selected experts' gate/up; the down weights start loading ------------
   tab.load(s, lane);
