@@ -72,51 +72,46 @@ __device__ __forceinline__ u64 peek(const u64* p) {
 
 // Polls a set of tagged words until their tags equal `tag`.  Each thread
 // owns words i = base + tid + NT*q, q < NB.  issue() sends the first poll (it
-// can fly while the thread does other work); finish() polls again until every
-// word has matched, then hands (i, value) to sink.  Every poll reads all NB
-// words (a word that already matched reads the same value again), so the
-// number of loads in flight never depends on data.  (A second poll in flight
-// did not shorten the hand-off: its time is the stores' way to the memory
-// side, not the polling rate.)  Past the deadline the error bit is set and
-// the words are taken as they are.
+// can fly while the thread does other work); finish() re-reads the words
+// that have not matched yet until all have, then hands (i, value) to sink.
+// (A second poll in flight did not shorten the hand-off: its time is the
+// stores' way to the memory side, not the polling rate.)  Past the deadline
+// the error bit is set and the words are taken as they are.
 template <int NB>
 struct Gather {
   u64 v[NB];
+  unsigned pend;
   int base, n;
 
-  template <typename Addr>
-  __device__ __forceinline__ void poll(u64 (&d)[NB], Addr&& addr) const {
-#pragma unroll
-    for (int q = 0; q < NB; ++q) {
-      const int i = base + q * NT + (int)threadIdx.x;
-      d[q] = peek(addr(i < n ? i : 0));
-    }
-  }
-  // true when every word of the thread in d carries the tag
-  __device__ __forceinline__ bool done(const u64 (&d)[NB], uint32_t tag) const {
-    bool ok = true;
-#pragma unroll
-    for (int q = 0; q < NB; ++q) {
-      const int i = base + q * NT + (int)threadIdx.x;
-      ok = ok && (i >= n || (uint32_t)(d[q] >> 32) == tag);
-    }
-    return ok;
-  }
   template <typename Addr>
   __device__ __forceinline__ void issue(int base_, int n_, Addr&& addr) {
     base = base_;
     n = n_;
-    poll(v, addr);
+    pend = 0u;
+#pragma unroll
+    for (int q = 0; q < NB; ++q) {
+      const int i = base + q * NT + (int)threadIdx.x;
+      v[q] = peek(addr(i < n ? i : 0));
+      if (i < n) pend |= 1u << q;
+    }
   }
   template <typename Addr, typename Sink>
   __device__ __forceinline__ void finish(uint32_t tag, u64 deadline, unsigned* err, unsigned bit, Addr&& addr,
                                          Sink&& sink) {
-    while (!done(v, tag)) {
+#pragma unroll
+    for (int q = 0; q < NB; ++q)
+      if (((pend >> q) & 1u) && (uint32_t)(v[q] >> 32) == tag) pend &= ~(1u << q);
+    while (pend != 0u) {
       if (clock100() > deadline) {
         __hip_atomic_fetch_or(err, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         break;
       }
-      poll(v, addr);
+#pragma unroll
+      for (int q = 0; q < NB; ++q)
+        if ((pend >> q) & 1u) v[q] = peek(addr(base + q * NT + (int)threadIdx.x));
+#pragma unroll
+      for (int q = 0; q < NB; ++q)
+        if (((pend >> q) & 1u) && (uint32_t)(v[q] >> 32) == tag) pend &= ~(1u << q);
     }
 #pragma unroll
     for (int q = 0; q < NB; ++q) {
