@@ -396,22 +396,30 @@ __device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f +
 // gate/up phases
 // ---------------------------------------------------------------------------
 
-// Gate/up items of one workgroup: item j = (slot j / gs2, step pair j % gs2),
-// block [lo, hi) of the phase's n items.  With one wave step per row (ns = 1)
-// each wave takes items lo + wave, lo + wave + NW, ... on its own and
-// publishes their SiLU*up words; with ns > 1 the ns waves of a group share
-// items, wave w taking slice w % ns, and after one barrier the workgroup
-// combines the slices in order.  PI items are loading at a time.
+// Gate/up items: item j = (slot j / gs2, step pair j % gs2) of the phase's n
+// items.  With more than one token, workgroup w takes items w, w + G, w + 2G,
+// ... (its m-th item is w + mG): every workgroup gets the same mix of experts,
+// and an expert chosen by many tokens (more work per item) does not load one
+// workgroup only.  With one token every item costs the same, and workgroup w
+// takes the block [nw/G, n(w+1)/G) (its m-th item is nw/G + m): a wave's
+// items then lie in one or two experts.
+// With one wave step per row (ns = 1) wave g takes the workgroup's items
+// m = g, g + NW, ... on its own and publishes their SiLU*up words; with ns > 1
+// the ns waves of a group share items, wave w taking slice w % ns, and after
+// one barrier the workgroup combines the slices in order.  PI items are
+// loading at a time.
 template <int TB, int WT>
 constexpr bool kSkipRefills = TB <= 2 && WT == WT_NVFP4;
 
 template <int TB, int WT, int PI>
 struct GateUp {
   Quad<WT> q[PI];
-  int qslot[PI], qt2[PI];
-  int shared, lo, hi, gs2, gate_steps;
+  int qslot[PI], qt2[PI], qm[PI];
+  int shared, cnt, gs2, gate_steps;   // cnt: the workgroup's items
+  int j0, lgj;                          // the workgroup's m-th item is j0 + (m << lgj)
   int ns, grp, ngr, lg_ngr, sl;
-  int nmine, nloaded, cslot, ct2;   // this wave's item count, items loaded, next item
+  int nmine, nloaded, cslot, ct2, cm;   // this wave's item count, items loaded, next item (slot, pair, m)
+  int dslot, dt2;                       // next item of the wave: + dslot slots, + dt2 pairs
   LaneGeo L;
 
   // Everything that does not depend on the routing.
@@ -431,17 +439,28 @@ struct GateUp {
     // never hold more routed items than the first ones
     if (shared) grp = ngr - 1 - grp;
   }
-  // The phase's item count n (items of the block are contiguous).
+  // The phase's item count n.
   template <class A>
   __device__ __forceinline__ void set_items(const A& a, int n) {
-    const uint32_t w = blockIdx.x;
-    lo = (int)(((uint32_t)n * w) >> a.log2G);
-    hi = (int)(((uint32_t)n * (w + 1)) >> a.log2G);
-    const int first = lo + grp;
-    nmine = (hi > first) ? (hi - first + ngr - 1) >> lg_ngr : 0;
+    const int w = blockIdx.x;
+    if constexpr (TB == 1) {
+      j0 = (int)(((uint32_t)n * w) >> a.log2G);
+      cnt = (int)(((uint32_t)n * (w + 1)) >> a.log2G) - j0;
+      lgj = 0;
+    } else {
+      j0 = w;
+      cnt = (n > w) ? ((n - 1 - w) >> a.log2G) + 1 : 0;
+      lgj = a.log2G;
+    }
+    nmine = (cnt > grp) ? ((cnt - 1 - grp) >> lg_ngr) + 1 : 0;
     nloaded = 0;
-    cslot = (int)fastdiv((uint32_t)first, a.dv_gs2);
-    ct2 = first - cslot * gs2;
+    cm = grp;
+    const uint32_t first = (uint32_t)j0 + ((uint32_t)grp << lgj);
+    cslot = (int)fastdiv(first, a.dv_gs2);
+    ct2 = (int)first - cslot * gs2;
+    const uint32_t stepj = (uint32_t)ngr << lgj;
+    dslot = (int)fastdiv(stepj, a.dv_gs2);
+    dt2 = (int)stepj - dslot * gs2;
   }
   template <class A>
   __device__ __forceinline__ void bases(const A& a, const SlotTab& tb, int slot, const uint8_t*& c,
@@ -467,10 +486,13 @@ struct GateUp {
     quad_load<WT>(q[p], c, sc, L, sl, gate_steps, ct2, dm, reinterpret_cast<const uint8_t*>(a.x));
     qslot[p] = cslot;
     qt2[p] = ct2;
+    qm[p] = cm;
     if (!dm) {
       ++nloaded;
-      ct2 += ngr;
-      if (ct2 >= gs2) {   // ngr <= gs2 (the plan checks it)
+      cm += ngr;
+      cslot += dslot;
+      ct2 += dt2;
+      if (ct2 >= gs2) {   // dt2 < gs2
         ct2 -= gs2;
         ++cslot;
       }
@@ -485,7 +507,7 @@ struct GateUp {
   // SiLU*up word (ns == 1) or the slice partials (ns > 1).  v holds the four
   // lane partials (gate t, gate t+1, up t, up t+1).
   template <class A>
-  __device__ __forceinline__ void finish_token(const A& a, const SlotTab& tb, float (&v)[4], int slot, int t2,
+  __device__ __forceinline__ void finish_token(const A& a, const SlotTab& tb, float (&v)[4], int slot, int t2, int m,
                                                int b, float g13, bool lead, float* part, uint32_t tag) const {
     if (!L.active) v[0] = v[1] = v[2] = v[3] = 0.f;
     if (ns == 1) {
@@ -501,18 +523,13 @@ struct GateUp {
         publish(a.xh + (size_t)pr * (a.I / 2) + t2 * a.g13.rpw + L.ri, f2bf(h0) | (f2bf(h1) << 16), tag);
       }
     } else {
-      const int il = slot * gs2 + t2 - lo;
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         const float sum = group_sum(v[c], 64);
-        if (lead) part[((il * TB + b) * 4 + c) * ns + sl] = sum;
+        if (lead) part[((m * TB + b) * 4 + c) * ns + sl] = sum;
       }
     }
   }
-  // xr: the tokens' activation chunks in registers (TB <= 2); otherwise each
-  // token's chunk is read from shared memory (xs + b H + xcol) per item, which
-  // leaves registers for more items in flight.  part: TB * 4 * ns floats per
-  // item of the block (ns > 1 only).
   // Item in buffer p (live: a real item of this wave).  RELOAD: refill the
   // buffer with the wave's next item (a dummy past the end) once it is read.
   template <bool RELOAD, int XR, class A>
@@ -539,7 +556,7 @@ struct GateUp {
       if (live) {
 #pragma unroll
         for (int b = 0; b < TB; ++b)
-          if ((mask >> b) & 1u) finish_token(a, tb, v[b], slot, t2, b, g13, lead, part, tag);
+          if ((mask >> b) & 1u) finish_token(a, tb, v[b], slot, t2, qm[p], b, g13, lead, part, tag);
       }
     } else {
       if (live) {
@@ -549,7 +566,7 @@ struct GateUp {
           lds_chunk(xs + (size_t)b * a.H + xcol, xb);
           float v[4];
           quad_dot<WT>(q[p], xb, v);
-          finish_token(a, tb, v, slot, t2, b, g13, lead, part, tag);
+          finish_token(a, tb, v, slot, t2, qm[p], b, g13, lead, part, tag);
         }
       }
       __asm__ volatile("" ::: "memory");
@@ -560,6 +577,10 @@ struct GateUp {
   // token's chunk is read from shared memory (xs + b H + xcol) per item, which
   // leaves registers for more items in flight.  part: TB * 4 * ns floats per
   // item of the block (ns > 1 only).
+  // xr: the tokens' activation chunks in registers (TB <= 2); otherwise each
+  // token's chunk is read from shared memory (xs + b H + xcol) per item, which
+  // leaves registers for more items in flight.  part: TB * 4 * ns floats per
+  // item of the workgroup (ns > 1 only).
   template <int XR, class A>
   __device__ __forceinline__ void run(const A& a, const Smem& s, const SlotTab& tb, const uint32_t (&xr)[XR][16],
                                       const uint16_t* xs, int xcol, float* part, uint32_t tag) {
@@ -578,9 +599,9 @@ struct GateUp {
     }
     if (ns > 1) {
       __syncthreads();
-      for (int idx = threadIdx.x; idx < (hi - lo) * TB; idx += NT) {
-        const int il = idx / TB, b = idx - il * TB;
-        const int j = lo + il, slot = (int)fastdiv((uint32_t)j, a.dv_gs2), t2 = j - slot * gs2;
+      for (int idx = threadIdx.x; idx < cnt * TB; idx += NT) {
+        const int m = idx / TB, b = idx - m * TB;
+        const int j = j0 + (m << lgj), slot = (int)fastdiv((uint32_t)j, a.dv_gs2), t2 = j - slot * gs2;
         const unsigned mask = shared ? (1u << a.B) - 1u : s.dmask[min(slot, kMaxD - 1)];
         if (!((mask >> b) & 1u)) continue;
         const float g13 = shared ? ((WT == WT_NVFP4) ? s.tss[min(slot, MOE_MAX_SHARED - 1)][0] : 1.0f)
@@ -589,7 +610,7 @@ struct GateUp {
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
           float acc = 0.f;
-          for (int u = 0; u < ns; ++u) acc += part[((il * TB + b) * 4 + c) * ns + u];
+          for (int u = 0; u < ns; ++u) acc += part[((m * TB + b) * 4 + c) * ns + u];
           v[c] = acc;
         }
         const float h0 = silu_mul(v[0] * g13, v[2] * g13);
@@ -997,7 +1018,7 @@ struct Down {
 // Items (gate/up) and tiles (down) in flight per wave.
 template <int TB, int WT> constexpr int gu_depth() { return WT == WT_NVFP4 ? (TB <= 2 ? 2 : 4) : 1; }
 template <int TB, int WTR, int WTS> constexpr int down_depth() {
-  return (WTR == WT_NVFP4 && WTS == WT_NVFP4) ? (TB == 1 ? 4 : (TB >= 8 ? 4 : 6)) : 3;
+  return (WTR == WT_NVFP4 && WTS == WT_NVFP4) ? (TB == 1 ? 4 : (TB == 2 ? 6 : 8)) : 3;
 }
 
 // Logit words each thread gathers: exact for a fixed shape, else enough for
