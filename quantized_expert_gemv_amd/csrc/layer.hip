@@ -236,7 +236,8 @@ struct SlotTab {
     const uint32_t a0 = rl(v[0], i), a1 = rl(v[1], i);
     return i >= 64 ? a1 : a0;
   }
-  __device__ __forceinline__ int expert(int d, int E) const { return min(max((int)pick2(id, d), 0), E - 1); }
+  // clamped to a valid expert (an unsigned min, which stays on the scalar unit)
+  __device__ __forceinline__ int expert(int d, int E) const { return (int)min(pick2(id, d), (uint32_t)(E - 1)); }
   __device__ __forceinline__ unsigned tokens(int d) const { return pick2(mask, d); }
   __device__ __forceinline__ float w13(int d) const { return __uint_as_float(pick2(g13, d)); }
   __device__ __forceinline__ int rank(int d, int b) const {
@@ -293,19 +294,35 @@ __device__ __forceinline__ const uint8_t* pick(bool dm, const uint8_t* real, con
   return reinterpret_cast<const uint8_t*>((uintptr_t)real ^ (((uintptr_t)real ^ (uintptr_t)dummy) & m));
 }
 
-__device__ __forceinline__ uint32_t ld32(const uint8_t* p) { return *reinterpret_cast<const uint32_t*>(p); }
+// Byte offset of expert (or shared expert) e in a region of the given stride:
+// 32-bit arithmetic for a fixed shape, whose regions the host checks to be
+// below 4 GiB.
+template <class A>
+__device__ __forceinline__ size_t expert_off(int e, size_t stride) {
+  if constexpr (std::is_base_of<DynShape, A>::value) return (size_t)e * stride;
+  else return (size_t)((uint32_t)e * (uint32_t)stride);
+}
 
-// NVFP4 byte offsets of (slice sl, step t): code unit, and the scale word
-// shared by steps t & ~1 and t | 1.
-__device__ __forceinline__ uint32_t code_off(const LaneGeo& L, int sl, int t) {
-  return (uint32_t)(sl * L.nsteps + t) * L.su16 + L.c_off;
+// Loads at a wave-uniform base plus the lane's 32-bit offset (the
+// scalar-base addressing form: no per-lane 64-bit address arithmetic).
+__device__ __forceinline__ uint4 ld16o(const uint8_t* base, uint32_t off) {
+  return *reinterpret_cast<const uint4*>(base + off);
 }
-__device__ __forceinline__ uint32_t scale_off(const LaneGeo& L, int sl, int t) {
-  return (uint32_t)(sl * (L.nsteps >> 1) + (t >> 1)) * L.su4 + L.s_off;
+__device__ __forceinline__ uint32_t ld32o(const uint8_t* base, uint32_t off) {
+  return *reinterpret_cast<const uint32_t*>(base + off);
 }
-// BF16 unit `sub` (elements 8 sub .. 8 sub + 7 of the lane's chunk) of (sl, t).
-__device__ __forceinline__ uint32_t bf16_off(const LaneGeo& L, int sl, int t, int sub) {
-  return (uint32_t)((sl * L.nsteps + t) * 4 + sub) * L.su16 + L.c_off;
+
+// Wave-uniform NVFP4 byte offsets of (slice sl, step t): code units, and the
+// scale words shared by steps t & ~1 and t | 1.  A lane adds L.c_off / L.s_off.
+__device__ __forceinline__ uint32_t code_step(const LaneGeo& L, int sl, int t) {
+  return (uint32_t)(sl * L.nsteps + t) * L.su16;
+}
+__device__ __forceinline__ uint32_t scale_step(const LaneGeo& L, int sl, int t) {
+  return (uint32_t)(sl * (L.nsteps >> 1) + (t >> 1)) * L.su4;
+}
+// BF16 unit `sub` (elements 8 sub .. 8 sub + 7 of a lane's chunk) of (sl, t).
+__device__ __forceinline__ uint32_t bf16_step(const LaneGeo& L, int sl, int t, int sub) {
+  return (uint32_t)((sl * L.nsteps + t) * 4 + sub) * L.su16;
 }
 
 // One lane's share of one wave step of a packed matrix.
@@ -319,12 +336,13 @@ template <> struct Tile<WT_BF16> { uint4 c[4]; };
 template <int WT>
 __device__ __forceinline__ void tile_load(Tile<WT>& tl, const uint8_t* codes, const uint8_t* scales,
                                           const LaneGeo& L, int sl, int t, bool dm, const uint8_t* dummy) {
+  const uint32_t lm = dm ? 0u : ~0u;
   if constexpr (WT == WT_NVFP4) {
-    tl.c = ld16(pick(dm, codes + code_off(L, sl, t), dummy));
-    tl.sw = ld32(pick(dm, scales + scale_off(L, sl, t), dummy));
+    tl.c = ld16o(pick(dm, codes + code_step(L, sl, t), dummy), L.c_off & lm);
+    tl.sw = ld32o(pick(dm, scales + scale_step(L, sl, t), dummy), L.s_off & lm);
   } else {
 #pragma unroll
-    for (int sub = 0; sub < 4; ++sub) tl.c[sub] = ld16(pick(dm, codes + bf16_off(L, sl, t, sub), dummy));
+    for (int sub = 0; sub < 4; ++sub) tl.c[sub] = ld16o(pick(dm, codes + bf16_step(L, sl, t, sub), dummy), L.c_off & lm);
   }
 }
 
@@ -356,19 +374,21 @@ template <> struct Quad<WT_BF16> { uint4 c[4][4]; };
 template <int WT>
 __device__ __forceinline__ void quad_load(Quad<WT>& q, const uint8_t* codes, const uint8_t* scales, const LaneGeo& L,
                                           int sl, int gate_steps, int t2, bool dm, const uint8_t* dummy) {
+  const uint32_t lm = dm ? 0u : ~0u;
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
     const int t = u * gate_steps + 2 * t2;
     if constexpr (WT == WT_NVFP4) {
-      const uint32_t co = code_off(L, sl, t);
-      q.c[2 * u] = ld16(pick(dm, codes + co, dummy));
-      q.c[2 * u + 1] = ld16(pick(dm, codes + co + L.su16, dummy));
-      q.sw[u] = ld32(pick(dm, scales + scale_off(L, sl, t), dummy));
+      const uint8_t* cb = pick(dm, codes + code_step(L, sl, t), dummy);
+      q.c[2 * u] = ld16o(cb, L.c_off & lm);
+      q.c[2 * u + 1] = ld16o(cb + (dm ? 0u : L.su16), L.c_off & lm);
+      q.sw[u] = ld32o(pick(dm, scales + scale_step(L, sl, t), dummy), L.s_off & lm);
     } else {
 #pragma unroll
       for (int st = 0; st < 2; ++st)
 #pragma unroll
-        for (int sub = 0; sub < 4; ++sub) q.c[2 * u + st][sub] = ld16(pick(dm, codes + bf16_off(L, sl, t + st, sub), dummy));
+        for (int sub = 0; sub < 4; ++sub)
+          q.c[2 * u + st][sub] = ld16o(pick(dm, codes + bf16_step(L, sl, t + st, sub), dummy), L.c_off & lm);
     }
   }
 }
@@ -469,12 +489,12 @@ struct GateUp {
       // a layer without shared experts has no shared buffer: x stands in (its
       // items are all dummies, whose loads read x anyway)
       const int sh = min(slot, MOE_MAX_SHARED - 1);
-      c = (a.s_codes ? a.s_codes : reinterpret_cast<const uint8_t*>(a.x)) + (size_t)sh * a.s_code_stride;
-      sc = (a.s_scales ? a.s_scales : reinterpret_cast<const uint8_t*>(a.x)) + (size_t)sh * a.s_scale_stride;
+      c = (a.s_codes ? a.s_codes : reinterpret_cast<const uint8_t*>(a.x)) + expert_off<A>(sh, a.s_code_stride);
+      sc = (a.s_scales ? a.s_scales : reinterpret_cast<const uint8_t*>(a.x)) + expert_off<A>(sh, a.s_scale_stride);
     } else {
       const int e = tb.expert(min(slot, kMaxD - 1), a.E);
-      c = a.r_codes + (size_t)e * a.r_code_stride;
-      sc = (WT == WT_NVFP4) ? a.r_scales + (size_t)e * a.r_scale_stride : reinterpret_cast<const uint8_t*>(a.x);
+      c = a.r_codes + expert_off<A>(e, a.r_code_stride);
+      sc = (WT == WT_NVFP4) ? a.r_scales + expert_off<A>(e, a.r_scale_stride) : reinterpret_cast<const uint8_t*>(a.x);
     }
   }
   // Loads the next item of this wave, or a dummy once they are all loaded.
@@ -915,14 +935,14 @@ struct Down {
     const int ex = dm ? 0 : ex_of(cx), t = dm ? t_lo : t_lo + cj;
     const uint8_t* dummy = reinterpret_cast<const uint8_t*>(a.x);
     if (ex < a.S) {
-      const uint8_t* c = a.s_codes + (size_t)ex * a.s_code_stride + a.s_w13_code;
-      const uint8_t* sc = (WTS == WT_NVFP4) ? a.s_scales + (size_t)ex * a.s_scale_stride + a.s_w13_scale : dummy;
+      const uint8_t* c = a.s_codes + expert_off<A>(ex, a.s_code_stride) + a.s_w13_code;
+      const uint8_t* sc = (WTS == WT_NVFP4) ? a.s_scales + expert_off<A>(ex, a.s_scale_stride) + a.s_w13_scale : dummy;
       if constexpr (WTR == WTS) tile_load<WTR>(br[p], c, sc, L, 0, t, dm, dummy);
       else tile_load<WTS>(bs[p], c, sc, L, 0, t, dm, dummy);
     } else {
       const int e = tb.expert(min(ex - a.S, kMaxD - 1), a.E);
-      const uint8_t* c = a.r_codes + (size_t)e * a.r_code_stride + a.r_w13_code;
-      const uint8_t* sc = (WTR == WT_NVFP4) ? a.r_scales + (size_t)e * a.r_scale_stride + a.r_w13_scale : dummy;
+      const uint8_t* c = a.r_codes + expert_off<A>(e, a.r_code_stride) + a.r_w13_code;
+      const uint8_t* sc = (WTR == WT_NVFP4) ? a.r_scales + expert_off<A>(e, a.r_scale_stride) + a.r_w13_scale : dummy;
       tile_load<WTR>(br[p], c, sc, L, 0, t, dm, dummy);
     }
     qj[p] = cj;
@@ -1381,6 +1401,9 @@ int launch_fused(const FusedArgs& a, int tb, int rwt, int swt, void* stream) {
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   (void)hipGetLastError();  // clear a stale error so it is not reported as ours
   const int shape = fixed_shape_of(a.H, a.I, a.E, a.k, a.S, a.Er);
+  // a fixed shape addresses experts with 32-bit offsets
+  if (shape != 0 && ((size_t)a.E * a.r_code_stride >= (1ull << 32) || (size_t)a.E * a.r_scale_stride >= (1ull << 32)))
+    return kNoVariant;
   return with_variant(shape, tb, fused_qx(a.H), rwt, swt,
                       [&](auto t) -> int { return decltype(t)::type::launch(a, st); });
 }
