@@ -12,9 +12,11 @@ i % L with its own input, so the touched bytes of a cycle (~631 MB at batch
 The timed region replays a HIP graph of the K steps (captured once, after W
 eager warm-up steps and one untimed replay), bracketed by
 torch.cuda.synchronize() and HIP events on the stream the kernels run on.
-A second timed region runs the same K steps eagerly with the library's
-profiling events around its one kernel; it gives the kernel's average
-duration, from which the roofline figure is computed.
+A step is one launch and the replayed launches run back to back, so the
+region's time per step is the kernel's average launch duration, from which
+the roofline figure is computed.  A second timed region runs the same K
+steps eagerly with the library's profiling events around each launch (a
+cross-check that also times the event packets and the dispatch).
 
 Prints one JSON line.
 """
@@ -184,7 +186,7 @@ def main():
     us_step = total_ms * 1e3 / K
     print(f"[bench] timed {K} steps ({mode}): {us_step:.2f} us/step", file=sys.stderr, flush=True)
 
-    # second timed region: eager, with events between the three kernels
+    # second timed region: eager, with events around each launch
     n_ev = 2 * K
     evs = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
     for e in evs:
@@ -219,7 +221,12 @@ def main():
     gbs = algo["total"] / (us_step * 1e-6) / 1e9
     roof = None
     if kern is not None:
-        k_us = kern["layer_kernel_us"]
+        # A layer step is one launch and graph-replayed launches run back to
+        # back (no gaps in rocprofv3's kernel trace), so the timed region's
+        # events give the average launch duration.  The eager per-launch
+        # events (kernels.layer_kernel_us) also time the event packets and
+        # the dispatch, and stay a cross-check.
+        k_us = us_step if mode == "hipgraph" else kern["layer_kernel_us"]
         achieved = algo["total"] / (k_us * 1e-6) / 1e9
         traffic = None
         tf = os.path.join(ROOT, "profiles", f"traffic_{args.workload}.json")
@@ -231,7 +238,10 @@ def main():
                 traffic = t.get("dominant_bytes_per_launch")
         roof = {"bound": "hbm", "kernel": "k_fused_layer", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "algorithmic_bytes_per_launch": int(round(algo["total"]))}
+                "algorithmic_bytes_per_launch": int(round(algo["total"])),
+                "launch_us": round(k_us, 3),
+                "launch_us_source": ("events around the graph-replayed timed region / launches"
+                                     if mode == "hipgraph" else "events around each eager launch")}
 
     cpu = None
     if not args.no_cpu:
