@@ -305,11 +305,16 @@ __device__ __forceinline__ size_t expert_off(int e, size_t stride) {
 
 // Loads at a wave-uniform base plus the lane's 32-bit offset (the
 // scalar-base addressing form: no per-lane 64-bit address arithmetic).
-__device__ __forceinline__ uint4 ld16o(const uint8_t* base, uint32_t off) {
-  return *reinterpret_cast<const uint4*>(base + off);
+// Weights are read once per call: non-temporal loads, so that they do not
+// push the kernel's code, arguments and small shared data out of the L2.
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 ld16nt(const void* p) {
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
 }
+__device__ __forceinline__ uint4 ld16o(const uint8_t* base, uint32_t off) { return ld16nt(base + off); }
 __device__ __forceinline__ uint32_t ld32o(const uint8_t* base, uint32_t off) {
-  return *reinterpret_cast<const uint32_t*>(base + off);
+  return __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(base + off));
 }
 
 // Wave-uniform NVFP4 byte offsets of (slice sl, step t): code units, and the
@@ -1073,7 +1078,7 @@ __global__ __launch_bounds__(NT) void k_fused_layer(A a) {
     for (int q = 0; q < QX; ++q) {
       const int u = min(tid + q * NT, U - 1);
       const int row = (rr < nrr) ? w + rr * G : w;   // second row: a duplicate when absent
-      rw[rr][q] = ld16(a.router_w + (size_t)row * a.H + u * 8);
+      rw[rr][q] = ld16nt(a.router_w + (size_t)row * a.H + u * 8);
     }
 #pragma unroll
   for (int b = 0; b < TB; ++b)
@@ -1119,7 +1124,6 @@ __global__ __launch_bounds__(NT) void k_fused_layer(A a) {
   GateUp<TB, WTS, 1> gus;   // one item in flight: its tiles stay in registers until after routing
   gus.init(a, L13, 1);
   gus.set_items(a, a.S * gs2);
-  gus.prime(a, tab);
 
   // ---- pre-norm: xhat = bf16(x / rms(x) * gamma) -----------------------------
   if (a.prenorm) {
@@ -1231,6 +1235,9 @@ __global__ __launch_bounds__(NT) void k_fused_layer(A a) {
               [&](int i, uint32_t v) { lg[(i % a.B) * a.Er + i / a.B] = __uint_as_float(v); });
   __syncthreads();
   if (w == 0 && tid == 0) __hip_atomic_store(a.epoch, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  // The shared experts' tiles load during routing (not earlier: the logit
+  // polls wait, in order, for every load of their wave).
+  gus.prime(a, tab);
 
   // ---- routing ---------------------------------------------------------------------
   constexpr int TPW = (TB > NW) ? 2 : 1;
