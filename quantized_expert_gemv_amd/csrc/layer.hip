@@ -1235,9 +1235,6 @@ __global__ __launch_bounds__(NT) void k_fused_layer(A a) {
               [&](int i, uint32_t v) { lg[(i % a.B) * a.Er + i / a.B] = __uint_as_float(v); });
   __syncthreads();
   if (w == 0 && tid == 0) __hip_atomic_store(a.epoch, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  // The shared experts' tiles load during routing (not earlier: the logit
-  // polls wait, in order, for every load of their wave).
-  gus.prime(a, tab);
 
   // ---- routing ---------------------------------------------------------------------
   constexpr int TPW = (TB > NW) ? 2 : 1;
@@ -1246,6 +1243,10 @@ __global__ __launch_bounds__(NT) void k_fused_layer(A a) {
   else route<8, TPW, TB, WTR, WTS>(a, s, lg, eb, er);
 
   // ---- phase 2: selected experts' gate/up; the down weights start loading ------------
+  // The shared experts' tiles first (not before the logit gather: the polls
+  // wait, in order, for every load of their wave; not before routing, which
+  // at batch 1 runs in wave 0 alone).
+  gus.prime(a, tab);
   tab.load(s, lane);
   const int nd = s.nd;
   down.set_experts(a.S + nd);
