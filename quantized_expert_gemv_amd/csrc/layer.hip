@@ -1242,7 +1242,7 @@ __global__ __launch_bounds__(NT) void k_fused_layer(A a) {
   else if (a.E <= 256) route<4, TPW, TB, WTR, WTS>(a, s, lg, eb, er);
   else route<8, TPW, TB, WTR, WTS>(a, s, lg, eb, er);
 
-  // ---- phase 2: selected experts' gate/up; the down weights start loading ------------
+  // ---- phase 2: shared and selected experts' gate/up --------------------------------
   // The shared experts' tiles first (not before the logit gather: the polls
   // wait, in order, for every load of their wave; not before routing, which
   // at batch 1 runs in wave 0 alone).
@@ -1255,12 +1255,17 @@ __global__ __launch_bounds__(NT) void k_fused_layer(A a) {
     gur.init(a, L13, 0);
     gur.set_items(a, nd * gs2);
     gur.prime(a, tab);
-    down.prime(a, tab);
-    // the shared experts' tiles were loaded at the start: their gate/up runs
-    // while the selected experts' first tiles are in flight
+    // At batch 4-8 gate/up is long enough to hide the down weights' loads too.
+    if constexpr (TB > 2) down.prime(a, tab);
+    // the shared experts' tiles are on their way: their gate/up runs while the
+    // selected experts' first tiles are in flight
     gus.run(a, s, tab, xr, act, xcol, part, tag);
     gur.run(a, s, tab, xr, act, xcol, part, tag);
   }
+  // At batch 1-2 the down weights load after gate/up, while the activations
+  // are exchanged: issued with the gate/up burst they arrived late, and the
+  // exchange's polls wait, in order, for every load of their wave.
+  if constexpr (TB <= 2) down.prime(a, tab);
 
   // ---- phase 3: gather activations, down GEMV + combine ---------------------------------
   // a wave with no expert of its subset writes no partial sums: start from zero
