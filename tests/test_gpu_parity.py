@@ -73,6 +73,28 @@ def test_ragged_batches_on_a_batch8_handle():
         assert not r["mismatched"] and r["rel_err"] <= 1e-2
 
 
+# Shapes other than Flint's run the kernel variants that read the shape from
+# the arguments; these two cover every batch bucket (1, 2, 4, 8) of them, with
+# one wave step per row (H=1024) and four rows per step (H=512) in gate/up.
+_GENERIC = {
+    "generic_h1024": dict(hidden=1024, inter=256, n_routed=64, top_k=4, n_shared=2),
+    "generic_h512": dict(hidden=512, inter=128, n_routed=32, top_k=3, n_shared=1),
+}
+
+
+@pytest.mark.parametrize("name", sorted(_GENERIC))
+def test_generic_shape_every_batch_bucket(name):
+    from quantized_expert_gemv_amd.device_layer import DeviceLayer
+    from quantized_expert_gemv_amd.synth import Workload
+    wl = Workload(6, name, batch=8, router_std=None, bias_std=0.5, description=name, **_GENERIC[name])
+    layer = SynthLayer(wl)
+    dev = DeviceLayer(layer, 8)
+    for n in (1, 2, 3, 5, 8):
+        r = compare_layer(dev, layer, layer.x(200 + n, batch=n))
+        _report(f"{name} batch {n} D={len(set(r['ids'].ravel().tolist()))}", r)
+        assert not r["mismatched"] and r["rel_err"] <= 1e-2 and r["w_err"] <= 1e-4
+
+
 def test_sink_parity_sampled_tokens():
     layer, dev = dev_layer("sink_b4")
     r = compare_layer(dev, layer, layer.x(0), tokens=[0, 3])
