@@ -445,6 +445,7 @@ struct GateUp {
   int ns, grp, ngr, lg_ngr, sl;
   int nmine, nloaded, cslot, ct2, cm;   // this wave's item count, items loaded, next item (slot, pair, m)
   int dslot, dt2;                       // next item of the wave: + dslot slots, + dt2 pairs
+  unsigned tmask;                       // tokens this wave computes (shared items at batch 4-8)
   LaneGeo L;
 
   // Everything that does not depend on the routing.
@@ -463,6 +464,16 @@ struct GateUp {
     // shared items (at most a few per workgroup) go to the last groups, which
     // never hold more routed items than the first ones
     if (shared) grp = ngr - 1 - grp;
+    tmask = ~0u;
+    if (shared && TB >= 4 && ns == 1) {
+      // A shared item carries every token (several routed items' work): each
+      // wave takes every shared item of the workgroup for its tokens b = wave
+      // (mod NW) only, so the waves stay balanced.
+      tmask = 0x11111111u << wave;
+      grp = 0;
+      ngr = 1;
+      lg_ngr = 0;
+    }
   }
   // The phase's item count n.
   template <class A>
@@ -562,7 +573,7 @@ struct GateUp {
                                        const uint16_t* xs, int xcol, float* part, uint32_t tag, int p, bool live,
                                        bool lead) {
     const int slot = qslot[p], t2 = qt2[p];
-    const unsigned mask = shared ? (1u << a.B) - 1u : tb.tokens(min(slot, kMaxD - 1));
+    const unsigned mask = shared ? ((1u << a.B) - 1u) & tmask : tb.tokens(min(slot, kMaxD - 1));
     const float g13 = shared ? ((WT == WT_NVFP4) ? s.tss[min(slot, MOE_MAX_SHARED - 1)][0] : 1.0f)
                              : tb.w13(min(slot, kMaxD - 1));
     if constexpr (XR == TB) {
