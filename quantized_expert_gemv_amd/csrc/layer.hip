@@ -904,6 +904,7 @@ __device__ __forceinline__ void route(const A& a, Smem& s, const float* lg, cons
 // order: shared 0..S-1, then routed slots 0..nd-1.  If spg >= NW, wave w
 // takes steps w, w + NW, ... with every expert; otherwise nsub = NW / spg
 // waves share a step, wave w taking experts w / spg, w / spg + nsub, ...
+// (at batch 4-8: every shared expert for its own tokens, see set_experts)
 // Per step the lane sums weight x partial dot over its experts in
 // registers; one lane reduction per (step, token) follows.  P tiles are
 // loading at a time.
@@ -912,6 +913,8 @@ struct Down {
   Tile<WTR> br[P];
   Tile<WTS> bs[(WTR == WTS) ? 1 : P];   // same types: shared tiles use br
   int t_lo, spg, nsub, lg_nsub, sub, nex, nj, ntiles;
+  int nsh;                             // shared experts every sub takes (batch 4-8 with nsub > 1), else 0
+  unsigned smask;                      // tokens of the shared tiles this wave computes
   int cj, cx, nloaded;                 // next tile to load: step index, expert index (mine)
   int qj[P], qx[P];
   LaneGeo L;
@@ -937,13 +940,28 @@ struct Down {
     }
     lg_nsub = (nsub == 4) ? 2 : (nsub == 2) ? 1 : 0;
   }
-  __device__ __forceinline__ void set_experts(int nexp) {
-    nex = (nexp > sub) ? (nexp - sub + nsub - 1) >> lg_nsub : 0;
+  // S shared experts, nd selected ones.  Experts in order: shared 0..S-1,
+  // then routed slots.  At batch 4-8 a shared tile carries every token
+  // (several routed tiles' work), so when waves share a step every sub takes
+  // every shared expert, for its tokens b = sub (mod nsub) only, and the
+  // routed slots alternate; otherwise the whole list alternates.
+  __device__ __forceinline__ void set_experts(int S, int nd) {
+    nsh = (TB >= 4 && nsub > 1) ? S : 0;
+    if (nsh > 0) {
+      nex = nsh + ((nd > sub) ? (nd - sub + nsub - 1) >> lg_nsub : 0);
+      smask = ((nsub == 4) ? 0x11111111u : 0x55555555u) << sub;
+    } else {
+      const int nexp = S + nd;
+      nex = (nexp > sub) ? (nexp - sub + nsub - 1) >> lg_nsub : 0;
+      smask = ~0u;
+    }
     ntiles = nj * nex;
     cx = 0;
     nloaded = 0;
   }
-  __device__ __forceinline__ int ex_of(int xi) const { return sub + xi * nsub; }
+  __device__ __forceinline__ int ex_of(int xi) const {
+    return (xi < nsh) ? xi : nsh + sub + ((xi - nsh) << lg_nsub);
+  }
   // Loads the next tile of this wave, or a dummy once they are all loaded.
   template <class A>
   __device__ __forceinline__ void load_next(const A& a, const SlotTab& tb, int p) {
@@ -989,7 +1007,7 @@ struct Down {
     if (live) {
       const bool sh = ex < a.S;
       const int slot = min(ex - a.S, kMaxD - 1);
-      const unsigned mask = sh ? (1u << a.B) - 1u : tb.tokens(slot);
+      const unsigned mask = sh ? ((1u << a.B) - 1u) & smask : tb.tokens(slot);
 #pragma unroll
       for (int b = 0; b < TB; ++b) {
         if ((mask >> b) & 1u) {
@@ -1260,7 +1278,7 @@ __global__ __launch_bounds__(NT) void k_fused_layer(A a) {
   gus.prime(a, tab);
   tab.load(s, lane);
   const int nd = s.nd;
-  down.set_experts(a.S + nd);
+  down.set_experts(a.S, nd);
   {
     GateUp<TB, WTR, gu_depth<TB, WTR>()> gur;
     gur.init(a, L13, 0);
