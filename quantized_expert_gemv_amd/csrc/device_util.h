@@ -19,12 +19,16 @@ enum { WT_NVFP4 = 0, WT_BF16 = 1 };
 __device__ __forceinline__ float bf16lo(uint32_t v) { return __uint_as_float(v << 16); }
 __device__ __forceinline__ float bf16hi(uint32_t v) { return __uint_as_float(v & 0xffff0000u); }
 
-// fp32 -> bf16 bits, round to nearest even; NaN -> canonical quiet NaN.
+// fp32 -> bf16 bits, round to nearest even (gfx950 converts in hardware:
+// v_cvt_pk_bf16_f32); a NaN stays a quiet NaN.
 __device__ __forceinline__ uint32_t f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
+  return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)f);
+}
+// Two values as one packed bf16 pair (lo in the low half): one conversion.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  const f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
 __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
@@ -95,7 +99,7 @@ __device__ __forceinline__ void unpack4(const uint4& v, uint32_t* d) {
 __device__ __forceinline__ uint32_t norm_pair(uint32_t xv, uint32_t gv, float rn) {
   const float lo = (bf16lo(xv) * rn) * bf16lo(gv);
   const float hi = (bf16hi(xv) * rn) * bf16hi(gv);
-  return f2bf(lo) | (f2bf(hi) << 16);
+  return pack_bf16x2(lo, hi);
 }
 
 }  // namespace moe

@@ -415,7 +415,11 @@ __device__ __forceinline__ void lds_chunk(const uint16_t* p, uint32_t (&a)[16]) 
   for (int i = 0; i < 4; ++i) unpack4(q[i], &a[4 * i]);
 }
 
-__device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + __expf(-g)) * u; }
+// SiLU(g) * u; the logistic's reciprocal is the hardware's (1 ulp), far
+// below the bf16 rounding of h that follows.
+__device__ __forceinline__ float silu_mul(float g, float u) {
+  return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
+}
 
 // ---------------------------------------------------------------------------
 // gate/up phases
@@ -556,7 +560,7 @@ struct GateUp {
       if (lead) {
         const float h0 = silu_mul(v[0] * g13, v[2] * g13);
         const float h1 = silu_mul(v[1] * g13, v[3] * g13);
-        publish(a.xh + (size_t)pr * (a.I / 2) + t2 * a.g13.rpw + L.ri, f2bf(h0) | (f2bf(h1) << 16), tag);
+        publish(a.xh + (size_t)pr * (a.I / 2) + t2 * a.g13.rpw + L.ri, pack_bf16x2(h0, h1), tag);
       }
     } else {
 #pragma unroll
@@ -653,7 +657,7 @@ struct GateUp {
         const float h1 = silu_mul(v[1] * g13, v[3] * g13);
         const int pr = shared ? a.B * a.k + slot * a.B + b
                               : b * a.k + (int)((s.pr[slot][b >> 2] >> (8 * (b & 3))) & 0xffu);
-        publish(a.xh + (size_t)pr * (a.I / 2) + t2, f2bf(h0) | (f2bf(h1) << 16), tag);
+        publish(a.xh + (size_t)pr * (a.I / 2) + t2, pack_bf16x2(h0, h1), tag);
       }
       // the partials are read: a following pass may overwrite them
       __syncthreads();
@@ -696,10 +700,13 @@ __device__ __forceinline__ void cas(unsigned& ka, int& ia, unsigned& kb, int& ib
 // [l MK, l MK + MK), sorted by key.  Each round the wave's largest head key
 // wins (ties to the lowest lane, i.e. the lowest expert), the winning lane
 // shifts its list; the lanes' chains for the TPW tokens are independent.
-// Lane r ends with the r-th selection: expert my_e, logit my_l.
+// Lane r ends with the r-th selection: expert my_e, logit my_l, and its
+// sigmoid my_sg; sg_sum (uniform) is the sum of the k sigmoids.  The winning
+// logit of a round is uniform, so its sigmoid is computed while the next
+// round's maximum is on its way through the lanes.
 template <int MK, int TPW, class A>
-__device__ __forceinline__ void topk(const A& a, const float* lg, int lane, int (&my_e)[TPW],
-                                     float (&my_l)[TPW]) {
+__device__ __forceinline__ void topk(const A& a, const float* lg, int lane, int (&my_e)[TPW], float (&my_l)[TPW],
+                                     float (&my_sg)[TPW], float (&sg_sum)[TPW]) {
   const int wave = wave_id();
   unsigned key[TPW][MK];
   int idx[TPW][MK];
@@ -729,6 +736,8 @@ __device__ __forceinline__ void topk(const A& a, const float* lg, int lane, int 
     }
     my_e[t] = 0;
     my_l[t] = 0.f;
+    my_sg[t] = 0.f;
+    sg_sum[t] = 0.f;
   }
   for (int r = 0; r < a.k; ++r) {
     unsigned M[TPW];
@@ -739,8 +748,12 @@ __device__ __forceinline__ void topk(const A& a, const float* lg, int lane, int 
       const int win = __builtin_ctzll(__ballot(key[t][0] == M[t]));
       const int e_sel = __builtin_amdgcn_readlane(idx[t][0], win);
       const bool mine = lane == r, me = lane == win;
+      const float l_sel = unkey(M[t]);
+      const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-l_sel));
+      sg_sum[t] += sg;
       my_e[t] = mine ? e_sel : my_e[t];
-      my_l[t] = mine ? unkey(M[t]) : my_l[t];
+      my_l[t] = mine ? l_sel : my_l[t];
+      my_sg[t] = mine ? sg : my_sg[t];
 #pragma unroll
       for (int i = 0; i + 1 < MK; ++i) {
         key[t][i] = me ? key[t][i + 1] : key[t][i];
@@ -752,10 +765,11 @@ __device__ __forceinline__ void topk(const A& a, const float* lg, int lane, int 
 }
 
 // One token's routing weight in lane r < k (its r-th selection, logit
-// my_l) and shared coefficient in lane s < S, from its logits l.
+// my_l, sigmoid my_sg; sg_sum the sum of the k sigmoids) and shared
+// coefficient in lane s < S, from its logits l.
 template <class A>
-__device__ __forceinline__ void token_weights(const A& a, const float* l, int lane, float my_l, float& wv,
-                                              float& shc) {
+__device__ __forceinline__ void token_weights(const A& a, const float* l, int lane, float my_l, float my_sg,
+                                              float sg_sum, float& wv, float& shc) {
   if (a.route == MOE_ROUTE_SOFTMAX_SINK) {
     unsigned mk = 0u;
     for (int e = lane; e < a.Er; e += 64) mk = max(mk, fkey(l[e]));
@@ -766,8 +780,7 @@ __device__ __forceinline__ void token_weights(const A& a, const float* l, int la
     wv = __expf(my_l - mx) / z;
     shc = (lane < a.S) ? __expf(l[a.E + min(lane, a.S - 1)] - mx) / z : 0.f;
   } else {
-    const float sg = (lane < a.k) ? 1.0f / (1.0f + __expf(-my_l)) : 0.f;
-    wv = sg / wave_sum(sg);
+    wv = my_sg * __builtin_amdgcn_rcpf(sg_sum);
     shc = 1.0f;
   }
 }
@@ -776,14 +789,15 @@ __device__ __forceinline__ void token_weights(const A& a, const float* l, int la
 // into shared memory, with the token masks of the selected experts.
 template <int TPW, class A>
 __device__ __forceinline__ void route_weights(const A& a, Smem& s, const float* lg, int lane,
-                                              const int (&my_e)[TPW], const float (&my_l)[TPW]) {
+                                              const int (&my_e)[TPW], const float (&my_l)[TPW],
+                                              const float (&my_sg)[TPW], const float (&sg_sum)[TPW]) {
   const int wave = wave_id();
 #pragma unroll
   for (int t = 0; t < TPW; ++t) {
     const int b = wave + t * NW;
     if (b >= a.B) continue;
     float wv, shc;
-    token_weights(a, lg + (size_t)b * a.Er, lane, my_l[t], wv, shc);
+    token_weights(a, lg + (size_t)b * a.Er, lane, my_l[t], my_sg[t], sg_sum[t], wv, shc);
     if (lane < a.S) s.shc[b][lane] = shc;
     if (lane < a.k) {
       s.sel[b][lane] = my_e[t];
@@ -851,10 +865,10 @@ __device__ __forceinline__ void route(const A& a, Smem& s, const float* lg, cons
     // so wave 0 fills the tables from its registers.
     if (wave == 0) {
       int my_e[1];
-      float my_l[1];
-      topk<MK, 1>(a, lg, lane, my_e, my_l);
+      float my_l[1], my_sg[1], sg_sum[1];
+      topk<MK, 1>(a, lg, lane, my_e, my_l, my_sg, sg_sum);
       float wv, shc;
-      token_weights(a, lg, lane, my_l[0], wv, shc);
+      token_weights(a, lg, lane, my_l[0], my_sg[0], sg_sum[0], wv, shc);
       if (lane < a.k) {
         const int e = my_e[0];
         s.ids[lane] = e;
@@ -879,9 +893,9 @@ __device__ __forceinline__ void route(const A& a, Smem& s, const float* lg, cons
   }
   if (wave < a.B) {
     int my_e[TPW];
-    float my_l[TPW];
-    topk<MK, TPW>(a, lg, lane, my_e, my_l);
-    route_weights<TPW>(a, s, lg, lane, my_e, my_l);
+    float my_l[TPW], my_sg[TPW], sg_sum[TPW];
+    topk<MK, TPW>(a, lg, lane, my_e, my_l, my_sg, sg_sum);
+    route_weights<TPW>(a, s, lg, lane, my_e, my_l, my_sg, sg_sum);
   }
   __syncthreads();
   if (wave == 0) number_slots<WTR, WTS>(a, s, lane, eb, er);
