@@ -540,6 +540,10 @@ struct GateUp {
   }
   template <class A>
   __device__ __forceinline__ void prime(const A& a, const SlotTab& tb) {
+    // a wave with no item of the phase reads none of its buffers (every step
+    // is dead), so it issues nothing: no address arithmetic on the scalar
+    // unit the CU's waves share, no dummy loads
+    if (nmine == 0) return;
 #pragma unroll
     for (int p = 0; p < PI; ++p) load_next(a, tb, p);
   }
