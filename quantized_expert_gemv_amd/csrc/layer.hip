@@ -356,7 +356,7 @@ __device__ __forceinline__ void tile_load(Tile<WT>& tl, const uint8_t* codes, co
 __device__ __forceinline__ float chunk_dot_fp4(const uint4& c, uint32_t sp, const uint32_t (&act)[16]) {
   uint32_t w[16];
   decode_chunk(c, w);
-  return fmaf(dot8<8>(w, act), e4m3f<1>(sp), dot8<0>(w, act) * e4m3f<0>(sp));
+  return fmaf(dot8c<8>(w, act), e4m3f<1>(sp), dot8c<0>(w, act) * e4m3f<0>(sp));
 }
 __device__ __forceinline__ float chunk_dot_bf16(const uint4 (&c)[4], const uint32_t (&act)[16]) {
   uint32_t w[16];
