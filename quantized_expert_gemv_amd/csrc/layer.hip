@@ -1284,16 +1284,19 @@ __global__ __launch_bounds__(NT) void k_fused_layer(A a) {
   if (w == 0 && tid == 0) __hip_atomic_store(a.epoch, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
   // ---- routing ---------------------------------------------------------------------
+  // At batch 1 routing runs in wave 0 alone; meanwhile the wave that owns the
+  // shared item issues its tiles (a wave without one issues nothing, so wave
+  // 0 starts routing at once).  Not before the logit gather: the polls wait,
+  // in order, for every load of their wave.
+  if constexpr (TB == 1) gus.prime(a, tab);
   constexpr int TPW = (TB > NW) ? 2 : 1;
   if (a.E <= 64) route<1, TPW, TB, WTR, WTS>(a, s, lg, eb, er);
   else if (a.E <= 256) route<4, TPW, TB, WTR, WTS>(a, s, lg, eb, er);
   else route<8, TPW, TB, WTR, WTS>(a, s, lg, eb, er);
 
   // ---- phase 2: shared and selected experts' gate/up --------------------------------
-  // The shared experts' tiles first (not before the logit gather: the polls
-  // wait, in order, for every load of their wave; not before routing, which
-  // at batch 1 runs in wave 0 alone).
-  gus.prime(a, tab);
+  // The shared experts' tiles first (at batch 1 they are already loading).
+  if constexpr (TB != 1) gus.prime(a, tab);
   tab.load(s, lane);
   const int nd = s.nd;
   down.set_experts(a.S, nd);
