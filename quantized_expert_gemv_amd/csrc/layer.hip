@@ -952,9 +952,13 @@ struct Down {
       cj = wave;
     } else {
       nsub = (spg == 1) ? 4 : (spg == 2) ? 2 : 1;
-      sub = wave / spg;
+      // at batch 1-2 the first waves own the most gate/up items and load
+      // their down tiles last: sub-group 0, which takes the most experts,
+      // goes to the last waves (partials still combine in sub order)
+      const int wv = (TB <= 2) ? NW - 1 - wave : wave;
+      sub = wv / spg;
       nj = (sub < nsub) ? 1 : 0;
-      cj = wave % spg;
+      cj = wv % spg;
     }
     lg_nsub = (nsub == 4) ? 2 : (nsub == 2) ? 1 : 0;
   }
