@@ -199,6 +199,7 @@ struct Smem {
   float rn[MOE_MAX_BATCH];                    // 1/rms per token
   int nd;
   uint32_t tag;
+  float kpart[8][4][NW];                      // batch-1 split-K gate/up partials [item][row][wave]
 };
 
 // Activation pairs: routed pair of token b's r-th selection = b k + r;
@@ -667,6 +668,121 @@ struct GateUp {
       __syncthreads();
     }
   }
+};
+
+// Batch 1, shapes whose gate/up rows span one 64-lane wave step (rpw = 1):
+// every wave takes every item of the workgroup over its quarter of the
+// hidden dimension, so six selected items and one shared item cost each wave
+// the same instead of two items on some waves and one on others.  Lane l
+// holds row l / 16 of the item (gate t, gate t + 1, up t, up t + 1; t = 2 t2)
+// at chunk 16 w + l % 16: one 16-byte load per item, the same lane offset for
+// every item, and a 16-lane sum; the four quarters meet in shared memory and
+// are summed in wave order.  KS shared and KR selected items per workgroup.
+template <int KS, int KR>
+struct SplitK {
+  uint4 c[KS + KR];
+  uint32_t sw[KS + KR];
+  int js, jr;                 // first shared / selected item of the workgroup
+  uint32_t off_c, off_s;      // this lane's code / scale-word byte offsets
+  int row, gate_steps;
+
+  template <class A>
+  __device__ __forceinline__ void init(const A& a, const LaneGeo& L) {
+    const int wave = wave_id(), lane = threadIdx.x & 63;
+    const int w = blockIdx.x;
+    gate_steps = a.I / a.g13.rpw;
+    js = (int)(((uint32_t)(a.S * (gate_steps >> 1)) * w) >> a.log2G);
+    jr = (int)(((uint32_t)(a.k * (gate_steps >> 1)) * w) >> a.log2G);
+    row = lane >> 4;
+    const uint32_t chunk = (uint32_t)(16 * wave + (lane & 15));
+    off_c = chunk * 16u + ((row & 1) ? L.su16 : 0u) + ((row >> 1) ? (uint32_t)gate_steps * L.su16 : 0u);
+    off_s = chunk * 4u + ((row >> 1) ? (uint32_t)(gate_steps >> 1) * L.su4 : 0u);
+  }
+  template <class A>
+  __device__ __forceinline__ void load_item(const A& a, int m, const uint8_t* cb, const uint8_t* sb, int t2,
+                                            const LaneGeo& L) {
+    c[m] = ld16o(cb + (uint32_t)(2 * t2) * L.su16, off_c);
+    sw[m] = ld32o(sb + (uint32_t)t2 * L.su4, off_s);
+  }
+  template <class A>
+  __device__ __forceinline__ void load_shared(const A& a, const LaneGeo& L) {
+    const int gs2 = gate_steps >> 1;
+#pragma unroll
+    for (int m = 0; m < KS; ++m) {
+      const int j = js + m, sh = j / gs2, t2 = j - sh * gs2;
+      load_item(a, m, a.s_codes + expert_off<A>(sh, a.s_code_stride), a.s_scales + expert_off<A>(sh, a.s_scale_stride),
+                t2, L);
+    }
+  }
+  template <class A>
+  __device__ __forceinline__ void load_routed(const A& a, const SlotTab& tb, const LaneGeo& L) {
+    const int gs2 = gate_steps >> 1;
+#pragma unroll
+    for (int m = 0; m < KR; ++m) {
+      const int j = jr + m, slot = j / gs2, t2 = j - slot * gs2;
+      const int e = tb.expert(min(slot, kMaxD - 1), a.E);
+      load_item(a, KS + m, a.r_codes + expert_off<A>(e, a.r_code_stride),
+                a.r_scales + expert_off<A>(e, a.r_scale_stride), t2, L);
+    }
+  }
+  // Dot products, quarter sums into shared memory, then (after a barrier)
+  // one thread per item adds the quarters and publishes the SiLU*up word.
+  template <class A>
+  __device__ __forceinline__ void run(const A& a, Smem& s, const uint16_t* xs, uint32_t tag) {
+    const int wave = wave_id(), lane = threadIdx.x & 63;
+    uint32_t xk[16];
+    lds_chunk(xs + (16 * wave + (lane & 15)) * 32, xk);
+#pragma unroll
+    for (int m = 0; m < KS + KR; ++m) {
+      const uint32_t sp = (row & 1) ? (sw[m] >> 16) : sw[m];
+      const float v = group_sum(chunk_dot_fp4(c[m], sp, xk), 16);
+      if ((lane & 15) == 15) s.kpart[m][row][wave] = v;
+    }
+    __syncthreads();
+    const int m = threadIdx.x;
+    if (m < KS + KR) {
+      const int gs2 = gate_steps >> 1;
+      float q[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float acc = 0.f;
+#pragma unroll
+        for (int u = 0; u < NW; ++u) acc += s.kpart[m][r][u];
+        q[r] = acc;
+      }
+      int pr, t2;
+      float g13;
+      if (m < KS) {
+        const int j = js + m, sh = j / gs2;
+        t2 = j - sh * gs2;
+        pr = a.k + sh;
+        g13 = s.tss[min(sh, MOE_MAX_SHARED - 1)][0];
+      } else {
+        const int j = jr + m - KS, slot = j / gs2;
+        t2 = j - slot * gs2;
+        pr = (int)(s.pr[min(slot, kMaxD - 1)][0] & 0xffu);
+        g13 = s.xg[min(slot, kMaxD - 1)];
+      }
+      const float h0 = silu_mul(q[0] * g13, q[2] * g13);
+      const float h1 = silu_mul(q[1] * g13, q[3] * g13);
+      publish(a.xh + (size_t)pr * (a.I / 2) + t2, pack_bf16x2(h0, h1), tag);
+    }
+  }
+};
+
+// Whether a variant runs SplitK, and its item counts with 256 workgroups
+// (the kernel checks the grid size at run time).
+template <class A, int TB, int WTR, int WTS, bool DYN = std::is_base_of<DynShape, A>::value>
+struct SplitKPlan {
+  static constexpr bool on = false;
+  static constexpr int KS = 1, KR = 1;
+};
+template <class A, int TB, int WTR, int WTS>
+struct SplitKPlan<A, TB, WTR, WTS, false> {
+  static constexpr int KS = A::S * (A::I / 2) / 256, KR = A::k * (A::I / 2) / 256;
+  static constexpr bool on = TB == 1 && WTR == WT_NVFP4 && WTS == WT_NVFP4 && A::g13.ns == 1 && A::g13.rpw == 1 &&
+                             A::g13.lpr == 64 && A::S >= 1 && (A::S * (A::I / 2)) % 256 == 0 &&
+                             (A::k * (A::I / 2)) % 256 == 0 && KS + KR <= 8;
 };
 
 // This lane's column (element offset) of the activation row for the gate/up
@@ -1175,6 +1291,10 @@ __global__ __launch_bounds__(NT) void k_fused_layer(A a) {
   GateUp<TB, WTS, 1> gus;   // one item in flight: its tiles stay in registers until after routing
   gus.init(a, L13, 1);
   gus.set_items(a, a.S * gs2);
+  using SKP = SplitKPlan<A, TB, WTR, WTS>;
+  const bool sk = SKP::on && a.log2G == 8;   // batch-1 split-K gate/up (uniform)
+  SplitK<SKP::KS, SKP::KR> skg;
+  if constexpr (SKP::on) skg.init(a, L13);
 
   // ---- pre-norm: xhat = bf16(x / rms(x) * gamma) -----------------------------
   if (a.prenorm) {
@@ -1292,7 +1412,10 @@ __global__ __launch_bounds__(NT) void k_fused_layer(A a) {
   // shared item issues its tiles (a wave without one issues nothing, so wave
   // 0 starts routing at once).  Not before the logit gather: the polls wait,
   // in order, for every load of their wave.
-  if constexpr (TB == 1) gus.prime(a, tab);
+  if constexpr (TB == 1) {
+    if (SKP::on && sk) skg.load_shared(a, L13);
+    else gus.prime(a, tab);
+  }
   constexpr int TPW = (TB > NW) ? 2 : 1;
   if (a.E <= 64) route<1, TPW, TB, WTR, WTS>(a, s, lg, eb, er);
   else if (a.E <= 256) route<4, TPW, TB, WTR, WTS>(a, s, lg, eb, er);
@@ -1304,7 +1427,12 @@ __global__ __launch_bounds__(NT) void k_fused_layer(A a) {
   tab.load(s, lane);
   const int nd = s.nd;
   down.set_experts(a.S, nd);
-  {
+  if (SKP::on && sk) {
+    if constexpr (SKP::on) {
+      skg.load_routed(a, tab, L13);
+      skg.run(a, s, act, tag);
+    }
+  } else {
     GateUp<TB, WTR, gu_depth<TB, WTR>()> gur;
     gur.init(a, L13, 0);
     gur.set_items(a, nd * gs2);
