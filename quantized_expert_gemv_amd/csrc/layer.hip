@@ -1159,8 +1159,14 @@ struct Down {
         }
       }
     }
-    __asm__ volatile("" ::: "memory");       // also keeps tiles from being interleaved
-    if constexpr (RELOAD) load_next(a, tb, p);   // unconditional, see GateUp::step
+    // The refill path keeps its reload below the reads (see GateUp::step) and
+    // tiles apart.  Without refills every tile's data have landed by now (the
+    // activation polls waited for them), so the compiler may overlap one
+    // tile's activation reads from shared memory with another's arithmetic.
+    if constexpr (RELOAD) {
+      __asm__ volatile("" ::: "memory");
+      load_next(a, tb, p);   // unconditional, see GateUp::step
+    }
     if (live && xi == nex - 1) {
       // step complete: reduce each token's row sums over the row's lanes
 #pragma unroll
