@@ -1193,6 +1193,12 @@ struct Down {
   // out directly; else partial sums into red2 [nsub][TB][spg * rpw].
   template <class A>
   __device__ __forceinline__ void run(const A& a, const SlotTab& tb, const uint16_t* hs, float* red2) {
+    if constexpr (TB == 1 && WTR == WTS && kSkipRefills<TB, WTR>) {
+      if (nj <= 1 && ntiles <= P) {
+        run1(a, tb, hs, red2);
+        return;
+      }
+    }
     float acc[TB];
 #pragma unroll
     for (int b = 0; b < TB; ++b) acc[b] = 0.f;
@@ -1204,6 +1210,44 @@ struct Down {
       for (int base = 0; base < ntiles; base += P) {
 #pragma unroll
         for (int p = 0; p < P; ++p) step<true>(a, tb, hs, red2, acc, p, base + p < ntiles, lead);
+      }
+    }
+  }
+  // Batch 1, every tile of the wave loaded and of one step: the tiles run
+  // without branches (a dead tile's term is dropped by a select, its
+  // activation row clamped to a real pair), so one tile's shared-memory
+  // reads overlap another's arithmetic; the same fused multiply-adds in the
+  // same order as step(), and one reduction at the end.
+  template <class A>
+  __device__ __forceinline__ void run1(const A& a, const SlotTab& tb, const uint16_t* hs, float* red2) {
+    const int rpw = a.g2.rpw, lpr = a.g2.lpr;
+    const int npairs = a.k + a.S;
+    float acc = 0.f;
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+      const bool live = p < ntiles;
+      const int ex = ex_of(qx[p]);
+      const bool sh = ex < a.S;
+      const int slot = min(max(ex - a.S, 0), kMaxD - 1);
+      const int pr = min(sh ? a.k + ex : tb.rank(slot, 0), npairs - 1);
+      uint32_t hv[16];
+      lds_chunk(hs + (size_t)pr * a.I + L.jc * 32, hv);
+      const float v = tile_dot<WTR>(br[p], t_lo + qj[p], hv);
+      const float w = tb.weight(pr);
+      acc = live ? fmaf(L.active ? v : 0.f, w, acc) : acc;
+    }
+    if (ntiles > 0) {
+      const float v = group_sum(acc, lpr);
+      if (L.jj == lpr - 1) {
+        const int j = qj[0], t = t_lo + j;
+        if (nsub == 1) {
+          const int row = t * rpw + L.ri;
+          float o = v;
+          if (a.residual) o += bf16lo(a.x[row]);
+          a.out[row] = (uint16_t)f2bf(o);
+        } else {
+          red2[sub * (spg * rpw) + j * rpw + L.ri] = v;
+        }
       }
     }
   }
