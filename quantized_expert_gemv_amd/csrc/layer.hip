@@ -732,11 +732,17 @@ struct SplitK {
     const int wave = wave_id(), lane = threadIdx.x & 63;
     uint32_t xk[16];
     lds_chunk(xs + (16 * wave + (lane & 15)) * 32, xk);
+    // all items' sums first, then one lane-conditional block of stores: a
+    // store per item under its own condition would keep the items apart
+    float v[KS + KR];
 #pragma unroll
     for (int m = 0; m < KS + KR; ++m) {
       const uint32_t sp = (row & 1) ? (sw[m] >> 16) : sw[m];
-      const float v = group_sum(chunk_dot_fp4(c[m], sp, xk), 16);
-      if ((lane & 15) == 15) s.kpart[m][row][wave] = v;
+      v[m] = group_sum(chunk_dot_fp4(c[m], sp, xk), 16);
+    }
+    if ((lane & 15) == 15) {
+#pragma unroll
+      for (int m = 0; m < KS + KR; ++m) s.kpart[m][row][wave] = v[m];
     }
     __syncthreads();
     const int m = threadIdx.x;
