@@ -82,7 +82,11 @@ def _topk_desc(keys: np.ndarray, k: int) -> np.ndarray:
 
 
 def _sigmoid(v):
-    return 1.0 / (1.0 + np.exp(-np.asarray(v, dtype=np.float64)))
+    """Logistic function 1 / (1 + exp(-v)), written so that exp never
+    overflows: for v < 0 it is evaluated as exp(v) / (1 + exp(v))."""
+    v = np.asarray(v, dtype=np.float64)
+    e = np.exp(-np.abs(v))
+    return np.where(v >= 0, 1.0 / (1.0 + e), e / (1.0 + e))
 
 
 def route_sigmoid_topk(logits: np.ndarray, k: int, n_shared: int):

@@ -80,10 +80,12 @@ def _bf16(bits):
     return struct.unpack("<f", struct.pack("<I", int(bits) << 16))[0]
 
 
-def _brute_layer(layer, x_bits):
+def _brute_layer(layer, x_bits, forced=None):
+    """forced: optional per-token list of experts used instead of the top-k
+    (their weights still follow the routing rule's definition)."""
     H, I, E, k, S = layer.hidden, layer.inter, layer.n_routed, layer.top_k, layer.n_shared
     outs = []
-    for row in x_bits:
+    for b_row, row in enumerate(x_bits):
         x = [_bf16(v) for v in row]
         if layer.gamma is not None:
             ms = math.fsum(v * v for v in x) / H
@@ -96,6 +98,8 @@ def _brute_layer(layer, x_bits):
             for e in range(E):
                 logit[e] += float(layer.router_bias[e])
         order = sorted(range(E), key=lambda e: (-logit[e], e))[:k]
+        if forced is not None:
+            order = [int(e) for e in forced[b_row]]
         if layer.route == "sigmoid":
             s = [1 / (1 + math.exp(-v)) for v in logit]
             tot = math.fsum(s[e] for e in order)
@@ -307,6 +311,51 @@ def test_forced_selection_recomputes_weights():
     forced = np.array([[int(a["ids"][0, 1]), int(a["ids"][0, 0])]])
     b = L.moe_layer(layer, x, force_ids=forced)
     np.testing.assert_allclose(b["out"], a["out"], rtol=1e-13)   # same set, other order
+
+
+@pytest.mark.parametrize("route", ["sigmoid", "sink"])
+def test_forced_selection_of_another_set_follows_the_routing_rule(route):
+    """The re-run used for near-tied tokens: a selection that is NOT the
+    top-k.  Sigmoid mode: w = s_T / sum s_T over the forced set T.  Sink
+    mode: w = p_T, the forced experts' own softmax probabilities, not
+    renormalised.  Checked against hand-written scalar formulas and the
+    scalar brute-force layer."""
+    rng = np.random.default_rng(26 if route == "sigmoid" else 27)
+    layer = _tiny_random_layer(rng, E=6, k=2, S=2 if route == "sink" else 1, route=route)
+    x = to_bf16_bits(rng.standard_normal((2, layer.hidden)))
+    a = L.moe_layer(layer, x)
+    # the two lowest-scoring routed experts of each token, lowest first
+    forced = np.array([sorted(range(6), key=lambda e: (a["logits"][b, e], e))[:2] for b in range(2)])
+    for b in range(2):
+        assert not set(forced[b].tolist()) & set(a["ids"][b].tolist())
+    r = L.moe_layer(layer, x, force_ids=forced)
+    assert r["ids"].tolist() == forced.tolist()
+    for b in range(2):
+        lg = [float(v) for v in a["logits"][b]]
+        if route == "sigmoid":
+            s = [1.0 / (1.0 + math.exp(-v)) for v in lg]
+            tot = s[forced[b, 0]] + s[forced[b, 1]]
+            want = [s[forced[b, 0]] / tot, s[forced[b, 1]] / tot]
+            assert abs(sum(r["w"][b]) - 1.0) < 1e-12
+        else:
+            mx = max(lg)
+            z = [math.exp(v - mx) for v in lg]
+            tot = math.fsum(z)
+            want = [z[forced[b, 0]] / tot, z[forced[b, 1]] / tot]
+            assert sum(r["w"][b]) < 0.5          # not renormalised: two low-probability experts
+            np.testing.assert_allclose(r["c"][b], [z[6] / tot, z[7] / tot], rtol=1e-12)
+        np.testing.assert_allclose(r["w"][b], want, rtol=1e-12)
+    np.testing.assert_allclose(r["out"], _brute_layer(layer, x, forced=forced), rtol=1e-9, atol=1e-9)
+    assert np.max(np.abs(r["out"] - a["out"])) > 1e-3 * np.max(np.abs(a["out"]))
+
+
+def test_sigmoid_is_finite_and_exact_at_large_arguments():
+    import warnings
+    with warnings.catch_warnings():
+        warnings.simplefilter("error")
+        v = L._sigmoid(np.array([-1000.0, -40.0, 0.0, 40.0, 1000.0]))
+    assert v[0] == 0.0 and v[-1] == 1.0 and v[2] == 0.5
+    np.testing.assert_allclose(v[1], math.exp(-40.0) / (1.0 + math.exp(-40.0)), rtol=1e-15)
 
 
 def test_synth_layer_is_deterministic_and_distributed_as_stated():
