@@ -1,22 +1,32 @@
 """Benchmark of the small-batch NVFP4 MoE decode layer on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload flint_b1]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload flint_b1] [--extra flint_b8] [--all]
 
 A step is one MoE layer call (router GEMV + routing, gate/up GEMV with
 SiLU*up, down GEMV with weighted combine, all in one kernel launch) over one
-batch of seeded synthetic tokens.  Weights stay cold: the layer is copied into L distinct device slots
-(47 by default, one per MoE layer of the Flint model) and step i uses slot
-i % L with its own input, so the touched bytes of a cycle (~631 MB at batch
-1) exceed the 256 MB Infinity Cache plus the 32 MB of L2.
+batch of seeded synthetic tokens.  Weights stay cold: the layer is copied
+into L distinct device slots (47 by default, one per MoE layer of the Flint
+model) and step i uses slot i % L with its own input.  One cycle over the
+slots (~631 MB at batch 1) exceeds the 256 MB Infinity Cache plus the 32 MB
+of L2, and a 1 GiB write pass runs right before the timed region, so every
+timed step reads its weights from HBM whatever K is.
 
-The timed region replays a HIP graph of the K steps (captured once, after W
-eager warm-up steps and one untimed replay), bracketed by
-torch.cuda.synchronize() and HIP events on the stream the kernels run on.
-A step is one launch and the replayed launches run back to back, so the
-region's time per step is the kernel's average launch duration, from which
-the roofline figure is computed.  A second timed region runs the same K
-steps eagerly with the library's profiling events around each launch (a
-cross-check that also times the event packets and the dispatch).
+Timed region: W eager warm-up steps, then a HIP graph of exactly the K steps
+(W + i) % L, replayed once between HIP events on the stream the kernels run
+on, after the write pass.  A step is one launch and replayed launches run
+back to back, so the region's time per step is the layer kernel's average
+launch duration (the roofline figure uses it).  Also reported:
+  * replays: a graph of one full cycle of L steps replayed R times, each
+    replay between events: p10 / p50 / p90 of elapsed / L;
+  * eager: the library's profiling events around each of L eager launches
+    (they also time the event packets and the dispatch);
+  * the measured HBM read-stream ceiling (4 GiB read once, best of 3) and
+    the per-launch floor (an empty 256-workgroup kernel, 200 launches in a
+    graph);
+  * the fp64 oracle on the host's cores at 1 thread and at all threads.
+Other workloads (--extra, default flint_b8; --all adds the BF16, chain and
+expert-sink workloads) are measured the same way and reported under
+"configs" in the same JSON line.
 
 Prints one JSON line.
 """
@@ -35,6 +45,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
+SLOTS = {"tiny": 1024, "sink_b4": 4}
 
 
 def parse():
@@ -43,18 +54,25 @@ def parse():
     p.add_argument("--steps", type=int, default=470)
     p.add_argument("--warmup", type=int, default=94)
     p.add_argument("--workload", default="flint_b1")
+    p.add_argument("--extra", default="flint_b8", help="comma-separated extra workloads ('' for none)")
+    p.add_argument("--all", action="store_true", help="also the BF16, chain and expert-sink workloads")
     p.add_argument("--slots", type=int, default=47)
-    p.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle CPU baseline")
+    p.add_argument("--replays", type=int, default=8)
+    p.add_argument("--cpu-seconds", type=float, default=16.0, help="budget of the oracle CPU baseline")
     p.add_argument("--no-cpu", action="store_true")
-    p.add_argument("--no-graph", action="store_true")
     p.add_argument("--calib-copy-mb", type=int, default=1024,
                    help="size of a plain device copy run once after timing (HBM counter calibration)")
     return p.parse_args()
 
 
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
 def algorithmic_bytes(wl, d_routed: float, batch: int) -> dict:
     """Bytes one layer step must move (selected experts deduplicated)."""
     H, I = wl.hidden, wl.inter
+
     def expert(wtype):
         if wtype == "nvfp4":
             return {"w13": 2 * I * H // 2 + 2 * I * H // 16 + 4, "w2": H * I // 2 + H * I // 16 + 4}
@@ -63,18 +81,34 @@ def algorithmic_bytes(wl, d_routed: float, batch: int) -> dict:
     er = wl.n_routed + (wl.n_shared if wl.route == "sink" else 0)
     router = er * H * 2
     x_io = batch * H * 2
-    k1 = router + wl.n_shared * s["w13"] + x_io
-    k2 = d_routed * r["w13"] + x_io
-    k3 = d_routed * r["w2"] + wl.n_shared * s["w2"] + x_io
-    total = router + d_routed * (r["w13"] + r["w2"]) + wl.n_shared * (s["w13"] + s["w2"]) + 2 * x_io
-    return {"k1": k1, "k2": k2, "k3": k3, "total": total}
+    gamma = H * 2 if wl.prenorm else 0
+    total = router + d_routed * (r["w13"] + r["w2"]) + wl.n_shared * (s["w13"] + s["w2"]) + 2 * x_io + gamma
+    return {"router": router, "routed": d_routed * (r["w13"] + r["w2"]),
+            "shared": wl.n_shared * (s["w13"] + s["w2"]), "total": total}
+
+
+def cpu_info() -> dict:
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except AttributeError:
+        avail = os.cpu_count()
+    return {"nproc": avail, "cpu_count": os.cpu_count(), "model": model}
 
 
 def cpu_baseline(layer, xs, budget_s: float, algo_total: float) -> dict:
     """The oracle as it stands, on host cores, over a bounded sample of the
-    workload's steps (inputs of the first slots)."""
+    workload's steps (inputs of the first slots), at 1 thread and at all."""
     import oracle
-    from threadpoolctl import threadpool_info
+    from threadpoolctl import threadpool_info, threadpool_limits
 
     class Cached:                     # experts generated once, outside the timed loop
         def __init__(self, base):
@@ -94,41 +128,42 @@ def cpu_baseline(layer, xs, budget_s: float, algo_total: float) -> dict:
             return self._s[s]
 
     lay = Cached(layer)
-    n = 0
     for x in xs[:4]:                  # populate the expert cache (untimed)
         oracle.moe_layer(lay, x)
-    t0 = time.perf_counter()
-    while True:
-        oracle.moe_layer(lay, xs[n % len(xs)])
-        n += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s or n >= 10 * len(xs):
-            break
-    per = el / n
+
+    def run(seconds):
+        n, t0 = 0, time.perf_counter()
+        while True:
+            oracle.moe_layer(lay, xs[n % len(xs)])
+            n += 1
+            el = time.perf_counter() - t0
+            if el >= seconds or n >= 10 * len(xs):
+                return n, el
+
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    return {"value": algo_total / per / 1e9, "unit": "GB/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{n} layer-steps (inputs of {min(n, len(xs))} slots) of the same workload in "
-                      f"{el:.1f} s; {per * 1e3:.1f} ms per layer-step; expert generation excluded",
-            "ms_per_step": per * 1e3}
+    n_all, el_all = run(budget_s / 2)
+    with threadpool_limits(1):
+        n_one, el_one = run(budget_s / 2)
+    per_all, per_one = el_all / n_all, el_one / n_one
+    info = cpu_info()
+    return {"value": algo_total / per_all / 1e9, "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{n_all} layer-steps (inputs of {min(n_all, len(xs))} slots) of the same workload in "
+                      f"{el_all:.1f} s at {threads} BLAS threads, {n_one} in {el_one:.1f} s at 1 thread; "
+                      "expert generation excluded",
+            "ms_per_step": per_all * 1e3, "ms_per_step_1thread": per_one * 1e3,
+            "value_1thread": algo_total / per_one / 1e9, "threads": int(threads), **info}
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (this build has no "
-              "multi-GPU path: the layer would shard by splitting each expert's intermediate "
-              "dimension across GPUs, see DESIGN.md)", file=sys.stderr)
-        sys.exit(2)
+def measure(name: str, K: int, W: int, L: int, R: int, flush) -> dict:
+    """Cold-weight timing of one workload; returns its record and the layer."""
     import torch
     from quantized_expert_gemv_amd import binding as B
     from quantized_expert_gemv_amd.device_layer import DeviceLayer, bits_to_bf16_tensor
     from quantized_expert_gemv_amd.synth import WORKLOADS, SynthLayer
 
-    wl = WORKLOADS[args.workload]
+    wl = WORKLOADS[name]
     batch = wl.batch
-    L = args.slots
-    dev_name = torch.cuda.get_device_name(0)
-    print(f"[bench] {wl.description}; {L} cold slots; device {dev_name}", file=sys.stderr, flush=True)
+    log(f"{wl.description}; {L} cold slots")
     layer = SynthLayer(wl)
     dev = DeviceLayer(layer, max_batch=batch)
     base = dev.buffers()
@@ -137,130 +172,204 @@ def main():
     xs = [bits_to_bf16_tensor(x, dev.device) for x in xs_bits]
     outs = [torch.empty((batch, wl.hidden), dtype=torch.bfloat16, device=dev.device) for _ in range(L)]
     torch.cuda.synchronize()
-    print(f"[bench] slots ready: {sum(v.numel() for v in base.values() if v is not None) * L / 1e9:.1f} GB "
-          "resident", file=sys.stderr, flush=True)
+    resident = sum(v.numel() for v in base.values() if v is not None) * L
+    log(f"slots ready: {resident / 1e9:.1f} GB resident")
 
-    def step(i, stream=None):
+    def step(i):
         s = i % L
-        dev(xs[s], out=outs[s], bufs=slots[s], stream=stream)
+        dev(xs[s], out=outs[s], bufs=slots[s])
 
-    # distinct routed experts per slot
     d_per_slot = []
-    for s in range(L):
+    for s in range(L):                    # distinct routed experts per slot
         step(s)
         ids, _, _ = dev.routing(batch)
         d_per_slot.append(len(set(ids.cpu().numpy().ravel().tolist())))
-    K, W = args.steps, args.warmup
-    d_avg = float(np.mean([d_per_slot[i % L] for i in range(K)]))
-    algo = algorithmic_bytes(wl, d_avg, batch)
+    d_timed = float(np.mean([d_per_slot[(W + i) % L] for i in range(K)]))
+    algo = algorithmic_bytes(wl, d_timed, batch)
 
     for i in range(W):
         step(i)
     torch.cuda.synchronize()
-
     stream = torch.cuda.current_stream()
-    mode = "eager"
-    if not args.no_graph:
+
+    def capture(first, n):
         g = torch.cuda.CUDAGraph()
         cap = torch.cuda.Stream()
         cap.wait_stream(stream)
         with torch.cuda.stream(cap):
             with torch.cuda.graph(g, stream=cap):
-                for i in range(K):
-                    step(W + i)
+                for i in range(n):
+                    step(first + i)
         stream.wait_stream(cap)
-        g.replay()                       # untimed first replay
         torch.cuda.synchronize()
-        mode = "hipgraph"
+        return g
+
+    gK = capture(W, K)
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    flush()
     torch.cuda.synchronize()
     ev0.record(stream)
-    if mode == "hipgraph":
-        g.replay()
-    else:
-        for i in range(K):
-            step(W + i)
+    gK.replay()
     ev1.record(stream)
     torch.cuda.synchronize()
-    total_ms = ev0.elapsed_time(ev1)
-    us_step = total_ms * 1e3 / K
-    print(f"[bench] timed {K} steps ({mode}): {us_step:.2f} us/step", file=sys.stderr, flush=True)
+    us_step = ev0.elapsed_time(ev1) * 1e3 / K
+    del gK
+    log(f"timed {K} steps (hipgraph, cold): {us_step:.3f} us/step")
 
-    # second timed region: eager, with events around each launch
-    n_ev = 2 * K
-    evs = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
+    gL = capture(0, L)
+    gL.replay()
+    torch.cuda.synchronize()
+    per = []
+    for _ in range(R):
+        ev0.record(stream)
+        gL.replay()
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        per.append(ev0.elapsed_time(ev1) * 1e3 / L)
+    del gL
+    per = np.array(per)
+    replays = {"n": R, "steps_per_replay": L, "p10_us": float(np.percentile(per, 10)),
+               "p50_us": float(np.percentile(per, 50)), "p90_us": float(np.percentile(per, 90))}
+    log(f"replays of {L} steps: {replays}")
+
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(2 * L)]
     for e in evs:
-        e.record(stream)                # materialise the underlying HIP events
+        e.record(stream)                  # materialise the underlying HIP events
     torch.cuda.synchronize()
-    ev_ptrs = (B.C.c_void_p * n_ev)(*[e.cuda_event for e in evs])
-    B.moe_layer_set_profiling(dev.handle, ev_ptrs, n_ev)
+    ev_ptrs = (B.C.c_void_p * (2 * L))(*[e.cuda_event for e in evs])
+    B.moe_layer_set_profiling(dev.handle, ev_ptrs, 2 * L)
+    for i in range(L):
+        step(i)
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(K):
-        step(W + i)
-    torch.cuda.synchronize()
-    eager_wall = time.perf_counter() - t0
     B.moe_layer_set_profiling(dev.handle, None, 0)
-    d = np.array([evs[2 * i].elapsed_time(evs[2 * i + 1]) for i in range(K)])
-    kern = {"layer_kernel_us": float(d.mean() * 1e3), "layer_kernel_us_p50": float(np.median(d) * 1e3),
-            "eager_us_per_step": eager_wall * 1e6 / K}
-    print(f"[bench] layer kernel (eager, events): {kern}", file=sys.stderr, flush=True)
+    d = np.array([evs[2 * i].elapsed_time(evs[2 * i + 1]) for i in range(L)]) * 1e3
+    eager = {"mean_us": float(d.mean()), "p10_us": float(np.percentile(d, 10)), "p50_us": float(np.median(d))}
     flags = dev.error()
     if flags:
-        raise SystemExit(f"[bench] the layer kernel reported error bits {flags:#x}")
+        raise SystemExit(f"[bench] the layer kernel reported error bits {flags:#x} on {name}")
+
+    gbs = algo["total"] / (us_step * 1e-6) / 1e9
+    rec = {"workload": wl.description, "batch": batch, "us_per_step": round(us_step, 3), "gbs": round(gbs, 1),
+           "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "cold_slots": L, "timing": "hipgraph, cold",
+           "distinct_routed_per_step": d_timed, "algorithmic_bytes_per_step": int(round(algo["total"])),
+           "bytes_breakdown": {k: int(round(v)) for k, v in algo.items()},
+           "replays": replays, "eager_per_launch": eager, "resident_gb": round(resident / 1e9, 2)}
+    del slots, xs, outs, base
+    dev.close()
+    del dev
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return rec, layer, xs_bits
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the layer runs on one GPU "
+              "here; how it would shard over several is described in DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from quantized_expert_gemv_amd import binding as B
+    from quantized_expert_gemv_amd.synth import WORKLOADS
+
+    dev_name = torch.cuda.get_device_name(0)
+    log(f"device {dev_name}")
+    flush_buf = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+
+    def flush():
+        B.moe_bench_fill(flush_buf, 0x5a5a5a5a)
+
+    K, W = args.steps, args.warmup
+    head, layer, xs_bits = measure(args.workload, K, W, SLOTS.get(args.workload, args.slots), args.replays, flush)
+    extras = [n for n in args.extra.split(",") if n]
+    if args.all:
+        extras += [n for n in ("flint_bf16_b1", "flint_bf16_b8", "sink_b4") if n not in extras]
+    configs = {}
+    for n in extras:
+        if n == args.workload or n not in WORKLOADS:
+            continue
+        rec, _, _ = measure(n, K, W, SLOTS.get(n, args.slots), args.replays, flush)
+        configs[n] = rec
+
+    # measured HBM read-stream ceiling and per-launch floor
+    sink = torch.zeros(16, dtype=torch.int32, device="cuda")
+    big = torch.empty(4 << 30, dtype=torch.uint8, device="cuda")
+    B.moe_bench_fill(big, 0x01020304)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    best = 1e9
+    for _ in range(3):
+        flush()
+        e0.record()
+        B.moe_bench_read_stream(big, sink)
+        e1.record()
+        torch.cuda.synchronize()
+        best = min(best, e0.elapsed_time(e1))
+    ceiling = big.numel() / (best * 1e-3) / 1e9
+    del big
+    g = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    with torch.cuda.stream(cap):
+        with torch.cuda.graph(g, stream=cap):
+            for _ in range(200):
+                B.moe_bench_empty(256)
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    e0.record()
+    g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    floor_us = e0.elapsed_time(e1) * 1e3 / 200
+    log(f"HBM read-stream ceiling {ceiling:.0f} GB/s; empty-launch floor {floor_us:.3f} us")
 
     # plain copy of known size, for HBM counter calibration under rocprofv3 --pmc
     if args.calib_copy_mb > 0:
         n = args.calib_copy_mb * (1 << 20)
-        a = torch.empty(n, dtype=torch.uint8, device=dev.device)
+        a = torch.empty(n, dtype=torch.uint8, device="cuda")
         b = torch.empty_like(a)
         b.copy_(a)
         torch.cuda.synchronize()
         del a, b
 
-    gbs = algo["total"] / (us_step * 1e-6) / 1e9
-    roof = None
-    if kern is not None:
-        # A layer step is one launch and graph-replayed launches run back to
-        # back (no gaps in rocprofv3's kernel trace), so the timed region's
-        # events give the average launch duration.  The eager per-launch
-        # events (kernels.layer_kernel_us) also time the event packets and
-        # the dispatch, and stay a cross-check.
-        k_us = us_step if mode == "hipgraph" else kern["layer_kernel_us"]
-        achieved = algo["total"] / (k_us * 1e-6) / 1e9
-        traffic = None
-        tf = os.path.join(ROOT, "profiles", f"traffic_{args.workload}.json")
-        if os.path.exists(tf):
-            with open(tf) as fh:
-                t = json.load(fh)
-            from quantized_expert_gemv_amd.profiling import src_digest
-            if t.get("src_digest") == src_digest():
-                traffic = t.get("dominant_bytes_per_launch")
-        roof = {"bound": "hbm", "kernel": "k_fused_layer", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "algorithmic_bytes_per_launch": int(round(algo["total"])),
-                "launch_us": round(k_us, 3),
-                "launch_us_source": ("events around the graph-replayed timed region / launches"
-                                     if mode == "hipgraph" else "events around each eager launch")}
+    us_step = head["us_per_step"]
+    achieved = head["gbs"]
+    traffic = None
+    tf = os.path.join(ROOT, "profiles", f"traffic_{args.workload}.json")
+    if os.path.exists(tf):
+        with open(tf) as fh:
+            t = json.load(fh)
+        from quantized_expert_gemv_amd.profiling import src_digest
+        if t.get("src_digest") == src_digest():
+            traffic = t.get("dominant_bytes_per_launch")
+    roof = {"bound": "hbm", "kernel": "k_fused_layer", "achieved": achieved, "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+            "algorithmic_bytes_per_launch": head["algorithmic_bytes_per_step"],
+            "launch_us": us_step,
+            "launch_us_source": "events around a graph of the K timed launches (back to back, cold) / K",
+            "measured_read_ceiling_gbs": round(ceiling, 1),
+            "frac_of_measured_ceiling": round(achieved / ceiling, 4),
+            "empty_launch_floor_us": round(floor_us, 3)}
 
     cpu = None
     if not args.no_cpu:
-        print("[bench] oracle cpu baseline ...", file=sys.stderr, flush=True)
-        cpu = cpu_baseline(layer, xs_bits, args.cpu_seconds, algo["total"])
+        log("oracle cpu baseline ...")
+        cpu = cpu_baseline(layer, xs_bits, args.cpu_seconds, head["algorithmic_bytes_per_step"])
 
+    wl = WORKLOADS[args.workload]
     line = {
         "metric": "MoE layer us/step + achieved HBM GB/s, NVFP4 W4A16 H=2048 E=256 top-6",
-        "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": K, "warmup": W,
-        "ms_per_step": round(us_step / 1e3, 6), "us_per_step": round(us_step, 3),
-        "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+        "value": achieved, "unit": "GB/s", "n_gpus": 1, "steps": K, "warmup": W,
+        "ms_per_step": round(us_step / 1e3, 6), "us_per_step": us_step, "hbm_frac": head["hbm_frac"],
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "nvfp4-w/bf16-a/f32-acc" if wl.routed_wtype == "nvfp4" else "bf16-w/bf16-a/f32-acc",
         "data": "synthetic (seeded; no checkpoint)",
-        "config": {"workload": wl.description, "hidden": wl.hidden, "inter": wl.inter,
-                   "n_routed": wl.n_routed, "top_k": wl.top_k, "n_shared": wl.n_shared, "batch": batch,
-                   "cold_slots": L, "timing": mode, "distinct_routed_per_step": d_avg,
-                   "algorithmic_bytes_per_step": int(round(algo["total"])), "device": dev_name},
-        "kernels": kern, "roofline": roof, "cpu_baseline": cpu,
+        "config": {"workload": wl.description, "hidden": wl.hidden, "inter": wl.inter, "n_routed": wl.n_routed,
+                   "top_k": wl.top_k, "n_shared": wl.n_shared, "batch": wl.batch, "cold_slots": head["cold_slots"],
+                   "timing": head["timing"], "distinct_routed_per_step": head["distinct_routed_per_step"],
+                   "algorithmic_bytes_per_step": head["algorithmic_bytes_per_step"], "device": dev_name},
+        "replays": head["replays"], "eager_per_launch": head["eager_per_launch"],
+        "roofline": roof, "cpu_baseline": cpu, "configs": configs,
     }
     print(json.dumps(line), flush=True)
 

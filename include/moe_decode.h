@@ -14,9 +14,9 @@
  *                                               the expert sink)
  *   h_e   = SiLU(W13_e[:I] xhat) * (W13_e[I:] xhat)     per selected/shared expert
  *   out   = sum_e w_e W2_e h_e  (+ x for pre-norm residual layers)
- * Only the selected experts' weights are read (Flint page, "From 1,096 kernels to
- * 346": router and expert GEMVs that read only the selected experts' weights;
- * routing and the expert combine fused into the neighbouring GEMV kernels).
+ * Only the chosen experts' weight bytes are fetched, and routing and the expert
+ * combine run inside the same launch as the GEMVs around them (Flint page, "From
+ * 1,096 kernels to 346": the small-batch MoE kernels and the low-latency decode path).
  *
  * Weight formats
  *   NVFP4: e2m1 codes, one e4m3 scale per 16 consecutive elements of a row, one fp32
@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 2
+#define MOE_ABI_VERSION 3
 
 /* limits of this implementation */
 #define MOE_MAX_BATCH 8      /* the low-latency decode path serves up to 8 requests  */
@@ -75,6 +75,14 @@ typedef enum {
 } moe_status;
 
 typedef enum { MOE_W_NVFP4 = 0, MOE_W_BF16 = 1 } moe_wtype;
+
+/* Where a packed expert set's scale region goes (moe_pack_experts). */
+typedef enum {
+  MOE_PLACE_TWO_REGIONS = 0, /* code region and scale region in two buffers (routed set:       */
+                             /* moe_decode_layer's expert_packed and scales)                    */
+  MOE_PLACE_ONE_BUFFER = 1   /* one buffer: code region, then the scale region at               */
+                             /* shared_scale_offset (shared set: moe_decode_layer's shared_w)   */
+} moe_placement;
 
 typedef enum {
   MOE_ROUTE_SIGMOID_TOPK = 0, /* s = sigmoid(l + bias), top-k of s, w = s / sum_topk s, shared c = 1 */
@@ -133,39 +141,83 @@ typedef struct {
 
 /* ---- host-only queries (no device access) -------------------------------------- */
 
+/* Version of this header's ABI (MOE_ABI_VERSION).  Host only, never fails.          */
 int moe_abi_version(void);
+/* Static text for a moe_status value (unknown values get "unknown status").          */
 const char* moe_status_str(int status);
 
-/* Checks a description (shapes, limits, dtype/routing combination) without touching
- * the device.  Device pointers inside it are not dereferenced.                       */
+/* Checks a description without touching the device: shapes and limits, the dtype /
+ * routing combination (Flint page, "A 40B MoE that activates 2.5B parameters": sigmoid
+ * top-6 plus a shared expert; Inkling page, "Model Architecture": the expert sink) and
+ * that a kernel is compiled for it at every batch up to max_batch.  Device pointers
+ * inside it are not dereferenced.  A description this accepts is accepted by
+ * moe_layer_create unless the device itself fails (MOE_ERR_DEVICE) or cannot hold the
+ * launch (MOE_ERR_UNSUPPORTED from the occupancy check).                              */
 int moe_layer_validate(const moe_layer_desc* desc);
 
-/* Layout of n experts of type wtype for hidden H / inter I (see moe_expert_layout). */
+/* Layout of n experts of type wtype for hidden H / inter I (see moe_expert_layout):
+ * the sizes a caller allocates for moe_pack_experts' outputs.  NVFP4 sizes follow the
+ * format's three parts ("Frontier MoE on consumer Blackwell (SM120)", section
+ * "GLM-5.2": e2m1 codes, e4m3 per 16-element block, one fp32 per tensor).            */
 int moe_expert_layout_query(int wtype, int hidden, int inter, int n_experts,
                             moe_expert_layout* out);
 
 /* ---- packers (host memory, lossless, load time) ----------------------------------- */
+/* The Flint page ("A 40B MoE that activates 2.5B parameters") repacks its checkpoint's
+ * NVFP4 blocks losslessly at load time into the order its kernels read; these do the
+ * same for the gfx950 kernels.  All buffers are host memory owned by the caller.      */
 
-/* Canonical NVFP4 matrix [rows][cols] -> kernel layout.  codes: host uint8
- * [rows][cols/2] in, code_bytes = rows*cols/2 out; scales: host uint8 [rows][cols/16]
- * in, rows*cols/16 out.  The output is a permutation of 16-byte code units and 2-byte
- * scale pairs; every byte (including -0 codes and NaN/zero scale bytes) is kept.
- * rows/cols must describe a W13 ([2I][H]) or W2 ([H][I]) matrix of a valid layer.  */
+/* Experts [first, first + count) of a set of n_experts, from canonical bytes into the
+ * set's packed regions, every offset placed by the library (moe_expert_layout).
+ *   NVFP4: w13 uint8 [count][2I][H/2], w13_scales uint8 [count][2I][H/16],
+ *          w2 uint8 [count][H][I/2],   w2_scales uint8 [count][H][I/16],
+ *          tensor_scales fp32 [count][2] = (W13, W2) per expert, or NULL for 1.0.
+ *   BF16:  w13 uint16 [count][2I][H], w2 uint16 [count][H][I]; the scale and
+ *          tensor-scale arguments are ignored (may be NULL).
+ * placement MOE_PLACE_TWO_REGIONS: code_region holds code_region_bytes, scale_region
+ * scale_region_bytes (NVFP4); MOE_PLACE_ONE_BUFFER: code_region holds shared_total_bytes
+ * and scale_region is ignored.  Bytes of other experts are left as they are, so a set
+ * can be packed a few experts at a time.  Lossless: every byte (-0 codes, zero and NaN
+ * scale bytes) is kept.  MOE_ERR_INVALID_ARG for a null required pointer or a range
+ * outside [0, n_experts); MOE_ERR_UNSUPPORTED for a shape without a kernel layout.   */
+int moe_pack_experts(int wtype, int hidden, int inter, int n_experts, int first, int count,
+                     const void* w13, const void* w13_scales, const void* w2,
+                     const void* w2_scales, const float* tensor_scales, int placement,
+                     void* code_region, void* scale_region);
+/* Exact inverse of moe_pack_experts (same arguments, data flowing the other way;
+ * tensor_scales may be NULL to skip them).                                            */
+int moe_unpack_experts(int wtype, int hidden, int inter, int n_experts, int first, int count,
+                       const void* code_region, const void* scale_region, int placement,
+                       void* w13, void* w13_scales, void* w2, void* w2_scales,
+                       float* tensor_scales);
+
+/* One canonical NVFP4 matrix [rows][cols] -> kernel layout (the building block of
+ * moe_pack_experts).  codes: uint8 [rows][cols/2] in, rows*cols/2 bytes out; scales:
+ * uint8 [rows][cols/16] in, rows*cols/16 bytes out.  A permutation of 16-byte code
+ * units and 2-byte scale pairs.  rows/cols must describe a W13 ([2I][H]) or W2
+ * ([H][I]) matrix of a valid layer.                                                  */
 int moe_pack_nvfp4(int rows, int cols, const uint8_t* codes, const uint8_t* scales,
                    uint8_t* codes_out, uint8_t* scales_out);
 /* Exact inverse of moe_pack_nvfp4. */
 int moe_unpack_nvfp4(int rows, int cols, const uint8_t* codes_packed,
                      const uint8_t* scales_packed, uint8_t* codes, uint8_t* scales);
-/* Canonical bf16 matrix [rows][cols] (uint16 bit patterns) -> kernel layout, and its
- * inverse.  A permutation of 16-byte units.                                           */
+/* One canonical bf16 matrix [rows][cols] (uint16 bit patterns) -> kernel layout, and
+ * its inverse.  A permutation of 16-byte units.                                       */
 int moe_pack_bf16(int rows, int cols, const uint16_t* w, uint16_t* w_out);
 int moe_unpack_bf16(int rows, int cols, const uint16_t* w_packed, uint16_t* w);
 
 /* ---- layer handle ------------------------------------------------------------------ */
 
-/* Validates desc and allocates the handle's device workspace on the current device
- * (once; no later allocation).  MOE_ERR_DEVICE if no device is usable.              */
+/* Validates desc (moe_layer_validate), plans the launch for the current device and
+ * allocates the handle's device workspace there, once: the cross-workgroup exchange
+ * words, the call counter and the routing readback (the layer of the Flint page, "A 40B
+ * MoE that activates 2.5B parameters", or the Inkling expert sink, "Model
+ * Architecture").  No later call allocates.  *out is NULL on failure; MOE_ERR_DEVICE
+ * if no device is usable.  The router bias and pre-norm gamma pointers in desc are
+ * kept (not copied) and must outlive the handle.                                     */
 int moe_layer_create(const moe_layer_desc* desc, moe_layer_t* out);
+/* Frees the handle's workspace.  The caller must have synchronised every stream that
+ * used it.  MOE_ERR_INVALID_ARG for NULL.                                             */
 int moe_layer_destroy(moe_layer_t layer);
 
 /* One MoE decode layer for `batch` tokens (1 <= batch <= max_batch).
@@ -194,11 +246,14 @@ int moe_decode_layer(moe_layer_t layer, const void* x, const void* router_w,
 
 /* Routing of the last moe_decode_layer call on this handle, copied on `stream` into
  * device buffers: ids int32 [batch][k] and w fp32 [batch][k] in selection order
- * (descending score, ties to the lower index); c fp32 [batch][S] shared coefficients.
- * Any pointer may be NULL to skip it.  MOE_ERR_STATE before the first call.          */
+ * (descending score, ties to the lower index); c fp32 [batch][S] shared coefficients
+ * (sigmoid top-k renormalised: Flint page, "A 40B MoE that activates 2.5B parameters";
+ * sink probabilities: Inkling page, "Model Architecture").  Any pointer may be NULL to
+ * skip it.  MOE_ERR_STATE before the first call.                                      */
 int moe_layer_routing(moe_layer_t layer, int32_t* ids, float* w, float* c, void* stream);
 
-/* Profiling hook for benchmarks.  events: n_events hipEvent_t handles (as void*), n_events a
+/* Profiling hook for benchmarks (the per-kernel timing the SM120 page, "SM120 decode
+ * kernels", reports for its decode kernels).  events: n_events hipEvent_t handles (as void*), n_events a
  * positive multiple of 2; the pointer array is copied, the events stay owned by the caller and
  * must outlive the setting.  Every later moe_decode_layer call number c on this handle records
  * events[2*(c mod n_events/2) + 0] before its kernel and events[... + 1] after it, on its
@@ -206,23 +261,29 @@ int moe_layer_routing(moe_layer_t layer, int32_t* ids, float* w, float* c, void*
  * stream capture.                                                                            */
 int moe_layer_set_profiling(moe_layer_t layer, void* const* events, int n_events);
 
-/* Test hook: the SiLU*up activations of the last call, bf16, gathered on `stream`
- * into h_routed [batch][k][I] (selection order) and h_shared [batch][S][I].  Either
- * pointer may be NULL.                                                               */
+/* Test hook: the SiLU*up activations h = SiLU(gate) * up of the last call (the
+ * SiLU-gated expert MLP of the Flint page, "From 1,096 kernels to 346"), bf16, gathered
+ * on `stream` into device buffers h_routed [batch][k][I] (selection order) and h_shared
+ * [batch][S][I].  Either pointer may be NULL.  MOE_ERR_STATE before the first call.  */
 int moe_layer_debug_h(moe_layer_t layer, void* h_routed, void* h_shared, void* stream);
 
 /* Sticky error bits of the handle's calls so far, read synchronously (waits for the
- * device): 1 = a workgroup gave up waiting for router logits, 2 = for activations (the
- * grid was not resident at once).  clear != 0 resets them.  After a non-zero result the
- * handle's later outputs are undefined until moe_layer_reset.                        */
+ * device): 1 = a workgroup gave up waiting for router logits, 2 = for activations, 4 =
+ * for partial outputs (the grid was not resident at once).  clear != 0 resets them.
+ * After a non-zero result the handle's later outputs are undefined until
+ * moe_layer_reset.  These waits replace the kernel boundaries of the Flint page's
+ * chained low-latency kernels ("From 1,096 kernels to 346").                         */
 int moe_layer_error(moe_layer_t layer, unsigned* flags, int clear);
 
 /* Waits for the device and returns the handle's workspace to its state after
- * moe_layer_create (call counter 0, no error bits, no last call).                   */
+ * moe_layer_create (call counter 0, no error bits, no last call).  Host-synchronous;
+ * MOE_ERR_DEVICE if the device fails.                                                */
 int moe_layer_reset(moe_layer_t layer);
 
-/* Launch plan of the handle: workgroups of its kernel (all resident at once) and the
- * shared-memory bytes each uses at max_batch.  Either pointer may be NULL.           */
+/* Launch plan of the handle: workgroups of its kernel (all resident at once, the one
+ * launch that stands for the Flint page's chain of layer kernels, "From 1,096 kernels
+ * to 346") and the shared-memory bytes each uses at max_batch.  Either pointer may be
+ * NULL.  Host only.                                                                   */
 int moe_layer_grid(moe_layer_t layer, int* workgroups, int* lds_bytes);
 
 #ifdef __cplusplus

@@ -21,14 +21,19 @@ STATUS = {0: "MOE_OK", -1: "MOE_ERR_INVALID_ARG", -2: "MOE_ERR_UNSUPPORTED", -3:
           -4: "MOE_ERR_BATCH", -5: "MOE_ERR_LAUNCH", -6: "MOE_ERR_DEVICE", -7: "MOE_ERR_STATE"}
 MOE_W_NVFP4, MOE_W_BF16 = 0, 1
 MOE_ROUTE_SIGMOID_TOPK, MOE_ROUTE_SOFTMAX_SINK = 0, 1
+MOE_PLACE_TWO_REGIONS, MOE_PLACE_ONE_BUFFER = 0, 1
 WTYPES = {"nvfp4": MOE_W_NVFP4, "bf16": MOE_W_BF16}
 ROUTES = {"sigmoid": MOE_ROUTE_SIGMOID_TOPK, "sink": MOE_ROUTE_SOFTMAX_SINK}
 
 EXPORTED = ("moe_abi_version", "moe_status_str", "moe_layer_validate", "moe_expert_layout_query",
+            "moe_pack_experts", "moe_unpack_experts",
             "moe_pack_nvfp4", "moe_unpack_nvfp4", "moe_pack_bf16", "moe_unpack_bf16",
             "moe_layer_create", "moe_layer_destroy", "moe_decode_layer", "moe_layer_routing",
             "moe_layer_set_profiling", "moe_layer_debug_h", "moe_layer_error", "moe_layer_reset",
             "moe_layer_grid")
+
+
+BENCH_EXPORTED = ("moe_bench_read_stream", "moe_bench_fill", "moe_bench_empty")
 
 
 class MoeError(RuntimeError):
@@ -70,6 +75,8 @@ def _load() -> C.CDLL:
         "moe_status_str": ([i32], C.c_char_p),
         "moe_layer_validate": ([C.POINTER(moe_layer_desc)], i32),
         "moe_expert_layout_query": ([i32, i32, i32, i32, C.POINTER(moe_expert_layout)], i32),
+        "moe_pack_experts": ([i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, i32, vp, vp], i32),
+        "moe_unpack_experts": ([i32, i32, i32, i32, i32, i32, vp, vp, i32, vp, vp, vp, vp, vp], i32),
         "moe_pack_nvfp4": ([i32, i32, vp, vp, vp, vp], i32),
         "moe_unpack_nvfp4": ([i32, i32, vp, vp, vp, vp], i32),
         "moe_pack_bf16": ([i32, i32, vp, vp], i32),
@@ -84,10 +91,14 @@ def _load() -> C.CDLL:
         "moe_layer_reset": ([vp], i32),
         "moe_layer_grid": ([vp, C.POINTER(i32), C.POINTER(i32)], i32),
     }
+    sig.update({
+        "moe_bench_read_stream": ([vp, sz, vp, vp], i32),
+        "moe_bench_fill": ([vp, sz, C.c_uint, vp], i32),
+        "moe_bench_empty": ([i32, vp], i32),
+    })
     for name, (args, res) in sig.items():
         f = getattr(lib, name)
         f.argtypes, f.restype = args, res
-    del sz
     return lib
 
 
@@ -147,6 +158,48 @@ def moe_expert_layout_query(wtype, hidden: int, inter: int, n_experts: int) -> d
     _check("moe_expert_layout_query",
            lib.moe_expert_layout_query(WTYPES.get(wtype, wtype), hidden, inter, n_experts, C.byref(out)))
     return out.as_dict()
+
+
+def _canon(ex: dict, wtype: str):
+    """Canonical arrays of one expert dict (codes13/scales13/codes2/scales2/g13/g2 or w13/w2)."""
+    if wtype == "nvfp4":
+        return (np.ascontiguousarray(ex["codes13"], np.uint8), np.ascontiguousarray(ex["scales13"], np.uint8),
+                np.ascontiguousarray(ex["codes2"], np.uint8), np.ascontiguousarray(ex["scales2"], np.uint8),
+                np.array([ex["g13"], ex["g2"]], np.float32))
+    return (np.ascontiguousarray(ex["w13"], np.uint16), None, np.ascontiguousarray(ex["w2"], np.uint16), None, None)
+
+
+def moe_pack_experts(wtype, hidden: int, inter: int, n_experts: int, first: int, experts: list,
+                     code_region: np.ndarray, scale_region=None, placement: int = MOE_PLACE_TWO_REGIONS) -> None:
+    """Packs the expert dicts `experts` as experts first.. of an n_experts set into the
+    set's host regions (the library places every byte)."""
+    wt = WTYPES.get(wtype, wtype)
+    parts = [_canon(ex, "nvfp4" if wt == MOE_W_NVFP4 else "bf16") for ex in experts]
+    stack = [np.ascontiguousarray(np.stack([p[i] for p in parts])) if parts[0][i] is not None else None
+             for i in range(5)]
+    _check("moe_pack_experts", lib.moe_pack_experts(wt, hidden, inter, n_experts, first, len(experts),
+                                                    *[_ptr(a) for a in stack], int(placement),
+                                                    _ptr(code_region), _ptr(scale_region)))
+
+
+def moe_unpack_experts(wtype, hidden: int, inter: int, n_experts: int, first: int, count: int,
+                       code_region: np.ndarray, scale_region=None, placement: int = MOE_PLACE_TWO_REGIONS) -> list:
+    """Inverse of moe_pack_experts: the canonical expert dicts of experts first..first+count-1."""
+    wt = WTYPES.get(wtype, wtype)
+    H, I = hidden, inter
+    if wt == MOE_W_NVFP4:
+        arrs = [np.empty((count, 2 * I, H // 2), np.uint8), np.empty((count, 2 * I, H // 16), np.uint8),
+                np.empty((count, H, I // 2), np.uint8), np.empty((count, H, I // 16), np.uint8),
+                np.empty((count, 2), np.float32)]
+    else:
+        arrs = [np.empty((count, 2 * I, H), np.uint16), None, np.empty((count, H, I), np.uint16), None, None]
+    _check("moe_unpack_experts", lib.moe_unpack_experts(wt, H, I, n_experts, first, count, _ptr(code_region),
+                                                        _ptr(scale_region), int(placement),
+                                                        *[_ptr(a) for a in arrs]))
+    if wt == MOE_W_NVFP4:
+        return [{"codes13": arrs[0][i], "scales13": arrs[1][i], "codes2": arrs[2][i], "scales2": arrs[3][i],
+                 "g13": arrs[4][i, 0], "g2": arrs[4][i, 1]} for i in range(count)]
+    return [{"w13": arrs[0][i], "w2": arrs[2][i]} for i in range(count)]
 
 
 def moe_pack_nvfp4(codes: np.ndarray, scales: np.ndarray, codes_out=None, scales_out=None):
@@ -232,3 +285,19 @@ def moe_layer_grid(handle) -> tuple[int, int]:
     g, l = C.c_int(0), C.c_int(0)
     _check("moe_layer_grid", lib.moe_layer_grid(handle, C.byref(g), C.byref(l)))
     return int(g.value), int(l.value)
+
+
+# ---- measurement utilities (include/moe_bench.h) -----------------------------------------
+
+def moe_bench_read_stream(buf, sink, stream=None) -> None:
+    _check("moe_bench_read_stream", lib.moe_bench_read_stream(_ptr(buf), buf.numel() * buf.element_size(),
+                                                              _ptr(sink), _stream(stream)))
+
+
+def moe_bench_fill(buf, value: int = 0, stream=None) -> None:
+    _check("moe_bench_fill", lib.moe_bench_fill(_ptr(buf), buf.numel() * buf.element_size(), int(value),
+                                                _stream(stream)))
+
+
+def moe_bench_empty(workgroups: int, stream=None) -> None:
+    _check("moe_bench_empty", lib.moe_bench_empty(int(workgroups), _stream(stream)))

@@ -62,6 +62,10 @@ int plan_shapes(const moe_layer_desc* d, Plan* p) {
   p->Er = Er;
   p->maxd = (d->max_batch * k < E) ? d->max_batch * k : E;
   p->G = 0;
+  // a kernel variant must exist for every batch bucket the layer may run
+  const int shape = moe::fixed_shape_of(H, I, E, k, S, Er, d->routed_wtype, d->shared_wtype);
+  for (int tb = 1; tb <= p->tbmax; tb *= 2)
+    if (!moe::fused_variant_exists(shape, tb, qx, d->routed_wtype, d->shared_wtype)) return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
 
@@ -123,6 +127,85 @@ int pack_geom(int rows, int cols, MatGeom* g) {
   return MOE_OK;
 }
 
+// One matrix, canonical <-> kernel layout.  PACK = true moves canonical bytes
+// (codes / scales / bf16 words) into the packed buffers, false the reverse.
+template <bool PACK>
+void move_nvfp4(const MatGeom& g, uint8_t* codes, uint8_t* scales, uint8_t* cp, uint8_t* sp) {
+  const size_t crow = (size_t)g.cols / 2, srow = (size_t)g.cols / 16;
+  for (int s = 0; s < g.ns; ++s)
+    for (int t = 0; t < g.nsteps; ++t)
+      for (int ri = 0; ri < g.rpw; ++ri)
+        for (int j = 0; j < g.cw; ++j) {
+          const size_t row = (size_t)t * g.rpw + ri, cc = (size_t)s * g.cw + j;
+          uint8_t* pc = cp + moe::code_unit(g, s, t, ri, j) * 16;
+          uint8_t* ps = sp + moe::scale_word(g, s, t, ri, j) + 2 * (t & 1);
+          if (PACK) {
+            memcpy(pc, codes + row * crow + cc * 16, 16);
+            memcpy(ps, scales + row * srow + cc * 2, 2);
+          } else {
+            memcpy(codes + row * crow + cc * 16, pc, 16);
+            memcpy(scales + row * srow + cc * 2, ps, 2);
+          }
+        }
+}
+template <bool PACK>
+void move_bf16(const MatGeom& g, uint16_t* w, uint16_t* wp) {
+  for (int s = 0; s < g.ns; ++s)
+    for (int t = 0; t < g.nsteps; ++t)
+      for (int sub = 0; sub < 4; ++sub)
+        for (int ri = 0; ri < g.rpw; ++ri)
+          for (int j = 0; j < g.cw; ++j) {
+            const size_t row = (size_t)t * g.rpw + ri, cc = (size_t)s * g.cw + j;
+            uint16_t* p = wp + moe::bf16_unit(g, s, t, sub, ri, j) * 8;
+            uint16_t* c = w + row * g.cols + cc * 32 + sub * 8;
+            if (PACK) memcpy(p, c, 16);
+            else memcpy(c, p, 16);
+          }
+}
+
+// Experts [first, first + count) of a set of n, canonical <-> the set's
+// regions (placement 0: code region + scale region; 1: one buffer, the scale
+// region at shared_scale_offset).
+template <bool PACK>
+int move_experts(int wtype, int H, int I, int n, int first, int count, uint8_t* w13, uint8_t* w13s, uint8_t* w2,
+                 uint8_t* w2s, float* ts, int placement, uint8_t* code_region, uint8_t* scale_region) {
+  moe_expert_layout lay;
+  if (int st = layout(wtype, H, I, n, &lay)) return st;
+  if (first < 0 || count < 0 || first > n || count > n - first) return MOE_ERR_INVALID_ARG;
+  if (placement != 0 && placement != 1) return MOE_ERR_INVALID_ARG;
+  if (code_region == nullptr || w13 == nullptr || w2 == nullptr) return MOE_ERR_INVALID_ARG;
+  MatGeom g13, g2;
+  if (int st = pack_geom(2 * I, H, &g13)) return st;
+  if (int st = pack_geom(H, I, &g2)) return st;
+  uint8_t* sreg = placement == 1 ? code_region + lay.shared_scale_offset : scale_region;
+  if (wtype == MOE_W_NVFP4 && (w13s == nullptr || w2s == nullptr || sreg == nullptr)) return MOE_ERR_INVALID_ARG;
+  for (int i = 0; i < count; ++i) {
+    const size_t e = (size_t)first + i;
+    uint8_t* cb = code_region + e * lay.code_stride;
+    if (wtype == MOE_W_NVFP4) {
+      const size_t c13 = (size_t)2 * I * H / 2, s13 = (size_t)2 * I * H / 16;
+      const size_t c2 = (size_t)H * I / 2, s2 = (size_t)H * I / 16;
+      uint8_t* sb = sreg + e * lay.scale_stride;
+      move_nvfp4<PACK>(g13, w13 + i * c13, w13s + i * s13, cb, sb);
+      move_nvfp4<PACK>(g2, w2 + i * c2, w2s + i * s2, cb + lay.w13_code_bytes, sb + lay.w13_scale_bytes);
+      float* tp = reinterpret_cast<float*>(sreg + lay.tensor_scale_offset) + 2 * e;
+      if (PACK) {
+        tp[0] = ts ? ts[2 * i] : 1.0f;
+        tp[1] = ts ? ts[2 * i + 1] : 1.0f;
+      } else if (ts) {
+        ts[2 * i] = tp[0];
+        ts[2 * i + 1] = tp[1];
+      }
+    } else {
+      const size_t n13 = (size_t)2 * I * H, n2 = (size_t)H * I;
+      move_bf16<PACK>(g13, reinterpret_cast<uint16_t*>(w13) + i * n13, reinterpret_cast<uint16_t*>(cb));
+      move_bf16<PACK>(g2, reinterpret_cast<uint16_t*>(w2) + i * n2,
+                      reinterpret_cast<uint16_t*>(cb + lay.w13_code_bytes));
+    }
+  }
+  return MOE_OK;
+}
+
 }  // namespace
 
 struct moe_layer {
@@ -176,15 +259,7 @@ int moe_pack_nvfp4(int rows, int cols, const uint8_t* codes, const uint8_t* scal
   if (!codes || !scales || !codes_out || !scales_out) return MOE_ERR_INVALID_ARG;
   MatGeom g;
   if (int st = pack_geom(rows, cols, &g)) return st;
-  const size_t crow = (size_t)cols / 2, srow = (size_t)cols / 16;
-  for (int s = 0; s < g.ns; ++s)
-    for (int t = 0; t < g.nsteps; ++t)
-      for (int ri = 0; ri < g.rpw; ++ri)
-        for (int j = 0; j < g.cw; ++j) {
-          const size_t row = (size_t)t * g.rpw + ri, cc = (size_t)s * g.cw + j;
-          memcpy(codes_out + moe::code_unit(g, s, t, ri, j) * 16, codes + row * crow + cc * 16, 16);
-          memcpy(scales_out + moe::scale_word(g, s, t, ri, j) + 2 * (t & 1), scales + row * srow + cc * 2, 2);
-        }
+  move_nvfp4<true>(g, const_cast<uint8_t*>(codes), const_cast<uint8_t*>(scales), codes_out, scales_out);
   return MOE_OK;
 }
 
@@ -193,15 +268,7 @@ int moe_unpack_nvfp4(int rows, int cols, const uint8_t* codes_packed, const uint
   if (!codes || !scales || !codes_packed || !scales_packed) return MOE_ERR_INVALID_ARG;
   MatGeom g;
   if (int st = pack_geom(rows, cols, &g)) return st;
-  const size_t crow = (size_t)cols / 2, srow = (size_t)cols / 16;
-  for (int s = 0; s < g.ns; ++s)
-    for (int t = 0; t < g.nsteps; ++t)
-      for (int ri = 0; ri < g.rpw; ++ri)
-        for (int j = 0; j < g.cw; ++j) {
-          const size_t row = (size_t)t * g.rpw + ri, cc = (size_t)s * g.cw + j;
-          memcpy(codes + row * crow + cc * 16, codes_packed + moe::code_unit(g, s, t, ri, j) * 16, 16);
-          memcpy(scales + row * srow + cc * 2, scales_packed + moe::scale_word(g, s, t, ri, j) + 2 * (t & 1), 2);
-        }
+  move_nvfp4<false>(g, codes, scales, const_cast<uint8_t*>(codes_packed), const_cast<uint8_t*>(scales_packed));
   return MOE_OK;
 }
 
@@ -209,14 +276,7 @@ int moe_pack_bf16(int rows, int cols, const uint16_t* w, uint16_t* w_out) {
   if (!w || !w_out) return MOE_ERR_INVALID_ARG;
   MatGeom g;
   if (int st = pack_geom(rows, cols, &g)) return st;
-  for (int s = 0; s < g.ns; ++s)
-    for (int t = 0; t < g.nsteps; ++t)
-      for (int sub = 0; sub < 4; ++sub)
-        for (int ri = 0; ri < g.rpw; ++ri)
-          for (int j = 0; j < g.cw; ++j) {
-            const size_t row = (size_t)t * g.rpw + ri, cc = (size_t)s * g.cw + j;
-            memcpy(w_out + moe::bf16_unit(g, s, t, sub, ri, j) * 8, w + row * cols + cc * 32 + sub * 8, 16);
-          }
+  move_bf16<true>(g, const_cast<uint16_t*>(w), w_out);
   return MOE_OK;
 }
 
@@ -224,15 +284,29 @@ int moe_unpack_bf16(int rows, int cols, const uint16_t* w_packed, uint16_t* w) {
   if (!w || !w_packed) return MOE_ERR_INVALID_ARG;
   MatGeom g;
   if (int st = pack_geom(rows, cols, &g)) return st;
-  for (int s = 0; s < g.ns; ++s)
-    for (int t = 0; t < g.nsteps; ++t)
-      for (int sub = 0; sub < 4; ++sub)
-        for (int ri = 0; ri < g.rpw; ++ri)
-          for (int j = 0; j < g.cw; ++j) {
-            const size_t row = (size_t)t * g.rpw + ri, cc = (size_t)s * g.cw + j;
-            memcpy(w + row * cols + cc * 32 + sub * 8, w_packed + moe::bf16_unit(g, s, t, sub, ri, j) * 8, 16);
-          }
+  move_bf16<false>(g, w, const_cast<uint16_t*>(w_packed));
   return MOE_OK;
+}
+
+int moe_pack_experts(int wtype, int hidden, int inter, int n_experts, int first, int count, const void* w13,
+                     const void* w13_scales, const void* w2, const void* w2_scales, const float* tensor_scales,
+                     int placement, void* code_region, void* scale_region) {
+  return move_experts<true>(wtype, hidden, inter, n_experts, first, count,
+                            static_cast<uint8_t*>(const_cast<void*>(w13)),
+                            static_cast<uint8_t*>(const_cast<void*>(w13_scales)),
+                            static_cast<uint8_t*>(const_cast<void*>(w2)),
+                            static_cast<uint8_t*>(const_cast<void*>(w2_scales)), const_cast<float*>(tensor_scales),
+                            placement, static_cast<uint8_t*>(code_region), static_cast<uint8_t*>(scale_region));
+}
+
+int moe_unpack_experts(int wtype, int hidden, int inter, int n_experts, int first, int count, const void* code_region,
+                       const void* scale_region, int placement, void* w13, void* w13_scales, void* w2, void* w2_scales,
+                       float* tensor_scales) {
+  return move_experts<false>(wtype, hidden, inter, n_experts, first, count, static_cast<uint8_t*>(w13),
+                             static_cast<uint8_t*>(w13_scales), static_cast<uint8_t*>(w2),
+                             static_cast<uint8_t*>(w2_scales), tensor_scales, placement,
+                             static_cast<uint8_t*>(const_cast<void*>(code_region)),
+                             static_cast<uint8_t*>(const_cast<void*>(scale_region)));
 }
 
 int moe_layer_create(const moe_layer_desc* desc, moe_layer_t* out) {
@@ -258,7 +332,8 @@ int moe_layer_create(const moe_layer_desc* desc, moe_layer_t* out) {
   for (int tb = 1; tb <= p.tbmax; tb *= 2) {
     int occ = 0;
     const int ti = tb_index(tb);
-    const int shape = moe::fixed_shape_of(desc->hidden, desc->inter, desc->n_routed, desc->top_k, desc->n_shared, p.Er);
+    const int shape = moe::fixed_shape_of(desc->hidden, desc->inter, desc->n_routed, desc->top_k, desc->n_shared, p.Er,
+                                          rwt, swt);
     if (moe::fused_occupancy(shape, tb, moe::fused_qx(desc->hidden), rwt, swt, p.lds_act[ti] + p.lds_acc[ti], &occ) != 0 ||
         occ < 1) {
       (void)hipGetLastError();

@@ -1276,6 +1276,14 @@ struct LogitWords { static constexpr int value = 2 * TB; };
 template <class A, int TB>
 struct LogitWords<A, TB, false> { static constexpr int value = (A::Er * TB + NT - 1) / NT; };
 
+// Routed tensor-scale words (W13, W2 per expert) each thread loads into the
+// shared-memory table: exact for a fixed shape, else enough for the largest
+// routed expert count.
+template <class A, bool DYN = std::is_base_of<DynShape, A>::value>
+struct TsWords { static constexpr int value = (2 * MOE_MAX_ROUTED + NT - 1) / NT; };
+template <class A>
+struct TsWords<A, false> { static constexpr int value = (2 * A::E + NT - 1) / NT; };
+
 // QX: 16-byte units of a router row per thread (H <= QX * NT * 8); the host
 // picks the smallest that fits, so every one of them is a real load.
 template <int TB, int QX, int WTR, int WTS, class A>
@@ -1325,9 +1333,10 @@ __global__ __launch_bounds__(NT) void k_fused_layer(A a) {
   const float* tsr_src = (WTR == WT_NVFP4 && a.r_tscale != nullptr) ? a.r_tscale : reinterpret_cast<const float*>(a.x);
   const float* tss_src = (WTS == WT_NVFP4 && a.S > 0 && a.s_tscale != nullptr)
                              ? a.s_tscale : reinterpret_cast<const float*>(a.x);
-  float tsv[2];
+  constexpr int NTS = TsWords<A>::value;
+  float tsv[NTS];
 #pragma unroll
-  for (int h = 0; h < 2; ++h) tsv[h] = tsr_src[min(tid + h * NT, max(nts, 1) - 1)];
+  for (int h = 0; h < NTS; ++h) tsv[h] = tsr_src[min(tid + h * NT, max(nts, 1) - 1)];
   const float tss = tss_src[min(tid, max(2 * a.S, 1) - 1)];
 
   // ---- set-up that needs no data (overlaps the loads above) -------------------
@@ -1429,7 +1438,7 @@ __global__ __launch_bounds__(NT) void k_fused_layer(A a) {
         for (int b = 0; b < TB; ++b) s.red[wave][rr][b] = racc[rr][b];
   }
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
+  for (int h = 0; h < NTS; ++h) {
     const int i = tid + h * NT;
     if (i < nts) (&s.tsr[0][0])[i] = tsv[h];
   }
@@ -1635,6 +1644,10 @@ static int with_variant(int shape, int tb, int qx, int rwt, int swt, F&& f) {
   return kNoVariant;
 }
 
+bool fused_variant_exists(int shape, int tb, int qx, int rwt, int swt) {
+  return with_variant(shape, tb, qx, rwt, swt, [](auto) -> int { return 0; }) == 0;
+}
+
 int fused_qx(int hidden) { return hidden / 8 <= NT ? 1 : (hidden / 8 <= 4 * NT ? 4 : 0); }
 
 int fused_occupancy(int shape, int tb, int qx, int rwt, int swt, int lds_bytes, int* blocks_per_cu) {
@@ -1651,7 +1664,7 @@ int fused_occupancy(int shape, int tb, int qx, int rwt, int swt, int lds_bytes, 
 int launch_fused(const FusedArgs& a, int tb, int rwt, int swt, void* stream) {
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   (void)hipGetLastError();  // clear a stale error so it is not reported as ours
-  const int shape = fixed_shape_of(a.H, a.I, a.E, a.k, a.S, a.Er);
+  const int shape = fixed_shape_of(a.H, a.I, a.E, a.k, a.S, a.Er, rwt, swt);
   // a fixed shape addresses experts with 32-bit offsets
   if (shape != 0 && ((size_t)a.E * a.r_code_stride >= (1ull << 32) || (size_t)a.E * a.r_scale_stride >= (1ull << 32)))
     return kNoVariant;

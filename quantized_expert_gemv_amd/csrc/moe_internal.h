@@ -209,9 +209,11 @@ inline KArgs<SH, BF> kargs_of(const FusedArgs& f) {
 }
 
 // Shape variant a layer runs with: 1 = FlintShape, 0 = read from the arguments.
-inline int fixed_shape_of(int H, int I, int E, int k, int S, int Er) {
+// The fixed shape is compiled for equal routed and shared weight types only;
+// any other pair runs the variant that reads the shape from the arguments.
+inline int fixed_shape_of(int H, int I, int E, int k, int S, int Er, int rwt, int swt) {
   using F = FlintShape;
-  return (H == F::H && I == F::I && E == F::E && k == F::k && S == F::S && Er == F::Er) ? 1 : 0;
+  return (H == F::H && I == F::I && E == F::E && k == F::k && S == F::S && Er == F::Er && rwt == swt) ? 1 : 0;
 }
 
 enum : unsigned { kErrLogitWait = 1u, kErrActWait = 2u };
@@ -222,6 +224,8 @@ MOE_HD inline int fused_lds_bytes(const KCommon& a) { return a.lds_act + a.lds_a
 int launch_fused(const FusedArgs& a, int tb, int rwt, int swt, void* stream);
 int launch_fused_debug_h(const FusedArgs& a, uint16_t* h_r, uint16_t* h_s, void* stream);
 int fused_occupancy(int shape, int tb, int qx, int rwt, int swt, int lds_bytes, int* blocks_per_cu);
+// Whether a kernel variant is compiled for (shape, batch bucket, qx, weight types); host only.
+bool fused_variant_exists(int shape, int tb, int qx, int rwt, int swt);
 // Router units per thread the kernel is built for at this hidden size (0: none).
 int fused_qx(int hidden);
 

@@ -24,27 +24,21 @@ def bf16_tensor_to_bits(t: torch.Tensor) -> np.ndarray:
     return t.detach().to("cpu").contiguous().view(torch.int16).numpy().view(np.uint16).copy()
 
 
-def pack_expert_set(get_expert, n: int, wtype: str, H: int, I: int):
-    """Host-side packing of n experts into (code region, scale region) bytes."""
+def pack_expert_set(get_expert, n: int, wtype: str, H: int, I: int, one_buffer: bool = False):
+    """Host-side packing of n experts, one at a time, by the library's set packer.
+
+    Returns (code region, scale region, layout); with one_buffer the code region
+    array is the whole one-buffer set and the scale region is None."""
     lay = B.moe_expert_layout_query(wtype, H, I, n)
-    codes = np.zeros(max(lay["code_region_bytes"], 16), np.uint8)
-    scales = np.zeros(max(lay["scale_region_bytes"], 16), np.uint8)
+    if one_buffer:
+        codes = np.zeros(max(lay["shared_total_bytes"], 16), np.uint8)
+        scales = None
+    else:
+        codes = np.zeros(max(lay["code_region_bytes"], 16), np.uint8)
+        scales = np.zeros(max(lay["scale_region_bytes"], 16), np.uint8)
     for e in range(n):
-        ex = get_expert(e)
-        c0 = e * lay["code_stride"]
-        c1 = c0 + lay["w13_code_bytes"]
-        c2 = c1 + lay["w2_code_bytes"]
-        if wtype == "nvfp4":
-            s0 = e * lay["scale_stride"]
-            s1 = s0 + lay["w13_scale_bytes"]
-            s2 = s1 + lay["w2_scale_bytes"]
-            B.moe_pack_nvfp4(ex["codes13"], ex["scales13"], codes[c0:c1], scales[s0:s1])
-            B.moe_pack_nvfp4(ex["codes2"], ex["scales2"], codes[c1:c2], scales[s1:s2])
-            ts = lay["tensor_scale_offset"] + 8 * e
-            scales[ts:ts + 8].view(np.float32)[:] = [np.float32(ex["g13"]), np.float32(ex["g2"])]
-        else:
-            B.moe_pack_bf16(ex["w13"], codes[c0:c1].view(np.uint16))
-            B.moe_pack_bf16(ex["w2"], codes[c1:c2].view(np.uint16))
+        B.moe_pack_experts(wtype, H, I, n, e, [get_expert(e)], codes, scales,
+                           B.MOE_PLACE_ONE_BUFFER if one_buffer else B.MOE_PLACE_TWO_REGIONS)
     return codes, scales, lay
 
 
@@ -61,12 +55,8 @@ class DeviceLayer:
         self.scales = torch.from_numpy(scales).to(self.device) if layer.routed_wtype == "nvfp4" else None
         del codes, scales
         if S > 0:
-            s_codes, s_scales, self.layout_s = pack_expert_set(layer.shared_expert, S, layer.shared_wtype, H, I)
-            blob = np.zeros(max(self.layout_s["shared_total_bytes"], 16), np.uint8)
-            blob[:self.layout_s["code_region_bytes"]] = s_codes[:self.layout_s["code_region_bytes"]]
-            if layer.shared_wtype == "nvfp4":
-                o = self.layout_s["shared_scale_offset"]
-                blob[o:o + self.layout_s["scale_region_bytes"]] = s_scales[:self.layout_s["scale_region_bytes"]]
+            blob, _, self.layout_s = pack_expert_set(layer.shared_expert, S, layer.shared_wtype, H, I,
+                                                     one_buffer=True)
             self.shared_w = torch.from_numpy(blob).to(self.device)
         else:
             self.layout_s, self.shared_w = None, None

@@ -33,6 +33,7 @@ _ROOT_SEED = 1234
 _T_ROUTER, _T_BIAS, _T_X = 0, 1, 3
 _T_CODES13, _T_SCALES13, _T_CODES2, _T_SCALES2 = 10, 11, 12, 13
 _T_BF13, _T_BF2 = 14, 15
+_T_TSCALE = 16
 _SHARED_OFFSET = 100  # shared expert s uses index _SHARED_OFFSET + s
 
 
@@ -119,6 +120,13 @@ class ArrayLayer:
         self.eps, self.residual = eps, residual
         self._routed, self._shared = routed, shared
 
+    def routed_tensor_scales(self, e: int) -> tuple:
+        """(W13, W2) fp32 tensor scales of routed expert e (NVFP4), without drawing its codes."""
+        return self._tscale(e, 0), self._tscale(e, 1)
+
+    def shared_tensor_scales(self, s: int) -> tuple:
+        return self._tscale(_SHARED_OFFSET + s, 0), self._tscale(_SHARED_OFFSET + s, 1)
+
     def routed_expert(self, e: int) -> dict:
         return self._routed[e]
 
@@ -129,11 +137,15 @@ class ArrayLayer:
 class SynthLayer:
     """One seeded synthetic layer of a workload; experts are drawn on demand."""
 
-    def __init__(self, workload: Workload | str, slot: int = 0):
+    def __init__(self, workload: Workload | str, slot: int = 0, tscale_set=None):
+        """tscale_set: optional values from which each NVFP4 expert's two fp32
+        tensor scales (W13, W2) are drawn, seeded per expert; default 1.0 (the
+        workloads' stated distribution)."""
         if isinstance(workload, str):
             workload = WORKLOADS[workload]
         wl = workload
         self.wl, self.slot = wl, slot
+        self.tscale_set = None if tscale_set is None else np.asarray(tscale_set, np.float32)
         self.hidden, self.inter = wl.hidden, wl.inter
         self.n_routed, self.top_k, self.n_shared = wl.n_routed, wl.top_k, wl.n_shared
         self.route = wl.route
@@ -167,9 +179,15 @@ class SynthLayer:
             "codes2": _rng(w, self.slot, _T_CODES2, index).integers(
                 0, 256, size=(H, I // 2), dtype=np.uint8),
             "scales2": scales(_T_SCALES2, (H, I // 16)),
-            "g13": np.float32(1.0),
-            "g2": np.float32(1.0),
+            "g13": self._tscale(index, 0),
+            "g2": self._tscale(index, 1),
         }
+
+    def _tscale(self, index: int, which: int) -> np.float32:
+        if self.tscale_set is None:
+            return np.float32(1.0)
+        pick = _rng(self.wl.wid, self.slot, _T_TSCALE, index).integers(0, self.tscale_set.size, size=2)
+        return np.float32(self.tscale_set[pick[which]])
 
     def _bf16_expert(self, index: int) -> dict:
         wl, H, I = self.wl, self.hidden, self.inter
@@ -179,6 +197,13 @@ class SynthLayer:
             "w13": to_bf16_bits(r13.standard_normal(size=(2 * I, H), dtype=np.float32) * np.float32(wl.bf16_std)),
             "w2": to_bf16_bits(r2.standard_normal(size=(H, I), dtype=np.float32) * np.float32(wl.bf16_std)),
         }
+
+    def routed_tensor_scales(self, e: int) -> tuple:
+        """(W13, W2) fp32 tensor scales of routed expert e (NVFP4), without drawing its codes."""
+        return self._tscale(e, 0), self._tscale(e, 1)
+
+    def shared_tensor_scales(self, s: int) -> tuple:
+        return self._tscale(_SHARED_OFFSET + s, 0), self._tscale(_SHARED_OFFSET + s, 1)
 
     def routed_expert(self, e: int) -> dict:
         if not 0 <= e < self.n_routed:

@@ -28,8 +28,20 @@ def test_every_declared_symbol_is_exported():
     assert set(names) == set(B.EXPORTED)
 
 
+def test_bench_header_symbols_are_exported():
+    text = open(os.path.join(ROOT, "include", "moe_bench.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = sorted(set(re.findall(r"^\s*int\s+(moe_\w+)\s*\(", text, flags=re.M)))
+    assert set(names) == set(B.BENCH_EXPORTED)
+    for n in names:
+        assert hasattr(B.lib, n), n
+    assert B.lib.moe_bench_read_stream(None, 65536, None, None) == -1
+    assert B.lib.moe_bench_fill(None, 16, 0, None) == -1
+    assert B.lib.moe_bench_empty(0, None) == -1
+
+
 def test_abi_version_and_status_strings():
-    assert B.moe_abi_version() == 2
+    assert B.moe_abi_version() == 3
     for code in B.STATUS:
         assert B.moe_status_str(code)
     assert B.moe_status_str(0) == "ok"
@@ -130,3 +142,81 @@ def test_create_fails_cleanly_without_gpu():
     h = B.C.c_void_p()
     st = B.lib.moe_layer_create(B.C.byref(_desc_for(WORKLOADS["tiny"])), B.C.byref(h))
     assert st == -6 and not h.value
+
+
+# ---- whole-set packers -------------------------------------------------------------------
+
+def _rand_expert(rng, wtype, H, I):
+    if wtype == "nvfp4":
+        return {"codes13": rng.integers(0, 256, (2 * I, H // 2), dtype=np.uint8),
+                "scales13": rng.integers(0, 256, (2 * I, H // 16), dtype=np.uint8),
+                "codes2": rng.integers(0, 256, (H, I // 2), dtype=np.uint8),
+                "scales2": rng.integers(0, 256, (H, I // 16), dtype=np.uint8),
+                "g13": np.float32(rng.choice([0.37, 0.7, 1.3, 2.0])),
+                "g2": np.float32(rng.choice([0.37, 0.7, 1.3, 2.0]))}
+    return {"w13": rng.integers(0, 1 << 16, (2 * I, H), dtype=np.uint32).astype(np.uint16),
+            "w2": rng.integers(0, 1 << 16, (H, I), dtype=np.uint32).astype(np.uint16)}
+
+
+@pytest.mark.parametrize("wtype,placement", [("nvfp4", 0), ("nvfp4", 1), ("bf16", 0), ("bf16", 1)])
+def test_expert_set_pack_roundtrip_and_placement(wtype, placement):
+    """moe_pack_experts places every expert (codes, block scales, tensor scales) where
+    moe_expert_layout_query says, packed in pieces; moe_unpack_experts inverts it."""
+    rng = np.random.default_rng(5 + placement)
+    H, I, n = 256, 128, 5
+    exps = [_rand_expert(rng, wtype, H, I) for _ in range(n)]
+    lay = B.moe_expert_layout_query(wtype, H, I, n)
+    if placement == 1:
+        code = np.zeros(lay["shared_total_bytes"], np.uint8)
+        scale = None
+    else:
+        code = np.zeros(lay["code_region_bytes"], np.uint8)
+        scale = np.zeros(max(lay["scale_region_bytes"], 1), np.uint8)
+    B.moe_pack_experts(wtype, H, I, n, 0, exps[:2], code, scale, placement)      # in two pieces
+    B.moe_pack_experts(wtype, H, I, n, 2, exps[2:], code, scale, placement)
+    back = B.moe_unpack_experts(wtype, H, I, n, 0, n, code, scale, placement)
+    for a, b in zip(exps, back):
+        for key in a:
+            assert np.array_equal(np.asarray(a[key]), np.asarray(b[key])), key
+    # each expert matches the single-matrix packer at the documented offsets
+    sreg = code[lay["shared_scale_offset"]:] if placement == 1 else scale
+    for e, ex in enumerate(exps):
+        c0 = e * lay["code_stride"]
+        if wtype == "nvfp4":
+            cp, sp = B.moe_pack_nvfp4(ex["codes13"], ex["scales13"])
+            s0 = e * lay["scale_stride"]
+            assert np.array_equal(code[c0:c0 + cp.size], cp) and np.array_equal(sreg[s0:s0 + sp.size], sp)
+            ts = sreg[lay["tensor_scale_offset"] + 8 * e:][:8].view(np.float32)
+            assert ts.tolist() == [np.float32(ex["g13"]), np.float32(ex["g2"])]
+        else:
+            wp = B.moe_pack_bf16(ex["w13"])
+            assert np.array_equal(code[c0:c0 + wp.nbytes].view(np.uint16), wp)
+
+
+def test_expert_set_pack_rejects_bad_ranges():
+    lay = B.moe_expert_layout_query("nvfp4", 256, 128, 2)
+    code = np.zeros(lay["code_region_bytes"], np.uint8)
+    scale = np.zeros(lay["scale_region_bytes"], np.uint8)
+    ex = _rand_expert(np.random.default_rng(1), "nvfp4", 256, 128)
+    with pytest.raises(B.MoeError):
+        B.moe_pack_experts("nvfp4", 256, 128, 2, 2, [ex], code, scale)          # first == n
+    with pytest.raises(B.MoeError):
+        B.moe_pack_experts("nvfp4", 256, 128, 2, 1, [ex, ex], code, scale)      # past the end
+    with pytest.raises(B.MoeError):
+        B.moe_pack_experts("nvfp4", 256, 128, 2, 0, [ex], code, None)          # scale region missing
+
+
+# ---- validate agrees with create on every weight-type pair --------------------------------
+
+@pytest.mark.parametrize("shape", ["flint", "generic"])
+@pytest.mark.parametrize("rwt,swt,want", [("nvfp4", "nvfp4", 0), ("bf16", "bf16", 0), ("nvfp4", "bf16", 0),
+                                          ("bf16", "nvfp4", -2)])
+def test_validate_accepts_exactly_the_compiled_type_pairs(shape, rwt, swt, want):
+    """Every pair validate accepts has a compiled kernel at every batch bucket (the
+    Flint shape falls back to the argument-shaped kernel for mixed pairs), so
+    create cannot fail for lack of a variant; the GPU test checks create itself."""
+    kw = dict(hidden=2048, inter=512, n_routed=256, top_k=6, n_shared=1) if shape == "flint" else \
+        dict(hidden=1024, inter=256, n_routed=64, top_k=4, n_shared=2)
+    for mb in (1, 2, 4, 8):
+        d = B.make_desc(max_batch=mb, routed_wtype=rwt, shared_wtype=swt, **kw)
+        assert B.moe_layer_validate(d) == want, (mb, rwt, swt)

@@ -95,9 +95,9 @@ def test_generic_shape_every_batch_bucket(name):
         assert not r["mismatched"] and r["rel_err"] <= 1e-2 and r["w_err"] <= 1e-4
 
 
-def test_sink_parity_sampled_tokens():
+def test_sink_parity_every_token():
     layer, dev = dev_layer("sink_b4")
-    r = compare_layer(dev, layer, layer.x(0), tokens=[0, 3])
+    r = compare_layer(dev, layer, layer.x(0), tokens=[0, 1, 2, 3])
     _report("sink_b4", r)
     assert not r["mismatched"] and r["rel_err"] <= 1e-2 and r["w_err"] <= 1e-5
     # the shared experts' coefficients are their softmax probabilities
@@ -396,3 +396,142 @@ def test_many_calls_alternating_batches():
             ref[n] = o
     torch.cuda.synchronize()
     assert dev.error() == 0
+
+
+# ---------------------------------------------------------------------------
+# per-expert tensor scales (NVFP4's third factor), other shapes, invariants
+# ---------------------------------------------------------------------------
+
+TS_SET = (0.37, 0.7, 1.3, 2.0)   # distinct, mostly not powers of two
+
+
+def _put_tensor_scales(dev, lt):
+    """Write lt's per-expert fp32 tensor scales into dev's packed buffers in
+    place (the code and block-scale bytes are those of the same seeded layer);
+    returns the saved buffers."""
+    saved = (dev.scales.clone() if dev.scales is not None else None,
+             dev.shared_w.clone() if dev.shared_w is not None else None)
+    if lt.routed_wtype == "nvfp4":
+        o = dev.layout_r["tensor_scale_offset"]
+        ts = torch.tensor([lt.routed_tensor_scales(e) for e in range(lt.n_routed)], dtype=torch.float32)
+        dev.scales[o:o + ts.numel() * 4].view(torch.float32).copy_(ts.view(-1).to(dev.device))
+    if lt.n_shared and lt.shared_wtype == "nvfp4":
+        o = dev.layout_s["shared_scale_offset"] + dev.layout_s["tensor_scale_offset"]
+        ts = torch.tensor([lt.shared_tensor_scales(q) for q in range(lt.n_shared)], dtype=torch.float32)
+        dev.shared_w[o:o + ts.numel() * 4].view(torch.float32).copy_(ts.view(-1).to(dev.device))
+    torch.cuda.synchronize()
+    return saved
+
+
+def _restore(dev, saved):
+    if saved[0] is not None:
+        dev.scales.copy_(saved[0])
+    if saved[1] is not None:
+        dev.shared_w.copy_(saved[1])
+    torch.cuda.synchronize()
+
+
+def _check_h_token(dev, r, batch, b=0):
+    hr, hs = dev.debug_h(batch)
+    hr, hs = hr.float().cpu().numpy(), hs.float().cpu().numpy()
+    i = r["rows"].index(b)
+    for j, e in enumerate(r["ids"][b].tolist()):
+        want = r["ref"]["h"][(i, e)]
+        assert np.max(np.abs(hr[b, j] - want)) <= 1e-2 * np.max(np.abs(want)), (b, j, e)
+    for q in range(hs.shape[1]):
+        want = r["ref"]["h"][(i, "shared", q)]
+        assert np.max(np.abs(hs[b, q] - want)) <= 1e-2 * np.max(np.abs(want)), (b, q)
+
+
+@pytest.mark.parametrize("name,tokens,steps", [("flint_b1", None, (0, 1, 2)), ("flint_b8", None, (0, 1)),
+                                               ("sink_b4", [1, 2], (2,))])
+def test_parity_with_distinct_tensor_scales(name, tokens, steps):
+    """Every routed and shared NVFP4 expert carries its own W13 and W2 tensor
+    scales drawn from {0.37, 0.7, 1.3, 2.0}: a scale read for the wrong expert,
+    slot or matrix moves the output or h far beyond the tolerance."""
+    layer, dev = dev_layer(name)
+    lt = SynthLayer(name, tscale_set=TS_SET)
+    saved = _put_tensor_scales(dev, lt)
+    try:
+        for step in steps:
+            x = lt.x(step)
+            r = compare_layer(dev, lt, x, tokens=tokens)
+            _report(f"{name} tensor scales step {step}", r)
+            assert not r["mismatched"] and r["rel_err"] <= 1e-2 and r["w_err"] <= 1e-4
+            _check_h_token(dev, r, x.shape[0], b=r["rows"][0])
+    finally:
+        _restore(dev, saved)
+
+
+def test_more_than_256_routed_experts_with_distinct_tensor_scales():
+    """E = 384: the routed tensor-scale table covers experts beyond the first 256."""
+    from quantized_expert_gemv_amd.device_layer import DeviceLayer
+    from quantized_expert_gemv_amd.synth import Workload
+    wl = Workload(8, "e384", 256, 128, 384, 4, 1, 8, router_std=None, bias_std=0.5, description="E=384")
+    layer = SynthLayer(wl, tscale_set=TS_SET)
+    dev = DeviceLayer(layer, 8)
+    try:
+        seen = set()
+        for n, step in ((1, 0), (3, 1), (8, 2), (8, 3)):
+            r = compare_layer(dev, layer, layer.x(step, batch=n))
+            seen |= set(r["ids"].ravel().tolist())
+            _report(f"E=384 batch {n}", r)
+            assert not r["mismatched"] and r["rel_err"] <= 1e-2 and r["w_err"] <= 1e-4
+        assert max(seen) >= 256, sorted(seen)       # experts past 256 were exercised
+    finally:
+        dev.close()
+
+
+def test_flint_shape_nvfp4_routed_bf16_shared():
+    """The precision split of the Inkling page (NVFP4 routed, BF16 shared
+    experts) at the Flint shape: validate accepts it, create runs it."""
+    from quantized_expert_gemv_amd import binding as B
+    from quantized_expert_gemv_amd.device_layer import DeviceLayer
+    from quantized_expert_gemv_amd.synth import Workload
+    wl = Workload(9, "flint_mixed", 2048, 512, 256, 6, 1, 2, shared_wtype="bf16", description="mixed")
+    layer = SynthLayer(wl)
+    dev = DeviceLayer(layer, 2)
+    try:
+        assert B.moe_layer_validate(dev.desc) == 0
+        for n in (1, 2):
+            r = compare_layer(dev, layer, layer.x(n, batch=n))
+            _report(f"flint mixed batch {n}", r)
+            assert not r["mismatched"] and r["rel_err"] <= 1e-2
+    finally:
+        dev.close()
+
+
+class _Permuted:
+    """The same layer with routed expert ids relabelled: new expert e is old
+    expert perm[e] (router row and bias move with it)."""
+
+    def __init__(self, base, perm):
+        self._b, self.perm = base, np.asarray(perm)
+        self.router_w = base.router_w[self.perm]
+        self.router_bias = None if base.router_bias is None else base.router_bias[self.perm]
+
+    def __getattr__(self, n):
+        return getattr(self._b, n)
+
+    def routed_expert(self, e):
+        return self._b.routed_expert(int(self.perm[e]))
+
+
+@pytest.mark.parametrize("name", ["flint_b1", "flint_b8"])
+def test_expert_permutation_permutes_ids_only(name):
+    from quantized_expert_gemv_amd.device_layer import DeviceLayer, bits_to_bf16_tensor
+    layer, dev = dev_layer(name)
+    perm = np.random.default_rng(31).permutation(layer.n_routed)
+    lp = _Permuted(layer, perm)
+    dp = DeviceLayer(lp, dev.max_batch)
+    try:
+        for step in (0, 1):
+            x = bits_to_bf16_tensor(layer.x(step), dev.device)
+            a, b = dev(x).clone(), dp(x).clone()
+            ia, _, _ = dev.routing(x.shape[0])
+            ib, _, _ = dp.routing(x.shape[0])
+            torch.cuda.synchronize()
+            assert (perm[ib.cpu().numpy()] == ia.cpu().numpy()).all()
+            assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    finally:
+        dp.close()
