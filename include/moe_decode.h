@@ -244,6 +244,26 @@ int moe_decode_layer(moe_layer_t layer, const void* x, const void* router_w,
                      const void* expert_packed, const void* scales, const void* shared_w,
                      void* out, int batch, void* stream);
 
+/* For callers that cannot allocate device memory: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc.  The same layer call as
+ * moe_decode_layer, on the same kernels, without a handle: desc (host, validated as
+ * moe_layer_validate does) replaces the handle, and the call's workspace (exchange
+ * words, call counter, routing copy) lives in a static device array of the library,
+ * MOE_STATIC_SCRATCH_BYTES per device, held by every device the library runs on until
+ * the process ends.  A description whose workspace does not fit is rejected with
+ * MOE_ERR_UNSUPPORTED before anything is enqueued.  The call performs no hipMalloc,
+ * hipFree or other allocation (the launch plan of a shape is made on its first call on a
+ * device and kept in a fixed table).  Every call on one GPU shares that GPU's array, which
+ * keeps the last call's contents: calls that overlap on one GPU (streams without an
+ * order between them) race and their outputs are undefined.  err_flags: optional device
+ * word (4-byte aligned) into which the call ORs the wait bits moe_layer_error would
+ * report; the caller clears it; NULL discards them.  x, router_w, expert_packed,
+ * scales, shared_w, out, batch and stream as for moe_decode_layer.                    */
+#define MOE_STATIC_SCRATCH_BYTES (1u << 20)
+int moe_decode_layer_static(const moe_layer_desc* desc, const void* x, const void* router_w,
+                            const void* expert_packed, const void* scales, const void* shared_w,
+                            void* out, int batch, unsigned* err_flags, void* stream);
+
 /* Routing of the last moe_decode_layer call on this handle, copied on `stream` into
  * device buffers: ids int32 [batch][k] and w fp32 [batch][k] in selection order
  * (descending score, ties to the lower index); c fp32 [batch][S] shared coefficients

@@ -28,7 +28,8 @@ ROUTES = {"sigmoid": MOE_ROUTE_SIGMOID_TOPK, "sink": MOE_ROUTE_SOFTMAX_SINK}
 EXPORTED = ("moe_abi_version", "moe_status_str", "moe_layer_validate", "moe_expert_layout_query",
             "moe_pack_experts", "moe_unpack_experts",
             "moe_pack_nvfp4", "moe_unpack_nvfp4", "moe_pack_bf16", "moe_unpack_bf16",
-            "moe_layer_create", "moe_layer_destroy", "moe_decode_layer", "moe_layer_routing",
+            "moe_layer_create", "moe_layer_destroy", "moe_decode_layer", "moe_decode_layer_static",
+            "moe_layer_routing",
             "moe_layer_set_profiling", "moe_layer_debug_h", "moe_layer_error", "moe_layer_reset",
             "moe_layer_grid")
 
@@ -84,6 +85,7 @@ def _load() -> C.CDLL:
         "moe_layer_create": ([C.POINTER(moe_layer_desc), C.POINTER(vp)], i32),
         "moe_layer_destroy": ([vp], i32),
         "moe_decode_layer": ([vp, vp, vp, vp, vp, vp, vp, i32, vp], i32),
+        "moe_decode_layer_static": ([C.POINTER(moe_layer_desc), vp, vp, vp, vp, vp, vp, i32, vp, vp], i32),
         "moe_layer_routing": ([vp, vp, vp, vp, vp], i32),
         "moe_layer_set_profiling": ([vp, vp, i32], i32),
         "moe_layer_debug_h": ([vp, vp, vp, vp], i32),
@@ -254,6 +256,13 @@ def moe_decode_layer(handle, x, router_w, expert_packed, scales, shared_w, out, 
     _check("moe_decode_layer", lib.moe_decode_layer(handle, _ptr(x), _ptr(router_w), _ptr(expert_packed),
                                                     _ptr(scales), _ptr(shared_w), _ptr(out), int(batch),
                                                     _stream(stream)))
+
+
+def moe_decode_layer_static(desc: moe_layer_desc, x, router_w, expert_packed, scales, shared_w, out, batch,
+                            err_flags=None, stream=None) -> None:
+    _check("moe_decode_layer_static",
+           lib.moe_decode_layer_static(C.byref(desc), _ptr(x), _ptr(router_w), _ptr(expert_packed), _ptr(scales),
+                                       _ptr(shared_w), _ptr(out), int(batch), _ptr(err_flags), _stream(stream)))
 
 
 def moe_layer_routing(handle, ids=None, w=None, c=None, stream=None) -> None:

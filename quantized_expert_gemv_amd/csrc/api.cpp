@@ -7,6 +7,7 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
 #include <new>
 #include <vector>
 
@@ -227,6 +228,110 @@ struct moe_layer {
   unsigned long long prof_call;
 };
 
+namespace {
+
+// Byte offsets of the workspace areas of a layer (one allocation, or the
+// library's static scratch array for moe_decode_layer_static).
+struct WsLayout {
+  size_t epoch, err, xlog, xh, tid, tw, c, total;
+};
+
+WsLayout ws_layout(const moe_layer_desc* d, const Plan& p) {
+  const size_t maxB = d->max_batch, k = d->top_k;
+  const size_t S1 = d->n_shared > 0 ? d->n_shared : 1;
+  const size_t npairs = maxB * (k + d->n_shared);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align_up(off + bytes, kAlign);
+    return o;
+  };
+  WsLayout w;
+  w.epoch = take(sizeof(unsigned));
+  w.err = take(sizeof(unsigned));
+  w.xlog = take((size_t)p.Er * moe::kLogitLine * 8);
+  w.xh = take(npairs * (d->inter / 2) * 8);
+  w.tid = take(maxB * k * sizeof(int));
+  w.tw = take(maxB * k * sizeof(float));
+  w.c = take(maxB * S1 * sizeof(float));
+  w.total = off;
+  return w;
+}
+
+void bind_ws(moe_layer* L, void* base, const WsLayout& wl) {
+  char* w = static_cast<char*>(base);
+  L->ws = base;
+  L->epoch = reinterpret_cast<unsigned*>(w + wl.epoch);
+  L->err = reinterpret_cast<unsigned*>(w + wl.err);
+  L->xlog = reinterpret_cast<unsigned long long*>(w + wl.xlog);
+  L->xh = reinterpret_cast<unsigned long long*>(w + wl.xh);
+  L->topk_ids = reinterpret_cast<int*>(w + wl.tid);
+  L->topk_w = reinterpret_cast<float*>(w + wl.tw);
+  L->shared_c = reinterpret_cast<float*>(w + wl.c);
+}
+
+// The gate/up item divisor, checked once per divisor value over every item
+// index a launch can form (n < 2^22; the method is exact for n < 2^31).
+// Checked divisors are remembered in a fixed table (no allocation).
+bool fastdiv_checked(uint32_t d, moe::FastDiv* out) {
+  static std::mutex mu;
+  static uint32_t done[64];
+  static int ndone = 0;
+  const moe::FastDiv dv = moe::make_fastdiv(d);
+  {
+    std::lock_guard<std::mutex> g(mu);
+    for (int i = 0; i < ndone; ++i)
+      if (done[i] == d) {
+        *out = dv;
+        return true;
+      }
+  }
+  for (uint32_t n = 0; n < (1u << 22); ++n)
+    if (moe::fastdiv(n, dv) != n / d) return false;
+  std::lock_guard<std::mutex> g(mu);
+  if (ndone < 64) done[ndone++] = d;
+  *out = dv;
+  return true;
+}
+
+// Grid of the launch on `device`: a power of two of workgroups (work splits
+// by shifts), at most one per router row (each publishes a logit, which is
+// how workgroup 0 knows every workgroup has read the call counter), at most
+// two rows each, and never more than can be resident together.
+int plan_device(const moe_layer_desc* desc, Plan* pp, int device) {
+  Plan& p = *pp;
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess || cus <= 0) {
+    (void)hipGetLastError();
+    return MOE_ERR_DEVICE;
+  }
+  int cap = p.Er < cus ? p.Er : cus;
+  const int rwt = desc->routed_wtype, swt = desc->shared_wtype;
+  int G = 1;
+  while (2 * G <= cap) G *= 2;
+  plan_grid(desc, &p, G);
+  const int shape = moe::fixed_shape_of(desc->hidden, desc->inter, desc->n_routed, desc->top_k, desc->n_shared, p.Er,
+                                        rwt, swt);
+  for (int tb = 1; tb <= p.tbmax; tb *= 2) {
+    int occ = 0;
+    const int ti = tb_index(tb);
+    if (moe::fused_occupancy(shape, tb, moe::fused_qx(desc->hidden), rwt, swt, p.lds_act[ti] + p.lds_acc[ti], &occ) != 0 ||
+        occ < 1) {
+      (void)hipGetLastError();
+      return MOE_ERR_UNSUPPORTED;
+    }
+    while (G > occ * cus) G /= 2;
+  }
+  if (2 * G < p.Er) return MOE_ERR_UNSUPPORTED;
+  plan_grid(desc, &p, G);
+  const int gs2 = desc->inter / p.g13.rpw / 2;
+  if (moe::kFusedWaves / p.g13.ns > gs2) return MOE_ERR_UNSUPPORTED;
+  if (!fastdiv_checked((uint32_t)gs2, &p.dv_gs2)) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 int moe_abi_version(void) { return MOE_ABI_VERSION; }
@@ -314,43 +419,12 @@ int moe_layer_create(const moe_layer_desc* desc, moe_layer_t* out) {
   *out = nullptr;
   Plan p;
   if (int st = plan_shapes(desc, &p)) return st;
-  int device = 0, cus = 0;
-  if (hipGetDevice(&device) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess || cus <= 0) {
+  int device = 0;
+  if (hipGetDevice(&device) != hipSuccess) {
     (void)hipGetLastError();
     return MOE_ERR_DEVICE;
   }
-  // A power of two of workgroups (work splits by shifts), at most one per
-  // router row (each publishes a logit, which is how workgroup 0 knows every
-  // workgroup has read the call counter), at most two rows each, and never
-  // more than can be resident together.
-  int cap = p.Er < cus ? p.Er : cus;
-  const int rwt = desc->routed_wtype, swt = desc->shared_wtype;
-  int G = 1;
-  while (2 * G <= cap) G *= 2;
-  plan_grid(desc, &p, G);
-  for (int tb = 1; tb <= p.tbmax; tb *= 2) {
-    int occ = 0;
-    const int ti = tb_index(tb);
-    const int shape = moe::fixed_shape_of(desc->hidden, desc->inter, desc->n_routed, desc->top_k, desc->n_shared, p.Er,
-                                          rwt, swt);
-    if (moe::fused_occupancy(shape, tb, moe::fused_qx(desc->hidden), rwt, swt, p.lds_act[ti] + p.lds_acc[ti], &occ) != 0 ||
-        occ < 1) {
-      (void)hipGetLastError();
-      return MOE_ERR_UNSUPPORTED;
-    }
-    while (G > occ * cus) G /= 2;
-  }
-  if (2 * G < p.Er) return MOE_ERR_UNSUPPORTED;
-  plan_grid(desc, &p, G);
-  // gate/up items: divisor of the step pairs, checked over every item count
-  const int gs2 = desc->inter / p.g13.rpw / 2;
-  if (moe::kFusedWaves / p.g13.ns > gs2) return MOE_ERR_UNSUPPORTED;
-  const moe::FastDiv dv = moe::make_fastdiv((uint32_t)gs2);
-  for (uint32_t n = 0; n < (1u << 22); ++n)
-    if (moe::fastdiv(n, dv) != n / (uint32_t)gs2) return MOE_ERR_UNSUPPORTED;
-  p.dv_gs2 = dv;
-
+  if (int st = plan_device(desc, &p, device)) return st;
   moe_layer* L = new (std::nothrow) moe_layer();
   if (L == nullptr) return MOE_ERR_DEVICE;
   L->d = *desc;
@@ -358,23 +432,8 @@ int moe_layer_create(const moe_layer_desc* desc, moe_layer_t* out) {
   L->device = device;
   layout(desc->routed_wtype, desc->hidden, desc->inter, desc->n_routed, &L->lr);
   layout(desc->shared_wtype, desc->hidden, desc->inter, desc->n_shared, &L->ls);
-  const size_t maxB = desc->max_batch, k = desc->top_k;
-  const size_t S1 = desc->n_shared > 0 ? desc->n_shared : 1;
-  const size_t npairs = maxB * (k + desc->n_shared);
-  size_t off = 0;
-  auto take = [&](size_t bytes) {
-    const size_t o = off;
-    off = align_up(off + bytes, kAlign);
-    return o;
-  };
-  const size_t o_epoch = take(sizeof(unsigned));
-  const size_t o_err = take(sizeof(unsigned));
-  const size_t o_xlog = take((size_t)p.Er * moe::kLogitLine * 8);
-  const size_t o_xh = take(npairs * (desc->inter / 2) * 8);
-  const size_t o_tid = take(maxB * k * sizeof(int));
-  const size_t o_tw = take(maxB * k * sizeof(float));
-  const size_t o_c = take(maxB * S1 * sizeof(float));
-  L->ws_bytes = off;
+  const WsLayout wl = ws_layout(desc, p);
+  L->ws_bytes = wl.total;
   if (hipMalloc(&L->ws, L->ws_bytes) != hipSuccess) {
     (void)hipGetLastError();
     delete L;
@@ -386,14 +445,7 @@ int moe_layer_create(const moe_layer_desc* desc, moe_layer_t* out) {
     delete L;
     return MOE_ERR_DEVICE;
   }
-  char* w = static_cast<char*>(L->ws);
-  L->epoch = reinterpret_cast<unsigned*>(w + o_epoch);
-  L->err = reinterpret_cast<unsigned*>(w + o_err);
-  L->xlog = reinterpret_cast<unsigned long long*>(w + o_xlog);
-  L->xh = reinterpret_cast<unsigned long long*>(w + o_xh);
-  L->topk_ids = reinterpret_cast<int*>(w + o_tid);
-  L->topk_w = reinterpret_cast<float*>(w + o_tw);
-  L->shared_c = reinterpret_cast<float*>(w + o_c);
+  bind_ws(L, L->ws, wl);
   *out = L;
   return MOE_OK;
 }
@@ -470,14 +522,9 @@ moe::FusedArgs make_args(const moe_layer* L, const void* x, const void* router_w
   return a;
 }
 
-}  // namespace
-
-extern "C" {
-
-int moe_decode_layer(moe_layer_t L, const void* x, const void* router_w, const void* expert_packed,
-                     const void* scales, const void* shared_w, void* out, int batch, void* stream) {
-  if (L == nullptr) return MOE_ERR_INVALID_ARG;
-  const moe_layer_desc& d = L->d;
+// Argument checks of one layer call (both entry points).
+int check_call(const moe_layer_desc& d, const void* x, const void* router_w, const void* expert_packed,
+               const void* scales, const void* shared_w, const void* out, int batch) {
   if (batch < 1 || batch > d.max_batch) return MOE_ERR_BATCH;
   if (!x || !router_w || !expert_packed || !out) return MOE_ERR_INVALID_ARG;
   if (d.routed_wtype == MOE_W_NVFP4 && !scales) return MOE_ERR_INVALID_ARG;
@@ -486,6 +533,51 @@ int moe_decode_layer(moe_layer_t L, const void* x, const void* router_w, const v
   if (!aligned16(x) || !aligned16(router_w) || !aligned16(expert_packed) || !aligned16(out) ||
       (scales && !aligned16(scales)) || (shared_w && !aligned16(shared_w)))
     return MOE_ERR_ALIGNMENT;
+  return MOE_OK;
+}
+
+// Plans of handle-less calls, per (device, layer shape), in a fixed table.
+bool cached_plan(const moe_layer_desc* d, int device, Plan* p) {
+  struct Key {
+    int device, H, I, E, k, S, maxb, rwt, swt, route;
+    bool operator==(const Key& o) const {
+      return device == o.device && H == o.H && I == o.I && E == o.E && k == o.k && S == o.S && maxb == o.maxb &&
+             rwt == o.rwt && swt == o.swt && route == o.route;
+    }
+  };
+  constexpr int kSlots = 16;
+  static std::mutex mu;
+  static Key keys[kSlots];
+  static Plan plans[kSlots];
+  static int used = 0, next = 0;
+  const Key key{device, d->hidden, d->inter, d->n_routed, d->top_k, d->n_shared, d->max_batch,
+                d->routed_wtype, d->shared_wtype, d->route};
+  {
+    std::lock_guard<std::mutex> g(mu);
+    for (int i = 0; i < used; ++i)
+      if (keys[i] == key) {
+        *p = plans[i];
+        return true;
+      }
+  }
+  if (plan_device(d, p, device) != MOE_OK) return false;
+  std::lock_guard<std::mutex> g(mu);
+  keys[next] = key;
+  plans[next] = *p;
+  next = (next + 1) % kSlots;
+  if (used < kSlots) ++used;
+  return true;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_decode_layer(moe_layer_t L, const void* x, const void* router_w, const void* expert_packed,
+                     const void* scales, const void* shared_w, void* out, int batch, void* stream) {
+  if (L == nullptr) return MOE_ERR_INVALID_ARG;
+  const moe_layer_desc& d = L->d;
+  if (int st = check_call(d, x, router_w, expert_packed, scales, shared_w, out, batch)) return st;
   const moe::FusedArgs a = make_args(L, x, router_w, expert_packed, scales, shared_w, out, batch);
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   if (!L->prof.empty()) {
@@ -499,6 +591,36 @@ int moe_decode_layer(moe_layer_t L, const void* x, const void* router_w, const v
     return MOE_ERR_LAUNCH;
   }
   L->last_batch = batch;
+  return MOE_OK;
+}
+
+int moe_decode_layer_static(const moe_layer_desc* desc, const void* x, const void* router_w,
+                            const void* expert_packed, const void* scales, const void* shared_w, void* out,
+                            int batch, unsigned* err_flags, void* stream) {
+  Plan p;
+  if (int st = plan_shapes(desc, &p)) return st;
+  const WsLayout wl = ws_layout(desc, p);
+  if (wl.total > moe::kStaticScratchBytes) return MOE_ERR_UNSUPPORTED;
+  if (int st = check_call(*desc, x, router_w, expert_packed, scales, shared_w, out, batch)) return st;
+  if (err_flags != nullptr && (reinterpret_cast<uintptr_t>(err_flags) & 3u)) return MOE_ERR_ALIGNMENT;
+  int device = 0;
+  if (hipGetDevice(&device) != hipSuccess) {
+    (void)hipGetLastError();
+    return MOE_ERR_DEVICE;
+  }
+  void* base = moe::static_scratch(device);
+  if (base == nullptr) return MOE_ERR_DEVICE;
+  if (!cached_plan(desc, device, &p)) return MOE_ERR_UNSUPPORTED;
+  moe_layer L;                      // on the stack: no workspace of its own
+  L.d = *desc;
+  L.p = p;
+  L.device = device;
+  layout(desc->routed_wtype, desc->hidden, desc->inter, desc->n_routed, &L.lr);
+  layout(desc->shared_wtype, desc->hidden, desc->inter, desc->n_shared, &L.ls);
+  bind_ws(&L, base, wl);
+  if (err_flags != nullptr) L.err = err_flags;
+  const moe::FusedArgs a = make_args(&L, x, router_w, expert_packed, scales, shared_w, out, batch);
+  if (moe::launch_fused(a, tb_of(batch), desc->routed_wtype, desc->shared_wtype, stream) != 0) return MOE_ERR_LAUNCH;
   return MOE_OK;
 }
 

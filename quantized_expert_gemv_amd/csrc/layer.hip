@@ -39,6 +39,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "moe_internal.h"
 
 #include "device_util.h"
@@ -1578,7 +1580,31 @@ __global__ __launch_bounds__(NT) void k_fused_debug_h(FusedArgs a, uint16_t* h_r
   }
 }
 
+// Workspace of moe_decode_layer_static: the exchange words, call counter,
+// error word and routing readback of handle-less calls, one copy per device
+// for the life of the process.  Zero at load (tag 0 marks never-written
+// words).  Host code never uses this name as an address: it reads the
+// per-device address once with hipGetSymbolAddress (static_scratch below).
+__device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
 }  // namespace
+
+void* static_scratch(int device) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  if (device < 0 || device >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> g(mu);
+  if (addr[device] == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) {
+      (void)hipGetLastError();
+      return nullptr;
+    }
+    addr[device] = ptr;
+  }
+  return addr[device];
+}
 
 // ---------------------------------------------------------------------------
 // launch

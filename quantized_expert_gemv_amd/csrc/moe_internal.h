@@ -218,6 +218,14 @@ inline int fixed_shape_of(int H, int I, int E, int k, int S, int Er, int rwt, in
 
 enum : unsigned { kErrLogitWait = 1u, kErrActWait = 2u };
 
+// Size of the library's static device scratch array (moe_decode_layer_static):
+// the largest workspace a layer may need to run without a handle.
+constexpr size_t kStaticScratchBytes = (size_t)1 << 20;
+static_assert(kStaticScratchBytes == MOE_STATIC_SCRATCH_BYTES, "scratch size differs from the header's");
+// Device address of the static scratch array on `device` (the current
+// device), looked up once per device; nullptr on failure.
+void* static_scratch(int device);
+
 // Dynamic LDS bytes of the kernel for a plan.
 MOE_HD inline int fused_lds_bytes(const KCommon& a) { return a.lds_act + a.lds_acc; }
 

@@ -220,3 +220,15 @@ def test_validate_accepts_exactly_the_compiled_type_pairs(shape, rwt, swt, want)
     for mb in (1, 2, 4, 8):
         d = B.make_desc(max_batch=mb, routed_wtype=rwt, shared_wtype=swt, **kw)
         assert B.moe_layer_validate(d) == want, (mb, rwt, swt)
+
+
+def test_static_entry_rejects_oversize_workspace_before_the_device():
+    """The handle-less call's workspace must fit the static scratch array: the
+    largest shapes at batch 8 do not, and are refused on the host."""
+    big = B.make_desc(hidden=2048, inter=2048, n_routed=512, top_k=16, n_shared=4, max_batch=8)
+    assert B.moe_layer_validate(big) == 0
+    st = B.lib.moe_decode_layer_static(B.C.byref(big), None, None, None, None, None, None, 1, None, None)
+    assert st == -2
+    ok = _desc_for(WORKLOADS["flint_b8"])
+    st = B.lib.moe_decode_layer_static(B.C.byref(ok), None, None, None, None, None, None, 1, None, None)
+    assert st == -1                  # fits; the missing buffers are the error
