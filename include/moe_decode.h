@@ -76,13 +76,10 @@ typedef enum {
 
 typedef enum { MOE_W_NVFP4 = 0, MOE_W_BF16 = 1 } moe_wtype;
 
-/* Where a packed expert set's scale region goes (moe_pack_experts). */
-typedef enum {
-  MOE_PLACE_TWO_REGIONS = 0, /* code region and scale region in two buffers (routed set:       */
-                             /* moe_decode_layer's expert_packed and scales)                    */
-  MOE_PLACE_ONE_BUFFER = 1   /* one buffer: code region, then the scale region at               */
-                             /* shared_scale_offset (shared set: moe_decode_layer's shared_w)   */
-} moe_placement;
+/* The two expert sets of a layer.  The routed set lives in two buffers (moe_decode_layer's
+ * expert_packed = its code region, scales = its scale region); the shared set in one
+ * (shared_w: code region, then the scale region at shared_scale_offset).              */
+typedef enum { MOE_SET_ROUTED = 0, MOE_SET_SHARED = 1 } moe_set;
 
 typedef enum {
   MOE_ROUTE_SIGMOID_TOPK = 0, /* s = sigmoid(l + bias), top-k of s, w = s / sum_topk s, shared c = 1 */
@@ -155,44 +152,45 @@ const char* moe_status_str(int status);
  * launch (MOE_ERR_UNSUPPORTED from the occupancy check).                              */
 int moe_layer_validate(const moe_layer_desc* desc);
 
-/* Layout of n experts of type wtype for hidden H / inter I (see moe_expert_layout):
- * the sizes a caller allocates for moe_pack_experts' outputs.  NVFP4 sizes follow the
- * format's three parts ("Frontier MoE on consumer Blackwell (SM120)", section
- * "GLM-5.2": e2m1 codes, e4m3 per 16-element block, one fp32 per tensor).            */
-int moe_expert_layout_query(int wtype, int hidden, int inter, int n_experts,
-                            moe_expert_layout* out);
+/* Byte layout of one expert set (MOE_SET_ROUTED or MOE_SET_SHARED) of the layer desc
+ * describes (see moe_expert_layout): the sizes a caller allocates for moe_pack_experts'
+ * outputs.  NVFP4 sizes follow the format's three parts ("Frontier MoE on consumer
+ * Blackwell (SM120)", section "GLM-5.2": e2m1 codes, e4m3 per 16-element block, one fp32
+ * per tensor).  Checks desc as moe_layer_validate does.                             */
+int moe_expert_layout_query(const moe_layer_desc* desc, int set, moe_expert_layout* out);
 
 /* ---- packers (host memory, lossless, load time) ----------------------------------- */
 /* The Flint page ("A 40B MoE that activates 2.5B parameters") repacks its checkpoint's
  * NVFP4 blocks losslessly at load time into the order its kernels read; these do the
  * same for the gfx950 kernels.  All buffers are host memory owned by the caller.      */
 
-/* Experts [first, first + count) of a set of n_experts, from canonical bytes into the
- * set's packed regions, every offset placed by the library (moe_expert_layout).
+/* Experts [first, first + count) of one expert set of the layer desc describes, from
+ * canonical bytes into the set's packed buffers, every offset and the order inside them
+ * chosen by the library (moe_expert_layout_query).
  *   NVFP4: w13 uint8 [count][2I][H/2], w13_scales uint8 [count][2I][H/16],
  *          w2 uint8 [count][H][I/2],   w2_scales uint8 [count][H][I/16],
  *          tensor_scales fp32 [count][2] = (W13, W2) per expert, or NULL for 1.0.
  *   BF16:  w13 uint16 [count][2I][H], w2 uint16 [count][H][I]; the scale and
  *          tensor-scale arguments are ignored (may be NULL).
- * placement MOE_PLACE_TWO_REGIONS: code_region holds code_region_bytes, scale_region
- * scale_region_bytes (NVFP4); MOE_PLACE_ONE_BUFFER: code_region holds shared_total_bytes
- * and scale_region is ignored.  Bytes of other experts are left as they are, so a set
- * can be packed a few experts at a time.  Lossless: every byte (-0 codes, zero and NaN
+ * MOE_SET_ROUTED: region holds code_region_bytes, scale_region scale_region_bytes
+ * (NVFP4; ignored for BF16).  MOE_SET_SHARED: region holds shared_total_bytes and
+ * scale_region is ignored.  Bytes of other experts are left as they are, so a set can
+ * be packed a few experts at a time.  Lossless: every byte (-0 codes, zero and NaN
  * scale bytes) is kept.  MOE_ERR_INVALID_ARG for a null required pointer or a range
- * outside [0, n_experts); MOE_ERR_UNSUPPORTED for a shape without a kernel layout.   */
-int moe_pack_experts(int wtype, int hidden, int inter, int n_experts, int first, int count,
+ * outside the set; the errors of moe_layer_validate for desc.                         */
+int moe_pack_experts(const moe_layer_desc* desc, int set, int first, int count,
                      const void* w13, const void* w13_scales, const void* w2,
-                     const void* w2_scales, const float* tensor_scales, int placement,
-                     void* code_region, void* scale_region);
-/* Exact inverse of moe_pack_experts (same arguments, data flowing the other way;
- * tensor_scales may be NULL to skip them).                                            */
-int moe_unpack_experts(int wtype, int hidden, int inter, int n_experts, int first, int count,
-                       const void* code_region, const void* scale_region, int placement,
-                       void* w13, void* w13_scales, void* w2, void* w2_scales,
-                       float* tensor_scales);
+                     const void* w2_scales, const float* tensor_scales, void* region,
+                     void* scale_region);
+/* Exact inverse of moe_pack_experts (data flowing the other way; tensor_scales may be
+ * NULL to skip them).                                                                  */
+int moe_unpack_experts(const moe_layer_desc* desc, int set, int first, int count,
+                       const void* region, const void* scale_region, void* w13,
+                       void* w13_scales, void* w2, void* w2_scales, float* tensor_scales);
 
-/* One canonical NVFP4 matrix [rows][cols] -> kernel layout (the building block of
- * moe_pack_experts).  codes: uint8 [rows][cols/2] in, rows*cols/2 bytes out; scales:
+/* One canonical NVFP4 matrix [rows][cols] -> the kernel layout (the building block of
+ * moe_pack_experts).
+ * codes: uint8 [rows][cols/2] in, rows*cols/2 bytes out; scales:
  * uint8 [rows][cols/16] in, rows*cols/16 bytes out.  A permutation of 16-byte code
  * units and 2-byte scale pairs.  rows/cols must describe a W13 ([2I][H]) or W2
  * ([H][I]) matrix of a valid layer.                                                  */
@@ -288,8 +286,8 @@ int moe_layer_set_profiling(moe_layer_t layer, void* const* events, int n_events
 int moe_layer_debug_h(moe_layer_t layer, void* h_routed, void* h_shared, void* stream);
 
 /* Sticky error bits of the handle's calls so far, read synchronously (waits for the
- * device): 1 = a workgroup gave up waiting for router logits, 2 = for activations, 4 =
- * for partial outputs (the grid was not resident at once).  clear != 0 resets them.
+ * device): 1 = a workgroup gave up waiting for router logits, 2 = for activations (the
+ * grid was not resident at once).  clear != 0 resets them.
  * After a non-zero result the handle's later outputs are undefined until
  * moe_layer_reset.  These waits replace the kernel boundaries of the Flint page's
  * chained low-latency kernels ("From 1,096 kernels to 346").                         */

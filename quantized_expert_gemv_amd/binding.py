@@ -21,7 +21,7 @@ STATUS = {0: "MOE_OK", -1: "MOE_ERR_INVALID_ARG", -2: "MOE_ERR_UNSUPPORTED", -3:
           -4: "MOE_ERR_BATCH", -5: "MOE_ERR_LAUNCH", -6: "MOE_ERR_DEVICE", -7: "MOE_ERR_STATE"}
 MOE_W_NVFP4, MOE_W_BF16 = 0, 1
 MOE_ROUTE_SIGMOID_TOPK, MOE_ROUTE_SOFTMAX_SINK = 0, 1
-MOE_PLACE_TWO_REGIONS, MOE_PLACE_ONE_BUFFER = 0, 1
+MOE_SET_ROUTED, MOE_SET_SHARED = 0, 1
 WTYPES = {"nvfp4": MOE_W_NVFP4, "bf16": MOE_W_BF16}
 ROUTES = {"sigmoid": MOE_ROUTE_SIGMOID_TOPK, "sink": MOE_ROUTE_SOFTMAX_SINK}
 
@@ -75,9 +75,9 @@ def _load() -> C.CDLL:
         "moe_abi_version": ([], i32),
         "moe_status_str": ([i32], C.c_char_p),
         "moe_layer_validate": ([C.POINTER(moe_layer_desc)], i32),
-        "moe_expert_layout_query": ([i32, i32, i32, i32, C.POINTER(moe_expert_layout)], i32),
-        "moe_pack_experts": ([i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, i32, vp, vp], i32),
-        "moe_unpack_experts": ([i32, i32, i32, i32, i32, i32, vp, vp, i32, vp, vp, vp, vp, vp], i32),
+        "moe_expert_layout_query": ([C.POINTER(moe_layer_desc), i32, C.POINTER(moe_expert_layout)], i32),
+        "moe_pack_experts": ([C.POINTER(moe_layer_desc), i32, i32, i32, vp, vp, vp, vp, vp, vp, vp], i32),
+        "moe_unpack_experts": ([C.POINTER(moe_layer_desc), i32, i32, i32, vp, vp, vp, vp, vp, vp, vp], i32),
         "moe_pack_nvfp4": ([i32, i32, vp, vp, vp, vp], i32),
         "moe_unpack_nvfp4": ([i32, i32, vp, vp, vp, vp], i32),
         "moe_pack_bf16": ([i32, i32, vp, vp], i32),
@@ -155,10 +155,9 @@ def moe_layer_validate(desc: moe_layer_desc) -> int:
     return lib.moe_layer_validate(C.byref(desc))
 
 
-def moe_expert_layout_query(wtype, hidden: int, inter: int, n_experts: int) -> dict:
+def moe_expert_layout_query(desc: "moe_layer_desc", set_: int = MOE_SET_ROUTED) -> dict:
     out = moe_expert_layout()
-    _check("moe_expert_layout_query",
-           lib.moe_expert_layout_query(WTYPES.get(wtype, wtype), hidden, inter, n_experts, C.byref(out)))
+    _check("moe_expert_layout_query", lib.moe_expert_layout_query(C.byref(desc), int(set_), C.byref(out)))
     return out.as_dict()
 
 
@@ -171,34 +170,35 @@ def _canon(ex: dict, wtype: str):
     return (np.ascontiguousarray(ex["w13"], np.uint16), None, np.ascontiguousarray(ex["w2"], np.uint16), None, None)
 
 
-def moe_pack_experts(wtype, hidden: int, inter: int, n_experts: int, first: int, experts: list,
-                     code_region: np.ndarray, scale_region=None, placement: int = MOE_PLACE_TWO_REGIONS) -> None:
-    """Packs the expert dicts `experts` as experts first.. of an n_experts set into the
-    set's host regions (the library places every byte)."""
-    wt = WTYPES.get(wtype, wtype)
-    parts = [_canon(ex, "nvfp4" if wt == MOE_W_NVFP4 else "bf16") for ex in experts]
+def _wtype_of(desc, set_):
+    return desc.routed_wtype if set_ == MOE_SET_ROUTED else desc.shared_wtype
+
+
+def moe_pack_experts(desc: "moe_layer_desc", set_: int, first: int, experts: list, region: np.ndarray,
+                     scale_region=None) -> None:
+    """Packs the expert dicts `experts` as experts first.. of one set of the layer
+    `desc` describes into the set's host buffers (the library places every byte)."""
+    nv = _wtype_of(desc, set_) == MOE_W_NVFP4
+    parts = [_canon(ex, "nvfp4" if nv else "bf16") for ex in experts]
     stack = [np.ascontiguousarray(np.stack([p[i] for p in parts])) if parts[0][i] is not None else None
              for i in range(5)]
-    _check("moe_pack_experts", lib.moe_pack_experts(wt, hidden, inter, n_experts, first, len(experts),
-                                                    *[_ptr(a) for a in stack], int(placement),
-                                                    _ptr(code_region), _ptr(scale_region)))
+    _check("moe_pack_experts", lib.moe_pack_experts(C.byref(desc), int(set_), first, len(experts),
+                                                    *[_ptr(a) for a in stack], _ptr(region), _ptr(scale_region)))
 
 
-def moe_unpack_experts(wtype, hidden: int, inter: int, n_experts: int, first: int, count: int,
-                       code_region: np.ndarray, scale_region=None, placement: int = MOE_PLACE_TWO_REGIONS) -> list:
+def moe_unpack_experts(desc: "moe_layer_desc", set_: int, first: int, count: int, region: np.ndarray,
+                       scale_region=None) -> list:
     """Inverse of moe_pack_experts: the canonical expert dicts of experts first..first+count-1."""
-    wt = WTYPES.get(wtype, wtype)
-    H, I = hidden, inter
-    if wt == MOE_W_NVFP4:
+    H, I = desc.hidden, desc.inter
+    if _wtype_of(desc, set_) == MOE_W_NVFP4:
         arrs = [np.empty((count, 2 * I, H // 2), np.uint8), np.empty((count, 2 * I, H // 16), np.uint8),
                 np.empty((count, H, I // 2), np.uint8), np.empty((count, H, I // 16), np.uint8),
                 np.empty((count, 2), np.float32)]
     else:
         arrs = [np.empty((count, 2 * I, H), np.uint16), None, np.empty((count, H, I), np.uint16), None, None]
-    _check("moe_unpack_experts", lib.moe_unpack_experts(wt, H, I, n_experts, first, count, _ptr(code_region),
-                                                        _ptr(scale_region), int(placement),
-                                                        *[_ptr(a) for a in arrs]))
-    if wt == MOE_W_NVFP4:
+    _check("moe_unpack_experts", lib.moe_unpack_experts(C.byref(desc), int(set_), first, count, _ptr(region),
+                                                        _ptr(scale_region), *[_ptr(a) for a in arrs]))
+    if arrs[1] is not None:
         return [{"codes13": arrs[0][i], "scales13": arrs[1][i], "codes2": arrs[2][i], "scales2": arrs[3][i],
                  "g13": arrs[4][i, 0], "g2": arrs[4][i, 1]} for i in range(count)]
     return [{"w13": arrs[0][i], "w2": arrs[2][i]} for i in range(count)]

@@ -164,6 +164,19 @@ void move_bf16(const MatGeom& g, uint16_t* w, uint16_t* wp) {
           }
 }
 
+// The weight type and expert count of one expert set of a layer.
+struct SetInfo {
+  int wtype, n;
+};
+int set_info(const moe_layer_desc* d, int set, SetInfo* si) {
+  if (d == nullptr || (set != MOE_SET_ROUTED && set != MOE_SET_SHARED)) return MOE_ERR_INVALID_ARG;
+  Plan p;
+  if (int st = plan_shapes(d, &p)) return st;
+  si->wtype = set == MOE_SET_ROUTED ? d->routed_wtype : d->shared_wtype;
+  si->n = set == MOE_SET_ROUTED ? d->n_routed : d->n_shared;
+  return MOE_OK;
+}
+
 // Experts [first, first + count) of a set of n, canonical <-> the set's
 // regions (placement 0: code region + scale region; 1: one buffer, the scale
 // region at shared_scale_offset).
@@ -355,8 +368,10 @@ int moe_layer_validate(const moe_layer_desc* desc) {
   return plan_shapes(desc, &p);
 }
 
-int moe_expert_layout_query(int wtype, int hidden, int inter, int n_experts, moe_expert_layout* out) {
-  return layout(wtype, hidden, inter, n_experts, out);
+int moe_expert_layout_query(const moe_layer_desc* desc, int set, moe_expert_layout* out) {
+  SetInfo si;
+  if (int st = set_info(desc, set, &si)) return st;
+  return layout(si.wtype, desc->hidden, desc->inter, si.n, out);
 }
 
 int moe_pack_nvfp4(int rows, int cols, const uint8_t* codes, const uint8_t* scales, uint8_t* codes_out,
@@ -393,24 +408,29 @@ int moe_unpack_bf16(int rows, int cols, const uint16_t* w_packed, uint16_t* w) {
   return MOE_OK;
 }
 
-int moe_pack_experts(int wtype, int hidden, int inter, int n_experts, int first, int count, const void* w13,
+int moe_pack_experts(const moe_layer_desc* desc, int set, int first, int count, const void* w13,
                      const void* w13_scales, const void* w2, const void* w2_scales, const float* tensor_scales,
-                     int placement, void* code_region, void* scale_region) {
-  return move_experts<true>(wtype, hidden, inter, n_experts, first, count,
+                     void* region, void* scale_region) {
+  SetInfo si;
+  if (int st = set_info(desc, set, &si)) return st;
+  return move_experts<true>(si.wtype, desc->hidden, desc->inter, si.n, first, count,
                             static_cast<uint8_t*>(const_cast<void*>(w13)),
                             static_cast<uint8_t*>(const_cast<void*>(w13_scales)),
                             static_cast<uint8_t*>(const_cast<void*>(w2)),
                             static_cast<uint8_t*>(const_cast<void*>(w2_scales)), const_cast<float*>(tensor_scales),
-                            placement, static_cast<uint8_t*>(code_region), static_cast<uint8_t*>(scale_region));
+                            set == MOE_SET_SHARED ? 1 : 0, static_cast<uint8_t*>(region),
+                            static_cast<uint8_t*>(scale_region));
 }
 
-int moe_unpack_experts(int wtype, int hidden, int inter, int n_experts, int first, int count, const void* code_region,
-                       const void* scale_region, int placement, void* w13, void* w13_scales, void* w2, void* w2_scales,
+int moe_unpack_experts(const moe_layer_desc* desc, int set, int first, int count, const void* region,
+                       const void* scale_region, void* w13, void* w13_scales, void* w2, void* w2_scales,
                        float* tensor_scales) {
-  return move_experts<false>(wtype, hidden, inter, n_experts, first, count, static_cast<uint8_t*>(w13),
-                             static_cast<uint8_t*>(w13_scales), static_cast<uint8_t*>(w2),
-                             static_cast<uint8_t*>(w2_scales), tensor_scales, placement,
-                             static_cast<uint8_t*>(const_cast<void*>(code_region)),
+  SetInfo si;
+  if (int st = set_info(desc, set, &si)) return st;
+  return move_experts<false>(si.wtype, desc->hidden, desc->inter, si.n, first, count,
+                             static_cast<uint8_t*>(w13), static_cast<uint8_t*>(w13_scales), static_cast<uint8_t*>(w2),
+                             static_cast<uint8_t*>(w2_scales), tensor_scales, set == MOE_SET_SHARED ? 1 : 0,
+                             static_cast<uint8_t*>(const_cast<void*>(region)),
                              static_cast<uint8_t*>(const_cast<void*>(scale_region)));
 }
 
@@ -430,8 +450,8 @@ int moe_layer_create(const moe_layer_desc* desc, moe_layer_t* out) {
   L->d = *desc;
   L->p = p;
   L->device = device;
-  layout(desc->routed_wtype, desc->hidden, desc->inter, desc->n_routed, &L->lr);
-  layout(desc->shared_wtype, desc->hidden, desc->inter, desc->n_shared, &L->ls);
+  (void)moe_expert_layout_query(desc, MOE_SET_ROUTED, &L->lr);
+  (void)moe_expert_layout_query(desc, MOE_SET_SHARED, &L->ls);
   const WsLayout wl = ws_layout(desc, p);
   L->ws_bytes = wl.total;
   if (hipMalloc(&L->ws, L->ws_bytes) != hipSuccess) {
@@ -522,6 +542,11 @@ moe::FusedArgs make_args(const moe_layer* L, const void* x, const void* router_w
   return a;
 }
 
+// One layer call.
+int launch_layer(const moe_layer* L, const moe::FusedArgs& a, void* stream) {
+  return moe::launch_fused(a, tb_of(a.B), L->d.routed_wtype, L->d.shared_wtype, stream);
+}
+
 // Argument checks of one layer call (both entry points).
 int check_call(const moe_layer_desc& d, const void* x, const void* router_w, const void* expert_packed,
                const void* scales, const void* shared_w, const void* out, int batch) {
@@ -584,10 +609,10 @@ int moe_decode_layer(moe_layer_t L, const void* x, const void* router_w, const v
     void* const* ev = L->prof.data() + 2 * (L->prof_call % (L->prof.size() / 2));
     ++L->prof_call;
     (void)hipEventRecord(reinterpret_cast<hipEvent_t>(ev[0]), st);
-    const int r = moe::launch_fused(a, tb_of(batch), d.routed_wtype, d.shared_wtype, stream);
+    const int r = launch_layer(L, a, stream);
     (void)hipEventRecord(reinterpret_cast<hipEvent_t>(ev[1]), st);
     if (r != 0) return MOE_ERR_LAUNCH;
-  } else if (moe::launch_fused(a, tb_of(batch), d.routed_wtype, d.shared_wtype, stream) != 0) {
+  } else if (launch_layer(L, a, stream) != 0) {
     return MOE_ERR_LAUNCH;
   }
   L->last_batch = batch;
@@ -615,12 +640,12 @@ int moe_decode_layer_static(const moe_layer_desc* desc, const void* x, const voi
   L.d = *desc;
   L.p = p;
   L.device = device;
-  layout(desc->routed_wtype, desc->hidden, desc->inter, desc->n_routed, &L.lr);
-  layout(desc->shared_wtype, desc->hidden, desc->inter, desc->n_shared, &L.ls);
+  (void)moe_expert_layout_query(desc, MOE_SET_ROUTED, &L.lr);
+  (void)moe_expert_layout_query(desc, MOE_SET_SHARED, &L.ls);
   bind_ws(&L, base, wl);
   if (err_flags != nullptr) L.err = err_flags;
   const moe::FusedArgs a = make_args(&L, x, router_w, expert_packed, scales, shared_w, out, batch);
-  if (moe::launch_fused(a, tb_of(batch), desc->routed_wtype, desc->shared_wtype, stream) != 0) return MOE_ERR_LAUNCH;
+  if (launch_layer(&L, a, stream) != 0) return MOE_ERR_LAUNCH;
   return MOE_OK;
 }
 

@@ -48,137 +48,7 @@
 namespace moe {
 namespace {
 
-typedef unsigned long long u64;
-constexpr int NW = kFusedWaves;
-constexpr int NT = kFusedThreads;
-constexpr int kMaxD = MOE_MAX_BATCH * MOE_MAX_TOPK;
-
-// ---------------------------------------------------------------------------
-// tagged words
-// ---------------------------------------------------------------------------
-
-__device__ __forceinline__ u64 clock100() { return __builtin_amdgcn_s_memrealtime(); }
-
-// The wavefront's index in its workgroup, as a uniform (scalar) value: the
-// compiler cannot tell that threadIdx.x / 64 is the same for a whole wave,
-// and per-wave loop bounds derived from it would otherwise become divergent
-// loops whose register copies wait for every load in flight.
-__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6); }
-
-__device__ __forceinline__ void publish(u64* p, uint32_t v, uint32_t tag) {
-  __hip_atomic_store(p, ((u64)tag << 32) | v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ u64 peek(const u64* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// Polls a set of tagged words until their tags equal `tag`.  Each thread
-// owns words i = base + tid + NT*q, q < NB.  issue() sends the first poll (it
-// can fly while the thread does other work); finish() re-reads the words
-// that have not matched yet until all have, then hands (i, value) to sink.
-// (A second poll in flight did not shorten the hand-off: its time is the
-// stores' way to the memory side, not the polling rate.)  Past the deadline
-// the error bit is set and the words are taken as they are.
-template <int NB>
-struct Gather {
-  u64 v[NB];
-  unsigned pend;
-  int base, n;
-
-  template <typename Addr>
-  __device__ __forceinline__ void issue(int base_, int n_, Addr&& addr) {
-    base = base_;
-    n = n_;
-    pend = 0u;
-#pragma unroll
-    for (int q = 0; q < NB; ++q) {
-      const int i = base + q * NT + (int)threadIdx.x;
-      v[q] = peek(addr(i < n ? i : 0));
-      if (i < n) pend |= 1u << q;
-    }
-  }
-  template <typename Addr, typename Sink>
-  __device__ __forceinline__ void finish(uint32_t tag, u64 deadline, unsigned* err, unsigned bit, Addr&& addr,
-                                         Sink&& sink) {
-#pragma unroll
-    for (int q = 0; q < NB; ++q)
-      if (((pend >> q) & 1u) && (uint32_t)(v[q] >> 32) == tag) pend &= ~(1u << q);
-    while (pend != 0u) {
-      if (clock100() > deadline) {
-        __hip_atomic_fetch_or(err, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        break;
-      }
-#pragma unroll
-      for (int q = 0; q < NB; ++q)
-        if ((pend >> q) & 1u) v[q] = peek(addr(base + q * NT + (int)threadIdx.x));
-#pragma unroll
-      for (int q = 0; q < NB; ++q)
-        if (((pend >> q) & 1u) && (uint32_t)(v[q] >> 32) == tag) pend &= ~(1u << q);
-    }
-#pragma unroll
-    for (int q = 0; q < NB; ++q) {
-      const int i = base + q * NT + (int)threadIdx.x;
-      if (i < n) sink(i, (uint32_t)v[q]);
-    }
-  }
-};
-
-// All n words, NB per thread per round.
-template <int NB, typename Addr, typename Sink>
-__device__ __forceinline__ void gather_all(int n, uint32_t tag, u64 deadline, unsigned* err, unsigned bit, Addr&& addr,
-                                           Sink&& sink) {
-  for (int base = 0; base < n; base += NB * NT) {
-    Gather<NB> g;
-    g.issue(base, n, addr);
-    g.finish(tag, deadline, err, bit, addr, sink);
-  }
-}
-
-// ---------------------------------------------------------------------------
-// cross-lane reductions
-// ---------------------------------------------------------------------------
-
-// Reductions inside rows of 16 lanes use DPP butterflies (every lane of a
-// group gets the group's result); across rows, DPP row broadcasts carry lane
-// 15 of each row into the next row and lane 31 into rows 2 and 3, so lane 63
-// ends with the result of all 64 lanes (lanes 31 and 63 with those of their
-// 32-lane halves).  No permlane or LDS traffic; the order of the operations
-// is fixed, so sums are deterministic.
-#define MOE_DPP_ROW_BCAST15 0x142
-#define MOE_DPP_ROW_BCAST31 0x143
-
-template <int CTRL>
-__device__ __forceinline__ float add_dpp(float v) {
-  return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
-}
-
-// Sum over groups of `width` consecutive lanes (a power of two <= 64); the
-// result is valid in lane width - 1 of each group (in every lane when width <= 16).
-__device__ __forceinline__ float group_sum(float v, int width) {
-  if (width >= 2) v = add_dpp<MOE_DPP_XOR1>(v);
-  if (width >= 4) v = add_dpp<MOE_DPP_XOR2>(v);
-  if (width >= 8) v = add_dpp<MOE_DPP_HALF_MIRROR>(v);
-  if (width >= 16) v = add_dpp<MOE_DPP_MIRROR>(v);
-  if (width >= 32)
-    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), MOE_DPP_ROW_BCAST15, 0xA, 0xF, false));
-  if (width >= 64)
-    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), MOE_DPP_ROW_BCAST31, 0xC, 0xF, false));
-  return v;
-}
-
-// Wave-wide max of an unsigned key and sum of a float, uniform results.
-__device__ __forceinline__ unsigned wave_max_u32(unsigned v) {
-  v = max(v, (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, MOE_DPP_XOR1, 0xF, 0xF, false));
-  v = max(v, (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, MOE_DPP_XOR2, 0xF, 0xF, false));
-  v = max(v, (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, MOE_DPP_HALF_MIRROR, 0xF, 0xF, false));
-  v = max(v, (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, MOE_DPP_MIRROR, 0xF, 0xF, false));
-  v = max(v, (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, MOE_DPP_ROW_BCAST15, 0xA, 0xF, false));
-  v = max(v, (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, MOE_DPP_ROW_BCAST31, 0xC, 0xF, false));
-  return (unsigned)__builtin_amdgcn_readlane((int)v, 63);
-}
-__device__ __forceinline__ float wave_sum(float v) {
-  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(group_sum(v, 64)), 63));
-}
+#include "kernel_common.h"
 
 // ---------------------------------------------------------------------------
 // shared-memory state
@@ -306,20 +176,6 @@ __device__ __forceinline__ size_t expert_off(int e, size_t stride) {
   else return (size_t)((uint32_t)e * (uint32_t)stride);
 }
 
-// Loads at a wave-uniform base plus the lane's 32-bit offset (the
-// scalar-base addressing form: no per-lane 64-bit address arithmetic).
-// Weights are read once per call: non-temporal loads, so that they do not
-// push the kernel's code, arguments and small shared data out of the L2.
-typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ uint4 ld16nt(const void* p) {
-  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
-  return make_uint4(v.x, v.y, v.z, v.w);
-}
-__device__ __forceinline__ uint4 ld16o(const uint8_t* base, uint32_t off) { return ld16nt(base + off); }
-__device__ __forceinline__ uint32_t ld32o(const uint8_t* base, uint32_t off) {
-  return __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(base + off));
-}
-
 // Wave-uniform NVFP4 byte offsets of (slice sl, step t): code units, and the
 // scale words shared by steps t & ~1 and t | 1.  A lane adds L.c_off / L.s_off.
 __device__ __forceinline__ uint32_t code_step(const LaneGeo& L, int sl, int t) {
@@ -354,13 +210,6 @@ __device__ __forceinline__ void tile_load(Tile<WT>& tl, const uint8_t* codes, co
   }
 }
 
-// sum of the lane's 32 weights times act (16 bf16 pairs).  NVFP4: the two
-// block scales are bytes 0, 1 of sp.
-__device__ __forceinline__ float chunk_dot_fp4(const uint4& c, uint32_t sp, const uint32_t (&act)[16]) {
-  uint32_t w[16];
-  decode_chunk(c, w);
-  return fmaf(dot8c<8>(w, act), e4m3f<1>(sp), dot8c<0>(w, act) * e4m3f<0>(sp));
-}
 __device__ __forceinline__ float chunk_dot_bf16(const uint4 (&c)[4], const uint32_t (&act)[16]) {
   uint32_t w[16];
 #pragma unroll
@@ -409,19 +258,6 @@ __device__ __forceinline__ void quad_dot(const Quad<WT>& q, const uint32_t (&x)[
     if constexpr (WT == WT_NVFP4) v[i] = chunk_dot_fp4(q.c[i], (i & 1) ? (q.sw[i >> 1] >> 16) : q.sw[i >> 1], x);
     else v[i] = chunk_dot_bf16(q.c[i], x);
   }
-}
-
-// 32 bf16 activations (16 pairs) at p (16-byte aligned, shared memory).
-__device__ __forceinline__ void lds_chunk(const uint16_t* p, uint32_t (&a)[16]) {
-  const uint4* q = reinterpret_cast<const uint4*>(p);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) unpack4(q[i], &a[4 * i]);
-}
-
-// SiLU(g) * u; the logistic's reciprocal is the hardware's (1 ulp), far
-// below the bf16 rounding of h that follows.
-__device__ __forceinline__ float silu_mul(float g, float u) {
-  return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
 }
 
 // ---------------------------------------------------------------------------
@@ -808,110 +644,6 @@ __device__ __forceinline__ void load_xr(const A& a, int col, const uint16_t* xs,
 // ---------------------------------------------------------------------------
 // routing (every workgroup, from the gathered logits)
 // ---------------------------------------------------------------------------
-
-// Key for selection: order-preserving integer of the logit; NaN ranks below
-// every number (key 1) and a taken or absent expert has key 0.
-__device__ __forceinline__ unsigned sel_key(float f) {
-  const unsigned k = fkey(f);
-  return k == 0u ? 1u : k;
-}
-
-// Compare-exchange for a descending order by key, ties to the lower expert.
-__device__ __forceinline__ void cas(unsigned& ka, int& ia, unsigned& kb, int& ib) {
-  const bool sw = kb > ka || (kb == ka && ib < ia);
-  const unsigned k0 = sw ? kb : ka, k1 = sw ? ka : kb;
-  const int i0 = sw ? ib : ia, i1 = sw ? ia : ib;
-  ka = k0; kb = k1; ia = i0; ib = i1;
-}
-
-// Top-k of TPW tokens at once (token wave + t NW): lane l holds experts
-// [l MK, l MK + MK), sorted by key.  Each round the wave's largest head key
-// wins (ties to the lowest lane, i.e. the lowest expert), the winning lane
-// shifts its list; the lanes' chains for the TPW tokens are independent.
-// Lane r ends with the r-th selection: expert my_e, logit my_l, and its
-// sigmoid my_sg; sg_sum (uniform) is the sum of the k sigmoids.  The winning
-// logit of a round is uniform, so its sigmoid is computed while the next
-// round's maximum is on its way through the lanes.
-template <int MK, int TPW, class A>
-__device__ __forceinline__ void topk(const A& a, const float* lg, int lane, int (&my_e)[TPW], float (&my_l)[TPW],
-                                     float (&my_sg)[TPW], float (&sg_sum)[TPW]) {
-  const int wave = wave_id();
-  unsigned key[TPW][MK];
-  int idx[TPW][MK];
-#pragma unroll
-  for (int t = 0; t < TPW; ++t) {
-    const int b = min(wave + t * NW, a.B - 1);
-    const float* l = lg + (size_t)b * a.Er;
-#pragma unroll
-    for (int i = 0; i < MK; ++i) {
-      const int e = lane * MK + i;
-      idx[t][i] = e;
-      key[t][i] = (e < a.E) ? sel_key(l[e]) : 0u;
-    }
-    if constexpr (MK == 2) {
-      cas(key[t][0], idx[t][0], key[t][1], idx[t][1]);
-    } else if constexpr (MK == 4) {
-      cas(key[t][0], idx[t][0], key[t][1], idx[t][1]);
-      cas(key[t][2], idx[t][2], key[t][3], idx[t][3]);
-      cas(key[t][0], idx[t][0], key[t][2], idx[t][2]);
-      cas(key[t][1], idx[t][1], key[t][3], idx[t][3]);
-      cas(key[t][1], idx[t][1], key[t][2], idx[t][2]);
-    } else if constexpr (MK == 8) {
-      constexpr int net[19][2] = {{0, 1}, {2, 3}, {4, 5}, {6, 7}, {0, 2}, {1, 3}, {4, 6}, {5, 7}, {1, 2}, {5, 6},
-                                  {0, 4}, {1, 5}, {2, 6}, {3, 7}, {2, 4}, {3, 5}, {1, 2}, {3, 4}, {5, 6}};
-#pragma unroll
-      for (int c = 0; c < 19; ++c) cas(key[t][net[c][0]], idx[t][net[c][0]], key[t][net[c][1]], idx[t][net[c][1]]);
-    }
-    my_e[t] = 0;
-    my_l[t] = 0.f;
-    my_sg[t] = 0.f;
-    sg_sum[t] = 0.f;
-  }
-  for (int r = 0; r < a.k; ++r) {
-    unsigned M[TPW];
-#pragma unroll
-    for (int t = 0; t < TPW; ++t) M[t] = wave_max_u32(key[t][0]);
-#pragma unroll
-    for (int t = 0; t < TPW; ++t) {
-      const int win = __builtin_ctzll(__ballot(key[t][0] == M[t]));
-      const int e_sel = __builtin_amdgcn_readlane(idx[t][0], win);
-      const bool mine = lane == r, me = lane == win;
-      const float l_sel = unkey(M[t]);
-      const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-l_sel));
-      sg_sum[t] += sg;
-      my_e[t] = mine ? e_sel : my_e[t];
-      my_l[t] = mine ? l_sel : my_l[t];
-      my_sg[t] = mine ? sg : my_sg[t];
-#pragma unroll
-      for (int i = 0; i + 1 < MK; ++i) {
-        key[t][i] = me ? key[t][i + 1] : key[t][i];
-        idx[t][i] = me ? idx[t][i + 1] : idx[t][i];
-      }
-      key[t][MK - 1] = me ? 0u : key[t][MK - 1];
-    }
-  }
-}
-
-// One token's routing weight in lane r < k (its r-th selection, logit
-// my_l, sigmoid my_sg; sg_sum the sum of the k sigmoids) and shared
-// coefficient in lane s < S, from its logits l.
-template <class A>
-__device__ __forceinline__ void token_weights(const A& a, const float* l, int lane, float my_l, float my_sg,
-                                              float sg_sum, float& wv, float& shc) {
-  if (a.route == MOE_ROUTE_SOFTMAX_SINK) {
-    unsigned mk = 0u;
-    for (int e = lane; e < a.Er; e += 64) mk = max(mk, fkey(l[e]));
-    const float mx = unkey(wave_max_u32(mk));
-    float z = 0.f;
-    for (int e = lane; e < a.Er; e += 64) z += __expf(l[e] - mx);
-    z = wave_sum(z);
-    wv = __expf(my_l - mx) / z;
-    shc = (lane < a.S) ? __expf(l[a.E + min(lane, a.S - 1)] - mx) / z : 0.f;
-  } else {
-    wv = my_sg * __builtin_amdgcn_rcpf(sg_sum);
-    shc = 1.0f;
-  }
-}
 
 // Routing weights and shared coefficients of the TPW tokens (wave + t NW),
 // into shared memory, with the token masks of the selected experts.

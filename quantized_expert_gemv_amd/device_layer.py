@@ -24,22 +24,22 @@ def bf16_tensor_to_bits(t: torch.Tensor) -> np.ndarray:
     return t.detach().to("cpu").contiguous().view(torch.int16).numpy().view(np.uint16).copy()
 
 
-def pack_expert_set(get_expert, n: int, wtype: str, H: int, I: int, one_buffer: bool = False):
-    """Host-side packing of n experts, one at a time, by the library's set packer.
+def pack_expert_set(desc, set_: int, get_expert, n: int):
+    """Host-side packing of one expert set of the layer `desc` describes, one
+    expert at a time, by the library's set packer.
 
-    Returns (code region, scale region, layout); with one_buffer the code region
-    array is the whole one-buffer set and the scale region is None."""
-    lay = B.moe_expert_layout_query(wtype, H, I, n)
-    if one_buffer:
-        codes = np.zeros(max(lay["shared_total_bytes"], 16), np.uint8)
+    Returns (region, scale region or None, layout): the routed set's code and
+    scale regions, or the shared set's one buffer."""
+    lay = B.moe_expert_layout_query(desc, set_)
+    if set_ == B.MOE_SET_SHARED:
+        region = np.zeros(max(lay["shared_total_bytes"], 16), np.uint8)
         scales = None
     else:
-        codes = np.zeros(max(lay["code_region_bytes"], 16), np.uint8)
+        region = np.zeros(max(lay["code_region_bytes"], 16), np.uint8)
         scales = np.zeros(max(lay["scale_region_bytes"], 16), np.uint8)
     for e in range(n):
-        B.moe_pack_experts(wtype, H, I, n, e, [get_expert(e)], codes, scales,
-                           B.MOE_PLACE_ONE_BUFFER if one_buffer else B.MOE_PLACE_TWO_REGIONS)
-    return codes, scales, lay
+        B.moe_pack_experts(desc, set_, e, [get_expert(e)], region, scales)
+    return region, scales, lay
 
 
 class DeviceLayer:
@@ -50,17 +50,6 @@ class DeviceLayer:
         self.H, self.I, self.E, self.S, self.k = H, I, E, S, layer.top_k
         self.max_batch = max_batch
 
-        codes, scales, self.layout_r = pack_expert_set(layer.routed_expert, E, layer.routed_wtype, H, I)
-        self.expert_packed = torch.from_numpy(codes).to(self.device)
-        self.scales = torch.from_numpy(scales).to(self.device) if layer.routed_wtype == "nvfp4" else None
-        del codes, scales
-        if S > 0:
-            blob, _, self.layout_s = pack_expert_set(layer.shared_expert, S, layer.shared_wtype, H, I,
-                                                     one_buffer=True)
-            self.shared_w = torch.from_numpy(blob).to(self.device)
-        else:
-            self.layout_s, self.shared_w = None, None
-
         self.router_w = bits_to_bf16_tensor(layer.router_w, self.device)
         self.router_bias = (torch.from_numpy(np.asarray(layer.router_bias, np.float32)).to(self.device)
                             if layer.router_bias is not None else None)
@@ -70,6 +59,15 @@ class DeviceLayer:
                                 shared_wtype=layer.shared_wtype, route=layer.route,
                                 router_bias=self.router_bias, prenorm_gamma=self.gamma,
                                 rms_eps=layer.eps, add_residual=layer.residual)
+        codes, scales, self.layout_r = pack_expert_set(self.desc, B.MOE_SET_ROUTED, layer.routed_expert, E)
+        self.expert_packed = torch.from_numpy(codes).to(self.device)
+        self.scales = torch.from_numpy(scales).to(self.device) if layer.routed_wtype == "nvfp4" else None
+        del codes, scales
+        if S > 0:
+            blob, _, self.layout_s = pack_expert_set(self.desc, B.MOE_SET_SHARED, layer.shared_expert, S)
+            self.shared_w = torch.from_numpy(blob).to(self.device)
+        else:
+            self.layout_s, self.shared_w = None, None
         self.handle = B.moe_layer_create(self.desc)
 
     # buffers of this layer as the C ABI takes them (may be swapped for copies)

@@ -80,7 +80,7 @@ def test_null_description_and_handle():
 
 
 def test_layout_sizes_flint():
-    lay = B.moe_expert_layout_query("nvfp4", 2048, 512, 256)
+    lay = B.moe_expert_layout_query(_desc_for(WORKLOADS["flint_b1"]), B.MOE_SET_ROUTED)
     assert lay["w13_code_bytes"] == 1024 * 2048 // 2
     assert lay["w2_code_bytes"] == 2048 * 512 // 2
     assert lay["w13_scale_bytes"] == 1024 * 2048 // 16
@@ -88,7 +88,7 @@ def test_layout_sizes_flint():
     per_expert = lay["code_stride"] + lay["scale_stride"]
     assert per_expert == 1_769_472          # bytes of one Flint expert in NVFP4
     assert lay["scale_region_bytes"] == lay["tensor_scale_offset"] + 256 * 8
-    bf = B.moe_expert_layout_query("bf16", 2048, 512, 1)
+    bf = B.moe_expert_layout_query(_desc_for(WORKLOADS["flint_bf16_b1"]), B.MOE_SET_SHARED)
     assert bf["code_stride"] == 3 * 2048 * 512 * 2 and bf["scale_region_bytes"] == 0
 
 
@@ -158,34 +158,43 @@ def _rand_expert(rng, wtype, H, I):
             "w2": rng.integers(0, 1 << 16, (H, I), dtype=np.uint32).astype(np.uint16)}
 
 
-@pytest.mark.parametrize("wtype,placement", [("nvfp4", 0), ("nvfp4", 1), ("bf16", 0), ("bf16", 1)])
-def test_expert_set_pack_roundtrip_and_placement(wtype, placement):
+def _small_desc(rwt="nvfp4", swt="nvfp4", E=5, S=2):
+    return B.make_desc(hidden=256, inter=128, n_routed=E, top_k=2, n_shared=S, max_batch=1,
+                       routed_wtype=rwt, shared_wtype=swt)
+
+
+@pytest.mark.parametrize("wtype,set_", [("nvfp4", 0), ("nvfp4", 1), ("bf16", 0), ("bf16", 1)])
+def test_expert_set_pack_roundtrip_and_placement(wtype, set_):
     """moe_pack_experts places every expert (codes, block scales, tensor scales) where
     moe_expert_layout_query says, packed in pieces; moe_unpack_experts inverts it."""
-    rng = np.random.default_rng(5 + placement)
-    H, I, n = 256, 128, 5
+    rng = np.random.default_rng(5 + set_)
+    H, I = 256, 128
+    desc = _small_desc(wtype, wtype)
+    n = desc.n_routed if set_ == 0 else desc.n_shared
     exps = [_rand_expert(rng, wtype, H, I) for _ in range(n)]
-    lay = B.moe_expert_layout_query(wtype, H, I, n)
-    if placement == 1:
+    lay = B.moe_expert_layout_query(desc, set_)
+    if set_ == 1:
         code = np.zeros(lay["shared_total_bytes"], np.uint8)
         scale = None
     else:
         code = np.zeros(lay["code_region_bytes"], np.uint8)
         scale = np.zeros(max(lay["scale_region_bytes"], 1), np.uint8)
-    B.moe_pack_experts(wtype, H, I, n, 0, exps[:2], code, scale, placement)      # in two pieces
-    B.moe_pack_experts(wtype, H, I, n, 2, exps[2:], code, scale, placement)
-    back = B.moe_unpack_experts(wtype, H, I, n, 0, n, code, scale, placement)
+    B.moe_pack_experts(desc, set_, 0, exps[:1], code, scale)      # in two pieces
+    B.moe_pack_experts(desc, set_, 1, exps[1:], code, scale)
+    back = B.moe_unpack_experts(desc, set_, 0, n, code, scale)
     for a, b in zip(exps, back):
         for key in a:
             assert np.array_equal(np.asarray(a[key]), np.asarray(b[key])), key
     # each expert matches the single-matrix packer at the documented offsets
-    sreg = code[lay["shared_scale_offset"]:] if placement == 1 else scale
+    sreg = code[lay["shared_scale_offset"]:] if set_ == 1 else scale
     for e, ex in enumerate(exps):
         c0 = e * lay["code_stride"]
         if wtype == "nvfp4":
             cp, sp = B.moe_pack_nvfp4(ex["codes13"], ex["scales13"])
             s0 = e * lay["scale_stride"]
             assert np.array_equal(code[c0:c0 + cp.size], cp) and np.array_equal(sreg[s0:s0 + sp.size], sp)
+            cp2, sp2 = B.moe_pack_nvfp4(ex["codes2"], ex["scales2"])
+            assert np.array_equal(code[c0 + cp.size:c0 + cp.size + cp2.size], cp2)
             ts = sreg[lay["tensor_scale_offset"] + 8 * e:][:8].view(np.float32)
             assert ts.tolist() == [np.float32(ex["g13"]), np.float32(ex["g2"])]
         else:
@@ -194,16 +203,19 @@ def test_expert_set_pack_roundtrip_and_placement(wtype, placement):
 
 
 def test_expert_set_pack_rejects_bad_ranges():
-    lay = B.moe_expert_layout_query("nvfp4", 256, 128, 2)
+    desc = _small_desc(E=2)
+    lay = B.moe_expert_layout_query(desc, 0)
     code = np.zeros(lay["code_region_bytes"], np.uint8)
     scale = np.zeros(lay["scale_region_bytes"], np.uint8)
     ex = _rand_expert(np.random.default_rng(1), "nvfp4", 256, 128)
     with pytest.raises(B.MoeError):
-        B.moe_pack_experts("nvfp4", 256, 128, 2, 2, [ex], code, scale)          # first == n
+        B.moe_pack_experts(desc, 0, 2, [ex], code, scale)          # first == n
     with pytest.raises(B.MoeError):
-        B.moe_pack_experts("nvfp4", 256, 128, 2, 1, [ex, ex], code, scale)      # past the end
+        B.moe_pack_experts(desc, 0, 1, [ex, ex], code, scale)      # past the end
     with pytest.raises(B.MoeError):
-        B.moe_pack_experts("nvfp4", 256, 128, 2, 0, [ex], code, None)          # scale region missing
+        B.moe_pack_experts(desc, 0, 0, [ex], code, None)           # scale region missing
+    with pytest.raises(B.MoeError):
+        B.moe_pack_experts(desc, 2, 0, [ex], code, scale)          # no such set
 
 
 # ---- validate agrees with create on every weight-type pair --------------------------------
