@@ -190,9 +190,9 @@ __device__ __forceinline__ void cas(unsigned& ka, int& ia, unsigned& kb, int& ib
 // wins (ties to the lowest lane, i.e. the lowest expert), the winning lane
 // shifts its list; the lanes' chains for the TPW tokens are independent.
 // Lane r ends with the r-th selection: expert my_e, logit my_l, and its
-// sigmoid my_sg; sg_sum (uniform) is the sum of the k sigmoids.  The winning
-// logit of a round is uniform, so its sigmoid is computed while the next
-// round's maximum is on its way through the lanes.
+// sigmoid my_sg; sg_sum (uniform) is the sum of the k sigmoids.  The rounds
+// carry only the keys: the logistic values are computed afterwards, each in
+// its own lane, which keeps them off the rounds' dependency chain.
 template <int MK, int TPW, class A>
 __device__ __forceinline__ void topk(const A& a, const float* lg, int lane, int (&my_e)[TPW], float (&my_l)[TPW],
                                      float (&my_sg)[TPW], float (&sg_sum)[TPW]) {
@@ -237,18 +237,29 @@ __device__ __forceinline__ void topk(const A& a, const float* lg, int lane, int 
       const int win = __builtin_ctzll(__ballot(key[t][0] == M[t]));
       const int e_sel = __builtin_amdgcn_readlane(idx[t][0], win);
       const bool mine = lane == r, me = lane == win;
-      const float l_sel = unkey(M[t]);
-      const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-l_sel));
-      sg_sum[t] += sg;
       my_e[t] = mine ? e_sel : my_e[t];
-      my_l[t] = mine ? l_sel : my_l[t];
-      my_sg[t] = mine ? sg : my_sg[t];
+      my_l[t] = mine ? __uint_as_float(M[t]) : my_l[t];   // the key; decoded below
 #pragma unroll
       for (int i = 0; i + 1 < MK; ++i) {
         key[t][i] = me ? key[t][i + 1] : key[t][i];
         idx[t][i] = me ? idx[t][i + 1] : idx[t][i];
       }
       key[t][MK - 1] = me ? 0u : key[t][MK - 1];
+    }
+  }
+  // the k selections' logistic values, in parallel lanes, and their sum
+#pragma unroll
+  for (int t = 0; t < TPW; ++t) {
+    const float l_sel = unkey(__float_as_uint(my_l[t]));
+    const float sg = (lane < a.k) ? __builtin_amdgcn_rcpf(1.0f + __expf(-l_sel)) : 0.0f;
+    my_l[t] = l_sel;
+    my_sg[t] = sg;
+    float sum = sg;
+    if (a.k <= 16) {
+      sum = group_sum(sum, 16);
+      sg_sum[t] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(sum)));
+    } else {
+      sg_sum[t] = wave_sum(sum);
     }
   }
 }
