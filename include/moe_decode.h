@@ -285,9 +285,20 @@ int moe_layer_set_profiling(moe_layer_t layer, void* const* events, int n_events
  * [batch][S][I].  Either pointer may be NULL.  MOE_ERR_STATE before the first call.  */
 int moe_layer_debug_h(moe_layer_t layer, void* h_routed, void* h_shared, void* stream);
 
+/* Test hook: which kernel runs the handle's later batch-1 calls.  MOE_PATH_AUTO (the
+ * default) takes the batch-1 kernel with role-split workgroups where the layer has it
+ * (the Flint shape, NVFP4 routed and shared experts, sigmoid router, a device with at
+ * least 256 compute units) and the general kernel otherwise; MOE_PATH_GENERAL always
+ * takes the general kernel.  Both compute the same layer (their sums run in different
+ * orders).  Returns the path now in force through *active (may be NULL):
+ * MOE_PATH_B1 or MOE_PATH_GENERAL.  Host-only; affects no call already made.        */
+enum moe_path { MOE_PATH_AUTO = 0, MOE_PATH_GENERAL = 1, MOE_PATH_B1 = 2 };
+int moe_layer_set_path(moe_layer_t layer, int path, int* active);
+
 /* Sticky error bits of the handle's calls so far, read synchronously (waits for the
  * device): 1 = a workgroup gave up waiting for router logits, 2 = for activations (the
- * grid was not resident at once).  clear != 0 resets them.
+ * grid was not resident at once), 4 = a wavefront gave up waiting for another of its
+ * workgroup (batch-1 kernel).  clear != 0 resets them.
  * After a non-zero result the handle's later outputs are undefined until
  * moe_layer_reset.  These waits replace the kernel boundaries of the Flint page's
  * chained low-latency kernels ("From 1,096 kernels to 346").                         */

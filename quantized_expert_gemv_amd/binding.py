@@ -30,7 +30,7 @@ EXPORTED = ("moe_abi_version", "moe_status_str", "moe_layer_validate", "moe_expe
             "moe_pack_nvfp4", "moe_unpack_nvfp4", "moe_pack_bf16", "moe_unpack_bf16",
             "moe_layer_create", "moe_layer_destroy", "moe_decode_layer", "moe_decode_layer_static",
             "moe_layer_routing",
-            "moe_layer_set_profiling", "moe_layer_debug_h", "moe_layer_error", "moe_layer_reset",
+            "moe_layer_set_profiling", "moe_layer_debug_h", "moe_layer_set_path", "moe_layer_error", "moe_layer_reset",
             "moe_layer_grid")
 
 
@@ -89,6 +89,7 @@ def _load() -> C.CDLL:
         "moe_layer_routing": ([vp, vp, vp, vp, vp], i32),
         "moe_layer_set_profiling": ([vp, vp, i32], i32),
         "moe_layer_debug_h": ([vp, vp, vp, vp], i32),
+        "moe_layer_set_path": ([vp, i32, vp], i32),
         "moe_layer_error": ([vp, C.POINTER(C.c_uint), i32], i32),
         "moe_layer_reset": ([vp], i32),
         "moe_layer_grid": ([vp, C.POINTER(i32), C.POINTER(i32)], i32),
@@ -276,6 +277,17 @@ def moe_layer_set_profiling(handle, events, n_events: int) -> None:
 
 def moe_layer_debug_h(handle, h_routed=None, h_shared=None, stream=None) -> None:
     _check("moe_layer_debug_h", lib.moe_layer_debug_h(handle, _ptr(h_routed), _ptr(h_shared), _stream(stream)))
+
+
+MOE_PATH_AUTO, MOE_PATH_GENERAL, MOE_PATH_B1 = 0, 1, 2
+
+
+def moe_layer_set_path(handle, path: int) -> int:
+    """Kernel of the handle's batch-1 calls (MOE_PATH_AUTO or MOE_PATH_GENERAL);
+    returns the path in force (MOE_PATH_B1 or MOE_PATH_GENERAL)."""
+    active = C.c_int(-1)
+    _check("moe_layer_set_path", lib.moe_layer_set_path(handle, int(path), C.byref(active)))
+    return active.value
 
 
 def moe_layer_error(handle, clear: bool = False) -> int:

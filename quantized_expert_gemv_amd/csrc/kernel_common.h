@@ -157,6 +157,31 @@ __device__ __forceinline__ float chunk_dot_fp4(const uint4& c, uint32_t sp, cons
   decode_chunk(c, w);
   return fmaf(dot8c<8>(w, act), e4m3f<1>(sp), dot8c<0>(w, act) * e4m3f<0>(sp));
 }
+// N chunk dot products at once, each equal bit for bit to chunk_dot_fp4(c[j],
+// sp[j], act(j)), with their dependent dot2 chains interleaved: a wave with
+// few chains waits on each step's latency, N chains hide it N-fold.
+template <int N, typename Act>
+__device__ __forceinline__ void dots_fp4(const uint4 (&c)[N], const uint32_t (&sp)[N], Act&& act, float (&out)[N]) {
+  uint32_t w[N][16];
+#pragma unroll
+  for (int j = 0; j < N; ++j) decode_chunk(c[j], w[j]);
+  float lo[N], hi[N];
+#pragma unroll
+  for (int j = 0; j < N; ++j) {
+    lo[j] = dot2(w[j][0], act(j)[0], 0.f);
+    hi[j] = dot2(w[j][8], act(j)[8], 0.f);
+  }
+#pragma unroll
+  for (int i = 1; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < N; ++j) {
+      lo[j] = dot2(w[j][i], act(j)[i], lo[j]);
+      hi[j] = dot2(w[j][8 + i], act(j)[8 + i], hi[j]);
+    }
+#pragma unroll
+  for (int j = 0; j < N; ++j) out[j] = fmaf(hi[j], e4m3f<1>(sp[j]), lo[j] * e4m3f<0>(sp[j]));
+}
+
 // 32 bf16 activations (16 pairs) at p (16-byte aligned, shared memory).
 __device__ __forceinline__ void lds_chunk(const uint16_t* p, uint32_t (&a)[16]) {
   const uint4* q = reinterpret_cast<const uint4*>(p);

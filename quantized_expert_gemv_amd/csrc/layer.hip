@@ -1212,12 +1212,13 @@ __global__ __launch_bounds__(NT) void k_fused_layer(A a) {
   if (w == 0 && tid == 0) __hip_atomic_store(a.epoch, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
   // ---- routing ---------------------------------------------------------------------
-  // At batch 1 routing runs in wave 0 alone; meanwhile the wave that owns the
-  // shared item issues its tiles (a wave without one issues nothing, so wave
-  // 0 starts routing at once).  Not before the logit gather: the polls wait,
-  // in order, for every load of their wave.
+  // At batch 1 routing runs in wave 0 alone; meanwhile the other waves issue
+  // their tiles of the shared item (a wave without one issues nothing).  Wave
+  // 0 issues its own after routing: loads in flight in wave 0 delay its
+  // routing code (about 0.2 us per step).  Not before the logit gather: the
+  // polls wait, in order, for every load of their wave.
   if constexpr (TB == 1) {
-    if (SKP::on && sk) skg.load_shared(a, L13);
+    if (SKP::on && sk) { if (wave != 0) skg.load_shared(a, L13); }
     else gus.prime(a, tab);
   }
   constexpr int TPW = (TB > NW) ? 2 : 1;
@@ -1233,6 +1234,7 @@ __global__ __launch_bounds__(NT) void k_fused_layer(A a) {
   down.set_experts(a.S, nd);
   if (SKP::on && sk) {
     if constexpr (SKP::on) {
+      if (wave == 0) skg.load_shared(a, L13);
       skg.load_routed(a, tab, L13);
       skg.run(a, s, act, tag);
     }

@@ -216,7 +216,7 @@ inline int fixed_shape_of(int H, int I, int E, int k, int S, int Er, int rwt, in
   return (H == F::H && I == F::I && E == F::E && k == F::k && S == F::S && Er == F::Er && rwt == swt) ? 1 : 0;
 }
 
-enum : unsigned { kErrLogitWait = 1u, kErrActWait = 2u };
+enum : unsigned { kErrLogitWait = 1u, kErrActWait = 2u, kErrLocalWait = 4u };
 
 // Size of the library's static device scratch array (moe_decode_layer_static):
 // the largest workspace a layer may need to run without a handle.
@@ -236,5 +236,11 @@ int fused_occupancy(int shape, int tb, int qx, int rwt, int swt, int lds_bytes, 
 bool fused_variant_exists(int shape, int tb, int qx, int rwt, int swt);
 // Router units per thread the kernel is built for at this hidden size (0: none).
 int fused_qx(int hidden);
+
+// Batch-1 kernel of the Flint shape with NVFP4 routed and shared experts and
+// the sigmoid router: 256 workgroups of 512 threads, all resident at once.
+constexpr int kB1Workgroups = 256;
+int launch_b1(const KCommon& a, void* stream);
+int b1_occupancy(int* blocks_per_cu);
 
 }  // namespace moe

@@ -161,23 +161,64 @@ def test_two_layer_prenorm_chain():
     assert e2e <= 2e-2
 
 
-def test_h_per_pair_flint():
-    """SiLU*up activations of every (token, selection) and shared pair at
-    batch 1.  With 256 workgroups (one per CU on MI355X) the Flint shape runs
-    the split-K gate/up (every wave takes every item over a quarter of H);
-    on any other grid the per-wave items: both write the same words."""
+@pytest.mark.parametrize("path", ["auto", "general"])
+def test_h_per_pair_flint(path):
+    """SiLU*up activations of every selection and of the shared expert at
+    batch 1, from both batch-1 kernels: the role-split one (one wavefront per
+    expert; the automatic choice on a device with 256 compute units) and the
+    general kernel (split-K gate/up on 256 workgroups).  Both write the same
+    words, and each output must meet the oracle."""
     layer, dev = dev_layer("flint_b1")
-    G, _ = dev.grid()
-    _note(f"[h per pair] flint_b1 on {G} workgroups: {'split-K' if G == 256 else 'per-wave'} gate/up")
-    for step in (7, 11, 19):
-        r = compare_layer(dev, layer, layer.x(step))
-        hr, hs = dev.debug_h(1)
-        hr, hs = hr.float().cpu().numpy(), hs.float().cpu().numpy()
-        for j, e in enumerate(r["ids"][0].tolist()):
-            want = r["ref"]["h"][(0, e)]
-            assert np.max(np.abs(hr[0, j] - want)) <= 1e-2 * np.max(np.abs(want)), (step, j, e)
-        want = r["ref"]["h"][(0, "shared", 0)]
-        assert np.max(np.abs(hs[0, 0] - want)) <= 1e-2 * np.max(np.abs(want)), step
+    active = dev.set_path(path)
+    try:
+        cus = torch.cuda.get_device_properties(0).multi_processor_count
+        G, _ = dev.grid()
+        _note(f"[h per pair] flint_b1 path={path} -> {active} kernel; general grid {G} workgroups, {cus} CUs")
+        if path == "general":
+            assert active == "general"
+        elif cus >= 256:
+            assert active == "b1"
+        for step in (7, 11, 19):
+            r = compare_layer(dev, layer, layer.x(step))
+            _report(f"flint_b1 {active} step {step}", r)
+            assert not r["mismatched"] and r["rel_err"] <= 1e-2 and r["w_err"] <= 1e-4
+            hr, hs = dev.debug_h(1)
+            hr, hs = hr.float().cpu().numpy(), hs.float().cpu().numpy()
+            for j, e in enumerate(r["ids"][0].tolist()):
+                want = r["ref"]["h"][(0, e)]
+                assert np.max(np.abs(hr[0, j] - want)) <= 1e-2 * np.max(np.abs(want)), (step, j, e)
+            want = r["ref"]["h"][(0, "shared", 0)]
+            assert np.max(np.abs(hs[0, 0] - want)) <= 1e-2 * np.max(np.abs(want)), step
+        assert dev.error() == 0
+    finally:
+        dev.set_path("auto")
+
+
+def test_batch1_kernels_agree_and_alternate():
+    """The two batch-1 kernels share the handle's call counter and words:
+    alternating them call by call keeps every output equal, bit for bit, to
+    the same kernel's output for that input, and within the parity bar of the
+    other kernel's."""
+    layer, dev = dev_layer("flint_b1")
+    from quantized_expert_gemv_amd.device_layer import bits_to_bf16_tensor
+    xs = [bits_to_bf16_tensor(layer.x(300 + i), dev.device) for i in range(3)]
+    ref = {}
+    try:
+        for rep in range(2):
+            for path in ("auto", "general"):
+                dev.set_path(path)
+                for i, x in enumerate(xs):
+                    o = dev(x).clone()
+                    if (path, i) in ref:
+                        assert torch.equal(o.view(torch.int16), ref[(path, i)].view(torch.int16)), (rep, path, i)
+                    ref[(path, i)] = o
+        torch.cuda.synchronize()
+        for i in range(len(xs)):
+            a, b = ref[("auto", i)].float(), ref[("general", i)].float()
+            assert (a - b).abs().max().item() <= 1e-2 * b.abs().max().item(), i
+        assert dev.error() == 0
+    finally:
+        dev.set_path("auto")
 
 
 def test_deterministic_bitwise():
