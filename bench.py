@@ -166,6 +166,8 @@ def measure(name: str, K: int, W: int, L: int, R: int, flush) -> dict:
     log(f"{wl.description}; {L} cold slots")
     layer = SynthLayer(wl)
     dev = DeviceLayer(layer, max_batch=batch)
+    # the kernel the calls run: the role-split batch-1 kernel where the layer has it
+    kernel = "k_b1_layer" if (batch == 1 and dev.set_path("auto") == "b1") else "k_fused_layer"
     base = dev.buffers()
     slots = [base] + [{k: (v.clone() if v is not None else None) for k, v in base.items()} for _ in range(L - 1)]
     xs_bits = [layer.x(step=s) for s in range(L)]
@@ -249,7 +251,8 @@ def measure(name: str, K: int, W: int, L: int, R: int, flush) -> dict:
         raise SystemExit(f"[bench] the layer kernel reported error bits {flags:#x} on {name}")
 
     gbs = algo["total"] / (us_step * 1e-6) / 1e9
-    rec = {"workload": wl.description, "batch": batch, "us_per_step": round(us_step, 3), "gbs": round(gbs, 1),
+    rec = {"workload": wl.description, "batch": batch, "kernel": kernel,
+           "us_per_step": round(us_step, 3), "gbs": round(gbs, 1),
            "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "cold_slots": L, "timing": "hipgraph, cold",
            "distinct_routed_per_step": d_timed, "algorithmic_bytes_per_step": int(round(algo["total"])),
            "bytes_breakdown": {k: int(round(v)) for k, v in algo.items()},
@@ -342,7 +345,7 @@ def main():
         from quantized_expert_gemv_amd.profiling import src_digest
         if t.get("src_digest") == src_digest():
             traffic = t.get("dominant_bytes_per_launch")
-    roof = {"bound": "hbm", "kernel": "k_fused_layer", "achieved": achieved, "peak": HBM_PEAK_GBS,
+    roof = {"bound": "hbm", "kernel": head["kernel"], "achieved": achieved, "peak": HBM_PEAK_GBS,
             "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
             "algorithmic_bytes_per_launch": head["algorithmic_bytes_per_step"],
             "launch_us": us_step,
