@@ -166,8 +166,9 @@ def measure(name: str, K: int, W: int, L: int, R: int, flush) -> dict:
     log(f"{wl.description}; {L} cold slots")
     layer = SynthLayer(wl)
     dev = DeviceLayer(layer, max_batch=batch)
-    # the kernel the calls run: the role-split batch-1 kernel where the layer has it
-    kernel = "k_b1_layer" if (batch == 1 and dev.set_path("auto") == "b1") else "k_fused_layer"
+    # the kernel the calls run: the kernels dedicated to the Flint shape where the layer has them
+    dedicated = dev.set_path("auto") == "dedicated"
+    kernel = ("k_b1_layer" if batch == 1 else "k_b8_layer") if dedicated else "k_fused_layer"
     base = dev.buffers()
     slots = [base] + [{k: (v.clone() if v is not None else None) for k, v in base.items()} for _ in range(L - 1)]
     xs_bits = [layer.x(step=s) for s in range(L)]

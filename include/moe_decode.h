@@ -285,14 +285,15 @@ int moe_layer_set_profiling(moe_layer_t layer, void* const* events, int n_events
  * [batch][S][I].  Either pointer may be NULL.  MOE_ERR_STATE before the first call.  */
 int moe_layer_debug_h(moe_layer_t layer, void* h_routed, void* h_shared, void* stream);
 
-/* Test hook: which kernel runs the handle's later batch-1 calls.  MOE_PATH_AUTO (the
- * default) takes the batch-1 kernel with role-split workgroups where the layer has it
- * (the Flint shape, NVFP4 routed and shared experts, sigmoid router, a device with at
- * least 256 compute units) and the general kernel otherwise; MOE_PATH_GENERAL always
- * takes the general kernel.  Both compute the same layer (their sums run in different
- * orders).  Returns the path now in force through *active (may be NULL):
- * MOE_PATH_B1 or MOE_PATH_GENERAL.  Host-only; affects no call already made.        */
-enum moe_path { MOE_PATH_AUTO = 0, MOE_PATH_GENERAL = 1, MOE_PATH_B1 = 2 };
+/* Test hook: which kernels run the handle's later calls.  MOE_PATH_AUTO (the default)
+ * takes the kernels dedicated to the Flint shape where the layer has them (NVFP4 routed
+ * and shared experts, sigmoid router, a device with at least 256 compute units): the
+ * batch-1 kernel with a wavefront per expert, and the batch 2-8 kernel; every other
+ * layer runs the general kernel.  MOE_PATH_GENERAL always takes the general kernel.
+ * Both compute the same layer (their sums run in different orders).  Returns the path
+ * now in force through *active (may be NULL): MOE_PATH_DEDICATED or MOE_PATH_GENERAL.
+ * Host-only; affects no call already made.                                           */
+enum moe_path { MOE_PATH_AUTO = 0, MOE_PATH_GENERAL = 1, MOE_PATH_DEDICATED = 2 };
 int moe_layer_set_path(moe_layer_t layer, int path, int* active);
 
 /* Sticky error bits of the handle's calls so far, read synchronously (waits for the

@@ -279,12 +279,12 @@ def moe_layer_debug_h(handle, h_routed=None, h_shared=None, stream=None) -> None
     _check("moe_layer_debug_h", lib.moe_layer_debug_h(handle, _ptr(h_routed), _ptr(h_shared), _stream(stream)))
 
 
-MOE_PATH_AUTO, MOE_PATH_GENERAL, MOE_PATH_B1 = 0, 1, 2
+MOE_PATH_AUTO, MOE_PATH_GENERAL, MOE_PATH_DEDICATED = 0, 1, 2
 
 
 def moe_layer_set_path(handle, path: int) -> int:
-    """Kernel of the handle's batch-1 calls (MOE_PATH_AUTO or MOE_PATH_GENERAL);
-    returns the path in force (MOE_PATH_B1 or MOE_PATH_GENERAL)."""
+    """Kernels of the handle's calls (MOE_PATH_AUTO or MOE_PATH_GENERAL);
+    returns the path in force (MOE_PATH_DEDICATED or MOE_PATH_GENERAL)."""
     active = C.c_int(-1)
     _check("moe_layer_set_path", lib.moe_layer_set_path(handle, int(path), C.byref(active)))
     return active.value

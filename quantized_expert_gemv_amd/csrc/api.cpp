@@ -31,6 +31,7 @@ struct Plan {
   int spg_max;                 // most down steps a workgroup owns (given G)
   int G;                       // workgroups (0 until the device is known)
   int b1 = 0;                  // batch-1 calls run the role-split kernel (launch_b1)
+  int b8 = 0;                  // batch 2-8 calls run the small-batch kernel (launch_b8)
   int lds_act[4], lds_acc[4];  // per token bucket 1, 2, 4, 8
 };
 
@@ -344,11 +345,12 @@ int plan_device(const moe_layer_desc* desc, Plan* pp, int device) {
   if (!fastdiv_checked((uint32_t)gs2, &p.dv_gs2)) return MOE_ERR_UNSUPPORTED;
   // Batch 1 of the Flint shape with NVFP4 experts and the sigmoid router runs
   // the role-split kernel when all of its workgroups fit on the device at once.
-  p.b1 = 0;
-  int occ1 = 0;
-  if (shape == 1 && rwt == MOE_W_NVFP4 && desc->route == MOE_ROUTE_SIGMOID_TOPK && cus >= moe::kB1Workgroups &&
-      moe::b1_occupancy(&occ1) == 0 && occ1 >= 1)
-    p.b1 = 1;
+  p.b1 = p.b8 = 0;
+  int occ1 = 0, occ8 = 0;
+  if (shape == 1 && rwt == MOE_W_NVFP4 && desc->route == MOE_ROUTE_SIGMOID_TOPK && cus >= moe::kB1Workgroups) {
+    if (moe::b1_occupancy(&occ1) == 0 && occ1 >= 1) p.b1 = 1;
+    if (moe::b8_occupancy(&occ8) == 0 && occ8 >= 1) p.b8 = 1;
+  }
   (void)hipGetLastError();
   return MOE_OK;
 }
@@ -554,7 +556,10 @@ moe::FusedArgs make_args(const moe_layer* L, const void* x, const void* router_w
 
 // One layer call.
 int launch_layer(const moe_layer* L, const moe::FusedArgs& a, void* stream) {
-  if (a.B == 1 && L->p.b1 && !L->force_general) return moe::launch_b1(a, stream);
+  if (!L->force_general) {
+    if (a.B == 1 && L->p.b1) return moe::launch_b1(a, stream);
+    if (a.B >= 2 && L->p.b8) return moe::launch_b8(a, a.B, stream);
+  }
   return moe::launch_fused(a, tb_of(a.B), L->d.routed_wtype, L->d.shared_wtype, stream);
 }
 
@@ -691,7 +696,7 @@ int moe_layer_set_profiling(moe_layer_t L, void* const* events, int n_events) {
 int moe_layer_set_path(moe_layer_t L, int path, int* active) {
   if (L == nullptr || (path != MOE_PATH_AUTO && path != MOE_PATH_GENERAL)) return MOE_ERR_INVALID_ARG;
   L->force_general = path == MOE_PATH_GENERAL;
-  if (active) *active = (L->p.b1 && !L->force_general) ? MOE_PATH_B1 : MOE_PATH_GENERAL;
+  if (active) *active = ((L->p.b1 || L->p.b8) && !L->force_general) ? MOE_PATH_DEDICATED : MOE_PATH_GENERAL;
   return MOE_OK;
 }
 

@@ -242,5 +242,8 @@ int fused_qx(int hidden);
 constexpr int kB1Workgroups = 256;
 int launch_b1(const KCommon& a, void* stream);
 int b1_occupancy(int* blocks_per_cu);
+// Batch 2-8 kernel of the same layers: 256 workgroups of 512 threads.
+int launch_b8(const KCommon& a, int batch, void* stream);
+int b8_occupancy(int* blocks_per_cu);
 
 }  // namespace moe

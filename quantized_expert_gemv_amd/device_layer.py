@@ -98,9 +98,9 @@ class DeviceLayer:
         return hr, hs[:, :self.S]
 
     def set_path(self, path: str) -> str:
-        """Kernel of later batch-1 calls: "auto" or "general"; returns the one in force ("b1" or "general")."""
+        """Kernels of later calls: "auto" or "general"; returns the path in force ("dedicated" or "general")."""
         code = {"auto": B.MOE_PATH_AUTO, "general": B.MOE_PATH_GENERAL}[path]
-        return "b1" if B.moe_layer_set_path(self.handle, code) == B.MOE_PATH_B1 else "general"
+        return "dedicated" if B.moe_layer_set_path(self.handle, code) == B.MOE_PATH_DEDICATED else "general"
 
     def error(self, clear: bool = False) -> int:
         return B.moe_layer_error(self.handle, clear)

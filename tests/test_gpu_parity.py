@@ -65,12 +65,25 @@ def test_layer_parity(name, steps):
         assert r["w_err"] <= 1e-4
 
 
-def test_ragged_batches_on_a_batch8_handle():
+@pytest.mark.parametrize("path", ["auto", "general"])
+def test_ragged_batches_on_a_batch8_handle(path):
+    """Every batch size on one handle, through the kernels dedicated to the
+    Flint shape (batch 1: a wavefront per expert; batch 2-8: the small-batch
+    kernel) and through the general kernel."""
     layer, dev = dev_layer("flint_b8")
-    for n in (1, 2, 3, 5, 7, 8):
-        r = compare_layer(dev, layer, layer.x(100 + n, batch=n))
-        _report(f"flint_b8 batch {n}", r)
-        assert not r["mismatched"] and r["rel_err"] <= 1e-2
+    active = dev.set_path(path)
+    try:
+        if path == "general":
+            assert active == "general"
+        elif torch.cuda.get_device_properties(0).multi_processor_count >= 256:
+            assert active == "dedicated"
+        for n in (1, 2, 3, 5, 7, 8):
+            r = compare_layer(dev, layer, layer.x(100 + n, batch=n))
+            _report(f"flint_b8 {active} batch {n}", r)
+            assert not r["mismatched"] and r["rel_err"] <= 1e-2 and r["w_err"] <= 1e-4
+        assert dev.error() == 0
+    finally:
+        dev.set_path("auto")
 
 
 # Shapes other than Flint's run the kernel variants that read the shape from
@@ -177,7 +190,7 @@ def test_h_per_pair_flint(path):
         if path == "general":
             assert active == "general"
         elif cus >= 256:
-            assert active == "b1"
+            assert active == "dedicated"
         for step in (7, 11, 19):
             r = compare_layer(dev, layer, layer.x(step))
             _report(f"flint_b1 {active} step {step}", r)
