@@ -12,6 +12,7 @@ Modules
               NVFP4 dequantisation.
   layer    -- RMSNorm, router GEMV, the two routing rules, the SiLU-gated
               expert MLP and the weighted combine.
+  dense    -- the small-batch dense NVFP4 GEMV y = x W^T.
 
 Every function cites the page passage it follows.  Readings adopted where
 the pages are silent are listed in the module docstrings.
@@ -26,6 +27,7 @@ from .formats import (  # noqa: F401
     e4m3_value,
     unpack_nibbles,
 )
+from .dense import dense_gemv  # noqa: F401
 from .layer import (  # noqa: F401
     expert_mlp,
     moe_layer,

@@ -474,9 +474,9 @@ __global__ __launch_bounds__(kSbThreads) void k_b8_layer(KCommon a, int B) {
     cwl = ((lane == SK) ? 1.0f : s.wv[b][min(lane, SK - 1)]) * ts[1];
   }
   // the token's 7 x 256 h words: lane l polls words l + 64 q of each pair.
-  // The first poll waits ~0.8 us (s_sleep 32), when the other workgroups'
+  // The first poll waits ~0.4 us (s_sleep 16), when the other workgroups'
   // words have about arrived, and repeats every ~0.2 us.
-  __builtin_amdgcn_s_sleep(32);
+  __builtin_amdgcn_s_sleep(16);
   {
     constexpr int NB = (SK + 1) * 4;
     auto word = [&](int q) {   // pair q / 4, word lane + 64 (q % 4)
