@@ -54,7 +54,8 @@ def parse():
     p.add_argument("--steps", type=int, default=470)
     p.add_argument("--warmup", type=int, default=94)
     p.add_argument("--workload", default="flint_b1")
-    p.add_argument("--extra", default="flint_b8", help="comma-separated extra workloads ('' for none)")
+    p.add_argument("--extra", default="flint_b8,dense_qkv_b1,dense_qkv_b8",
+                   help="comma-separated extra workloads ('' for none)")
     p.add_argument("--all", action="store_true", help="also the BF16, chain and expert-sink workloads")
     p.add_argument("--slots", type=int, default=47)
     p.add_argument("--replays", type=int, default=8)
@@ -266,6 +267,85 @@ def measure(name: str, K: int, W: int, L: int, R: int, flush) -> dict:
     return rec, layer, xs_bits
 
 
+# Dense NVFP4 GEMVs of a Flint-shaped decode step (hidden 2048, 32 query and 4
+# KV heads of 64): the fused QKV projection.  name -> (rows, cols, batch)
+DENSE = {"dense_qkv_b1": (2560, 2048, 1), "dense_qkv_b8": (2560, 2048, 8)}
+
+
+def measure_dense(name: str, K: int, W: int, L: int, R: int, flush) -> dict:
+    """Cold-weight timing of the dense GEMV on L device copies of one matrix."""
+    import torch
+    from quantized_expert_gemv_amd import binding as B
+    rows, cols, batch = DENSE[name]
+    log(f"dense NVFP4 GEMV {rows}x{cols}, batch {batch}; {L} cold slots")
+    rng = np.random.default_rng(7)
+    codes = rng.integers(0, 256, size=(rows, cols // 2), dtype=np.uint8)
+    scales = rng.integers(0x30, 0x41, size=(rows, cols // 16), dtype=np.uint8)
+    cr, sr = B.moe_pack_dense(codes, scales, 0.37)
+    dev = torch.device("cuda")
+    slots = [(torch.from_numpy(cr).to(dev), torch.from_numpy(sr).to(dev)) for _ in range(L)]
+    f = rng.standard_normal((batch, cols)).astype(np.float32).view(np.uint32).astype(np.uint64)
+    xb = ((f + 0x7FFF + ((f >> 16) & 1)) >> 16).astype(np.uint16)
+    x = torch.from_numpy(xb.view(np.int16)).to(dev).view(torch.bfloat16)
+    ys = [torch.empty((batch, rows), dtype=torch.bfloat16, device=dev) for _ in range(L)]
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        c, sc = slots[i % L]
+        B.moe_dense_gemv(rows, cols, c, sc, x, ys[i % L], batch)
+
+    for i in range(W):
+        step(i)
+    torch.cuda.synchronize()
+
+    def capture(first, n):
+        g = torch.cuda.CUDAGraph()
+        cap = torch.cuda.Stream()
+        cap.wait_stream(stream)
+        with torch.cuda.stream(cap):
+            with torch.cuda.graph(g, stream=cap):
+                for i in range(n):
+                    step(first + i)
+        stream.wait_stream(cap)
+        torch.cuda.synchronize()
+        return g
+
+    gK = capture(W, K)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    flush()
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    gK.replay()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    us = ev0.elapsed_time(ev1) * 1e3 / K
+    del gK
+    gL = capture(0, L)
+    gL.replay()
+    torch.cuda.synchronize()
+    per = []
+    for _ in range(R):
+        ev0.record(stream)
+        gL.replay()
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        per.append(ev0.elapsed_time(ev1) * 1e3 / L)
+    del gL
+    per = np.array(per)
+    lay_bytes = cr.nbytes + sr.nbytes + x.numel() * 2 + batch * rows * 2
+    algo = lay_bytes
+    gbs = algo / (us * 1e-6) / 1e9
+    log(f"timed {K} GEMVs (hipgraph, cold): {us:.3f} us each, {gbs:.0f} GB/s")
+    del slots, ys
+    torch.cuda.empty_cache()
+    return {"workload": f"dense NVFP4 GEMV [{rows}x{cols}] (fused QKV of a Flint-shaped layer), b{batch}",
+            "kernel": "k_dense_gemv", "batch": batch, "us_per_step": round(us, 3), "gbs": round(gbs, 1),
+            "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "cold_slots": L, "timing": "hipgraph, cold",
+            "algorithmic_bytes_per_step": int(lay_bytes),
+            "replays": {"n": R, "steps_per_replay": L, "p10_us": float(np.percentile(per, 10)),
+                        "p50_us": float(np.percentile(per, 50)), "p90_us": float(np.percentile(per, 90))}}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -290,6 +370,9 @@ def main():
         extras += [n for n in ("flint_bf16_b1", "flint_bf16_b8", "sink_b4") if n not in extras]
     configs = {}
     for n in extras:
+        if n in DENSE:
+            configs[n] = measure_dense(n, K, W, args.slots, args.replays, flush)
+            continue
         if n == args.workload or n not in WORKLOADS:
             continue
         rec, _, _ = measure(n, K, W, SLOTS.get(n, args.slots), args.replays, flush)

@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 3
+#define MOE_ABI_VERSION 4
 
 /* limits of this implementation */
 #define MOE_MAX_BATCH 8      /* the low-latency decode path serves up to 8 requests  */
@@ -203,6 +203,45 @@ int moe_unpack_nvfp4(int rows, int cols, const uint8_t* codes_packed,
  * its inverse.  A permutation of 16-byte units.                                       */
 int moe_pack_bf16(int rows, int cols, const uint16_t* w, uint16_t* w_out);
 int moe_unpack_bf16(int rows, int cols, const uint16_t* w_packed, uint16_t* w);
+
+/* ---- small-batch dense NVFP4 GEMV ---------------------------------------------------- */
+/* The Flint page ("From 1,096 kernels to 346") runs a small-batch dense GEMV on the same
+ * packed NVFP4 weights as its other kernels: the attention projections (GQA with 32
+ * query and 4 KV heads at hidden 2048) and the dense MLP of layers 0 and 1 ("A 40B MoE
+ * that activates 2.5B parameters").  Here one matrix W [rows][cols] (cols the reduction)
+ * is packed with the experts' layout and y = x W^T is computed for 1-8 bf16 tokens.
+ * Limits: 1 <= rows <= 1048576, 32 <= cols <= 2048, cols a multiple of 32.           */
+typedef struct {
+  int rows, cols;
+  int packed_rows;            /* rows rounded up to whole scale-word step pairs; the   */
+                              /* rows past `rows` are packed as zeros                  */
+  size_t code_bytes;          /* code region: packed e2m1 codes                         */
+  size_t scale_bytes;         /* packed e4m3 block scales, at the start of the scale    */
+                              /* region                                                 */
+  size_t tensor_scale_offset; /* the fp32 per-tensor scale, inside the scale region     */
+  size_t scale_region_bytes;
+} moe_dense_layout;
+/* Host only.  MOE_ERR_INVALID_ARG for a shape outside the limits or out == NULL.       */
+int moe_dense_layout_query(int rows, int cols, moe_dense_layout* out);
+/* Canonical NVFP4 matrix -> its packed regions (host memory, caller-owned):
+ * codes uint8 [rows][cols/2], scales uint8 [rows][cols/16] (e4m3, block 16 along cols),
+ * tensor_scale the fp32 per-tensor scale ("Frontier MoE on consumer Blackwell (SM120)",
+ * section "GLM-5.2").  Lossless; MOE_ERR_INVALID_ARG for a null pointer or bad shape. */
+int moe_pack_dense(int rows, int cols, const void* codes, const void* scales, float tensor_scale,
+                   void* code_region, void* scale_region);
+/* Exact inverse of moe_pack_dense (tensor_scale may be NULL to skip it).              */
+int moe_unpack_dense(int rows, int cols, const void* code_region, const void* scale_region,
+                     void* codes, void* scales, float* tensor_scale);
+/* y[b][n] = sum_k W[n][k] x[b][k], rounded once to bf16, for 1 <= batch <= 8:
+ *   code_region, scale_region  device, as moe_pack_dense wrote them (16-byte aligned)
+ *   x  device bf16 [batch][cols], y  device bf16 [batch][rows] (16-byte aligned, not
+ *   overlapping x).
+ * Enqueues one kernel on `stream` (a hipStream_t, NULL for the default stream); returns
+ * without waiting.  Allocates nothing.  MOE_ERR_INVALID_ARG / MOE_ERR_BATCH /
+ * MOE_ERR_ALIGNMENT for bad arguments (nothing is enqueued), MOE_ERR_LAUNCH if the
+ * launch fails.                                                                        */
+int moe_dense_gemv(int rows, int cols, const void* code_region, const void* scale_region,
+                   const void* x, void* y, int batch, void* stream);
 
 /* ---- layer handle ------------------------------------------------------------------ */
 

@@ -31,7 +31,8 @@ EXPORTED = ("moe_abi_version", "moe_status_str", "moe_layer_validate", "moe_expe
             "moe_layer_create", "moe_layer_destroy", "moe_decode_layer", "moe_decode_layer_static",
             "moe_layer_routing",
             "moe_layer_set_profiling", "moe_layer_debug_h", "moe_layer_set_path", "moe_layer_error", "moe_layer_reset",
-            "moe_layer_grid")
+            "moe_layer_grid", "moe_dense_layout_query", "moe_pack_dense", "moe_unpack_dense",
+            "moe_dense_gemv")
 
 
 BENCH_EXPORTED = ("moe_bench_read_stream", "moe_bench_fill", "moe_bench_empty")
@@ -55,6 +56,14 @@ class moe_expert_layout(C.Structure):
         "w13_code_bytes", "w2_code_bytes", "code_stride", "code_region_bytes", "w13_scale_bytes",
         "w2_scale_bytes", "scale_stride", "tensor_scale_offset", "scale_region_bytes",
         "shared_scale_offset", "shared_total_bytes")]
+
+    def as_dict(self) -> dict:
+        return {n: int(getattr(self, n)) for n, _ in self._fields_}
+
+
+class moe_dense_layout(C.Structure):
+    _fields_ = [("rows", C.c_int), ("cols", C.c_int), ("packed_rows", C.c_int)] + [(n, C.c_size_t) for n in (
+        "code_bytes", "scale_bytes", "tensor_scale_offset", "scale_region_bytes")]
 
     def as_dict(self) -> dict:
         return {n: int(getattr(self, n)) for n, _ in self._fields_}
@@ -93,6 +102,10 @@ def _load() -> C.CDLL:
         "moe_layer_error": ([vp, C.POINTER(C.c_uint), i32], i32),
         "moe_layer_reset": ([vp], i32),
         "moe_layer_grid": ([vp, C.POINTER(i32), C.POINTER(i32)], i32),
+        "moe_dense_layout_query": ([i32, i32, C.POINTER(moe_dense_layout)], i32),
+        "moe_pack_dense": ([i32, i32, vp, vp, C.c_float, vp, vp], i32),
+        "moe_unpack_dense": ([i32, i32, vp, vp, vp, vp, C.POINTER(C.c_float)], i32),
+        "moe_dense_gemv": ([i32, i32, vp, vp, vp, vp, i32, vp], i32),
     }
     sig.update({
         "moe_bench_read_stream": ([vp, sz, vp, vp], i32),
@@ -322,3 +335,39 @@ def moe_bench_fill(buf, value: int = 0, stream=None) -> None:
 
 def moe_bench_empty(workgroups: int, stream=None) -> None:
     _check("moe_bench_empty", lib.moe_bench_empty(int(workgroups), _stream(stream)))
+
+
+# ---- small-batch dense NVFP4 GEMV ----------------------------------------------------
+
+def moe_dense_layout_query(rows: int, cols: int) -> dict:
+    lay = moe_dense_layout()
+    _check("moe_dense_layout_query", lib.moe_dense_layout_query(int(rows), int(cols), C.byref(lay)))
+    return lay.as_dict()
+
+
+def moe_pack_dense(codes: np.ndarray, scales: np.ndarray, tensor_scale: float):
+    """Canonical NVFP4 matrix (codes uint8 [rows][cols/2], scales uint8 [rows][cols/16])
+    -> (code_region, scale_region) host arrays."""
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.uint8)
+    rows, cols = codes.shape[0], 2 * codes.shape[1]
+    lay = moe_dense_layout_query(rows, cols)
+    cr = np.zeros(lay["code_bytes"], dtype=np.uint8)
+    sr = np.zeros(lay["scale_region_bytes"], dtype=np.uint8)
+    _check("moe_pack_dense", lib.moe_pack_dense(rows, cols, _ptr(codes), _ptr(scales), float(tensor_scale),
+                                                _ptr(cr), _ptr(sr)))
+    return cr, sr
+
+
+def moe_unpack_dense(rows: int, cols: int, code_region: np.ndarray, scale_region: np.ndarray):
+    codes = np.zeros((rows, cols // 2), dtype=np.uint8)
+    scales = np.zeros((rows, cols // 16), dtype=np.uint8)
+    ts = C.c_float(0.0)
+    _check("moe_unpack_dense", lib.moe_unpack_dense(int(rows), int(cols), _ptr(code_region), _ptr(scale_region),
+                                                    _ptr(codes), _ptr(scales), C.byref(ts)))
+    return codes, scales, ts.value
+
+
+def moe_dense_gemv(rows: int, cols: int, code_region, scale_region, x, y, batch: int, stream=None) -> None:
+    _check("moe_dense_gemv", lib.moe_dense_gemv(int(rows), int(cols), _ptr(code_region), _ptr(scale_region),
+                                                _ptr(x), _ptr(y), int(batch), _stream(stream)))

@@ -123,6 +123,16 @@ int layout(int wtype, int H, int I, int n, moe_expert_layout* o) {
 }
 
 
+// Geometry of a dense GEMV matrix: rows padded up to whole scale-word step
+// pairs, one wave step per rpw rows (cols <= 2048: no slices).
+int dense_geom(int rows, int cols, MatGeom* g) {
+  if (rows <= 0 || rows > (1 << 20) || cols < 32 || cols > 2048 || cols % 32) return -1;
+  const int rpw = moe::geom_of(1, cols).rpw;
+  const int prows = (rows + 2 * rpw - 1) / (2 * rpw) * (2 * rpw);
+  if (moe::make_geom(prows, cols, g) || g->ns != 1) return -1;
+  return 0;
+}
+
 // Matrices the packers accept: a geometry must exist for them.
 int pack_geom(int rows, int cols, MatGeom* g) {
   if (rows <= 0 || cols <= 0) return MOE_ERR_INVALID_ARG;
@@ -402,6 +412,80 @@ int moe_unpack_nvfp4(int rows, int cols, const uint8_t* codes_packed, const uint
   if (int st = pack_geom(rows, cols, &g)) return st;
   move_nvfp4<false>(g, codes, scales, const_cast<uint8_t*>(codes_packed), const_cast<uint8_t*>(scales_packed));
   return MOE_OK;
+}
+
+int moe_dense_layout_query(int rows, int cols, moe_dense_layout* o) {
+  MatGeom g;
+  if (o == nullptr || dense_geom(rows, cols, &g)) return MOE_ERR_INVALID_ARG;
+  memset(o, 0, sizeof(*o));
+  o->rows = rows;
+  o->cols = cols;
+  o->packed_rows = g.rows;
+  o->code_bytes = (size_t)g.rows * cols / 2;
+  o->scale_bytes = (size_t)g.rows * cols / 16;
+  o->tensor_scale_offset = align_up(o->scale_bytes, kAlign);
+  o->scale_region_bytes = o->tensor_scale_offset + kAlign;
+  return MOE_OK;
+}
+
+int moe_pack_dense(int rows, int cols, const void* codes, const void* scales, float tensor_scale,
+                   void* code_region, void* scale_region) {
+  MatGeom g;
+  if (!codes || !scales || !code_region || !scale_region || dense_geom(rows, cols, &g)) return MOE_ERR_INVALID_ARG;
+  // the rows past `rows` are zero codes with zero scales
+  const size_t crow = (size_t)cols / 2, srow = (size_t)cols / 16;
+  std::vector<uint8_t> c((size_t)g.rows * crow, 0), s((size_t)g.rows * srow, 0);
+  memcpy(c.data(), codes, (size_t)rows * crow);
+  memcpy(s.data(), scales, (size_t)rows * srow);
+  uint8_t* sr = static_cast<uint8_t*>(scale_region);
+  move_nvfp4<true>(g, c.data(), s.data(), static_cast<uint8_t*>(code_region), sr);
+  moe_dense_layout lay;
+  (void)moe_dense_layout_query(rows, cols, &lay);
+  memset(sr + lay.scale_bytes, 0, lay.scale_region_bytes - lay.scale_bytes);
+  memcpy(sr + lay.tensor_scale_offset, &tensor_scale, sizeof(float));
+  return MOE_OK;
+}
+
+int moe_unpack_dense(int rows, int cols, const void* code_region, const void* scale_region, void* codes,
+                     void* scales, float* tensor_scale) {
+  MatGeom g;
+  if (!codes || !scales || !code_region || !scale_region || dense_geom(rows, cols, &g)) return MOE_ERR_INVALID_ARG;
+  const size_t crow = (size_t)cols / 2, srow = (size_t)cols / 16;
+  std::vector<uint8_t> c((size_t)g.rows * crow), s((size_t)g.rows * srow);
+  move_nvfp4<false>(g, c.data(), s.data(), const_cast<uint8_t*>(static_cast<const uint8_t*>(code_region)),
+                    const_cast<uint8_t*>(static_cast<const uint8_t*>(scale_region)));
+  memcpy(codes, c.data(), (size_t)rows * crow);
+  memcpy(scales, s.data(), (size_t)rows * srow);
+  if (tensor_scale) {
+    moe_dense_layout lay;
+    (void)moe_dense_layout_query(rows, cols, &lay);
+    memcpy(tensor_scale, static_cast<const uint8_t*>(scale_region) + lay.tensor_scale_offset, sizeof(float));
+  }
+  return MOE_OK;
+}
+
+int moe_dense_gemv(int rows, int cols, const void* code_region, const void* scale_region, const void* x, void* y,
+                   int batch, void* stream) {
+  MatGeom g;
+  if (!code_region || !scale_region || !x || !y || dense_geom(rows, cols, &g)) return MOE_ERR_INVALID_ARG;
+  if (batch < 1 || batch > MOE_MAX_BATCH) return MOE_ERR_BATCH;
+  if (!aligned16(code_region) || !aligned16(scale_region) || !aligned16(x) || !aligned16(y)) return MOE_ERR_ALIGNMENT;
+  const uint8_t* xb = static_cast<const uint8_t*>(x);
+  const uint8_t* yb = static_cast<const uint8_t*>(y);
+  const size_t xn = (size_t)batch * cols * 2, yn = (size_t)batch * rows * 2;
+  if (xb < yb + yn && yb < xb + xn) return MOE_ERR_INVALID_ARG;
+  moe_dense_layout lay;
+  (void)moe_dense_layout_query(rows, cols, &lay);
+  moe::DenseArgs a;
+  a.codes = static_cast<const uint8_t*>(code_region);
+  a.scales = static_cast<const uint8_t*>(scale_region);
+  a.tscale = reinterpret_cast<const float*>(a.scales + lay.tensor_scale_offset);
+  a.x = static_cast<const uint16_t*>(x);
+  a.y = static_cast<uint16_t*>(y);
+  a.rows = rows;
+  a.B = batch;
+  a.g = g;
+  return moe::launch_dense(a, stream) == 0 ? MOE_OK : MOE_ERR_LAUNCH;
 }
 
 int moe_pack_bf16(int rows, int cols, const uint16_t* w, uint16_t* w_out) {

@@ -242,6 +242,20 @@ int fused_qx(int hidden);
 constexpr int kB1Workgroups = 256;
 int launch_b1(const KCommon& a, void* stream);
 int b1_occupancy(int* blocks_per_cu);
+// Small-batch dense NVFP4 GEMV on a matrix packed with geometry g (ns == 1,
+// rows padded to whole step pairs; only the first `rows` outputs are written).
+struct DenseArgs {
+  const uint8_t* codes;
+  const uint8_t* scales;
+  const float* tscale;
+  const uint16_t* x;   // bf16 [B][cols]
+  uint16_t* y;         // bf16 [B][rows]
+  int rows, B;
+  MatGeom g;
+};
+int launch_dense(const DenseArgs& a, void* stream);
+int dense_grid(const MatGeom& g);
+
 // Batch 2-8 kernel of the same layers: 256 workgroups of 512 threads.
 int launch_b8(const KCommon& a, int batch, void* stream);
 int b8_occupancy(int* blocks_per_cu);

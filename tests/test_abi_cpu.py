@@ -41,7 +41,7 @@ def test_bench_header_symbols_are_exported():
 
 
 def test_abi_version_and_status_strings():
-    assert B.moe_abi_version() == 3
+    assert B.moe_abi_version() == 4
     for code in B.STATUS:
         assert B.moe_status_str(code)
     assert B.moe_status_str(0) == "ok"
@@ -245,3 +245,37 @@ def test_static_entry_rejects_oversize_workspace_before_the_device():
     ok = _desc_for(WORKLOADS["flint_b8"])
     st = B.lib.moe_decode_layer_static(B.C.byref(ok), None, None, None, None, None, None, 1, None, None)
     assert st == -1                  # fits; the missing buffers are the error
+
+
+# ---- dense NVFP4 GEMV packing ------------------------------------------------------
+
+@pytest.mark.parametrize("rows,cols", [(1, 32), (7, 96), (100, 96), (333, 512), (2560, 2048), (64, 2048)])
+def test_dense_pack_round_trip(rows, cols):
+    rng = np.random.default_rng(rows * 7 + cols)
+    codes = rng.integers(0, 256, size=(rows, cols // 2), dtype=np.uint8)
+    scales = rng.integers(0, 256, size=(rows, cols // 16), dtype=np.uint8)
+    cr, sr = B.moe_pack_dense(codes, scales, 0.625)
+    lay = B.moe_dense_layout_query(rows, cols)
+    assert lay["packed_rows"] >= rows and lay["code_bytes"] == lay["packed_rows"] * cols // 2
+    assert cr.nbytes == lay["code_bytes"] and sr.nbytes == lay["scale_region_bytes"]
+    c2, s2, ts = B.moe_unpack_dense(rows, cols, cr, sr)
+    assert np.array_equal(c2, codes) and np.array_equal(s2, scales) and ts == 0.625
+    # every canonical byte appears in the packed region (a permutation plus zero padding)
+    assert np.array_equal(np.sort(cr)[-codes.size:], np.sort(codes.ravel()))
+
+
+@pytest.mark.parametrize("rows,cols", [(0, 64), (8, 0), (8, 48), (8, 4096), (8, 2080)])
+def test_dense_bad_shapes(rows, cols):
+    lay = B.moe_dense_layout()
+    assert B.lib.moe_dense_layout_query(rows, cols, B.C.byref(lay)) == -1
+    assert B.lib.moe_dense_gemv(rows, cols, None, None, None, None, 1, None) == -1
+
+
+def test_dense_gemv_rejects_without_a_device_call():
+    # null pointers and batch outside 1..8 are refused before any launch
+    assert B.lib.moe_dense_gemv(64, 64, None, None, None, None, 1, None) == -1
+    x = np.zeros(256, dtype=np.uint8)
+    p = x.ctypes.data
+    assert B.lib.moe_dense_gemv(64, 64, p, p, p, p + 128, 9, None) == -4
+    assert B.lib.moe_dense_gemv(64, 64, p, p, p, p + 128, 0, None) == -4
+    assert B.lib.moe_dense_gemv(64, 64, p + 1, p, p, p + 128, 1, None) == -3
