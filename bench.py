@@ -24,9 +24,10 @@ launch duration (the roofline figure uses it).  Also reported:
     the per-launch floor (an empty 256-workgroup kernel, 200 launches in a
     graph);
   * the fp64 oracle on the host's cores at 1 thread and at all threads.
-Other workloads (--extra, default flint_b8; --all adds the BF16, chain and
-expert-sink workloads) are measured the same way and reported under
-"configs" in the same JSON line.
+Other workloads (--extra, default flint_b8, a 16-layer chain in one launch
+and the dense QKV GEMV at batch 1 and 8; --all adds the BF16 and expert-sink
+workloads) are measured the same way and reported under "configs" in the
+same JSON line.
 
 Prints one JSON line.
 """
@@ -45,7 +46,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
-SLOTS = {"tiny": 1024, "sink_b4": 4}
+SLOTS = {"tiny": 1024, "sink_b4": 4, "flint_chain16_b1": 48}
 
 
 def parse():
@@ -54,9 +55,9 @@ def parse():
     p.add_argument("--steps", type=int, default=470)
     p.add_argument("--warmup", type=int, default=94)
     p.add_argument("--workload", default="flint_b1")
-    p.add_argument("--extra", default="flint_b8,dense_qkv_b1,dense_qkv_b8",
+    p.add_argument("--extra", default="flint_b8,flint_chain16_b1,dense_qkv_b1,dense_qkv_b8",
                    help="comma-separated extra workloads ('' for none)")
-    p.add_argument("--all", action="store_true", help="also the BF16, chain and expert-sink workloads")
+    p.add_argument("--all", action="store_true", help="also the BF16 and expert-sink workloads")
     p.add_argument("--slots", type=int, default=47)
     p.add_argument("--replays", type=int, default=8)
     p.add_argument("--cpu-seconds", type=float, default=16.0, help="budget of the oracle CPU baseline")
@@ -346,6 +347,141 @@ def measure_dense(name: str, K: int, W: int, L: int, R: int, flush) -> dict:
                         "p50_us": float(np.percentile(per, 50)), "p90_us": float(np.percentile(per, 90))}}
 
 
+# Layer chains: one moe_decode_chain launch runs n pre-norm residual layers of
+# the Flint shape at batch 1.  name -> n
+CHAIN = {"flint_chain16_b1": 16}
+
+
+def measure_chain(name: str, K: int, W: int, L: int, R: int, flush) -> dict:
+    """Cold-weight timing of an n-layer chain: L device slots (a multiple of n),
+    chain step j runs the n consecutive slots of group j % (L / n)."""
+    import torch
+    from quantized_expert_gemv_amd import binding as B
+    from quantized_expert_gemv_amd.device_layer import DeviceLayer, bits_to_bf16_tensor
+    from quantized_expert_gemv_amd.synth import WORKLOADS, SynthLayer
+
+    n = CHAIN[name]
+    L = max(n, L - L % n)
+    groups = L // n
+    wl = WORKLOADS["flint_chain"]
+    log(f"{n}-layer chain of: {wl.description}; {L} cold slots")
+    layer = SynthLayer(wl)
+    dev = DeviceLayer(layer, max_batch=1)
+    if dev.set_path("auto") != "dedicated":
+        dev.close()
+        return {"workload": f"{n}-layer chain", "skipped": "the chain needs the batch-1 kernel of the Flint shape"}
+    base = dev.buffers()
+    slots = [base] + [{k: (v.clone() if v is not None else None) for k, v in base.items()} for _ in range(L - 1)]
+    xs = [bits_to_bf16_tensor(layer.x(step=j), dev.device) for j in range(groups)]
+    outs = [torch.empty((1, wl.hidden), dtype=torch.bfloat16, device=dev.device) for _ in range(groups)]
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        j = i % groups
+        sl = slots[j * n:(j + 1) * n]
+        B.moe_decode_chain([dev.handle] * n, xs[j], [b["router_w"] for b in sl], [b["expert_packed"] for b in sl],
+                           [b["scales"] for b in sl], [b["shared_w"] for b in sl], outs[j], 1)
+
+    for i in range(W):
+        step(i)
+    torch.cuda.synchronize()
+
+    def capture(first, m):
+        g = torch.cuda.CUDAGraph()
+        cap = torch.cuda.Stream()
+        cap.wait_stream(stream)
+        with torch.cuda.stream(cap):
+            with torch.cuda.graph(g, stream=cap):
+                for i in range(m):
+                    step(first + i)
+        stream.wait_stream(cap)
+        torch.cuda.synchronize()
+        return g
+
+    Kc = max(1, K // n)                   # about K layers in the timed region
+    gK = capture(W, Kc)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    flush()
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    gK.replay()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    us_chain = ev0.elapsed_time(ev1) * 1e3 / Kc
+    del gK
+    gL = capture(0, groups)
+    gL.replay()
+    torch.cuda.synchronize()
+    per = []
+    for _ in range(R):
+        ev0.record(stream)
+        gL.replay()
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        per.append(ev0.elapsed_time(ev1) * 1e3 / groups)
+    del gL
+    per = np.array(per)
+    # the same layers launched one by one (the single-layer kernel), for comparison
+    ys = [torch.empty((1, wl.hidden), dtype=torch.bfloat16, device=dev.device) for _ in range(L)]
+
+    def single(i):
+        s = i % L
+        j = s // n
+        dev(xs[j] if s % n == 0 else ys[s - 1], out=ys[s], bufs=slots[s])
+
+    for i in range(L):
+        single(i)
+    torch.cuda.synchronize()
+    gS = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(stream)
+    with torch.cuda.stream(cap):
+        with torch.cuda.graph(gS, stream=cap):
+            for i in range(L):
+                single(i)
+    stream.wait_stream(cap)
+    torch.cuda.synchronize()
+    gS.replay()
+    torch.cuda.synchronize()
+    per_s = []
+    for _ in range(R):
+        ev0.record(stream)
+        gS.replay()
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        per_s.append(ev0.elapsed_time(ev1) * 1e3 / L)
+    del gS
+    # the chain's output equals the layers' one by one
+    same = all(torch.equal(outs[j].view(torch.int16), ys[(j + 1) * n - 1].view(torch.int16)) for j in range(groups))
+    singles_us = float(np.median(per_s))
+    log(f"same layers one launch each: {singles_us:.3f} us/layer; chain output equal to them: {same}")
+    flags = dev.error()
+    if flags:
+        raise SystemExit(f"[bench] the chain kernel reported error bits {flags:#x}")
+    if not same:
+        raise SystemExit("[bench] the chain's output differs from its layers run one by one")
+    lay = algorithmic_bytes(wl, float(wl.top_k), 1)
+    x_io = wl.hidden * 2
+    algo = n * (lay["total"] - 2 * x_io) + 2 * x_io     # x read once and the last output written once
+    gbs = algo / (us_chain * 1e-6) / 1e9
+    log(f"timed {Kc} chains of {n} (hipgraph, cold): {us_chain:.3f} us/chain, {us_chain / n:.3f} us/layer, "
+        f"{gbs:.0f} GB/s")
+    del slots, xs, outs, base, ys
+    dev.close()
+    del dev
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return {"workload": f"{n}-layer chain, one launch: {wl.description}", "kernel": "k_b1_layer", "batch": 1,
+            "layers_per_launch": n, "us_per_launch": round(us_chain, 3), "us_per_layer": round(us_chain / n, 3),
+            "gbs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "cold_slots": L,
+            "timing": "hipgraph, cold", "launches_timed": Kc, "algorithmic_bytes_per_launch": int(round(algo)),
+            "replays": {"n": R, "launches_per_replay": groups, "p10_us": float(np.percentile(per, 10)),
+                        "p50_us": float(np.percentile(per, 50)), "p90_us": float(np.percentile(per, 90))},
+            "one_launch_per_layer_us": round(singles_us, 3),
+            "one_launch_per_layer_timing": f"graph of the same {L} layers, one launch each, replayed {R} times, p50"}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -372,6 +508,9 @@ def main():
     for n in extras:
         if n in DENSE:
             configs[n] = measure_dense(n, K, W, args.slots, args.replays, flush)
+            continue
+        if n in CHAIN:
+            configs[n] = measure_chain(n, K, W, SLOTS.get(n, args.slots), args.replays, flush)
             continue
         if n == args.workload or n not in WORKLOADS:
             continue

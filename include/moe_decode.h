@@ -324,6 +324,30 @@ int moe_layer_set_profiling(moe_layer_t layer, void* const* events, int n_events
  * [batch][S][I].  Either pointer may be NULL.  MOE_ERR_STATE before the first call.  */
 int moe_layer_debug_h(moe_layer_t layer, void* h_routed, void* h_shared, void* stream);
 
+/* A chain of n_layers (1 <= n_layers <= MOE_MAX_CHAIN) decode layers in ONE launch: layer
+ * l + 1 takes layer l's output (bf16) as its x, and the launch writes the last layer's
+ * output to `out`.  This is the Flint page's low-latency path across layers ("From 1,096
+ * kernels to 346": each kernel loads its weights while the previous one still runs,
+ * through programmatic dependent launch): inside the launch, layer l + 1's router row
+ * and shared expert load while layer l finishes, and the output rows travel to every
+ * workgroup as tagged words in the first layer's workspace.
+ *   layers                  host array of n_layers handles with the same shape, weight
+ *                           types and routing (their own pre-norm γ, bias, residual flag
+ *                           and readback buffers apply); all created on one device
+ *   x, out                  device bf16 [batch][H] (16-byte aligned, not overlapping)
+ *   router_w, expert_packed, scales, shared_w   host arrays of n_layers device
+ *                           pointers, each as for moe_decode_layer
+ * Batch 1 on layers that run the batch-1 kernel dedicated to the Flint shape
+ * (moe_layer_set_path reports MOE_PATH_DEDICATED for layers[0]); MOE_ERR_UNSUPPORTED
+ * otherwise (call moe_decode_layer per layer then).  Uses layers[0]'s workspace and
+ * call counter (the launch takes n_layers of its tags); after it moe_layer_routing works
+ * on every layer's handle and moe_layer_debug_h on none.  Allocates nothing.          */
+#define MOE_MAX_CHAIN 16
+int moe_decode_chain(const moe_layer_t* layers, int n_layers, const void* x,
+                     const void* const* router_w, const void* const* expert_packed,
+                     const void* const* scales, const void* const* shared_w, void* out,
+                     int batch, void* stream);
+
 /* Test hook: which kernels run the handle's later calls.  MOE_PATH_AUTO (the default)
  * takes the kernels dedicated to the Flint shape where the layer has them (NVFP4 routed
  * and shared experts, sigmoid router, a device with at least 256 compute units): the

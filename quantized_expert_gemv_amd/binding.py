@@ -30,7 +30,7 @@ EXPORTED = ("moe_abi_version", "moe_status_str", "moe_layer_validate", "moe_expe
             "moe_pack_nvfp4", "moe_unpack_nvfp4", "moe_pack_bf16", "moe_unpack_bf16",
             "moe_layer_create", "moe_layer_destroy", "moe_decode_layer", "moe_decode_layer_static",
             "moe_layer_routing",
-            "moe_layer_set_profiling", "moe_layer_debug_h", "moe_layer_set_path", "moe_layer_error", "moe_layer_reset",
+            "moe_layer_set_profiling", "moe_layer_debug_h", "moe_layer_set_path", "moe_decode_chain", "moe_layer_error", "moe_layer_reset",
             "moe_layer_grid", "moe_dense_layout_query", "moe_pack_dense", "moe_unpack_dense",
             "moe_dense_gemv")
 
@@ -99,6 +99,7 @@ def _load() -> C.CDLL:
         "moe_layer_set_profiling": ([vp, vp, i32], i32),
         "moe_layer_debug_h": ([vp, vp, vp, vp], i32),
         "moe_layer_set_path": ([vp, i32, vp], i32),
+        "moe_decode_chain": ([vp, i32, vp, vp, vp, vp, vp, vp, i32, vp], i32),
         "moe_layer_error": ([vp, C.POINTER(C.c_uint), i32], i32),
         "moe_layer_reset": ([vp], i32),
         "moe_layer_grid": ([vp, C.POINTER(i32), C.POINTER(i32)], i32),
@@ -293,6 +294,16 @@ def moe_layer_debug_h(handle, h_routed=None, h_shared=None, stream=None) -> None
 
 
 MOE_PATH_AUTO, MOE_PATH_GENERAL, MOE_PATH_DEDICATED = 0, 1, 2
+MOE_MAX_CHAIN = 16
+
+
+def moe_decode_chain(handles, x, router_w, expert_packed, scales, shared_w, out, batch: int, stream=None) -> None:
+    """handles and the four weight arguments: sequences of one entry per layer."""
+    n = len(handles)
+    arr = lambda items: (C.c_void_p * n)(*[_ptr(t) for t in items])   # noqa: E731
+    hs = (C.c_void_p * n)(*handles)
+    _check("moe_decode_chain", lib.moe_decode_chain(hs, n, _ptr(x), arr(router_w), arr(expert_packed), arr(scales),
+                                                    arr(shared_w), _ptr(out), int(batch), _stream(stream)))
 
 
 def moe_layer_set_path(handle, path: int) -> int:

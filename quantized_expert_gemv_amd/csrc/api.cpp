@@ -245,6 +245,7 @@ struct moe_layer {
   unsigned* err;
   unsigned long long* xlog;
   unsigned long long* xh;
+  unsigned long long* xx;
   int* topk_ids;
   float* topk_w;
   float* shared_c;
@@ -259,7 +260,7 @@ namespace {
 // Byte offsets of the workspace areas of a layer (one allocation, or the
 // library's static scratch array for moe_decode_layer_static).
 struct WsLayout {
-  size_t epoch, err, xlog, xh, tid, tw, c, total;
+  size_t epoch, err, xlog, xh, xx, tid, tw, c, total;
 };
 
 WsLayout ws_layout(const moe_layer_desc* d, const Plan& p) {
@@ -277,6 +278,7 @@ WsLayout ws_layout(const moe_layer_desc* d, const Plan& p) {
   w.err = take(sizeof(unsigned));
   w.xlog = take((size_t)p.Er * moe::kLogitLine * 8);
   w.xh = take(npairs * (d->inter / 2) * 8);
+  w.xx = take((size_t)(d->hidden / 2) * 8);   // a chain's layer outputs, one token
   w.tid = take(maxB * k * sizeof(int));
   w.tw = take(maxB * k * sizeof(float));
   w.c = take(maxB * S1 * sizeof(float));
@@ -291,6 +293,7 @@ void bind_ws(moe_layer* L, void* base, const WsLayout& wl) {
   L->err = reinterpret_cast<unsigned*>(w + wl.err);
   L->xlog = reinterpret_cast<unsigned long long*>(w + wl.xlog);
   L->xh = reinterpret_cast<unsigned long long*>(w + wl.xh);
+  L->xx = reinterpret_cast<unsigned long long*>(w + wl.xx);
   L->topk_ids = reinterpret_cast<int*>(w + wl.tid);
   L->topk_w = reinterpret_cast<float*>(w + wl.tw);
   L->shared_c = reinterpret_cast<float*>(w + wl.c);
@@ -641,7 +644,14 @@ moe::FusedArgs make_args(const moe_layer* L, const void* x, const void* router_w
 // One layer call.
 int launch_layer(const moe_layer* L, const moe::FusedArgs& a, void* stream) {
   if (!L->force_general) {
-    if (a.B == 1 && L->p.b1) return moe::launch_b1(a, stream);
+    if (a.B == 1 && L->p.b1) {
+      moe::B1Args b;
+      b.a = a;
+      b.xx = L->xx;
+      b.n = 1;
+      b.L[0] = moe::chain_layer_of(a);
+      return moe::launch_b1(b, stream);
+    }
     if (a.B >= 2 && L->p.b8) return moe::launch_b8(a, a.B, stream);
   }
   return moe::launch_fused(a, tb_of(a.B), L->d.routed_wtype, L->d.shared_wtype, stream);
@@ -774,6 +784,38 @@ int moe_layer_set_profiling(moe_layer_t L, void* const* events, int n_events) {
     if (events[i] == nullptr) return MOE_ERR_INVALID_ARG;
   L->prof.assign(events, events + n_events);
   L->prof_call = 0;
+  return MOE_OK;
+}
+
+int moe_decode_chain(const moe_layer_t* layers, int n_layers, const void* x, const void* const* router_w,
+                     const void* const* expert_packed, const void* const* scales, const void* const* shared_w,
+                     void* out, int batch, void* stream) {
+  if (layers == nullptr || n_layers < 1 || n_layers > MOE_MAX_CHAIN || !router_w || !expert_packed || !scales ||
+      !shared_w)
+    return MOE_ERR_INVALID_ARG;
+  const moe_layer* L0 = layers[0];
+  if (L0 == nullptr) return MOE_ERR_INVALID_ARG;
+  if (batch != 1) return MOE_ERR_UNSUPPORTED;
+  if (!L0->p.b1 || L0->force_general) return MOE_ERR_UNSUPPORTED;
+  const moe_layer_desc& d0 = L0->d;
+  moe::B1Args b;
+  b.xx = L0->xx;
+  b.n = n_layers;
+  for (int l = 0; l < n_layers; ++l) {
+    const moe_layer* Ll = layers[l];
+    if (Ll == nullptr) return MOE_ERR_INVALID_ARG;
+    const moe_layer_desc& d = Ll->d;
+    if (d.hidden != d0.hidden || d.inter != d0.inter || d.n_routed != d0.n_routed || d.top_k != d0.top_k ||
+        d.n_shared != d0.n_shared || d.routed_wtype != d0.routed_wtype || d.shared_wtype != d0.shared_wtype ||
+        d.route != d0.route || Ll->device != L0->device || !Ll->p.b1)
+      return MOE_ERR_UNSUPPORTED;
+    if (int st = check_call(d, x, router_w[l], expert_packed[l], scales[l], shared_w[l], out, batch)) return st;
+    const moe::FusedArgs a = make_args(Ll, x, router_w[l], expert_packed[l], scales[l], shared_w[l], out, batch);
+    if (l == 0) b.a = a;
+    b.L[l] = moe::chain_layer_of(a);
+  }
+  if (moe::launch_b1(b, stream) != 0) return MOE_ERR_LAUNCH;
+  for (int l = 0; l < n_layers; ++l) layers[l]->last_batch = batch;
   return MOE_OK;
 }
 

@@ -239,8 +239,55 @@ int fused_qx(int hidden);
 
 // Batch-1 kernel of the Flint shape with NVFP4 routed and shared experts and
 // the sigmoid router: 256 workgroups of 512 threads, all resident at once.
+// One launch runs a chain of 1 .. kMaxChain such layers: layer l + 1 takes
+// layer l's output as its input.
 constexpr int kB1Workgroups = 256;
-int launch_b1(const KCommon& a, void* stream);
+constexpr int kMaxChain = 16;
+static_assert(kMaxChain == MOE_MAX_CHAIN, "chain length differs from the header's");
+// What differs between the layers of a chain.
+struct ChainLayer {
+  const uint16_t* router_w;
+  const float* bias;
+  const uint16_t* gamma;
+  const uint8_t* r_codes;
+  const uint8_t* r_scales;
+  const float* r_tscale;
+  const uint8_t* s_codes;
+  const uint8_t* s_scales;
+  const float* s_tscale;
+  int* topk_ids;   // readback of the layer's handle
+  float* topk_w;
+  float* shared_c;
+  float eps;
+  int prenorm, residual;
+};
+struct B1Args {
+  KCommon a;                   // the call's common fields: x, out, workspace, strides, wait bound
+  unsigned long long* xx;      // [H / 2] tagged words: a layer's output, the next layer's input
+  int n;                       // layers
+  ChainLayer L[kMaxChain];
+};
+// The layer fields of a's single layer as a chain entry.
+inline ChainLayer chain_layer_of(const KCommon& a) {
+  ChainLayer c;
+  c.router_w = a.router_w;
+  c.bias = a.bias;
+  c.gamma = a.gamma;
+  c.r_codes = a.r_codes;
+  c.r_scales = a.r_scales;
+  c.r_tscale = a.r_tscale;
+  c.s_codes = a.s_codes;
+  c.s_scales = a.s_scales;
+  c.s_tscale = a.s_tscale;
+  c.topk_ids = a.topk_ids;
+  c.topk_w = a.topk_w;
+  c.shared_c = a.shared_c;
+  c.eps = a.eps;
+  c.prenorm = a.prenorm;
+  c.residual = a.residual;
+  return c;
+}
+int launch_b1(const B1Args& a, void* stream);
 int b1_occupancy(int* blocks_per_cu);
 // Small-batch dense NVFP4 GEMV on a matrix packed with geometry g (ns == 1,
 // rows padded to whole step pairs; only the first `rows` outputs are written).

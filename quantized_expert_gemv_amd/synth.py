@@ -75,7 +75,7 @@ WORKLOADS = {
                               description="Flint-shaped, BF16 experts N(0,0.02), b8"),
     "flint_chain": Workload(5, "flint_chain", 2048, 512, 256, 6, 1, 1,
                             prenorm=True,
-                            description="2-layer chain of the NVFP4 Flint layer with pre-norm RMSNorm, b1"),
+                            description="Flint-shaped NVFP4 layer with pre-norm RMSNorm and residual, b1"),
     "sink_b4": Workload(4, "sink_b4", 7168, 2048, 256, 6, 2, 4,
                         route="sink", shared_wtype="bf16",
                         description="expert sink: H=7168 I=2048 E=256 NVFP4 top-6 + 2 BF16 shared in a 258-way softmax, b4"),

@@ -78,6 +78,7 @@ def test_null_description_and_handle():
     assert B.lib.moe_layer_routing(None, None, None, None, None) == -1
     assert B.lib.moe_layer_destroy(None) == -1
     assert B.lib.moe_layer_set_path(None, B.MOE_PATH_AUTO, None) == -1
+    assert B.lib.moe_decode_chain(None, 1, None, None, None, None, None, None, 1, None) == -1
 
 
 def test_layout_sizes_flint():
