@@ -348,6 +348,45 @@ int moe_decode_chain(const moe_layer_t* layers, int n_layers, const void* x,
                      const void* const* scales, const void* const* shared_w, void* out,
                      int batch, void* stream);
 
+/* ---- prefill / large batch ------------------------------------------------------
+ * The same layer for T tokens at once (prompt processing), as grouped GEMMs on the
+ * matrix cores instead of the decode kernels' GEMVs.  The Flint page ("From 1,096
+ * kernels to 346") counts the MoE kernel work as the largest prefill gain, and the SM120
+ * page ("How it fits - 2-bit experts at FP4 quality") replaces the [tokens * top_k,
+ * hidden] fp32 scatter buffer of the expert outputs by a direct, deterministic
+ * gather/reduce; both are what this call does:
+ *   route   the router GEMM (bf16, fp32 sums) of every token, its top-k and weights
+ *           (the decode kernels' selection rule and weights);
+ *   group   the (token, slot) pairs sorted by expert, tokens in order within an expert;
+ *   gate/up per expert, its tokens' rows times the decoded NVFP4 gate and up rows,
+ *           h = SiLU(g) * up in bf16; each shared expert takes all T tokens;
+ *   down    y = W2 h in fp32 at the same sorted rows;
+ *   combine out[t] = sum of the token's shared experts' y, then its routed slots' w * y in
+ *           selection order (each times its W2 tensor scale), (+ x), one bf16 rounding.
+ * Shapes it takes (else MOE_ERR_UNSUPPORTED): NVFP4 routed and shared experts, sigmoid
+ * routing, H <= 2048 with H % 128 == 0 and (H <= 512 or H % 512 == 0), I % 64 == 0 and
+ * (I <= 512 or I % 512 == 0), E <= 256 with E % 16 == 0.  1 <= tokens <=
+ * MOE_PREFILL_MAX_TOKENS (else MOE_ERR_BATCH).                                        */
+#define MOE_PREFILL_MAX_TOKENS 65536
+
+/* Bytes of device workspace moe_prefill_layer needs for `tokens` tokens on this layer
+ * (logits' selection, the sorted pairs, h and y: about tokens * (k + S) * (2 I + 4 H)
+ * bytes).  Host only.                                                                 */
+int moe_prefill_workspace_bytes(moe_layer_t layer, int tokens, size_t* bytes);
+
+/* Enqueues the prefill of `tokens` tokens on `stream` (six kernels, no host sync, no
+ * allocation).  x, router_w, expert_packed, scales, shared_w as for moe_decode_layer;
+ * x and out bf16 [tokens][H], out must not overlap x.  workspace: device, 16-byte
+ * aligned, at least moe_prefill_workspace_bytes(layer, tokens) bytes, owned by the
+ * caller and not read after the call's kernels end.  topk_ids / topk_w: optional device
+ * int32 / fp32 [tokens][k] copies of the selection (selection order) and its weights,
+ * or NULL.  Deterministic: fixed summation orders, no atomics.  The layer's handle
+ * workspace is not used: prefill calls do not disturb the decode calls' state.        */
+int moe_prefill_layer(moe_layer_t layer, const void* x, const void* router_w,
+                      const void* expert_packed, const void* scales, const void* shared_w,
+                      void* out, int tokens, void* workspace, size_t workspace_bytes,
+                      int32_t* topk_ids, float* topk_w, void* stream);
+
 /* Test hook: which kernels run the handle's later calls.  MOE_PATH_AUTO (the default)
  * takes the kernels dedicated to the Flint shape where the layer has them (NVFP4 routed
  * and shared experts, sigmoid router, a device with at least 256 compute units): the

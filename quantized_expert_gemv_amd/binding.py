@@ -32,7 +32,7 @@ EXPORTED = ("moe_abi_version", "moe_status_str", "moe_layer_validate", "moe_expe
             "moe_layer_routing",
             "moe_layer_set_profiling", "moe_layer_debug_h", "moe_layer_set_path", "moe_decode_chain", "moe_layer_error", "moe_layer_reset",
             "moe_layer_grid", "moe_dense_layout_query", "moe_pack_dense", "moe_unpack_dense",
-            "moe_dense_gemv")
+            "moe_dense_gemv", "moe_prefill_workspace_bytes", "moe_prefill_layer")
 
 
 BENCH_EXPORTED = ("moe_bench_read_stream", "moe_bench_fill", "moe_bench_empty")
@@ -107,6 +107,8 @@ def _load() -> C.CDLL:
         "moe_pack_dense": ([i32, i32, vp, vp, C.c_float, vp, vp], i32),
         "moe_unpack_dense": ([i32, i32, vp, vp, vp, vp, C.POINTER(C.c_float)], i32),
         "moe_dense_gemv": ([i32, i32, vp, vp, vp, vp, i32, vp], i32),
+        "moe_prefill_workspace_bytes": ([vp, i32, C.POINTER(sz)], i32),
+        "moe_prefill_layer": ([vp, vp, vp, vp, vp, vp, vp, i32, vp, sz, vp, vp, vp], i32),
     }
     sig.update({
         "moe_bench_read_stream": ([vp, sz, vp, vp], i32),
@@ -304,6 +306,23 @@ def moe_decode_chain(handles, x, router_w, expert_packed, scales, shared_w, out,
     hs = (C.c_void_p * n)(*handles)
     _check("moe_decode_chain", lib.moe_decode_chain(hs, n, _ptr(x), arr(router_w), arr(expert_packed), arr(scales),
                                                     arr(shared_w), _ptr(out), int(batch), _stream(stream)))
+
+
+MOE_PREFILL_MAX_TOKENS = 65536
+
+
+def moe_prefill_workspace_bytes(handle, tokens: int) -> int:
+    n = C.c_size_t(0)
+    _check("moe_prefill_workspace_bytes", lib.moe_prefill_workspace_bytes(handle, int(tokens), C.byref(n)))
+    return int(n.value)
+
+
+def moe_prefill_layer(handle, x, router_w, expert_packed, scales, shared_w, out, tokens: int, workspace,
+                      workspace_bytes: int, topk_ids=None, topk_w=None, stream=None) -> None:
+    _check("moe_prefill_layer",
+           lib.moe_prefill_layer(handle, _ptr(x), _ptr(router_w), _ptr(expert_packed), _ptr(scales), _ptr(shared_w),
+                                 _ptr(out), int(tokens), _ptr(workspace), int(workspace_bytes), _ptr(topk_ids),
+                                 _ptr(topk_w), _stream(stream)))
 
 
 def moe_layer_set_path(handle, path: int) -> int:

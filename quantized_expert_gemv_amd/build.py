@@ -28,7 +28,7 @@ def hipcc() -> str:
 
 
 def build(verbose: bool = False) -> str:
-    srcs = [os.path.join(CSRC, "api.cpp"), os.path.join(CSRC, "layer.hip"), os.path.join(CSRC, "b1_layer.hip"), os.path.join(CSRC, "b8_layer.hip"), os.path.join(CSRC, "dense.hip"),
+    srcs = [os.path.join(CSRC, "api.cpp"), os.path.join(CSRC, "layer.hip"), os.path.join(CSRC, "b1_layer.hip"), os.path.join(CSRC, "b8_layer.hip"), os.path.join(CSRC, "dense.hip"), os.path.join(CSRC, "prefill.hip"),
             os.path.join(CSRC, "bench_util.hip")]
     tmp = LIB + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",

@@ -708,6 +708,124 @@ bool cached_plan(const moe_layer_desc* d, int device, Plan* p) {
 
 extern "C" {
 
+// ---- prefill / large batch ----
+
+namespace {
+
+bool prefill_supported(const moe_layer_desc& d, const Plan& p) {
+  const auto slice_ok = [](int n) { return n <= 512 ? true : n % 512 == 0; };
+  return d.routed_wtype == MOE_W_NVFP4 && (d.n_shared == 0 || d.shared_wtype == MOE_W_NVFP4) &&
+         d.route == MOE_ROUTE_SIGMOID_TOPK && d.hidden <= moe::kPfMaxH && d.hidden % 128 == 0 &&
+         d.inter % 64 == 0 && slice_ok(d.hidden) && slice_ok(d.inter) && d.n_routed <= moe::kPfMaxE &&
+         d.n_routed % 16 == 0 && p.g13.ns == 1 && p.g2.ns == 1;
+}
+
+struct PfLayout {
+  size_t xhat, ids, wts, counts, offs, toff, perm, inv, h, y, total;
+};
+
+PfLayout pf_layout(const moe_layer_desc& d, int T) {
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align_up(off + bytes, kAlign);
+    return o;
+  };
+  const size_t Tk = (size_t)T * d.top_k, rows = Tk + (size_t)T * d.n_shared;
+  const size_t ng = (size_t)d.n_routed + d.n_shared + 1;
+  PfLayout w;
+  w.xhat = take(d.prenorm_gamma ? (size_t)T * d.hidden * 2 : 0);
+  w.ids = take(Tk * 4);
+  w.wts = take(Tk * 4);
+  w.counts = take((size_t)d.n_routed * 4);
+  w.offs = take(ng * 4);
+  w.toff = take(ng * 4);
+  w.perm = take(Tk * 4);
+  w.inv = take(Tk * 4);
+  w.h = take(rows * d.inter * 2);
+  w.y = take(rows * d.hidden * 4);
+  w.total = off;
+  return w;
+}
+
+}  // namespace
+
+int moe_prefill_workspace_bytes(moe_layer_t L, int tokens, size_t* bytes) {
+  if (L == nullptr || bytes == nullptr) return MOE_ERR_INVALID_ARG;
+  *bytes = 0;
+  if (!prefill_supported(L->d, L->p)) return MOE_ERR_UNSUPPORTED;
+  if (tokens < 1 || tokens > MOE_PREFILL_MAX_TOKENS) return MOE_ERR_BATCH;
+  *bytes = pf_layout(L->d, tokens).total;
+  return MOE_OK;
+}
+
+int moe_prefill_layer(moe_layer_t L, const void* x, const void* router_w, const void* expert_packed,
+                      const void* scales, const void* shared_w, void* out, int tokens, void* workspace,
+                      size_t workspace_bytes, int32_t* topk_ids, float* topk_w, void* stream) {
+  if (L == nullptr) return MOE_ERR_INVALID_ARG;
+  const moe_layer_desc& d = L->d;
+  if (!prefill_supported(d, L->p)) return MOE_ERR_UNSUPPORTED;
+  if (tokens < 1 || tokens > MOE_PREFILL_MAX_TOKENS) return MOE_ERR_BATCH;
+  if (!x || !router_w || !expert_packed || !scales || !out || !workspace) return MOE_ERR_INVALID_ARG;
+  if (d.n_shared > 0 && !shared_w) return MOE_ERR_INVALID_ARG;
+  const size_t xbytes = (size_t)tokens * d.hidden * 2;
+  const char *xb = static_cast<const char*>(x), *ob = static_cast<const char*>(out);
+  if (xb < ob + xbytes && ob < xb + xbytes) return MOE_ERR_INVALID_ARG;   // out overlaps x
+  const PfLayout wl = pf_layout(d, tokens);
+  if (workspace_bytes < wl.total) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(router_w) || !aligned16(expert_packed) || !aligned16(scales) ||
+      !aligned16(out) || !aligned16(workspace) || (shared_w && !aligned16(shared_w)) ||
+      (reinterpret_cast<uintptr_t>(topk_ids) & 3u) || (reinterpret_cast<uintptr_t>(topk_w) & 3u))
+    return MOE_ERR_ALIGNMENT;
+  const moe::FusedArgs f = make_args(L, x, router_w, expert_packed, scales, shared_w, out, 1);
+  moe::PrefillArgs a;
+  memset(&a, 0, sizeof(a));
+  a.x = f.x;
+  a.out = f.out;
+  a.router_w = f.router_w;
+  a.bias = f.bias;
+  a.gamma = f.gamma;
+  a.eps = f.eps;
+  a.prenorm = f.prenorm;
+  a.residual = f.residual;
+  a.r_codes = f.r_codes;
+  a.r_scales = f.r_scales;
+  a.r_tscale = f.r_tscale;
+  a.s_codes = f.s_codes;
+  a.s_scales = f.s_scales;
+  a.s_tscale = f.s_tscale;
+  a.r_code_stride = f.r_code_stride;
+  a.r_w13_code = f.r_w13_code;
+  a.r_scale_stride = f.r_scale_stride;
+  a.r_w13_scale = f.r_w13_scale;
+  a.s_code_stride = f.s_code_stride;
+  a.s_w13_code = f.s_w13_code;
+  a.s_scale_stride = f.s_scale_stride;
+  a.s_w13_scale = f.s_w13_scale;
+  a.T = tokens;
+  a.H = d.hidden;
+  a.I = d.inter;
+  a.E = d.n_routed;
+  a.k = d.top_k;
+  a.S = d.n_shared;
+  a.g13 = L->p.g13;
+  a.g2 = L->p.g2;
+  char* w = static_cast<char*>(workspace);
+  a.xhat = reinterpret_cast<uint16_t*>(w + wl.xhat);
+  a.ids = reinterpret_cast<int*>(w + wl.ids);
+  a.wts = reinterpret_cast<float*>(w + wl.wts);
+  a.counts = reinterpret_cast<int*>(w + wl.counts);
+  a.offs = reinterpret_cast<int*>(w + wl.offs);
+  a.tile_off = reinterpret_cast<int*>(w + wl.toff);
+  a.perm = reinterpret_cast<int*>(w + wl.perm);
+  a.inv = reinterpret_cast<int*>(w + wl.inv);
+  a.h = reinterpret_cast<uint16_t*>(w + wl.h);
+  a.y = reinterpret_cast<float*>(w + wl.y);
+  a.out_ids = topk_ids;
+  a.out_w = topk_w;
+  return moe::launch_prefill(a, stream) == 0 ? MOE_OK : MOE_ERR_LAUNCH;
+}
+
 int moe_decode_layer(moe_layer_t L, const void* x, const void* router_w, const void* expert_packed,
                      const void* scales, const void* shared_w, void* out, int batch, void* stream) {
   if (L == nullptr) return MOE_ERR_INVALID_ARG;

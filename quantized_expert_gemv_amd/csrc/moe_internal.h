@@ -288,6 +288,45 @@ inline ChainLayer chain_layer_of(const KCommon& a) {
   return c;
 }
 int launch_b1(const B1Args& a, void* stream);
+
+// Prefill / large-batch path: T tokens as grouped GEMMs on the matrix cores
+// (six launches on one stream).  Shapes it takes: NVFP4 routed and shared
+// experts, sigmoid routing, H <= kPfMaxH, E <= kPfMaxE (both tile sizes
+// divide them; checked by the library).
+constexpr int kPfMaxH = 2048;
+constexpr int kPfMaxE = 256;
+struct PrefillArgs {
+  const uint16_t* x;         // bf16 [T][H]
+  uint16_t* out;             // bf16 [T][H]
+  const uint16_t* router_w;  // bf16 [E][H]
+  const float* bias;         // fp32 [E] or null
+  const uint16_t* gamma;     // bf16 [H] (prenorm)
+  float eps;
+  int prenorm, residual;
+  const uint8_t *r_codes, *r_scales;
+  const float* r_tscale;
+  const uint8_t *s_codes, *s_scales;
+  const float* s_tscale;
+  size_t r_code_stride, r_w13_code, r_scale_stride, r_w13_scale;
+  size_t s_code_stride, s_w13_code, s_scale_stride, s_w13_scale;
+  int T, H, I, E, k, S;
+  MatGeom g13, g2;
+  // caller's workspace
+  uint16_t* xhat;   // bf16 [T][H] (prenorm only)
+  int* ids;         // [T][k] selection order
+  float* wts;       // [T][k]
+  int* counts;      // [E] pairs per expert
+  int* offs;        // [E + S + 1] first sorted row of each group
+  int* tile_off;    // [E + S + 1] first tile of each group
+  int* perm;        // [T k] sorted row -> token * k + slot
+  int* inv;         // [T k] token * k + slot -> sorted row
+  uint16_t* h;      // bf16 [T k + T S][I] at sorted rows
+  float* y;         // fp32 [T k + T S][H] at sorted rows
+  int32_t* out_ids; // optional copies of ids / wts (caller's)
+  float* out_w;
+};
+int prefill_max_tiles(int T, int k, int E, int S);
+int launch_prefill(const PrefillArgs& a, void* stream);
 int b1_occupancy(int* blocks_per_cu);
 // Small-batch dense NVFP4 GEMV on a matrix packed with geometry g (ns == 1,
 // rows padded to whole step pairs; only the first `rows` outputs are written).

@@ -84,6 +84,24 @@ class DeviceLayer:
                            out, batch, stream)
         return out
 
+    def prefill(self, x: torch.Tensor, out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                routing: bool = False, stream=None, bufs: dict | None = None):
+        """The prefill path on x [T, H]: returns out (and the selection ids,
+        weights [T, k] if routing).  workspace: a uint8 device tensor of at
+        least moe_prefill_workspace_bytes, or None to allocate one here."""
+        b = bufs or self.buffers()
+        T = x.shape[0]
+        if out is None:
+            out = torch.empty((T, self.H), dtype=torch.bfloat16, device=self.device)
+        need = B.moe_prefill_workspace_bytes(self.handle, T)
+        if workspace is None:
+            workspace = torch.empty(need, dtype=torch.uint8, device=self.device)
+        ids = torch.empty((T, self.k), dtype=torch.int32, device=self.device) if routing else None
+        w = torch.empty((T, self.k), dtype=torch.float32, device=self.device) if routing else None
+        B.moe_prefill_layer(self.handle, x, b["router_w"], b["expert_packed"], b["scales"], b["shared_w"], out, T,
+                            workspace, workspace.numel(), ids, w, stream)
+        return (out, ids, w) if routing else out
+
     def routing(self, batch: int):
         ids = torch.empty((batch, self.k), dtype=torch.int32, device=self.device)
         w = torch.empty((batch, self.k), dtype=torch.float32, device=self.device)

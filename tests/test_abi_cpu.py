@@ -79,6 +79,9 @@ def test_null_description_and_handle():
     assert B.lib.moe_layer_destroy(None) == -1
     assert B.lib.moe_layer_set_path(None, B.MOE_PATH_AUTO, None) == -1
     assert B.lib.moe_decode_chain(None, 1, None, None, None, None, None, None, 1, None) == -1
+    n = B.C.c_size_t(7)
+    assert B.lib.moe_prefill_workspace_bytes(None, 1, B.C.byref(n)) == -1
+    assert B.lib.moe_prefill_layer(None, None, None, None, None, None, None, 1, None, 0, None, None, None) == -1
 
 
 def test_layout_sizes_flint():
