@@ -24,10 +24,10 @@ launch duration (the roofline figure uses it).  Also reported:
     the per-launch floor (an empty 256-workgroup kernel, 200 launches in a
     graph);
   * the fp64 oracle on the host's cores at 1 thread and at all threads.
-Other workloads (--extra, default flint_b8, a 16-layer chain in one launch
-and the dense QKV GEMV at batch 1 and 8; --all adds the BF16 and expert-sink
-workloads) are measured the same way and reported under "configs" in the
-same JSON line.
+Other workloads (--extra, default flint_b8, a 16-layer chain in one launch,
+the dense QKV GEMV at batch 1 and 8, and the prefill of 1024 and 8192 tokens;
+--all adds the BF16 and expert-sink workloads) are measured the same way and
+reported under "configs" in the same JSON line.
 
 Prints one JSON line.
 """
@@ -55,7 +55,7 @@ def parse():
     p.add_argument("--steps", type=int, default=470)
     p.add_argument("--warmup", type=int, default=94)
     p.add_argument("--workload", default="flint_b1")
-    p.add_argument("--extra", default="flint_b8,flint_chain16_b1,dense_qkv_b1,dense_qkv_b8",
+    p.add_argument("--extra", default="flint_b8,flint_chain16_b1,dense_qkv_b1,dense_qkv_b8,flint_prefill_t1024,flint_prefill_t8192",
                    help="comma-separated extra workloads ('' for none)")
     p.add_argument("--all", action="store_true", help="also the BF16 and expert-sink workloads")
     p.add_argument("--slots", type=int, default=47)
@@ -482,6 +482,94 @@ def measure_chain(name: str, K: int, W: int, L: int, R: int, flush) -> dict:
             "one_launch_per_layer_timing": f"graph of the same {L} layers, one launch each, replayed {R} times, p50"}
 
 
+# Prefill of T tokens through the Flint-shaped NVFP4 layer (moe_prefill_layer:
+# grouped GEMMs on the matrix cores).  name -> T
+PREFILL = {"flint_prefill_t1024": 1024, "flint_prefill_t8192": 8192}
+MFMA_BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 matrix peak
+
+
+def measure_prefill(name: str, K: int, W: int, R: int, flush) -> dict:
+    """Prefill calls over two device copies of the layer (a call touches every
+    expert: ~453 MB, above the 256 MB Infinity Cache), timed as a graph of K
+    calls between HIP events after the write pass."""
+    import torch
+    from quantized_expert_gemv_amd import binding as B
+    from quantized_expert_gemv_amd.device_layer import DeviceLayer, bits_to_bf16_tensor
+    from quantized_expert_gemv_amd.synth import WORKLOADS, SynthLayer
+
+    T = PREFILL[name]
+    wl = WORKLOADS["flint_b1"]
+    log(f"prefill of {T} tokens: {wl.description}")
+    layer = SynthLayer(wl)
+    dev = DeviceLayer(layer, max_batch=1)
+    base = dev.buffers()
+    slots = [base, {k: (v.clone() if v is not None else None) for k, v in base.items()}]
+    xs = [bits_to_bf16_tensor(layer.x(step=j, batch=T), dev.device) for j in range(2)]
+    outs = [torch.empty((T, wl.hidden), dtype=torch.bfloat16, device=dev.device) for _ in range(2)]
+    need = B.moe_prefill_workspace_bytes(dev.handle, T)
+    ws = torch.empty(need, dtype=torch.uint8, device=dev.device)
+    ids = torch.empty((T, wl.top_k), dtype=torch.int32, device=dev.device)
+    stream = torch.cuda.current_stream()
+
+    def step(i, routing=False):
+        j = i % 2
+        b = slots[j]
+        B.moe_prefill_layer(dev.handle, xs[j], b["router_w"], b["expert_packed"], b["scales"], b["shared_w"],
+                            outs[j], T, ws, need, ids if routing else None, None, None)
+
+    distinct = []
+    for j in range(2):
+        step(j, routing=True)
+        torch.cuda.synchronize()
+        distinct.append(len(set(ids.cpu().numpy().ravel().tolist())))
+    for i in range(W):
+        step(i)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(stream)
+    with torch.cuda.stream(cap):
+        with torch.cuda.graph(g, stream=cap):
+            for i in range(K):
+                step(i)
+    stream.wait_stream(cap)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    per = []
+    for _ in range(R):
+        flush()
+        torch.cuda.synchronize()
+        ev0.record(stream)
+        g.replay()
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        per.append(ev0.elapsed_time(ev1) * 1e3 / K)
+    del g
+    us = float(np.median(per))
+    H, I, E, k, S = wl.hidden, wl.inter, wl.n_routed, wl.top_k, wl.n_shared
+    d = float(np.mean(distinct))
+    lay = algorithmic_bytes(wl, d, T)
+    flops = 2.0 * T * E * H + 2.0 * T * (k + S) * (2 * I * H + H * I)
+    gbs = lay["total"] / (us * 1e-6) / 1e9
+    tfs = flops / (us * 1e-6) / 1e12
+    bound = "mfma" if flops / (MFMA_BF16_PEAK_TFLOPS * 1e12) > lay["total"] / (HBM_PEAK_GBS * 1e9) else "hbm"
+    frac = tfs / MFMA_BF16_PEAK_TFLOPS if bound == "mfma" else gbs / HBM_PEAK_GBS
+    log(f"prefill T={T}: {us:.1f} us/call, {T / (us * 1e-6):.3g} tokens/s, {tfs:.1f} TFLOP/s, {gbs:.0f} GB/s "
+        f"({bound}-bound roofline frac {frac:.3f})")
+    del slots, xs, outs, ws, base
+    dev.close()
+    del dev
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return {"workload": f"prefill of {T} tokens, {wl.description.replace(', b1', '')}", "tokens": T,
+            "kernels": "k_pf_route, k_pf_count, k_pf_place, k_pf_gateup, k_pf_down, k_pf_combine",
+            "us_per_call": round(us, 2), "tokens_per_s": round(T / (us * 1e-6), 1), "tflops": round(tfs, 2),
+            "gbs": round(gbs, 1), "bound": bound, "roofline_frac": round(frac, 4),
+            "flops_per_call": flops, "algorithmic_bytes_per_call": int(round(lay["total"])),
+            "distinct_routed": d, "timing": f"graph of {K} calls over 2 weight copies, after the write pass, "
+                                            f"p50 of {R} replays", "workspace_bytes": need}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -508,6 +596,9 @@ def main():
     for n in extras:
         if n in DENSE:
             configs[n] = measure_dense(n, K, W, args.slots, args.replays, flush)
+            continue
+        if n in PREFILL:
+            configs[n] = measure_prefill(n, max(2, min(K, 20)), 2, args.replays, flush)
             continue
         if n in CHAIN:
             configs[n] = measure_chain(n, K, W, SLOTS.get(n, args.slots), args.replays, flush)

@@ -364,17 +364,17 @@ int moe_decode_chain(const moe_layer_t* layers, int n_layers, const void* x,
  *   combine out[t] = sum of the token's shared experts' y, then its routed slots' w * y in
  *           selection order (each times its W2 tensor scale), (+ x), one bf16 rounding.
  * Shapes it takes (else MOE_ERR_UNSUPPORTED): NVFP4 routed and shared experts, sigmoid
- * routing, H <= 2048 with H % 128 == 0 and (H <= 512 or H % 512 == 0), I % 64 == 0 and
- * (I <= 512 or I % 512 == 0), E <= 256 with E % 16 == 0.  1 <= tokens <=
+ * routing, H <= 2048 with H % 256 == 0, I % 64 == 0 and (I <= 256 or I % 256 == 0),
+ * E <= 256 with E % 16 == 0.  1 <= tokens <=
  * MOE_PREFILL_MAX_TOKENS (else MOE_ERR_BATCH).                                        */
 #define MOE_PREFILL_MAX_TOKENS 65536
 
 /* Bytes of device workspace moe_prefill_layer needs for `tokens` tokens on this layer
- * (logits' selection, the sorted pairs, h and y: about tokens * (k + S) * (2 I + 4 H)
+ * (logits, the selection, the sorted pairs, h and y: about tokens * (k + S) * (2 I + 4 H)
  * bytes).  Host only.                                                                 */
 int moe_prefill_workspace_bytes(moe_layer_t layer, int tokens, size_t* bytes);
 
-/* Enqueues the prefill of `tokens` tokens on `stream` (six kernels, no host sync, no
+/* Enqueues the prefill of `tokens` tokens on `stream` (seven kernels, no host sync, no
  * allocation).  x, router_w, expert_packed, scales, shared_w as for moe_decode_layer;
  * x and out bf16 [tokens][H], out must not overlap x.  workspace: device, 16-byte
  * aligned, at least moe_prefill_workspace_bytes(layer, tokens) bytes, owned by the

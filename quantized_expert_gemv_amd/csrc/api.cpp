@@ -713,15 +713,17 @@ extern "C" {
 namespace {
 
 bool prefill_supported(const moe_layer_desc& d, const Plan& p) {
-  const auto slice_ok = [](int n) { return n <= 512 ? true : n % 512 == 0; };
+  // the router GEMM takes 256 columns per pass, the expert GEMMs stage K in
+  // slices of min(256, K) columns
+  const auto slice_ok = [](int n) { return n <= 256 || n % 256 == 0; };
   return d.routed_wtype == MOE_W_NVFP4 && (d.n_shared == 0 || d.shared_wtype == MOE_W_NVFP4) &&
-         d.route == MOE_ROUTE_SIGMOID_TOPK && d.hidden <= moe::kPfMaxH && d.hidden % 128 == 0 &&
+         d.route == MOE_ROUTE_SIGMOID_TOPK && d.hidden <= moe::kPfMaxH && d.hidden % 256 == 0 &&
          d.inter % 64 == 0 && slice_ok(d.hidden) && slice_ok(d.inter) && d.n_routed <= moe::kPfMaxE &&
          d.n_routed % 16 == 0 && p.g13.ns == 1 && p.g2.ns == 1;
 }
 
 struct PfLayout {
-  size_t xhat, ids, wts, counts, offs, toff, perm, inv, h, y, total;
+  size_t xhat, logits, ids, wts, counts, offs, toff, perm, inv, h, y, total;
 };
 
 PfLayout pf_layout(const moe_layer_desc& d, int T) {
@@ -735,6 +737,7 @@ PfLayout pf_layout(const moe_layer_desc& d, int T) {
   const size_t ng = (size_t)d.n_routed + d.n_shared + 1;
   PfLayout w;
   w.xhat = take(d.prenorm_gamma ? (size_t)T * d.hidden * 2 : 0);
+  w.logits = take((size_t)T * d.n_routed * 4);
   w.ids = take(Tk * 4);
   w.wts = take(Tk * 4);
   w.counts = take((size_t)d.n_routed * 4);
@@ -812,6 +815,7 @@ int moe_prefill_layer(moe_layer_t L, const void* x, const void* router_w, const 
   a.g2 = L->p.g2;
   char* w = static_cast<char*>(workspace);
   a.xhat = reinterpret_cast<uint16_t*>(w + wl.xhat);
+  a.logits = reinterpret_cast<float*>(w + wl.logits);
   a.ids = reinterpret_cast<int*>(w + wl.ids);
   a.wts = reinterpret_cast<float*>(w + wl.wts);
   a.counts = reinterpret_cast<int*>(w + wl.counts);

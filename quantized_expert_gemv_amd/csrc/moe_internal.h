@@ -290,7 +290,7 @@ inline ChainLayer chain_layer_of(const KCommon& a) {
 int launch_b1(const B1Args& a, void* stream);
 
 // Prefill / large-batch path: T tokens as grouped GEMMs on the matrix cores
-// (six launches on one stream).  Shapes it takes: NVFP4 routed and shared
+// (seven launches on one stream).  Shapes it takes: NVFP4 routed and shared
 // experts, sigmoid routing, H <= kPfMaxH, E <= kPfMaxE (both tile sizes
 // divide them; checked by the library).
 constexpr int kPfMaxH = 2048;
@@ -313,6 +313,7 @@ struct PrefillArgs {
   MatGeom g13, g2;
   // caller's workspace
   uint16_t* xhat;   // bf16 [T][H] (prenorm only)
+  float* logits;    // fp32 [T][E]
   int* ids;         // [T][k] selection order
   float* wts;       // [T][k]
   int* counts;      // [E] pairs per expert

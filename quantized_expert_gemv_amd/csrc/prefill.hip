@@ -5,28 +5,29 @@
 // The Flint page ("From 1,096 kernels to 346") counts the MoE kernel work as
 // the largest prefill gain; the SM120 page ("How it fits") replaces a
 // [tokens * top_k, hidden] fp32 scatter buffer and its weighted temporary by a
-// direct gather/reduce.  Here, in six launches on one stream:
+// direct gather/reduce.  Here, in seven launches on one stream:
 //
-//   k_pf_route    16 tokens per workgroup: the rows (pre-norm), the router
-//                 logits on MFMA (bf16 x bf16 -> fp32), the top-k and weights.
+//   k_pf_logits   16 tokens x 64 experts per workgroup: the rows (pre-norm),
+//                 the router logits on MFMA (bf16 x bf16 -> fp32).
+//   k_pf_topk     one wave per token: the top-k and weights.
 //   k_pf_count    one workgroup per expert: its number of (token, slot) pairs.
 //   k_pf_place    one workgroup per expert: its pairs in token order, as the
 //                 expert's rows of the sorted list (perm) and the inverse map
 //                 (inv); workgroup 0 also writes the group and tile offsets.
-//   k_pf_gateup   one workgroup per (32-row tile of a group, 64 intermediates):
+//   k_pf_gateup   one workgroup per (64-row tile of a group, 64 intermediates):
 //                 the group's tokens' xhat rows staged in shared memory, the
 //                 expert's gate and up rows decoded in registers; h = SiLU(g)*u
 //                 in bf16 at the tile's sorted rows.  A group is an expert's
 //                 sorted rows, or all T tokens for a shared expert.
-//   k_pf_down     one workgroup per (32-row tile, 128 outputs): y = W2 h in
+//   k_pf_down     one workgroup per (64-row tile, 128 outputs): y = W2 h in
 //                 fp32 at the same sorted rows.
 //   k_pf_combine  one workgroup per token: out = sum over its shared then its
 //                 routed slots (selection order) of coef * tensor scale * y,
 //                 gathered through inv (+ residual), one bf16 rounding.
 //
-// The NVFP4 products e2m1 * bf16 are exact in the matrix core's fp32 sums;
-// each 16-column block gets its own MFMA (16x16x16) so that its e4m3 scale
-// multiplies the block's partial sum, as the decode kernels do.  Every sum
+// The weights reach the matrix cores (MFMA 16x16x32 bf16, fp32 sums) as
+// e2m1 code times e4m3 block scale, which bf16 holds exactly; the fp32
+// tensor scale multiplies the finished sums.  Every sum
 // has a fixed order: the result does not depend on scheduling.
 
 #include <hip/hip_runtime.h>
@@ -42,38 +43,20 @@ namespace {
 
 #include "kernel_common.h"
 
-typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kPfThreads = 256;   // four waves
 constexpr int kRouteTok = 16;     // tokens per routing workgroup (one MFMA row block)
-constexpr int kTileTok = 32;      // rows per gate/up and down tile (two MFMA row blocks)
-constexpr int kSlice = 512;       // K columns staged in shared memory at a time
+constexpr int kTileTok = 64;      // rows per gate/up and down tile (four MFMA row blocks)
+constexpr int kSlice = 256;       // K columns staged in shared memory at a time
 constexpr int kSlicePad = kSlice + 8;   // row stride in bf16: 16 B of padding spreads the rows over the banks
 constexpr int kGuCols = 64;       // intermediates per gate/up workgroup (16 per wave)
 constexpr int kDnCols = 128;      // outputs per down workgroup (32 per wave)
 
-__device__ __forceinline__ f32x4_t mfma16(s16x4_t a, s16x4_t b, f32x4_t c) {
-  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
-}
 __device__ __forceinline__ f32x4_t mfma32(const uint4& a, const uint4& b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c,
                                                  0, 0, 0);
-}
-__device__ __forceinline__ s16x4_t as_s16x4(uint32_t lo, uint32_t hi) {
-  return __builtin_bit_cast(s16x4_t, make_uint2(lo, hi));
-}
-
-// The 4 + 4 weights lane group kb (= lane / 16) feeds to the MFMA from one
-// 32-column NVFP4 chunk: columns 4 kb .. 4 kb + 3 of each 16-column block
-// (b[0]: block 0, b[1]: block 1), as bf16 (codes unscaled, exact).
-__device__ __forceinline__ void chunk_frags(const uint4& c, int kb, s16x4_t (&b)[2]) {
-  const int sh = (kb & 1) << 4;
-  const uint32_t d0 = ((kb & 2) ? c.y : c.x) >> sh;
-  const uint32_t d1 = ((kb & 2) ? c.w : c.z) >> sh;
-  b[0] = as_s16x4(fp4pair<0>(d0), fp4pair<1>(d0));
-  b[1] = as_s16x4(fp4pair<0>(d1), fp4pair<1>(d1));
 }
 
 // Block scales (e4m3) of chunk cc of row `row` of a matrix with geometry g.
@@ -84,20 +67,24 @@ __device__ __forceinline__ uint32_t scale_word_off(const MatGeom& g, int row, in
 __device__ __forceinline__ uint32_t scale_half(const MatGeom& g, int row) { return ((row / g.rpw) & 1) << 4; }
 
 // ---------------------------------------------------------------- routing
-__global__ __launch_bounds__(kPfThreads) void k_pf_route(PrefillArgs a) {
-  // xhat rows [16][H] (+ one 16-byte unit of padding per row) and the logits
+// Logits: workgroup (token block, expert block) takes 16 tokens x 64 experts;
+// wave w the 16 experts 64 y + 16 w.  The 16 rows (pre-normed if the layer
+// has a pre-norm; blocks of y = 0 write them to xhat) sit in shared memory;
+// lane (m = lane % 16, kb = lane / 16) feeds row m and columns 8 kb .. + 8 of
+// each 32-column step, router rows stream from memory 8 steps at a time.
+constexpr int kLogitSteps = 8;
+
+__global__ __launch_bounds__(kPfThreads) void k_pf_logits(PrefillArgs a) {
   __shared__ uint4 xs[kRouteTok * (kPfMaxH / 8 + 1)];
-  __shared__ float lg[kRouteTok][kPfMaxE];
   const int wave = wave_id(), lane = (int)threadIdx.x & 63;
   const int t0 = blockIdx.x * kRouteTok;
-  const int H = a.H, upr = H / 8, ups = upr + 1;   // 16-byte units per row, row stride in units
+  const int H = a.H, upr = H / 8, ups = upr + 1;   // 16-byte units per row; row stride (+1: banks)
   for (int u = (int)threadIdx.x; u < kRouteTok * upr; u += kPfThreads) {
     const int m = u / upr, q = u - m * upr, t = t0 + m;
     xs[m * ups + q] = t < a.T ? ld16(a.x + (size_t)t * H + q * 8) : make_uint4(0u, 0u, 0u, 0u);
   }
   __syncthreads();
   if (a.prenorm) {
-    // wave w normalises rows 4w .. 4w + 3 and writes them to xhat for the gate/up GEMM
     for (int i = 0; i < kRouteTok / 4; ++i) {
       const int m = 4 * wave + i, t = t0 + m;
       float ss = 0.f;
@@ -117,85 +104,76 @@ __global__ __launch_bounds__(kPfThreads) void k_pf_route(PrefillArgs a) {
         const uint4 o = make_uint4(norm_pair(v.x, gm.x, rn), norm_pair(v.y, gm.y, rn), norm_pair(v.z, gm.z, rn),
                                    norm_pair(v.w, gm.w, rn));
         xs[m * ups + q] = o;
-        if (t < a.T) *reinterpret_cast<uint4*>(a.xhat + (size_t)t * H + q * 8) = o;
+        if (blockIdx.y == 0 && t < a.T) *reinterpret_cast<uint4*>(a.xhat + (size_t)t * H + q * 8) = o;
       }
     }
     __syncthreads();
   }
-  // logits: wave w takes experts [64 w, 64 w + 64) as four 16-expert tiles;
-  // lane (m = lane % 16, kb = lane / 16) feeds row m and columns 8 kb .. 8 kb + 7
-  // of each 32-column step
   const int mi = lane & 15, kb = lane >> 4;
-  f32x4_t acc[4];
+  const int e0 = blockIdx.y * 64 + 16 * wave;
+  if (e0 >= a.E) return;
+  const uint16_t* rrow = a.router_w + (size_t)(e0 + mi) * H + 8 * kb;
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  for (int c = 0; c < H / 32; c += kLogitSteps) {
+    uint4 bv[kLogitSteps];
 #pragma unroll
-  for (int nt = 0; nt < 4; ++nt) acc[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  const int e_base = 64 * wave;
-  if (e_base < a.E) {
-    const int ntiles = min(4, (a.E - e_base) / 16);
-    for (int c = 0; c < H / 32; ++c) {
-      const uint4 av = xs[mi * ups + 4 * c + kb];
+    for (int i = 0; i < kLogitSteps; ++i) bv[i] = ld16(rrow + 32 * (c + i));
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
-        if (nt < ntiles) {
-          const uint4 bv = ld16(a.router_w + (size_t)(e_base + 16 * nt + mi) * H + 32 * c + 8 * kb);
-          acc[nt] = mfma32(av, bv, acc[nt]);
-        }
-      }
-    }
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      if (nt < ntiles) {
-        const int e = e_base + 16 * nt + mi;
-        const float bias = a.bias ? a.bias[e] : 0.0f;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) lg[4 * kb + r][e] = acc[nt][r] + bias;
-      }
-    }
+    for (int i = 0; i < kLogitSteps; ++i) acc = mfma32(xs[mi * ups + 4 * (c + i) + kb], bv[i], acc);
   }
-  __syncthreads();
-  // top-k of rows 4w .. 4w + 3: lane l holds experts 4 l .. 4 l + 3, sorted;
-  // each round the largest head key wins (ties to the lowest expert)
-  for (int i = 0; i < kRouteTok / 4; ++i) {
-    const int m = 4 * wave + i, t = t0 + m;
-    if (t >= a.T) break;
-    unsigned key[4];
-    int idx[4];
+  const int e = e0 + mi;
+  const float bias = a.bias ? a.bias[e] : 0.0f;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      idx[j] = 4 * lane + j;
-      key[j] = idx[j] < a.E ? sel_key(lg[m][idx[j]]) : 0u;
-    }
-    cas(key[0], idx[0], key[1], idx[1]);
-    cas(key[2], idx[2], key[3], idx[3]);
-    cas(key[0], idx[0], key[2], idx[2]);
-    cas(key[1], idx[1], key[3], idx[3]);
-    cas(key[1], idx[1], key[2], idx[2]);
-    int my_e = 0;
-    unsigned my_key = 0u;
-    for (int r = 0; r < a.k; ++r) {
-      const unsigned M = wave_max_u32(key[0]);
-      const int win = __builtin_ctzll(__ballot(key[0] == M));
-      const int e_sel = __builtin_amdgcn_readlane(idx[0], win);
-      my_e = (lane == r) ? e_sel : my_e;
-      my_key = (lane == r) ? M : my_key;
-      const bool me = lane == win;
+  for (int r = 0; r < 4; ++r) {
+    const int t = t0 + 4 * kb + r;
+    if (t < a.T) a.logits[(size_t)t * a.E + e] = acc[r] + bias;
+  }
+}
+
+// Top-k and weights: one wave per token.  Lane l holds experts 4 l .. 4 l + 3,
+// sorted; each round the largest head key wins (ties to the lowest expert),
+// the decode kernels' rule; weights are the selections' logistic values over
+// their sum.
+__global__ __launch_bounds__(kPfThreads) void k_pf_topk(PrefillArgs a) {
+  const int lane = (int)threadIdx.x & 63;
+  const int t = blockIdx.x * (kPfThreads / 64) + wave_id();
+  if (t >= a.T) return;
+  unsigned key[4];
+  int idx[4];
 #pragma unroll
-      for (int j = 0; j < 3; ++j) {
-        key[j] = me ? key[j + 1] : key[j];
-        idx[j] = me ? idx[j + 1] : idx[j];
-      }
-      key[3] = me ? 0u : key[3];
+  for (int j = 0; j < 4; ++j) {
+    idx[j] = 4 * lane + j;
+    key[j] = idx[j] < a.E ? sel_key(a.logits[(size_t)t * a.E + idx[j]]) : 0u;
+  }
+  cas(key[0], idx[0], key[1], idx[1]);
+  cas(key[2], idx[2], key[3], idx[3]);
+  cas(key[0], idx[0], key[2], idx[2]);
+  cas(key[1], idx[1], key[3], idx[3]);
+  cas(key[1], idx[1], key[2], idx[2]);
+  int my_e = 0;
+  unsigned my_key = 0u;
+  for (int r = 0; r < a.k; ++r) {
+    const unsigned M = wave_max_u32(key[0]);
+    const int win = __builtin_ctzll(__ballot(key[0] == M));
+    const int e_sel = __builtin_amdgcn_readlane(idx[0], win);
+    my_e = (lane == r) ? e_sel : my_e;
+    my_key = (lane == r) ? M : my_key;
+    const bool me = lane == win;
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+      key[j] = me ? key[j + 1] : key[j];
+      idx[j] = me ? idx[j + 1] : idx[j];
     }
-    // weights: each selection's logistic value over their sum
-    const float sg = (lane < a.k) ? __builtin_amdgcn_rcpf(1.0f + __expf(-unkey(my_key))) : 0.0f;
-    const float sum = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(group_sum(sg, 16))));
-    const float wgt = sg * __builtin_amdgcn_rcpf(sum);
-    if (lane < a.k) {
-      a.ids[(size_t)t * a.k + lane] = my_e;
-      a.wts[(size_t)t * a.k + lane] = wgt;
-      if (a.out_ids) a.out_ids[(size_t)t * a.k + lane] = my_e;
-      if (a.out_w) a.out_w[(size_t)t * a.k + lane] = wgt;
-    }
+    key[3] = me ? 0u : key[3];
+  }
+  const float sg = (lane < a.k) ? __builtin_amdgcn_rcpf(1.0f + __expf(-unkey(my_key))) : 0.0f;
+  const float sum = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(group_sum(sg, 16))));
+  const float wgt = sg * __builtin_amdgcn_rcpf(sum);
+  if (lane < a.k) {
+    a.ids[(size_t)t * a.k + lane] = my_e;
+    a.wts[(size_t)t * a.k + lane] = wgt;
+    if (a.out_ids) a.out_ids[(size_t)t * a.k + lane] = my_e;
+    if (a.out_w) a.out_w[(size_t)t * a.k + lane] = wgt;
   }
 }
 
@@ -312,101 +290,167 @@ __device__ __forceinline__ TileRows tile_rows(const PrefillArgs& a, int* toff_s)
   return tr;
 }
 
-// ---------------------------------------------------------------- gate/up
+// ---------------------------------------------------------------- gate/up and down
+// Both GEMMs run slice by slice over K (kSlice columns): the workgroup stages
+// the slice of its 64 activation rows and of its 128 weight rows (codes and
+// block scales) in shared memory, every thread issuing all of its loads
+// before its first store, so that one memory round trip brings the whole
+// slice; each wave then multiplies its rows out of shared memory.
+constexpr int kWRows = 128;                        // weight rows per workgroup
+constexpr int kWStride = kSlice / 2 + 16;          // bytes per staged weight row (+16 B: banks)
+constexpr int kChunks = kSlice / 32;               // 32-column chunks per slice
+
+struct __align__(16) GemmSmem {
+  uint16_t act[kTileTok * kSlicePad];              // activation rows, bf16
+  uint8_t wc[kWRows * kWStride];                   // weight codes
+  uint16_t wsc[kWRows][kChunks];                   // block scale pair (2 x e4m3) per row and chunk
+  int toff[kPfMaxE + MOE_MAX_SHARED + 1];
+  int tok[kTileTok];
+};
+
+// One slice of the tile in flight: this thread's share of the activation
+// rows and of the weight codes and scales, loaded into registers (load) and
+// then written to shared memory (store).  The workgroup loads slice i + 1
+// while it multiplies slice i, so that the loads' round trip overlaps the
+// matrix work.  Activation row m comes from act_row(m) (a bf16 row, or null
+// for a zero row), local weight row r from matrix row wrow(r) of (codes,
+// scales) with geometry g.
+struct SliceRegs {
+  static constexpr int kA = kTileTok * kSlice / 8 / kPfThreads;   // 16-byte activation units per thread
+  static constexpr int kW = kWRows * kSlice / 32 / kPfThreads;    // 16-byte code units (chunks) per thread
+  uint4 av[kA], wv[kW];
+  uint32_t sv[kW];
+};
+
+template <class ActRow, class WRow>
+__device__ __forceinline__ void load_slice(SliceRegs& r, int k0, int slice, const MatGeom& g, const uint8_t* codes,
+                                           const uint8_t* scales, const uint16_t* any_row, ActRow&& act_row,
+                                           WRow&& wrow) {
+  const int aups = slice / 8, nch = slice / 32, c0 = k0 / 32;
+  // every lane loads (a zero row reads any_row and drops it): no branch
+  // around the loads, so that they all issue back to back
+#pragma unroll
+  for (int i = 0; i < SliceRegs::kA; ++i) {
+    const int u = (int)threadIdx.x + kPfThreads * i, m = u / aups, q = u - m * aups;
+    const uint16_t* src = act_row(m < kTileTok ? m : 0);
+    const bool ok = m < kTileTok && src != nullptr;
+    const uint4 v = ld16((ok ? src : any_row) + k0 + q * 8);
+    r.av[i] = ok ? v : make_uint4(0u, 0u, 0u, 0u);
+  }
+#pragma unroll
+  for (int i = 0; i < SliceRegs::kW; ++i) {
+    const int u = (int)threadIdx.x + kPfThreads * i, lr = u / nch, q = u - lr * nch;
+    const int row = wrow(lr < kWRows ? lr : 0);
+    r.wv[i] = ld16o(codes, (uint32_t)(row * g.cw + c0 + q) * 16u);
+    r.sv[i] = ld32o(scales, scale_word_off(g, row, c0 + q)) >> scale_half(g, row);
+  }
+}
+
+__device__ __forceinline__ void store_slice(GemmSmem& s, const SliceRegs& r, int slice) {
+  const int aups = slice / 8, nch = slice / 32;
+#pragma unroll
+  for (int i = 0; i < SliceRegs::kA; ++i) {
+    const int u = (int)threadIdx.x + kPfThreads * i, m = u / aups, q = u - m * aups;
+    if (m < kTileTok) *reinterpret_cast<uint4*>(&s.act[m * kSlicePad + q * 8]) = r.av[i];
+  }
+#pragma unroll
+  for (int i = 0; i < SliceRegs::kW; ++i) {
+    const int u = (int)threadIdx.x + kPfThreads * i, lr = u / nch, q = u - lr * nch;
+    if (lr < kWRows) {
+      *reinterpret_cast<uint4*>(&s.wc[lr * kWStride + q * 16]) = r.wv[i];
+      s.wsc[lr][q] = (uint16_t)r.sv[i];
+    }
+  }
+}
+
+// B operand of lane group kb (= lane / 16) from local weight row r, chunk q
+// of the staged slice: columns 8 kb .. 8 kb + 7, codes times their block's
+// e4m3 scale, as bf16.  Exact: an e2m1 value has at most 2 significant bits
+// and an e4m3 scale 4, so the product fits bf16's 8.
+__device__ __forceinline__ uint4 wfrag(const GemmSmem& s, int r, int q, int kb) {
+  const uint32_t d = *reinterpret_cast<const uint32_t*>(&s.wc[r * kWStride + q * 16 + 4 * kb]);
+  const float sc = e4m3f<0>((uint32_t)s.wsc[r][q] >> (kb & 2) * 4);   // block kb / 2 of the chunk
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  const f32x2_t v0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d, 1.0f, 0);
+  const f32x2_t v1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d, 1.0f, 1);
+  const f32x2_t v2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d, 1.0f, 2);
+  const f32x2_t v3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d, 1.0f, 3);
+  return make_uint4(pack_bf16x2(v0.x * sc, v0.y * sc), pack_bf16x2(v1.x * sc, v1.y * sc),
+                    pack_bf16x2(v2.x * sc, v2.y * sc), pack_bf16x2(v3.x * sc, v3.y * sc));
+}
+// A operand of lane (mi, kb) for row block mt, chunk q: activation row
+// 16 mt + mi, columns 32 q + 8 kb .. + 8.
+__device__ __forceinline__ uint4 afrag(const GemmSmem& s, int mt, int q, int mi, int kb) {
+  return *reinterpret_cast<const uint4*>(&s.act[(16 * mt + mi) * kSlicePad + 32 * q + 8 * kb]);
+}
+
+// gate/up: workgroup (tile, y) takes intermediates [64 y, 64 y + 64): local
+// weight rows 0..63 are their gate rows, 64..127 their up rows; wave w's
+// lanes take intermediate 64 y + 16 w + lane % 16.
 __global__ __launch_bounds__(kPfThreads) void k_pf_gateup(PrefillArgs a) {
-  __shared__ uint16_t xs[kTileTok * kSlicePad];
-  __shared__ int toff_s[kPfMaxE + MOE_MAX_SHARED + 1];
-  __shared__ int tok_s[kTileTok];
-  const TileRows tr = tile_rows(a, toff_s);
+  __shared__ GemmSmem s;
+  const TileRows tr = tile_rows(a, s.toff);
   if (tr.g < 0) return;
   const int wave = wave_id(), lane = (int)threadIdx.x & 63;
   const int mi = lane & 15, kb = lane >> 4;
   const bool routed = tr.g < a.E;
   if (threadIdx.x < kTileTok) {
     const int r = (int)threadIdx.x;
-    tok_s[r] = r >= tr.nrows ? -1 : routed ? a.perm[tr.row0 + r] / a.k : tr.r0 + r;
+    s.tok[r] = r >= tr.nrows ? -1 : routed ? a.perm[tr.row0 + r] / a.k : tr.r0 + r;
   }
   const uint8_t* codes = routed ? a.r_codes + (size_t)tr.g * a.r_code_stride
                                 : a.s_codes + (size_t)(tr.g - a.E) * a.s_code_stride;
   const uint8_t* scales = routed ? a.r_scales + (size_t)tr.g * a.r_scale_stride
                                  : a.s_scales + (size_t)(tr.g - a.E) * a.s_scale_stride;
   const float ts13 = routed ? a.r_tscale[2 * tr.g] : a.s_tscale[2 * (tr.g - a.E)];
-  const MatGeom& g = a.g13;
-  const int j = blockIdx.y * kGuCols + 16 * wave + mi;   // this lane's intermediate (weight rows j and I + j)
-  const uint32_t crow_g = (uint32_t)j * g.cw, crow_u = (uint32_t)(a.I + j) * g.cw;
-  const uint32_t sh_g = scale_half(g, j), sh_u = scale_half(g, a.I + j);
+  const int j0 = blockIdx.y * kGuCols, j = j0 + 16 * wave + mi;
   const uint16_t* xsrc = a.prenorm ? a.xhat : a.x;
-  f32x4_t accg[2], accu[2];
+  const int H = a.H, I = a.I;
+  f32x4_t accg[4], accu[4];
 #pragma unroll
-  for (int mt = 0; mt < 2; ++mt) accg[mt] = accu[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  const int slice = min(kSlice, a.H);
-  for (int k0 = 0; k0 < a.H; k0 += slice) {
-    __syncthreads();   // tok_s written; the previous slice consumed
-    // the tile's rows, columns k0 .. k0 + slice, 16 bytes per thread and step
-    const int ups = slice / 8;
-    for (int u = (int)threadIdx.x; u < kTileTok * ups; u += kPfThreads) {
-      const int m = u / ups, q = u - m * ups, t = tok_s[m];
-      const uint4 v = t >= 0 ? ld16(xsrc + (size_t)t * a.H + k0 + q * 8) : make_uint4(0u, 0u, 0u, 0u);
-      *reinterpret_cast<uint4*>(&xs[m * kSlicePad + q * 8]) = v;
-    }
+  for (int mt = 0; mt < 4; ++mt) accg[mt] = accu[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const int slice = min(kSlice, H);
+  const auto act_row = [&](int m) -> const uint16_t* {
+    const int t = s.tok[m];
+    return t >= 0 ? xsrc + (size_t)t * H : nullptr;
+  };
+  const auto wrow = [&](int r) { return r < kGuCols ? j0 + r : I + j0 + (r - kGuCols); };
+  __syncthreads();   // the token list is written
+  SliceRegs sr;
+  load_slice(sr, 0, slice, a.g13, codes, scales, xsrc, act_row, wrow);
+  for (int k0 = 0; k0 < H; k0 += slice) {
+    __syncthreads();   // the previous slice is consumed
+    store_slice(s, sr, slice);
     __syncthreads();
-    const int c0 = k0 / 32;
-    for (int cs = 0; cs < slice / 32; cs += 4) {
-      uint4 cg[4], cu[4];
-      uint32_t sg[4], su[4];
+    if (k0 + slice < H) load_slice(sr, k0 + slice, slice, a.g13, codes, scales, xsrc, act_row, wrow);
+    const int nq = slice / 32;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int cc = c0 + cs + q;
-        cg[q] = ld16o(codes, (crow_g + cc) * 16u);
-        cu[q] = ld16o(codes, (crow_u + cc) * 16u);
-        sg[q] = ld32o(scales, scale_word_off(g, j, cc)) >> sh_g;
-        su[q] = ld32o(scales, scale_word_off(g, a.I + j, cc)) >> sh_u;
-      }
+    for (int q = 0; q < kChunks; ++q) {
+      if (q >= nq) break;
+      const uint4 bg = wfrag(s, 16 * wave + mi, q, kb), bu = wfrag(s, kGuCols + 16 * wave + mi, q, kb);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        s16x4_t bg[2], bu[2];
-        chunk_frags(cg[q], kb, bg);
-        chunk_frags(cu[q], kb, bu);
-        const float g0 = e4m3f<0>(sg[q]), g1 = e4m3f<1>(sg[q]);
-        const float u0 = e4m3f<0>(su[q]), u1 = e4m3f<1>(su[q]);
-        const int col = 32 * (cs + q);
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
-          const uint16_t* xr = &xs[(16 * mt + mi) * kSlicePad + col + 4 * kb];
-          const uint2 a0 = *reinterpret_cast<const uint2*>(xr);
-          const uint2 a1 = *reinterpret_cast<const uint2*>(xr + 16);
-          const s16x4_t x0 = __builtin_bit_cast(s16x4_t, a0), x1 = __builtin_bit_cast(s16x4_t, a1);
-          const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
-          const f32x4_t pg0 = mfma16(x0, bg[0], z), pg1 = mfma16(x1, bg[1], z);
-          const f32x4_t pu0 = mfma16(x0, bu[0], z), pu1 = mfma16(x1, bu[1], z);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            accg[mt][r] = fmaf(pg1[r], g1, fmaf(pg0[r], g0, accg[mt][r]));
-            accu[mt][r] = fmaf(pu1[r], u1, fmaf(pu0[r], u0, accu[mt][r]));
-          }
-        }
+      for (int mt = 0; mt < 4; ++mt) {
+        const uint4 av = afrag(s, mt, q, mi, kb);
+        accg[mt] = mfma32(av, bg, accg[mt]);
+        accu[mt] = mfma32(av, bu, accu[mt]);
       }
     }
   }
-  // h = SiLU(g) * u at the tile's sorted rows; lane holds rows 16 mt + 4 kb + r, intermediate j
+  // h = SiLU(g) * u at the tile's sorted rows; the lane holds rows 16 mt + 4 kb + i
 #pragma unroll
-  for (int mt = 0; mt < 2; ++mt) {
+  for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int m = 16 * mt + 4 * kb + r;
-      if (m < tr.nrows) {
-        const float hv = silu_mul(accg[mt][r] * ts13, accu[mt][r] * ts13);
-        a.h[(size_t)(tr.row0 + m) * a.I + j] = (uint16_t)f2bf(hv);
-      }
+    for (int i = 0; i < 4; ++i) {
+      const int m = 16 * mt + 4 * kb + i;
+      if (m < tr.nrows) a.h[(size_t)(tr.row0 + m) * I + j] = (uint16_t)f2bf(silu_mul(accg[mt][i] * ts13, accu[mt][i] * ts13));
     }
-  }
 }
 
-// ---------------------------------------------------------------- down
+// down: workgroup (tile, y) takes outputs [128 y, 128 y + 128) (W2 rows);
+// wave w's lanes take outputs 128 y + 32 w + 16 nt + lane % 16, nt = 0, 1.
 __global__ __launch_bounds__(kPfThreads) void k_pf_down(PrefillArgs a) {
-  __shared__ uint16_t hs[kTileTok * kSlicePad];
-  __shared__ int toff_s[kPfMaxE + MOE_MAX_SHARED + 1];
-  const TileRows tr = tile_rows(a, toff_s);
+  __shared__ GemmSmem s;
+  const TileRows tr = tile_rows(a, s.toff);
   if (tr.g < 0) return;
   const int wave = wave_id(), lane = (int)threadIdx.x & 63;
   const int mi = lane & 15, kb = lane >> 4;
@@ -415,76 +459,45 @@ __global__ __launch_bounds__(kPfThreads) void k_pf_down(PrefillArgs a) {
                                 : a.s_codes + (size_t)(tr.g - a.E) * a.s_code_stride + a.s_w13_code;
   const uint8_t* scales = routed ? a.r_scales + (size_t)tr.g * a.r_scale_stride + a.r_w13_scale
                                  : a.s_scales + (size_t)(tr.g - a.E) * a.s_scale_stride + a.s_w13_scale;
-  const MatGeom& g = a.g2;
-  int n[2];
-  uint32_t crow[2], sh[2];
-#pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
-    n[nt] = blockIdx.y * kDnCols + 32 * wave + 16 * nt + mi;   // output (W2 row) of this lane
-    crow[nt] = (uint32_t)n[nt] * g.cw;
-    sh[nt] = scale_half(g, n[nt]);
-  }
-  f32x4_t acc[2][2];
+  const int n0 = blockIdx.y * kDnCols, H = a.H, I = a.I;
+  f32x4_t acc[2][4];
 #pragma unroll
   for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) acc[nt][mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  const int slice = min(kSlice, a.I);
-  for (int k0 = 0; k0 < a.I; k0 += slice) {
+    for (int mt = 0; mt < 4; ++mt) acc[nt][mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const int slice = min(kSlice, I);
+  const auto act_row = [&](int m) -> const uint16_t* {
+    return m < tr.nrows ? a.h + (size_t)(tr.row0 + m) * I : nullptr;
+  };
+  const auto wrow = [&](int r) { return n0 + r; };
+  SliceRegs sr;
+  load_slice(sr, 0, slice, a.g2, codes, scales, a.h, act_row, wrow);
+  for (int k0 = 0; k0 < I; k0 += slice) {
     __syncthreads();
-    const int ups = slice / 8;
-    for (int u = (int)threadIdx.x; u < kTileTok * ups; u += kPfThreads) {
-      const int m = u / ups, q = u - m * ups;
-      const uint4 v = m < tr.nrows ? ld16(a.h + (size_t)(tr.row0 + m) * a.I + k0 + q * 8) : make_uint4(0u, 0u, 0u, 0u);
-      *reinterpret_cast<uint4*>(&hs[m * kSlicePad + q * 8]) = v;
-    }
+    store_slice(s, sr, slice);
     __syncthreads();
-    const int c0 = k0 / 32;
-    for (int cs = 0; cs < slice / 32; cs += 2) {
-      uint4 cw[2][2];
-      uint32_t sw[2][2];
+    if (k0 + slice < I) load_slice(sr, k0 + slice, slice, a.g2, codes, scales, a.h, act_row, wrow);
+    const int nq = slice / 32;
 #pragma unroll
-      for (int q = 0; q < 2; ++q)
+    for (int q = 0; q < kChunks; ++q) {
+      if (q >= nq) break;
+      const uint4 b0 = wfrag(s, 32 * wave + mi, q, kb), b1 = wfrag(s, 32 * wave + 16 + mi, q, kb);
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
-          const int cc = c0 + cs + q;
-          cw[q][nt] = ld16o(codes, (crow[nt] + cc) * 16u);
-          sw[q][nt] = ld32o(scales, scale_word_off(g, n[nt], cc)) >> sh[nt];
-        }
-#pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        const int col = 32 * (cs + q);
-        s16x4_t xa[2][2];
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
-          const uint16_t* hr = &hs[(16 * mt + mi) * kSlicePad + col + 4 * kb];
-          xa[mt][0] = __builtin_bit_cast(s16x4_t, *reinterpret_cast<const uint2*>(hr));
-          xa[mt][1] = __builtin_bit_cast(s16x4_t, *reinterpret_cast<const uint2*>(hr + 16));
-        }
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
-          s16x4_t b[2];
-          chunk_frags(cw[q][nt], kb, b);
-          const float s0 = e4m3f<0>(sw[q][nt]), s1 = e4m3f<1>(sw[q][nt]);
-#pragma unroll
-          for (int mt = 0; mt < 2; ++mt) {
-            const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
-            const f32x4_t p0 = mfma16(xa[mt][0], b[0], z), p1 = mfma16(xa[mt][1], b[1], z);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) acc[nt][mt][r] = fmaf(p1[r], s1, fmaf(p0[r], s0, acc[nt][mt][r]));
-          }
-        }
+      for (int mt = 0; mt < 4; ++mt) {
+        const uint4 av = afrag(s, mt, q, mi, kb);
+        acc[0][mt] = mfma32(av, b0, acc[0][mt]);
+        acc[1][mt] = mfma32(av, b1, acc[1][mt]);
       }
     }
   }
 #pragma unroll
   for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
+    for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int m = 16 * mt + 4 * kb + r;
-        if (m < tr.nrows) a.y[(size_t)(tr.row0 + m) * a.H + n[nt]] = acc[nt][mt][r];
+      for (int i = 0; i < 4; ++i) {
+        const int m = 16 * mt + 4 * kb + i;
+        if (m < tr.nrows) a.y[(size_t)(tr.row0 + m) * H + n0 + 32 * wave + 16 * nt + mi] = acc[nt][mt][i];
       }
 }
 
@@ -545,7 +558,8 @@ int launch_prefill(const PrefillArgs& a, void* stream) {
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const int tiles = prefill_max_tiles(a.T, a.k, a.E, a.S);
   (void)hipGetLastError();
-  hipLaunchKernelGGL(k_pf_route, dim3((a.T + kRouteTok - 1) / kRouteTok), dim3(kPfThreads), 0, st, a);
+  hipLaunchKernelGGL(k_pf_logits, dim3((a.T + kRouteTok - 1) / kRouteTok, (a.E + 63) / 64), dim3(kPfThreads), 0, st, a);
+  hipLaunchKernelGGL(k_pf_topk, dim3((a.T + kPfThreads / 64 - 1) / (kPfThreads / 64)), dim3(kPfThreads), 0, st, a);
   hipLaunchKernelGGL(k_pf_count, dim3(a.E), dim3(kPfThreads), 0, st, a);
   hipLaunchKernelGGL(k_pf_place, dim3(a.E), dim3(kPfThreads), 0, st, a);
   hipLaunchKernelGGL(k_pf_gateup, dim3(tiles, a.I / kGuCols), dim3(kPfThreads), 0, st, a);
