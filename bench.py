@@ -562,7 +562,7 @@ def measure_prefill(name: str, K: int, W: int, R: int, flush) -> dict:
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
     return {"workload": f"prefill of {T} tokens, {wl.description.replace(', b1', '')}", "tokens": T,
-            "kernels": "k_pf_route, k_pf_count, k_pf_place, k_pf_gateup, k_pf_down, k_pf_combine",
+            "kernels": "k_pf_logits, k_pf_topk, k_pf_count, k_pf_place, k_pf_gateup, k_pf_down, k_pf_combine",
             "us_per_call": round(us, 2), "tokens_per_s": round(T / (us * 1e-6), 1), "tflops": round(tfs, 2),
             "gbs": round(gbs, 1), "bound": bound, "roofline_frac": round(frac, 4),
             "flops_per_call": flops, "algorithmic_bytes_per_call": int(round(lay["total"])),

@@ -271,13 +271,24 @@ struct TileRows {
   int row0;    // sorted row of the tile's first row (rows are consecutive)
 };
 
+// Workgroup -> (tile, column block y) for a grid of whole chunks of 8 tiles
+// x ny column blocks.  Workgroups are dealt to the 8 XCDs in turn (b % 8), so
+// within a chunk of 8 ny consecutive workgroups tile 8 c + (b % 8) keeps one
+// XCD: its ny column blocks run there at about the same time and read its
+// activation rows from that XCD's L2 instead of memory.
+__device__ __forceinline__ void tile_and_block(int ny, int& tile, int& y) {
+  const int b = blockIdx.x, per = 8 * ny;
+  const int c = b / per, r = b - c * per;
+  tile = 8 * c + (r & 7);
+  y = r >> 3;
+}
+
 // The tile this workgroup takes, or g = -1 past the last tile.
-__device__ __forceinline__ TileRows tile_rows(const PrefillArgs& a, int* toff_s) {
+__device__ __forceinline__ TileRows tile_rows(const PrefillArgs& a, int* toff_s, int tile) {
   const int ng = a.E + a.S;
   for (int i = (int)threadIdx.x; i <= ng; i += kPfThreads) toff_s[i] = a.tile_off[i];
   __syncthreads();
   TileRows tr;
-  const int tile = blockIdx.x;
   if (tile >= toff_s[ng]) {
     tr.g = -1;
     return tr;
@@ -389,7 +400,9 @@ __device__ __forceinline__ uint4 afrag(const GemmSmem& s, int mt, int q, int mi,
 // lanes take intermediate 64 y + 16 w + lane % 16.
 __global__ __launch_bounds__(kPfThreads) void k_pf_gateup(PrefillArgs a) {
   __shared__ GemmSmem s;
-  const TileRows tr = tile_rows(a, s.toff);
+  int tile, yb;
+  tile_and_block(a.I / kGuCols, tile, yb);
+  const TileRows tr = tile_rows(a, s.toff, tile);
   if (tr.g < 0) return;
   const int wave = wave_id(), lane = (int)threadIdx.x & 63;
   const int mi = lane & 15, kb = lane >> 4;
@@ -403,7 +416,7 @@ __global__ __launch_bounds__(kPfThreads) void k_pf_gateup(PrefillArgs a) {
   const uint8_t* scales = routed ? a.r_scales + (size_t)tr.g * a.r_scale_stride
                                  : a.s_scales + (size_t)(tr.g - a.E) * a.s_scale_stride;
   const float ts13 = routed ? a.r_tscale[2 * tr.g] : a.s_tscale[2 * (tr.g - a.E)];
-  const int j0 = blockIdx.y * kGuCols, j = j0 + 16 * wave + mi;
+  const int j0 = yb * kGuCols, j = j0 + 16 * wave + mi;
   const uint16_t* xsrc = a.prenorm ? a.xhat : a.x;
   const int H = a.H, I = a.I;
   f32x4_t accg[4], accu[4];
@@ -450,7 +463,9 @@ __global__ __launch_bounds__(kPfThreads) void k_pf_gateup(PrefillArgs a) {
 // wave w's lanes take outputs 128 y + 32 w + 16 nt + lane % 16, nt = 0, 1.
 __global__ __launch_bounds__(kPfThreads) void k_pf_down(PrefillArgs a) {
   __shared__ GemmSmem s;
-  const TileRows tr = tile_rows(a, s.toff);
+  int tile, yb;
+  tile_and_block(a.H / kDnCols, tile, yb);
+  const TileRows tr = tile_rows(a, s.toff, tile);
   if (tr.g < 0) return;
   const int wave = wave_id(), lane = (int)threadIdx.x & 63;
   const int mi = lane & 15, kb = lane >> 4;
@@ -459,7 +474,7 @@ __global__ __launch_bounds__(kPfThreads) void k_pf_down(PrefillArgs a) {
                                 : a.s_codes + (size_t)(tr.g - a.E) * a.s_code_stride + a.s_w13_code;
   const uint8_t* scales = routed ? a.r_scales + (size_t)tr.g * a.r_scale_stride + a.r_w13_scale
                                  : a.s_scales + (size_t)(tr.g - a.E) * a.s_scale_stride + a.s_w13_scale;
-  const int n0 = blockIdx.y * kDnCols, H = a.H, I = a.I;
+  const int n0 = yb * kDnCols, H = a.H, I = a.I;
   f32x4_t acc[2][4];
 #pragma unroll
   for (int nt = 0; nt < 2; ++nt)
@@ -556,14 +571,14 @@ int prefill_max_tiles(int T, int k, int E, int S) {
 
 int launch_prefill(const PrefillArgs& a, void* stream) {
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  const int tiles = prefill_max_tiles(a.T, a.k, a.E, a.S);
+  const int chunks = (prefill_max_tiles(a.T, a.k, a.E, a.S) + 7) / 8;   // of 8 tiles
   (void)hipGetLastError();
   hipLaunchKernelGGL(k_pf_logits, dim3((a.T + kRouteTok - 1) / kRouteTok, (a.E + 63) / 64), dim3(kPfThreads), 0, st, a);
   hipLaunchKernelGGL(k_pf_topk, dim3((a.T + kPfThreads / 64 - 1) / (kPfThreads / 64)), dim3(kPfThreads), 0, st, a);
   hipLaunchKernelGGL(k_pf_count, dim3(a.E), dim3(kPfThreads), 0, st, a);
   hipLaunchKernelGGL(k_pf_place, dim3(a.E), dim3(kPfThreads), 0, st, a);
-  hipLaunchKernelGGL(k_pf_gateup, dim3(tiles, a.I / kGuCols), dim3(kPfThreads), 0, st, a);
-  hipLaunchKernelGGL(k_pf_down, dim3(tiles, a.H / kDnCols), dim3(kPfThreads), 0, st, a);
+  hipLaunchKernelGGL(k_pf_gateup, dim3(chunks * 8 * (a.I / kGuCols)), dim3(kPfThreads), 0, st, a);
+  hipLaunchKernelGGL(k_pf_down, dim3(chunks * 8 * (a.H / kDnCols)), dim3(kPfThreads), 0, st, a);
   hipLaunchKernelGGL(k_pf_combine, dim3(a.T), dim3(kPfThreads), 0, st, a);
   return (int)hipGetLastError();
 }

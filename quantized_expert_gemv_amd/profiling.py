@@ -26,7 +26,8 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 
 def src_digest() -> str:
     h = hashlib.sha256()
-    for f in ("layer.hip", "b1_layer.hip", "b8_layer.hip", "dense.hip", "kernel_common.h", "device_util.h", "api.cpp", "moe_internal.h"):
+    for f in ("layer.hip", "b1_layer.hip", "b8_layer.hip", "dense.hip", "prefill.hip", "kernel_common.h",
+              "device_util.h", "api.cpp", "moe_internal.h"):
         with open(os.path.join(_PKG, "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
