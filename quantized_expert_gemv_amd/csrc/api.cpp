@@ -715,7 +715,7 @@ namespace {
 bool prefill_supported(const moe_layer_desc& d, const Plan& p) {
   // the router GEMM takes 256 columns per pass, the expert GEMMs stage K in
   // slices of min(256, K) columns
-  const auto slice_ok = [](int n) { return n <= 256 || n % 256 == 0; };
+  const auto slice_ok = [](int n) { return n % 256 == 0 || n == 64 || n == 128; };   // power-of-two slices
   return d.routed_wtype == MOE_W_NVFP4 && (d.n_shared == 0 || d.shared_wtype == MOE_W_NVFP4) &&
          d.route == MOE_ROUTE_SIGMOID_TOPK && d.hidden <= moe::kPfMaxH && d.hidden % 256 == 0 &&
          d.inter % 64 == 0 && slice_ok(d.hidden) && slice_ok(d.inter) && d.n_routed <= moe::kPfMaxE &&

@@ -59,13 +59,6 @@ __device__ __forceinline__ f32x4_t mfma32(const uint4& a, const uint4& b, f32x4_
                                                  0, 0, 0);
 }
 
-// Block scales (e4m3) of chunk cc of row `row` of a matrix with geometry g.
-__device__ __forceinline__ uint32_t scale_word_off(const MatGeom& g, int row, int cc) {
-  const int t = row / g.rpw, ri = row - t * g.rpw;
-  return (uint32_t)((t >> 1) * g.su + ri * g.cw + cc) * 4u;
-}
-__device__ __forceinline__ uint32_t scale_half(const MatGeom& g, int row) { return ((row / g.rpw) & 1) << 4; }
-
 // ---------------------------------------------------------------- routing
 // Logits: workgroup (token block, expert block) takes 16 tokens x 64 experts;
 // wave w the 16 experts 64 y + 16 w.  The 16 rows (pre-normed if the layer
@@ -333,16 +326,27 @@ struct SliceRegs {
   uint32_t sv[kW];
 };
 
+// log2 of the slice's 16-byte activation units and chunks per row, and of
+// the geometry's rows per step (all powers of two): the staging splits a
+// thread's unit index with shifts, not divisions.
+struct SliceShape {
+  int ash, nsh, rsh;
+};
+__device__ __forceinline__ SliceShape slice_shape(int slice, const MatGeom& g) {
+  return SliceShape{__builtin_ctz((unsigned)slice / 8u), __builtin_ctz((unsigned)slice / 32u),
+                    __builtin_ctz((unsigned)g.rpw)};
+}
+
 template <class ActRow, class WRow>
-__device__ __forceinline__ void load_slice(SliceRegs& r, int k0, int slice, const MatGeom& g, const uint8_t* codes,
+__device__ __forceinline__ void load_slice(SliceRegs& r, int k0, SliceShape sh, const MatGeom& g, const uint8_t* codes,
                                            const uint8_t* scales, const uint16_t* any_row, ActRow&& act_row,
                                            WRow&& wrow) {
-  const int aups = slice / 8, nch = slice / 32, c0 = k0 / 32;
+  const int c0 = k0 >> 5;
   // every lane loads (a zero row reads any_row and drops it): no branch
   // around the loads, so that they all issue back to back
 #pragma unroll
   for (int i = 0; i < SliceRegs::kA; ++i) {
-    const int u = (int)threadIdx.x + kPfThreads * i, m = u / aups, q = u - m * aups;
+    const int u = (int)threadIdx.x + kPfThreads * i, m = u >> sh.ash, q = u & ((1 << sh.ash) - 1);
     const uint16_t* src = act_row(m < kTileTok ? m : 0);
     const bool ok = m < kTileTok && src != nullptr;
     const uint4 v = ld16((ok ? src : any_row) + k0 + q * 8);
@@ -350,23 +354,23 @@ __device__ __forceinline__ void load_slice(SliceRegs& r, int k0, int slice, cons
   }
 #pragma unroll
   for (int i = 0; i < SliceRegs::kW; ++i) {
-    const int u = (int)threadIdx.x + kPfThreads * i, lr = u / nch, q = u - lr * nch;
-    const int row = wrow(lr < kWRows ? lr : 0);
-    r.wv[i] = ld16o(codes, (uint32_t)(row * g.cw + c0 + q) * 16u);
-    r.sv[i] = ld32o(scales, scale_word_off(g, row, c0 + q)) >> scale_half(g, row);
+    const int u = (int)threadIdx.x + kPfThreads * i, lr = u >> sh.nsh, q = u & ((1 << sh.nsh) - 1);
+    const int row = wrow(lr < kWRows ? lr : 0), cc = c0 + q;
+    const int t = row >> sh.rsh, ri = row & ((1 << sh.rsh) - 1);
+    r.wv[i] = ld16o(codes, (uint32_t)(row * g.cw + cc) * 16u);
+    r.sv[i] = ld32o(scales, (uint32_t)((t >> 1) * g.su + ri * g.cw + cc) * 4u) >> ((t & 1) << 4);
   }
 }
 
-__device__ __forceinline__ void store_slice(GemmSmem& s, const SliceRegs& r, int slice) {
-  const int aups = slice / 8, nch = slice / 32;
+__device__ __forceinline__ void store_slice(GemmSmem& s, const SliceRegs& r, SliceShape sh) {
 #pragma unroll
   for (int i = 0; i < SliceRegs::kA; ++i) {
-    const int u = (int)threadIdx.x + kPfThreads * i, m = u / aups, q = u - m * aups;
+    const int u = (int)threadIdx.x + kPfThreads * i, m = u >> sh.ash, q = u & ((1 << sh.ash) - 1);
     if (m < kTileTok) *reinterpret_cast<uint4*>(&s.act[m * kSlicePad + q * 8]) = r.av[i];
   }
 #pragma unroll
   for (int i = 0; i < SliceRegs::kW; ++i) {
-    const int u = (int)threadIdx.x + kPfThreads * i, lr = u / nch, q = u - lr * nch;
+    const int u = (int)threadIdx.x + kPfThreads * i, lr = u >> sh.nsh, q = u & ((1 << sh.nsh) - 1);
     if (lr < kWRows) {
       *reinterpret_cast<uint4*>(&s.wc[lr * kWStride + q * 16]) = r.wv[i];
       s.wsc[lr][q] = (uint16_t)r.sv[i];
@@ -428,14 +432,15 @@ __global__ __launch_bounds__(kPfThreads) void k_pf_gateup(PrefillArgs a) {
     return t >= 0 ? xsrc + (size_t)t * H : nullptr;
   };
   const auto wrow = [&](int r) { return r < kGuCols ? j0 + r : I + j0 + (r - kGuCols); };
+  const SliceShape shp = slice_shape(slice, a.g13);
   __syncthreads();   // the token list is written
   SliceRegs sr;
-  load_slice(sr, 0, slice, a.g13, codes, scales, xsrc, act_row, wrow);
+  load_slice(sr, 0, shp, a.g13, codes, scales, xsrc, act_row, wrow);
   for (int k0 = 0; k0 < H; k0 += slice) {
     __syncthreads();   // the previous slice is consumed
-    store_slice(s, sr, slice);
+    store_slice(s, sr, shp);
     __syncthreads();
-    if (k0 + slice < H) load_slice(sr, k0 + slice, slice, a.g13, codes, scales, xsrc, act_row, wrow);
+    if (k0 + slice < H) load_slice(sr, k0 + slice, shp, a.g13, codes, scales, xsrc, act_row, wrow);
     const int nq = slice / 32;
 #pragma unroll
     for (int q = 0; q < kChunks; ++q) {
@@ -485,13 +490,14 @@ __global__ __launch_bounds__(kPfThreads) void k_pf_down(PrefillArgs a) {
     return m < tr.nrows ? a.h + (size_t)(tr.row0 + m) * I : nullptr;
   };
   const auto wrow = [&](int r) { return n0 + r; };
+  const SliceShape shp = slice_shape(slice, a.g2);
   SliceRegs sr;
-  load_slice(sr, 0, slice, a.g2, codes, scales, a.h, act_row, wrow);
+  load_slice(sr, 0, shp, a.g2, codes, scales, a.h, act_row, wrow);
   for (int k0 = 0; k0 < I; k0 += slice) {
     __syncthreads();
-    store_slice(s, sr, slice);
+    store_slice(s, sr, shp);
     __syncthreads();
-    if (k0 + slice < I) load_slice(sr, k0 + slice, slice, a.g2, codes, scales, a.h, act_row, wrow);
+    if (k0 + slice < I) load_slice(sr, k0 + slice, shp, a.g2, codes, scales, a.h, act_row, wrow);
     const int nq = slice / 32;
 #pragma unroll
     for (int q = 0; q < kChunks; ++q) {
