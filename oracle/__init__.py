@@ -13,6 +13,8 @@ Modules
   layer    -- RMSNorm, router GEMV, the two routing rules, the SiLU-gated
               expert MLP and the weighted combine.
   dense    -- the small-batch dense NVFP4 GEMV y = x W^T.
+  codec2   -- the sign-symmetric 2-bit expert planes: decoding and the
+              re-quantisation from NVFP4.
 
 Every function cites the page passage it follows.  Readings adopted where
 the pages are silent are listed in the module docstrings.
@@ -27,6 +29,7 @@ from .formats import (  # noqa: F401
     e4m3_value,
     unpack_nibbles,
 )
+from .codec2 import dequant_2bit, nearest_codes, pack_2bit, requant_from_nvfp4, unpack_2bit  # noqa: F401
 from .dense import dense_gemv  # noqa: F401
 from .layer import (  # noqa: F401
     expert_mlp,

@@ -41,6 +41,7 @@ import math
 
 import numpy as np
 
+from .codec2 import dequant_2bit
 from .formats import bf16_bits_to_f64, dequant_bf16, dequant_nvfp4
 
 
@@ -154,6 +155,9 @@ def _dequant_expert(mats: dict, wtype: str):
     elif wtype == "bf16":
         w13 = dequant_bf16(mats["w13"])
         w2 = dequant_bf16(mats["w2"])
+    elif wtype == "2bit":
+        w13 = dequant_2bit(mats["codes13"], mats["scales13"], mats["g13"])
+        w2 = dequant_2bit(mats["codes2"], mats["scales2"], mats["g2"])
     else:
         raise ValueError(f"unknown weight type {wtype!r}")
     return w13, w2
@@ -163,7 +167,8 @@ def moe_layer(layer, x_bits, force_ids=None) -> dict:
     """Evaluate one MoE decode layer for a batch of tokens.
 
     ``layer`` supplies: hidden, inter, n_routed, top_k, n_shared, route
-    ("sigmoid" or "sink"), routed_wtype / shared_wtype ("nvfp4" or "bf16"),
+    ("sigmoid" or "sink"), routed_wtype / shared_wtype ("nvfp4", "bf16", or
+    for the routed set "2bit", the sign-symmetric planes of codec2),
     router_w (uint16 bf16 bits [E_r, H]), router_bias (float32 [E] or None),
     gamma (uint16 bf16 bits [H] or None), eps, residual (bool), and the
     accessors routed_expert(e) / shared_expert(s) returning the canonical
