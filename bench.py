@@ -55,7 +55,7 @@ def parse():
     p.add_argument("--steps", type=int, default=470)
     p.add_argument("--warmup", type=int, default=94)
     p.add_argument("--workload", default="flint_b1")
-    p.add_argument("--extra", default="flint_b8,flint_chain16_b1,dense_qkv_b1,dense_qkv_b8,flint_prefill_t1024,flint_prefill_t8192",
+    p.add_argument("--extra", default="flint_b8,flint_2bit_b1,flint_chain16_b1,dense_qkv_b1,dense_qkv_b8,flint_prefill_t1024,flint_prefill_t8192",
                    help="comma-separated extra workloads ('' for none)")
     p.add_argument("--all", action="store_true", help="also the BF16 and expert-sink workloads")
     p.add_argument("--slots", type=int, default=47)
@@ -76,6 +76,8 @@ def algorithmic_bytes(wl, d_routed: float, batch: int) -> dict:
     H, I = wl.hidden, wl.inter
 
     def expert(wtype):
+        if wtype == "2bit":
+            return {"w13": 2 * I * H // 4 + 2 * I * H // 16 + 4, "w2": H * I // 4 + H * I // 16 + 4}
         if wtype == "nvfp4":
             return {"w13": 2 * I * H // 2 + 2 * I * H // 16 + 4, "w2": H * I // 2 + H * I // 16 + 4}
         return {"w13": 2 * I * H * 2, "w2": H * I * 2}

@@ -74,7 +74,13 @@ typedef enum {
   MOE_ERR_STATE = -7        /* readback before any moe_decode_layer call on a handle  */
 } moe_status;
 
-typedef enum { MOE_W_NVFP4 = 0, MOE_W_BF16 = 1 } moe_wtype;
+/* MOE_W_2BIT: the SM120 page's sign-symmetric 2-bit expert planes ("How it fits - 2-bit
+ * experts at FP4 quality"): W = LEVEL[q] * e4m3 block-16 scale * fp32 tensor scale,
+ * LEVEL = {-4, -1, 1, 4} for q = 0..3; canonical codes uint8 [rows][cols/4], element 4j+i
+ * in bits 2i..2i+1 of byte j; scales and tensor scales as NVFP4.  Routed experts only,
+ * on the Flint shape at batch 1 (max_batch 1, NVFP4 shared expert, sigmoid routing);
+ * moe_requant_2bit makes the planes from NVFP4 experts.                                */
+typedef enum { MOE_W_NVFP4 = 0, MOE_W_BF16 = 1, MOE_W_2BIT = 2 } moe_wtype;
 
 /* The two expert sets of a layer.  The routed set lives in two buffers (moe_decode_layer's
  * expert_packed = its code region, scales = its scale region); the shared set in one
@@ -203,6 +209,19 @@ int moe_unpack_nvfp4(int rows, int cols, const uint8_t* codes_packed,
  * its inverse.  A permutation of 16-byte units.                                       */
 int moe_pack_bf16(int rows, int cols, const uint16_t* w, uint16_t* w_out);
 int moe_unpack_bf16(int rows, int cols, const uint16_t* w_packed, uint16_t* w);
+
+/* Re-quantises one canonical NVFP4 matrix [rows][cols] (codes uint8 [rows][cols/2],
+ * e4m3 scales [rows][cols/16]) to the 2-bit planes (codes2 uint8 [rows][cols/4], new
+ * e4m3 scales2 [rows][cols/16]); the matrix's fp32 tensor scale is kept.  SM120 page,
+ * "How it fits - 2-bit experts at FP4 quality": the sign-symmetric codebook {-4, -1, 1,
+ * 4}, re-quantised from NVFP4 after an exact float64 dequantisation.  Each 16-element
+ * block v (e2m1 x e4m3, exact in float64) gets the non-negative finite e4m3 scale s
+ * (bytes 0x00..0x7E) with the least sum over the block, in element order, of
+ * (v_i - LEVEL[q_i] s)^2, each q_i the nearest level (|v| = 2.5 s takes 1; the level's
+ * sign is v's sign bit); equal errors take the smaller scale.  Host only, no device
+ * access; cols % 16 == 0.                                                             */
+int moe_requant_2bit(int rows, int cols, const uint8_t* codes, const uint8_t* scales,
+                     uint8_t* codes2, uint8_t* scales2);
 
 /* ---- small-batch dense NVFP4 GEMV ---------------------------------------------------- */
 /* The Flint page ("From 1,096 kernels to 346") runs a small-batch dense GEMV on the same

@@ -19,10 +19,10 @@ LIB_PATH = os.path.join(_PKG, "libmoe_decode.so")
 MOE_OK = 0
 STATUS = {0: "MOE_OK", -1: "MOE_ERR_INVALID_ARG", -2: "MOE_ERR_UNSUPPORTED", -3: "MOE_ERR_ALIGNMENT",
           -4: "MOE_ERR_BATCH", -5: "MOE_ERR_LAUNCH", -6: "MOE_ERR_DEVICE", -7: "MOE_ERR_STATE"}
-MOE_W_NVFP4, MOE_W_BF16 = 0, 1
+MOE_W_NVFP4, MOE_W_BF16, MOE_W_2BIT = 0, 1, 2
 MOE_ROUTE_SIGMOID_TOPK, MOE_ROUTE_SOFTMAX_SINK = 0, 1
 MOE_SET_ROUTED, MOE_SET_SHARED = 0, 1
-WTYPES = {"nvfp4": MOE_W_NVFP4, "bf16": MOE_W_BF16}
+WTYPES = {"nvfp4": MOE_W_NVFP4, "bf16": MOE_W_BF16, "2bit": MOE_W_2BIT}
 ROUTES = {"sigmoid": MOE_ROUTE_SIGMOID_TOPK, "sink": MOE_ROUTE_SOFTMAX_SINK}
 
 EXPORTED = ("moe_abi_version", "moe_status_str", "moe_layer_validate", "moe_expert_layout_query",
@@ -32,7 +32,7 @@ EXPORTED = ("moe_abi_version", "moe_status_str", "moe_layer_validate", "moe_expe
             "moe_layer_routing",
             "moe_layer_set_profiling", "moe_layer_debug_h", "moe_layer_set_path", "moe_decode_chain", "moe_layer_error", "moe_layer_reset",
             "moe_layer_grid", "moe_dense_layout_query", "moe_pack_dense", "moe_unpack_dense",
-            "moe_dense_gemv", "moe_prefill_workspace_bytes", "moe_prefill_layer")
+            "moe_dense_gemv", "moe_prefill_workspace_bytes", "moe_prefill_layer", "moe_requant_2bit")
 
 
 BENCH_EXPORTED = ("moe_bench_read_stream", "moe_bench_fill", "moe_bench_empty")
@@ -109,6 +109,7 @@ def _load() -> C.CDLL:
         "moe_dense_gemv": ([i32, i32, vp, vp, vp, vp, i32, vp], i32),
         "moe_prefill_workspace_bytes": ([vp, i32, C.POINTER(sz)], i32),
         "moe_prefill_layer": ([vp, vp, vp, vp, vp, vp, vp, i32, vp, sz, vp, vp, vp], i32),
+        "moe_requant_2bit": ([i32, i32, vp, vp, vp, vp], i32),
     }
     sig.update({
         "moe_bench_read_stream": ([vp, sz, vp, vp], i32),
@@ -179,8 +180,9 @@ def moe_expert_layout_query(desc: "moe_layer_desc", set_: int = MOE_SET_ROUTED) 
 
 
 def _canon(ex: dict, wtype: str):
-    """Canonical arrays of one expert dict (codes13/scales13/codes2/scales2/g13/g2 or w13/w2)."""
-    if wtype == "nvfp4":
+    """Canonical arrays of one expert dict (codes13/scales13/codes2/scales2/g13/g2 for
+    NVFP4 and the 2-bit planes, or w13/w2)."""
+    if wtype in ("nvfp4", "2bit"):
         return (np.ascontiguousarray(ex["codes13"], np.uint8), np.ascontiguousarray(ex["scales13"], np.uint8),
                 np.ascontiguousarray(ex["codes2"], np.uint8), np.ascontiguousarray(ex["scales2"], np.uint8),
                 np.array([ex["g13"], ex["g2"]], np.float32))
@@ -195,8 +197,8 @@ def moe_pack_experts(desc: "moe_layer_desc", set_: int, first: int, experts: lis
                      scale_region=None) -> None:
     """Packs the expert dicts `experts` as experts first.. of one set of the layer
     `desc` describes into the set's host buffers (the library places every byte)."""
-    nv = _wtype_of(desc, set_) == MOE_W_NVFP4
-    parts = [_canon(ex, "nvfp4" if nv else "bf16") for ex in experts]
+    wt = _wtype_of(desc, set_)
+    parts = [_canon(ex, "bf16" if wt == MOE_W_BF16 else "nvfp4") for ex in experts]
     stack = [np.ascontiguousarray(np.stack([p[i] for p in parts])) if parts[0][i] is not None else None
              for i in range(5)]
     _check("moe_pack_experts", lib.moe_pack_experts(C.byref(desc), int(set_), first, len(experts),
@@ -207,9 +209,11 @@ def moe_unpack_experts(desc: "moe_layer_desc", set_: int, first: int, count: int
                        scale_region=None) -> list:
     """Inverse of moe_pack_experts: the canonical expert dicts of experts first..first+count-1."""
     H, I = desc.hidden, desc.inter
-    if _wtype_of(desc, set_) == MOE_W_NVFP4:
-        arrs = [np.empty((count, 2 * I, H // 2), np.uint8), np.empty((count, 2 * I, H // 16), np.uint8),
-                np.empty((count, H, I // 2), np.uint8), np.empty((count, H, I // 16), np.uint8),
+    wt = _wtype_of(desc, set_)
+    if wt != MOE_W_BF16:
+        per = 2 if wt == MOE_W_NVFP4 else 4        # codes per byte
+        arrs = [np.empty((count, 2 * I, H // per), np.uint8), np.empty((count, 2 * I, H // 16), np.uint8),
+                np.empty((count, H, I // per), np.uint8), np.empty((count, H, I // 16), np.uint8),
                 np.empty((count, 2), np.float32)]
     else:
         arrs = [np.empty((count, 2 * I, H), np.uint16), None, np.empty((count, H, I), np.uint16), None, None]
@@ -306,6 +310,18 @@ def moe_decode_chain(handles, x, router_w, expert_packed, scales, shared_w, out,
     hs = (C.c_void_p * n)(*handles)
     _check("moe_decode_chain", lib.moe_decode_chain(hs, n, _ptr(x), arr(router_w), arr(expert_packed), arr(scales),
                                                     arr(shared_w), _ptr(out), int(batch), _stream(stream)))
+
+
+def moe_requant_2bit(codes, scales):
+    """NVFP4 canonical (codes uint8 [R, K/2], e4m3 scales [R, K/16]) -> the 2-bit
+    planes (codes uint8 [R, K/4], e4m3 scales [R, K/16]), on the host."""
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.uint8)
+    R, K = codes.shape[0], 2 * codes.shape[1]
+    q = np.empty((R, K // 4), dtype=np.uint8)
+    s2 = np.empty((R, K // 16), dtype=np.uint8)
+    _check("moe_requant_2bit", lib.moe_requant_2bit(R, K, _ptr(codes), _ptr(scales), _ptr(q), _ptr(s2)))
+    return q, s2
 
 
 MOE_PREFILL_MAX_TOKENS = 65536

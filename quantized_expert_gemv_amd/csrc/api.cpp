@@ -7,6 +7,7 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <cmath>
 #include <mutex>
 #include <new>
 #include <vector>
@@ -40,7 +41,8 @@ int plan_shapes(const moe_layer_desc* d, Plan* p) {
   if (d == nullptr) return MOE_ERR_INVALID_ARG;
   const int H = d->hidden, I = d->inter, E = d->n_routed, k = d->top_k, S = d->n_shared;
   if (H <= 0 || I <= 0 || E <= 0 || k <= 0 || S < 0 || d->max_batch <= 0) return MOE_ERR_INVALID_ARG;
-  if (d->routed_wtype != MOE_W_NVFP4 && d->routed_wtype != MOE_W_BF16) return MOE_ERR_INVALID_ARG;
+  if (d->routed_wtype != MOE_W_NVFP4 && d->routed_wtype != MOE_W_BF16 && d->routed_wtype != MOE_W_2BIT)
+    return MOE_ERR_INVALID_ARG;
   if (d->shared_wtype != MOE_W_NVFP4 && d->shared_wtype != MOE_W_BF16) return MOE_ERR_INVALID_ARG;
   if (d->route != MOE_ROUTE_SIGMOID_TOPK && d->route != MOE_ROUTE_SOFTMAX_SINK) return MOE_ERR_INVALID_ARG;
   if (k > E) return MOE_ERR_INVALID_ARG;
@@ -65,6 +67,13 @@ int plan_shapes(const moe_layer_desc* d, Plan* p) {
   p->Er = Er;
   p->maxd = (d->max_batch * k < E) ? d->max_batch * k : E;
   p->G = 0;
+  // 2-bit routed experts run on the batch-1 kernel of the Flint shape only
+  if (d->routed_wtype == MOE_W_2BIT)
+    return (H == moe::FlintShape::H && I == moe::FlintShape::I && E == moe::FlintShape::E && k == moe::FlintShape::k &&
+            S == moe::FlintShape::S && d->shared_wtype == MOE_W_NVFP4 && d->route == MOE_ROUTE_SIGMOID_TOPK &&
+            d->max_batch == 1)
+               ? MOE_OK
+               : MOE_ERR_UNSUPPORTED;
   // a kernel variant must exist for every batch bucket the layer may run
   const int shape = moe::fixed_shape_of(H, I, E, k, S, Er, d->routed_wtype, d->shared_wtype);
   for (int tb = 1; tb <= p->tbmax; tb *= 2)
@@ -107,13 +116,18 @@ int layout(int wtype, int H, int I, int n, moe_expert_layout* o) {
   } else if (wtype == MOE_W_BF16) {
     o->w13_code_bytes = IH * 4;       // 2I * H * 2
     o->w2_code_bytes = IH * 2;
+  } else if (wtype == MOE_W_2BIT) {
+    o->w13_code_bytes = IH / 2;       // 2I * H / 4
+    o->w2_code_bytes = IH / 4;        // H * I / 4
+    o->w13_scale_bytes = IH / 8;
+    o->w2_scale_bytes = IH / 16;
   } else {
     return MOE_ERR_INVALID_ARG;
   }
   o->code_stride = o->w13_code_bytes + o->w2_code_bytes;
   o->code_region_bytes = o->code_stride * (size_t)n;
   o->scale_stride = o->w13_scale_bytes + o->w2_scale_bytes;
-  if (wtype == MOE_W_NVFP4) {
+  if (wtype == MOE_W_NVFP4 || wtype == MOE_W_2BIT) {
     o->tensor_scale_offset = align_up(o->scale_stride * (size_t)n, kAlign);
     o->scale_region_bytes = o->tensor_scale_offset + (size_t)n * 2 * sizeof(float);
   }
@@ -161,6 +175,27 @@ void move_nvfp4(const MatGeom& g, uint8_t* codes, uint8_t* scales, uint8_t* cp, 
           }
         }
 }
+// The 2-bit planes: the NVFP4 geometry with 8-byte code chunks (32 codes of
+// 2 bits, in canonical order) and the same scale words.
+template <bool PACK>
+void move_2bit(const MatGeom& g, uint8_t* codes, uint8_t* scales, uint8_t* cp, uint8_t* sp) {
+  const size_t crow = (size_t)g.cols / 4, srow = (size_t)g.cols / 16;
+  for (int s = 0; s < g.ns; ++s)
+    for (int t = 0; t < g.nsteps; ++t)
+      for (int ri = 0; ri < g.rpw; ++ri)
+        for (int j = 0; j < g.cw; ++j) {
+          const size_t row = (size_t)t * g.rpw + ri, cc = (size_t)s * g.cw + j;
+          uint8_t* pc = cp + moe::code_unit(g, s, t, ri, j) * 8;
+          uint8_t* ps = sp + moe::scale_word(g, s, t, ri, j) + 2 * (t & 1);
+          if (PACK) {
+            memcpy(pc, codes + row * crow + cc * 8, 8);
+            memcpy(ps, scales + row * srow + cc * 2, 2);
+          } else {
+            memcpy(codes + row * crow + cc * 8, pc, 8);
+            memcpy(scales + row * srow + cc * 2, ps, 2);
+          }
+        }
+}
 template <bool PACK>
 void move_bf16(const MatGeom& g, uint16_t* w, uint16_t* wp) {
   for (int s = 0; s < g.ns; ++s)
@@ -204,16 +239,23 @@ int move_experts(int wtype, int H, int I, int n, int first, int count, uint8_t* 
   if (int st = pack_geom(2 * I, H, &g13)) return st;
   if (int st = pack_geom(H, I, &g2)) return st;
   uint8_t* sreg = placement == 1 ? code_region + lay.shared_scale_offset : scale_region;
-  if (wtype == MOE_W_NVFP4 && (w13s == nullptr || w2s == nullptr || sreg == nullptr)) return MOE_ERR_INVALID_ARG;
+  const bool scaled = wtype == MOE_W_NVFP4 || wtype == MOE_W_2BIT;
+  if (scaled && (w13s == nullptr || w2s == nullptr || sreg == nullptr)) return MOE_ERR_INVALID_ARG;
   for (int i = 0; i < count; ++i) {
     const size_t e = (size_t)first + i;
     uint8_t* cb = code_region + e * lay.code_stride;
-    if (wtype == MOE_W_NVFP4) {
-      const size_t c13 = (size_t)2 * I * H / 2, s13 = (size_t)2 * I * H / 16;
-      const size_t c2 = (size_t)H * I / 2, s2 = (size_t)H * I / 16;
+    if (scaled) {
+      const size_t per = wtype == MOE_W_NVFP4 ? 2 : 4;   // codes per byte
+      const size_t c13 = (size_t)2 * I * H / per, s13 = (size_t)2 * I * H / 16;
+      const size_t c2 = (size_t)H * I / per, s2 = (size_t)H * I / 16;
       uint8_t* sb = sreg + e * lay.scale_stride;
-      move_nvfp4<PACK>(g13, w13 + i * c13, w13s + i * s13, cb, sb);
-      move_nvfp4<PACK>(g2, w2 + i * c2, w2s + i * s2, cb + lay.w13_code_bytes, sb + lay.w13_scale_bytes);
+      if (wtype == MOE_W_NVFP4) {
+        move_nvfp4<PACK>(g13, w13 + i * c13, w13s + i * s13, cb, sb);
+        move_nvfp4<PACK>(g2, w2 + i * c2, w2s + i * s2, cb + lay.w13_code_bytes, sb + lay.w13_scale_bytes);
+      } else {
+        move_2bit<PACK>(g13, w13 + i * c13, w13s + i * s13, cb, sb);
+        move_2bit<PACK>(g2, w2 + i * c2, w2s + i * s2, cb + lay.w13_code_bytes, sb + lay.w13_scale_bytes);
+      }
       float* tp = reinterpret_cast<float*>(sreg + lay.tensor_scale_offset) + 2 * e;
       if (PACK) {
         tp[0] = ts ? ts[2 * i] : 1.0f;
@@ -334,8 +376,18 @@ int plan_device(const moe_layer_desc* desc, Plan* pp, int device) {
     (void)hipGetLastError();
     return MOE_ERR_DEVICE;
   }
-  int cap = p.Er < cus ? p.Er : cus;
   const int rwt = desc->routed_wtype, swt = desc->shared_wtype;
+  if (rwt == MOE_W_2BIT) {
+    // only the batch-1 kernel takes 2-bit routed experts
+    p.b8 = 0;
+    int occ1 = 0;
+    p.b1 = cus >= moe::kB1Workgroups && moe::b1_occupancy(&occ1) == 0 && occ1 >= 1;
+    (void)hipGetLastError();
+    if (!p.b1) return MOE_ERR_UNSUPPORTED;
+    plan_grid(desc, &p, moe::kB1Workgroups);
+    return MOE_OK;
+  }
+  int cap = p.Er < cus ? p.Er : cus;
   int G = 1;
   while (2 * G <= cap) G *= 2;
   plan_grid(desc, &p, G);
@@ -507,6 +559,61 @@ int moe_unpack_bf16(int rows, int cols, const uint16_t* w_packed, uint16_t* w) {
   return MOE_OK;
 }
 
+int moe_requant_2bit(int rows, int cols, const uint8_t* codes, const uint8_t* scales, uint8_t* codes2,
+                     uint8_t* scales2) {
+#pragma clang fp contract(off)
+  if (!codes || !scales || !codes2 || !scales2 || rows <= 0 || cols <= 0 || cols % 16) return MOE_ERR_INVALID_ARG;
+  static const double kE2m1[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
+  static const double kLevel[4] = {-4.0, -1.0, 1.0, 4.0};
+  const auto e4m3 = [](int b) {
+    const int e = (b >> 3) & 15, m = b & 7;
+    const double mag = e == 0 ? ldexp((double)m, -9) : ldexp(8.0 + m, e - 10);
+    return (b & 0x80) ? -mag : mag;
+  };
+  double cand[0x7F];
+  for (int sb = 0; sb < 0x7F; ++sb) cand[sb] = e4m3(sb);
+  const size_t nb = (size_t)cols / 16;
+  for (size_t r = 0; r < (size_t)rows; ++r) {
+    for (size_t b = 0; b < nb; ++b) {
+      double v[16];
+      const double bs = e4m3(scales[r * nb + b]);
+      for (int i = 0; i < 16; ++i) {
+        const size_t c = b * 16 + i;
+        const int code = (codes[r * (cols / 2) + c / 2] >> (4 * (c & 1))) & 15;
+        const double m = (code & 8) ? -kE2m1[code & 7] : kE2m1[code & 7];
+        v[i] = m * bs;
+      }
+      double best = INFINITY;
+      int best_sb = 0;
+      uint8_t best_q[16] = {0};
+      for (int sb = 0; sb < 0x7F; ++sb) {
+        const double sc = cand[sb];
+        uint8_t q[16];
+        double err = 0.0;
+        for (int i = 0; i < 16; ++i) {
+          const bool neg = std::signbit(v[i]);
+          const bool big = sc > 0.0 && 2.0 * fabs(v[i]) > 5.0 * sc;
+          q[i] = neg ? (big ? 0 : 1) : (big ? 3 : 2);
+          const double rec = kLevel[q[i]] * sc;
+          const double d = v[i] - rec;
+          const double dd = d * d;
+          err = err + dd;
+        }
+        if (err < best) {
+          best = err;
+          best_sb = sb;
+          memcpy(best_q, q, 16);
+        }
+      }
+      scales2[r * nb + b] = (uint8_t)best_sb;
+      for (int j = 0; j < 4; ++j)
+        codes2[r * (cols / 4) + b * 4 + j] =
+            (uint8_t)(best_q[4 * j] | (best_q[4 * j + 1] << 2) | (best_q[4 * j + 2] << 4) | (best_q[4 * j + 3] << 6));
+    }
+  }
+  return MOE_OK;
+}
+
 int moe_pack_experts(const moe_layer_desc* desc, int set, int first, int count, const void* w13,
                      const void* w13_scales, const void* w2, const void* w2_scales, const float* tensor_scales,
                      void* region, void* scale_region) {
@@ -592,7 +699,7 @@ moe::FusedArgs make_args(const moe_layer* L, const void* x, const void* router_w
   a.gamma = static_cast<const uint16_t*>(d.prenorm_gamma);
   a.r_codes = static_cast<const uint8_t*>(expert_packed);
   a.r_scales = static_cast<const uint8_t*>(scales);
-  a.r_tscale = (d.routed_wtype == MOE_W_NVFP4 && scales)
+  a.r_tscale = ((d.routed_wtype == MOE_W_NVFP4 || d.routed_wtype == MOE_W_2BIT) && scales)
                    ? reinterpret_cast<const float*>(static_cast<const uint8_t*>(scales) + L->lr.tensor_scale_offset)
                    : nullptr;
   a.s_codes = static_cast<const uint8_t*>(shared_w);
@@ -650,6 +757,7 @@ int launch_layer(const moe_layer* L, const moe::FusedArgs& a, void* stream) {
       b.xx = L->xx;
       b.n = 1;
       b.L[0] = moe::chain_layer_of(a);
+      b.r2bit = L->d.routed_wtype == MOE_W_2BIT;
       return moe::launch_b1(b, stream);
     }
     if (a.B >= 2 && L->p.b8) return moe::launch_b8(a, a.B, stream);
@@ -662,7 +770,7 @@ int check_call(const moe_layer_desc& d, const void* x, const void* router_w, con
                const void* scales, const void* shared_w, const void* out, int batch) {
   if (batch < 1 || batch > d.max_batch) return MOE_ERR_BATCH;
   if (!x || !router_w || !expert_packed || !out) return MOE_ERR_INVALID_ARG;
-  if (d.routed_wtype == MOE_W_NVFP4 && !scales) return MOE_ERR_INVALID_ARG;
+  if ((d.routed_wtype == MOE_W_NVFP4 || d.routed_wtype == MOE_W_2BIT) && !scales) return MOE_ERR_INVALID_ARG;
   if (d.n_shared > 0 && !shared_w) return MOE_ERR_INVALID_ARG;
   if (x == out) return MOE_ERR_INVALID_ARG;
   if (!aligned16(x) || !aligned16(router_w) || !aligned16(expert_packed) || !aligned16(out) ||
@@ -920,7 +1028,9 @@ int moe_decode_chain(const moe_layer_t* layers, int n_layers, const void* x, con
   if (batch != 1) return MOE_ERR_UNSUPPORTED;
   if (!L0->p.b1 || L0->force_general) return MOE_ERR_UNSUPPORTED;
   const moe_layer_desc& d0 = L0->d;
+  if (d0.routed_wtype != MOE_W_NVFP4) return MOE_ERR_UNSUPPORTED;   // the chain kernel reads NVFP4 experts
   moe::B1Args b;
+  b.r2bit = 0;
   b.xx = L0->xx;
   b.n = n_layers;
   for (int l = 0; l < n_layers; ++l) {
@@ -943,6 +1053,7 @@ int moe_decode_chain(const moe_layer_t* layers, int n_layers, const void* x, con
 
 int moe_layer_set_path(moe_layer_t L, int path, int* active) {
   if (L == nullptr || (path != MOE_PATH_AUTO && path != MOE_PATH_GENERAL)) return MOE_ERR_INVALID_ARG;
+  if (path == MOE_PATH_GENERAL && L->d.routed_wtype == MOE_W_2BIT) return MOE_ERR_UNSUPPORTED;   // no general kernel
   L->force_general = path == MOE_PATH_GENERAL;
   if (active) *active = ((L->p.b1 || L->p.b8) && !L->force_general) ? MOE_PATH_DEDICATED : MOE_PATH_GENERAL;
   return MOE_OK;

@@ -100,6 +100,27 @@ __device__ __forceinline__ uint32_t tag_at(uint32_t t0, int l) {
   return t;
 }
 
+// One 8-byte chunk of the 2-bit planes (32 codes, element k in bits 2k,
+// 2k+1) as the 16-byte e2m1 chunk of the same values: code q -> nibble
+// {-4, -1, 1, 4} = {0xE, 0xA, 0x2, 0x6}, i.e. 0b0010 with bit 3 = NOT q1 and
+// bit 2 = (q0 == q1).  The 2-bit fields are first spread to nibbles.
+__device__ __forceinline__ uint32_t widen_2bit_half(uint32_t h) {
+  uint32_t x = h & 0xFFFFu;
+  x = (x | (x << 8)) & 0x00FF00FFu;
+  x = (x | (x << 4)) & 0x0F0F0F0Fu;
+  x = (x | (x << 2)) & 0x33333333u;
+  const uint32_t b0 = x & 0x11111111u, b1 = (x >> 1) & 0x11111111u;
+  return 0x22222222u | ((b1 ^ 0x11111111u) << 3) | ((~(b0 ^ b1) & 0x11111111u) << 2);
+}
+__device__ __forceinline__ uint4 widen_2bit(const uint2& v) {
+  return make_uint4(widen_2bit_half(v.x), widen_2bit_half(v.x >> 16), widen_2bit_half(v.y), widen_2bit_half(v.y >> 16));
+}
+__device__ __forceinline__ uint2 ld8o(const uint8_t* base, uint32_t off) {
+  typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+  const u32x2_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(base + off));
+  return make_uint2(v.x, v.y);
+}
+
 // Shared-memory position of 16-byte unit q of 64-byte chunk c: the units a
 // wave reads in one instruction (one per chunk, same q) fall in distinct banks.
 __device__ __forceinline__ int unit_pos(int c, int q) { return (c << 2) | (q ^ ((c >> 2) & 3)); }
@@ -317,7 +338,7 @@ __device__ __forceinline__ void control(const B1ArgsT<NMAX>& args, B1Smem& s, in
 // gate 2w + 1, up 2w, up 2w + 1), chunks (lane % 16) + 16 i, i < 4, of 32
 // columns.  Down: lane = (row ri of the step's 4, 32-column chunk jj), steps
 // 2w and 2w + 1, whose block scales share one word per lane.
-template <int NMAX>
+template <int NMAX, bool R2>
 __device__ __forceinline__ void item(const B1ArgsT<NMAX>& args, B1Smem& s, int w, int m, int lane, u64 deadline) {
   const KCommon& a = args.a;
   const int n = NMAX == 1 ? 1 : args.n;
@@ -355,21 +376,34 @@ __device__ __forceinline__ void item(const B1ArgsT<NMAX>& args, B1Smem& s, int w
       w2s = (uint32_t)a.r_w13_scale;
     }
     // the tensor scales first, then the gate/up rows, then the down rows:
-    // each wait below is for the oldest loads only
+    // each wait below is for the oldest loads only.  A routed expert in the
+    // 2-bit planes has 8-byte chunks at half the offsets (the same scales);
+    // they are widened to e2m1 once they are in.
+    const bool two = R2 && m > 0;
     const float ts13 = tsp[0], ts2 = tsp[1];
-    uint4 c[4];
+    uint4 c[4], d[2];
+    uint2 c8[4], d8[2];
     uint32_t sw[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      c[i] = ld16o(cb, off_c + 256u * i);
+      if (two) c8[i] = ld8o(cb, (off_c >> 1) + 128u * i);
+      else c[i] = ld16o(cb, off_c + 256u * i);
       sw[i] = ld32o(sb, off_s + 64u * i);
     }
-    uint4 d[2];
 #pragma unroll
-    for (int st = 0; st < 2; ++st) d[st] = ld16o(cb + w2c, dn_c + kStepBytes2 * st);
+    for (int st = 0; st < 2; ++st) {
+      if (two) d8[st] = ld8o(cb + w2c, (dn_c >> 1) + (kStepBytes2 / 2) * st);
+      else d[st] = ld16o(cb + w2c, dn_c + kStepBytes2 * st);
+    }
     const uint32_t dsw = ld32o(sb + w2s, dn_s);
     // gate/up: four chunks per lane, then the row sums of 16 lanes
     lds_wait(&s.x_ready, l + 1, deadline, a.err);
+    if (two) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) c[i] = widen_2bit(c8[i]);
+#pragma unroll
+      for (int st = 0; st < 2; ++st) d[st] = widen_2bit(d8[st]);
+    }
     uint32_t xk[4][16], sp[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -446,7 +480,7 @@ __device__ __forceinline__ void item(const B1ArgsT<NMAX>& args, B1Smem& s, int w
   }
 }
 
-template <int NMAX>
+template <int NMAX, bool R2>
 __global__ __launch_bounds__(kB1Threads) void k_b1_layer(B1ArgsT<NMAX> args) {
   __shared__ B1Smem s;
   const int wave = wave_id(), lane = (int)threadIdx.x & 63;
@@ -460,13 +494,13 @@ __global__ __launch_bounds__(kB1Threads) void k_b1_layer(B1ArgsT<NMAX> args) {
   __syncthreads();
   const u64 deadline = clock100() + args.a.wait_ticks;
   if (wave == 0) control(args, s, w, lane, deadline);
-  else item(args, s, w, wave - 1, lane, deadline);
+  else item<NMAX, R2>(args, s, w, wave - 1, lane, deadline);
 }
 
 }  // namespace
 
 int launch_b1(const B1Args& a, void* stream) {
-  if (a.n < 1 || a.n > kMaxChain) return (int)hipErrorInvalidValue;
+  if (a.n < 1 || a.n > kMaxChain || (a.r2bit && a.n != 1)) return (int)hipErrorInvalidValue;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   (void)hipGetLastError();
   if (a.n == 1) {
@@ -475,26 +509,30 @@ int launch_b1(const B1Args& a, void* stream) {
     one.xx = a.xx;
     one.n = 1;
     one.L[0] = a.L[0];
-    hipLaunchKernelGGL(k_b1_layer<1>, dim3(256), dim3(kB1Threads), 0, st, one);
+    if (a.r2bit) hipLaunchKernelGGL((k_b1_layer<1, true>), dim3(256), dim3(kB1Threads), 0, st, one);
+    else hipLaunchKernelGGL((k_b1_layer<1, false>), dim3(256), dim3(kB1Threads), 0, st, one);
   } else {
     B1ArgsT<kMaxChain> all;
     all.a = a.a;
     all.xx = a.xx;
     all.n = a.n;
     for (int l = 0; l < kMaxChain; ++l) all.L[l] = a.L[l];
-    hipLaunchKernelGGL(k_b1_layer<kMaxChain>, dim3(256), dim3(kB1Threads), 0, st, all);
+    hipLaunchKernelGGL((k_b1_layer<kMaxChain, false>), dim3(256), dim3(kB1Threads), 0, st, all);
   }
   return (int)hipGetLastError();
 }
 
 int b1_occupancy(int* blocks_per_cu) {
-  int one = 0, all = 0;
-  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&one, reinterpret_cast<const void*>(&k_b1_layer<1>),
-                                                              kB1Threads, 0);
+  int one = 0, two = 0, all = 0;
+  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+      &one, reinterpret_cast<const void*>(&k_b1_layer<1, false>), kB1Threads, 0);
   if (e == hipSuccess)
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&all, reinterpret_cast<const void*>(&k_b1_layer<kMaxChain>),
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&two, reinterpret_cast<const void*>(&k_b1_layer<1, true>),
                                                      kB1Threads, 0);
-  *blocks_per_cu = one < all ? one : all;
+  if (e == hipSuccess)
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+        &all, reinterpret_cast<const void*>(&k_b1_layer<kMaxChain, false>), kB1Threads, 0);
+  *blocks_per_cu = one < all ? (one < two ? one : two) : (all < two ? all : two);
   return (int)e;
 }
 

@@ -265,6 +265,7 @@ struct B1Args {
   KCommon a;                   // the call's common fields: x, out, workspace, strides, wait bound
   unsigned long long* xx;      // [H / 2] tagged words: a layer's output, the next layer's input
   int n;                       // layers
+  int r2bit;                   // routed experts in the 2-bit planes (single layer only)
   ChainLayer L[kMaxChain];
 };
 // The layer fields of a's single layer as a chain entry.

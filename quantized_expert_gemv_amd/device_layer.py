@@ -61,7 +61,7 @@ class DeviceLayer:
                                 rms_eps=layer.eps, add_residual=layer.residual)
         codes, scales, self.layout_r = pack_expert_set(self.desc, B.MOE_SET_ROUTED, layer.routed_expert, E)
         self.expert_packed = torch.from_numpy(codes).to(self.device)
-        self.scales = torch.from_numpy(scales).to(self.device) if layer.routed_wtype == "nvfp4" else None
+        self.scales = torch.from_numpy(scales).to(self.device) if layer.routed_wtype != "bf16" else None
         del codes, scales
         if S > 0:
             blob, _, self.layout_s = pack_expert_set(self.desc, B.MOE_SET_SHARED, layer.shared_expert, S)

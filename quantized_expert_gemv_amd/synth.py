@@ -48,7 +48,7 @@ class Workload:
     n_shared: int
     batch: int
     route: str = "sigmoid"            # "sigmoid" | "sink"
-    routed_wtype: str = "nvfp4"       # "nvfp4" | "bf16"
+    routed_wtype: str = "nvfp4"       # "nvfp4" | "bf16" | "2bit"
     shared_wtype: str = "nvfp4"
     router_std: float = 0.02          # None -> 1/sqrt(hidden)
     bias_std: float | None = None     # per-expert router bias, fp32
@@ -76,6 +76,9 @@ WORKLOADS = {
     "flint_chain": Workload(5, "flint_chain", 2048, 512, 256, 6, 1, 1,
                             prenorm=True,
                             description="Flint-shaped NVFP4 layer with pre-norm RMSNorm and residual, b1"),
+    "flint_2bit_b1": Workload(10, "flint_2bit_b1", 2048, 512, 256, 6, 1, 1, routed_wtype="2bit",
+                              description="Flint-shaped: H=2048 I=512 E=256 top-6, routed experts in 2-bit "
+                                          "sign-symmetric planes, 1 NVFP4 shared, b1"),
     "sink_b4": Workload(4, "sink_b4", 7168, 2048, 256, 6, 2, 4,
                         route="sink", shared_wtype="bf16",
                         description="expert sink: H=7168 I=2048 E=256 NVFP4 top-6 + 2 BF16 shared in a 258-way softmax, b4"),
@@ -183,6 +186,26 @@ class SynthLayer:
             "g2": self._tscale(index, 1),
         }
 
+    def _2bit_expert(self, index: int) -> dict:
+        """The sign-symmetric 2-bit planes: codes uniform over the four levels,
+        e4m3 block scales drawn as for NVFP4."""
+        wl, H, I = self.wl, self.hidden, self.inter
+        w = wl.wid
+
+        def scales(tid, shape):
+            a = np.abs(_rng(w, self.slot, tid, index).standard_normal(size=shape, dtype=np.float32))
+            a *= np.float32(wl.scale_mult)
+            return to_e4m3_bytes(a)
+
+        return {
+            "codes13": _rng(w, self.slot, _T_CODES13, index).integers(0, 256, size=(2 * I, H // 4), dtype=np.uint8),
+            "scales13": scales(_T_SCALES13, (2 * I, H // 16)),
+            "codes2": _rng(w, self.slot, _T_CODES2, index).integers(0, 256, size=(H, I // 4), dtype=np.uint8),
+            "scales2": scales(_T_SCALES2, (H, I // 16)),
+            "g13": self._tscale(index, 0),
+            "g2": self._tscale(index, 1),
+        }
+
     def _tscale(self, index: int, which: int) -> np.float32:
         if self.tscale_set is None:
             return np.float32(1.0)
@@ -208,6 +231,8 @@ class SynthLayer:
     def routed_expert(self, e: int) -> dict:
         if not 0 <= e < self.n_routed:
             raise IndexError(e)
+        if self.routed_wtype == "2bit":
+            return self._2bit_expert(e)
         return (self._nvfp4_expert(e) if self.routed_wtype == "nvfp4"
                 else self._bf16_expert(e))
 

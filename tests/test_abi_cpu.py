@@ -283,3 +283,61 @@ def test_dense_gemv_rejects_without_a_device_call():
     assert B.lib.moe_dense_gemv(64, 64, p, p, p, p + 128, 9, None) == -4
     assert B.lib.moe_dense_gemv(64, 64, p, p, p, p + 128, 0, None) == -4
     assert B.lib.moe_dense_gemv(64, 64, p + 1, p, p, p + 128, 1, None) == -3
+
+
+# ---- the 2-bit expert planes (host side) -----------------------------------------------------
+
+@pytest.mark.parametrize("seed,rows,cols", [(0, 8, 64), (1, 3, 256), (2, 16, 2048)])
+def test_library_requant_matches_the_oracle_bit_for_bit(seed, rows, cols):
+    """moe_requant_2bit (C++, float64 with no fused multiply-adds) against the
+    oracle's re-quantisation: the same scale bytes and codes, every block."""
+    import oracle
+    rng = np.random.default_rng(seed)
+    codes = rng.integers(0, 256, size=(rows, cols // 2), dtype=np.uint8)
+    scales = rng.integers(0x00, 0x7F, size=(rows, cols // 16), dtype=np.uint8)
+    scales[0, 0] = 0x00                                           # a zero block scale
+    q_lib, s_lib = B.moe_requant_2bit(codes, scales)
+    q_ref, s_ref = oracle.requant_from_nvfp4(codes, scales)
+    assert np.array_equal(s_lib, s_ref)
+    assert np.array_equal(q_lib, q_ref)
+
+
+def test_requant_argument_checks():
+    assert B.lib.moe_requant_2bit(1, 24, None, None, None, None) == -1
+    z = np.zeros(64, np.uint8)
+    assert B.lib.moe_requant_2bit(1, 24, B._ptr(z), B._ptr(z), B._ptr(z), B._ptr(z)) == -1   # cols % 16
+
+
+def test_2bit_layer_validation_rules():
+    """2-bit routed experts: the Flint shape at batch 1 with an NVFP4 shared
+    expert and sigmoid routing; anything else is unsupported."""
+    flint = dict(hidden=2048, inter=512, n_routed=256, top_k=6, n_shared=1, routed_wtype="2bit")
+    assert B.moe_layer_validate(B.make_desc(max_batch=1, **flint)) == 0
+    assert B.moe_layer_validate(B.make_desc(max_batch=2, **flint)) == -2
+    assert B.moe_layer_validate(B.make_desc(max_batch=1, shared_wtype="bf16", **flint)) == -2
+    assert B.moe_layer_validate(B.make_desc(max_batch=1, route="sink", **flint)) == -2
+    assert B.moe_layer_validate(B.make_desc(hidden=1024, inter=256, n_routed=64, top_k=4, n_shared=1, max_batch=1,
+                                            routed_wtype="2bit")) == -2
+
+
+def test_2bit_expert_pack_round_trip_and_layout():
+    d = B.make_desc(hidden=2048, inter=512, n_routed=256, top_k=6, n_shared=1, max_batch=1, routed_wtype="2bit")
+    lay = B.moe_expert_layout_query(d, B.MOE_SET_ROUTED)
+    assert lay["w13_code_bytes"] == 2 * 512 * 2048 // 4 and lay["w2_code_bytes"] == 2048 * 512 // 4
+    assert lay["w13_scale_bytes"] == 2 * 512 * 2048 // 16 and lay["w2_scale_bytes"] == 2048 * 512 // 16
+    rng = np.random.default_rng(4)
+    ex = {"codes13": rng.integers(0, 256, size=(1024, 512), dtype=np.uint8),
+          "scales13": rng.integers(0, 256, size=(1024, 128), dtype=np.uint8),
+          "codes2": rng.integers(0, 256, size=(2048, 128), dtype=np.uint8),
+          "scales2": rng.integers(0, 256, size=(2048, 32), dtype=np.uint8),
+          "g13": np.float32(0.7), "g2": np.float32(1.3)}
+    code = np.zeros(lay["code_region_bytes"], np.uint8)
+    scale = np.zeros(lay["scale_region_bytes"], np.uint8)
+    B.moe_pack_experts(d, B.MOE_SET_ROUTED, 5, [ex], code, scale)
+    back = B.moe_unpack_experts(d, B.MOE_SET_ROUTED, 5, 1, code, scale)[0]
+    for k in ("codes13", "scales13", "codes2", "scales2"):
+        assert np.array_equal(back[k], ex[k]), k
+    assert back["g13"] == np.float32(0.7) and back["g2"] == np.float32(1.3)
+    # the packed chunk (row r, 32-column chunk j) of W13 is the row's canonical bytes 8 j .. 8 j + 8
+    base = 5 * lay["code_stride"]
+    assert np.array_equal(code[base + (3 * 64 + 7) * 8: base + (3 * 64 + 7) * 8 + 8], ex["codes13"][3, 56:64])
