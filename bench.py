@@ -8,12 +8,16 @@ batch of seeded synthetic tokens.  Weights stay cold: the layer is copied
 into L distinct device slots (47 by default, one per MoE layer of the Flint
 model) and step i uses slot i % L with its own input.  One cycle over the
 slots (~631 MB at batch 1) exceeds the 256 MB Infinity Cache plus the 32 MB
-of L2, and a 1 GiB write pass runs right before the timed region, so every
-timed step reads its weights from HBM whatever K is.
+of L2, and a 1 GiB read pass runs before the timed region.
 
-Timed region: W eager warm-up steps, then a HIP graph of exactly the K steps
-(W + i) % L, replayed once between HIP events on the stream the kernels run
-on, after the write pass.  A step is one launch and replayed launches run
+Timed region: W eager warm-up steps and one untimed launch of each graph
+below (a graph's first launch also uploads it); then, after the read pass, one
+untimed replay of a graph of the L steps 0 .. L-1 and right behind it a HIP
+graph of exactly the K steps (W + i) % L, replayed once between HIP events on
+the stream the kernels run on.  The untimed cycle leaves the page translations
+and caches as a running model leaves them; each timed step's weights were
+last touched about L - W steps (over 500 MB of other weights) earlier, so
+they come from HBM whatever K is.  A step is one launch and replayed launches run
 back to back, so the region's time per step is the layer kernel's average
 launch duration (the roofline figure uses it).  Also reported:
   * replays: a graph of one full cycle of L steps replayed R times, each
@@ -212,9 +216,13 @@ def measure(name: str, K: int, W: int, L: int, R: int, flush) -> dict:
         return g
 
     gK = capture(W, K)
+    gL = capture(0, L)
+    gK.replay()                   # each graph's first launch uploads it: keep that out of the timed region
+    gL.replay()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    flush()
     torch.cuda.synchronize()
+    flush()
+    gL.replay()                   # one untimed cycle over the slots, then the timed steps right behind it
     ev0.record(stream)
     gK.replay()
     ev1.record(stream)
@@ -223,7 +231,6 @@ def measure(name: str, K: int, W: int, L: int, R: int, flush) -> dict:
     del gK
     log(f"timed {K} steps (hipgraph, cold): {us_step:.3f} us/step")
 
-    gL = capture(0, L)
     gL.replay()
     torch.cuda.synchronize()
     per = []
@@ -314,16 +321,19 @@ def measure_dense(name: str, K: int, W: int, L: int, R: int, flush) -> dict:
         return g
 
     gK = capture(W, K)
+    gL = capture(0, L)
+    gK.replay()                   # each graph's first launch uploads it: keep that out of the timed region
+    gL.replay()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    flush()
     torch.cuda.synchronize()
+    flush()
+    gL.replay()                   # one untimed cycle over the slots, then the timed steps right behind it
     ev0.record(stream)
     gK.replay()
     ev1.record(stream)
     torch.cuda.synchronize()
     us = ev0.elapsed_time(ev1) * 1e3 / K
     del gK
-    gL = capture(0, L)
     gL.replay()
     torch.cuda.synchronize()
     per = []
@@ -403,16 +413,19 @@ def measure_chain(name: str, K: int, W: int, L: int, R: int, flush) -> dict:
 
     Kc = max(1, K // n)                   # about K layers in the timed region
     gK = capture(W, Kc)
+    gL = capture(0, groups)
+    gK.replay()                   # each graph's first launch uploads it: keep that out of the timed region
+    gL.replay()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    flush()
     torch.cuda.synchronize()
+    flush()
+    gL.replay()                   # one untimed cycle over the slots, then the timed chains right behind it
     ev0.record(stream)
     gK.replay()
     ev1.record(stream)
     torch.cuda.synchronize()
     us_chain = ev0.elapsed_time(ev1) * 1e3 / Kc
     del gK
-    gL = capture(0, groups)
     gL.replay()
     torch.cuda.synchronize()
     per = []
@@ -493,7 +506,7 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 matrix peak
 def measure_prefill(name: str, K: int, W: int, R: int, flush) -> dict:
     """Prefill calls over two device copies of the layer (a call touches every
     expert: ~453 MB, above the 256 MB Infinity Cache), timed as a graph of K
-    calls between HIP events after the write pass."""
+    calls between HIP events after the read pass."""
     import torch
     from quantized_expert_gemv_amd import binding as B
     from quantized_expert_gemv_amd.device_layer import DeviceLayer, bits_to_bf16_tensor
@@ -536,11 +549,12 @@ def measure_prefill(name: str, K: int, W: int, R: int, flush) -> dict:
                 step(i)
     stream.wait_stream(cap)
     torch.cuda.synchronize()
+    g.replay()                        # the graph's first launch uploads it
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     per = []
     for _ in range(R):
-        flush()
         torch.cuda.synchronize()
+        flush()                       # queued ahead of the timed calls: they start as it ends
         ev0.record(stream)
         g.replay()
         ev1.record(stream)
@@ -568,7 +582,7 @@ def measure_prefill(name: str, K: int, W: int, R: int, flush) -> dict:
             "us_per_call": round(us, 2), "tokens_per_s": round(T / (us * 1e-6), 1), "tflops": round(tfs, 2),
             "gbs": round(gbs, 1), "bound": bound, "roofline_frac": round(frac, 4),
             "flops_per_call": flops, "algorithmic_bytes_per_call": int(round(lay["total"])),
-            "distinct_routed": d, "timing": f"graph of {K} calls over 2 weight copies, after the write pass, "
+            "distinct_routed": d, "timing": f"graph of {K} calls over 2 weight copies, after the read pass, "
                                             f"p50 of {R} replays", "workspace_bytes": need}
 
 
@@ -585,9 +599,14 @@ def main():
     dev_name = torch.cuda.get_device_name(0)
     log(f"device {dev_name}")
     flush_buf = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    B.moe_bench_fill(flush_buf, 0x5a5a5a5a)
+    flush_sink = torch.zeros(16, dtype=torch.int32, device="cuda")
 
     def flush():
-        B.moe_bench_fill(flush_buf, 0x5a5a5a5a)
+        # a 1 GiB read pass: it evicts the weights from the L2s and the
+        # Infinity Cache and, unlike a write pass, leaves no dirty lines whose
+        # write-back would run during the timed steps
+        B.moe_bench_read_stream(flush_buf, flush_sink)
 
     K, W = args.steps, args.warmup
     head, layer, xs_bits = measure(args.workload, K, W, SLOTS.get(args.workload, args.slots), args.replays, flush)
