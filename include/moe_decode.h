@@ -290,7 +290,7 @@ int moe_layer_destroy(moe_layer_t layer);
  * selected experts' gate/up GEMV with SiLU*up, and the down GEMV of every selected and
  * shared expert with the weighted, fixed-order combine (+ residual).  The Flint page
  * ("From 1,096 kernels to 346") fuses routing and the combine into the neighbouring
- * GEMVs and reads only the selected experts' weights; this call does the same in one
+ * GEMVs, and no expert outside the top-k has its bytes fetched; this call does the same in one
  * launch.  Deterministic: no floating-point atomics; the result does not depend on
  * scheduling.  Every cross-workgroup wait is bounded (0.2 s): if the grid cannot be
  * resident at once (for example another such call of a different handle runs

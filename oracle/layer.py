@@ -8,7 +8,7 @@ Sources
     experts with sigmoid top-6 routing plus one shared expert; weight-only
     NVFP4 with BF16 activations.
   * same page, section "From 1,096 kernels to 346": the router and expert
-    GEMVs read only the selected experts' weights; routing and the expert
+    GEMVs fetch no bytes of experts outside the top-k; routing and the expert
     combine sit next to the GEMVs.
   * "TML Inkling on vLLM ...", section "Model Architecture" (MoE paragraph):
     the two shared experts take part in the routing-score computation and

@@ -5,7 +5,7 @@
 // 2048, 256 routed experts of intermediate 512, sigmoid top-6 plus one shared
 // expert; NVFP4 weights, bf16 activations) at batch B reads the union of the
 // tokens' selected experts once (Flint page, "From 1,096 kernels to 346": the
-// MoE path reads only the selected experts' weights).  Workgroup w owns
+// weight bytes of experts nobody chose are never fetched).  Workgroup w owns
 // gate/up rows 2w, 2w + 1 (and the matching up rows) and down rows
 // [8w, 8w + 8) of every expert in the union.
 //
