@@ -152,6 +152,9 @@ def _stream(stream) -> int | None:
 
 # ---- host-only entry points ---------------------------------------------------------
 
+ABI_VERSION = 4   # MOE_ABI_VERSION of the header these wrappers follow
+
+
 def moe_abi_version() -> int:
     return lib.moe_abi_version()
 

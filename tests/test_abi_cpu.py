@@ -40,8 +40,14 @@ def test_bench_header_symbols_are_exported():
     assert B.lib.moe_bench_empty(0, None) == -1
 
 
+def test_binding_follows_the_header_abi_version():
+    with open(HEADER) as f:
+        m = re.search(r"#define MOE_ABI_VERSION (\d+)", f.read())
+    assert m and int(m.group(1)) == B.ABI_VERSION
+
+
 def test_abi_version_and_status_strings():
-    assert B.moe_abi_version() == 4
+    assert B.moe_abi_version() == 4 == B.ABI_VERSION
     for code in B.STATUS:
         assert B.moe_status_str(code)
     assert B.moe_status_str(0) == "ok"
