@@ -384,8 +384,8 @@ int moe_decode_chain(const moe_layer_t* layers, int n_layers, const void* x,
  *           selection order (each times its W2 tensor scale), (+ x), one bf16 rounding.
  * Shapes it takes (else MOE_ERR_UNSUPPORTED): NVFP4 routed and shared experts, sigmoid
  * routing, H <= 2048 with H % 256 == 0, I = 64, 128 or a multiple of 256,
- * E <= 256 with E % 16 == 0.  1 <= tokens <=
- * MOE_PREFILL_MAX_TOKENS (else MOE_ERR_BATCH).                                        */
+ * E <= 256 with E % 16 == 0.  1 <= tokens <= MOE_PREFILL_MAX_TOKENS and
+ * tokens * (k + S) * I < 2^32 (else MOE_ERR_BATCH).                                   */
 #define MOE_PREFILL_MAX_TOKENS 65536
 
 /* Bytes of device workspace moe_prefill_layer needs for `tokens` tokens on this layer

@@ -830,6 +830,15 @@ bool prefill_supported(const moe_layer_desc& d, const Plan& p) {
          d.n_routed % 16 == 0 && p.g13.ns == 1 && p.g2.ns == 1;
 }
 
+// Token counts the prefill takes: 1 .. MOE_PREFILL_MAX_TOKENS, and few enough
+// that every element offset into the sorted intermediate rows ((top_k +
+// n_shared) rows per token, `inter` wide) fits 32 bits (the GEMMs stage rows
+// by 32-bit element offsets).
+bool prefill_tokens_ok(const moe_layer_desc& d, int tokens) {
+  return tokens >= 1 && tokens <= MOE_PREFILL_MAX_TOKENS &&
+         (uint64_t)tokens * (uint64_t)(d.top_k + d.n_shared) * (uint64_t)d.inter < (1ull << 32);
+}
+
 struct PfLayout {
   size_t xhat, logits, ids, wts, counts, offs, toff, perm, inv, h, y, total;
 };
@@ -865,7 +874,7 @@ int moe_prefill_workspace_bytes(moe_layer_t L, int tokens, size_t* bytes) {
   if (L == nullptr || bytes == nullptr) return MOE_ERR_INVALID_ARG;
   *bytes = 0;
   if (!prefill_supported(L->d, L->p)) return MOE_ERR_UNSUPPORTED;
-  if (tokens < 1 || tokens > MOE_PREFILL_MAX_TOKENS) return MOE_ERR_BATCH;
+  if (!prefill_tokens_ok(L->d, tokens)) return MOE_ERR_BATCH;
   *bytes = pf_layout(L->d, tokens).total;
   return MOE_OK;
 }
@@ -876,7 +885,7 @@ int moe_prefill_layer(moe_layer_t L, const void* x, const void* router_w, const 
   if (L == nullptr) return MOE_ERR_INVALID_ARG;
   const moe_layer_desc& d = L->d;
   if (!prefill_supported(d, L->p)) return MOE_ERR_UNSUPPORTED;
-  if (tokens < 1 || tokens > MOE_PREFILL_MAX_TOKENS) return MOE_ERR_BATCH;
+  if (!prefill_tokens_ok(d, tokens)) return MOE_ERR_BATCH;
   if (!x || !router_w || !expert_packed || !scales || !out || !workspace) return MOE_ERR_INVALID_ARG;
   if (d.n_shared > 0 && !shared_w) return MOE_ERR_INVALID_ARG;
   const size_t xbytes = (size_t)tokens * d.hidden * 2;

@@ -264,25 +264,24 @@ struct TileRows {
   int row0;    // sorted row of the tile's first row (rows are consecutive)
 };
 
-// Workgroup -> (tile, column block y) for a grid of whole chunks of 8 tiles
-// x ny column blocks.  Workgroups are dealt to the 8 XCDs in turn (b % 8), so
-// within a chunk of 8 ny consecutive workgroups tile 8 c + (b % 8) keeps one
-// XCD: its ny column blocks run there at about the same time and read its
-// activation rows from that XCD's L2 instead of memory.
-__device__ __forceinline__ void tile_and_block(int ny, int& tile, int& y) {
-  const int b = blockIdx.x, per = 8 * ny;
-  const int c = b / per, r = b - c * per;
-  tile = 8 * c + (r & 7);
-  y = r >> 3;
-}
-
-// The tile this workgroup takes, or g = -1 past the last tile.
-__device__ __forceinline__ TileRows tile_rows(const PrefillArgs& a, int* toff_s, int tile) {
+// The tile and column block this workgroup takes, or g = -1 past the last
+// tile.  Workgroup b runs on XCD b % 8 (workgroups are dealt to the 8 XCDs in
+// turn); XCD x takes the tiles [x M, x M + M) of the N tiles of this call
+// (M = ceil(N / 8)), in order, each with its ny column blocks back to back.
+// A tile's column blocks then share its activation rows in that XCD's L2,
+// and the consecutive tiles of one expert share its weight rows there.  The
+// grid holds 8 ny workgroups per 8 tiles of the host's bound on N; the rest
+// find no tile.
+__device__ __forceinline__ TileRows tile_rows(const PrefillArgs& a, int* toff_s, int ny, int& yb) {
   const int ng = a.E + a.S;
   for (int i = (int)threadIdx.x; i <= ng; i += kPfThreads) toff_s[i] = a.tile_off[i];
   __syncthreads();
+  const int n = toff_s[ng], per = (n + 7) >> 3;
+  const int x = (int)blockIdx.x & 7, i = (int)blockIdx.x >> 3, t = i / ny;
+  yb = i - t * ny;
+  const int tile = x * per + t;
   TileRows tr;
-  if (tile >= toff_s[ng]) {
+  if (t >= per || tile >= n) {
     tr.g = -1;
     return tr;
   }
@@ -295,14 +294,17 @@ __device__ __forceinline__ TileRows tile_rows(const PrefillArgs& a, int* toff_s,
 }
 
 // ---------------------------------------------------------------- gate/up and down
-// Both GEMMs run slice by slice over K (kSlice columns): the workgroup stages
-// the slice of its 64 activation rows and of its 128 weight rows (codes and
-// block scales) in shared memory, every thread issuing all of its loads
-// before its first store, so that one memory round trip brings the whole
-// slice; each wave then multiplies its rows out of shared memory.
+// Both GEMMs run slice by slice over K (SLICE columns, a power of two that
+// divides K): the workgroup stages the slice of its 64 activation rows and of
+// its 128 weight rows (codes and block scales) in shared memory, every thread
+// issuing all of its loads before its first store, so that one memory round
+// trip brings the whole slice; each wave then multiplies its rows out of
+// shared memory.  The workgroup loads slice i + 1 while it multiplies slice
+// i.  Which rows and columns a thread moves does not change from slice to
+// slice: the offsets are worked out once, before the first slice.
 constexpr int kWRows = 128;                        // weight rows per workgroup
 constexpr int kWStride = kSlice / 2 + 16;          // bytes per staged weight row (+16 B: banks)
-constexpr int kChunks = kSlice / 32;               // 32-column chunks per slice
+constexpr int kChunks = kSlice / 32;               // 32-column chunks per slice at most
 
 struct __align__(16) GemmSmem {
   uint16_t act[kTileTok * kSlicePad];              // activation rows, bf16
@@ -312,71 +314,79 @@ struct __align__(16) GemmSmem {
   int tok[kTileTok];
 };
 
-// One slice of the tile in flight: this thread's share of the activation
-// rows and of the weight codes and scales, loaded into registers (load) and
-// then written to shared memory (store).  The workgroup loads slice i + 1
-// while it multiplies slice i, so that the loads' round trip overlaps the
-// matrix work.  Activation row m comes from act_row(m) (a bf16 row, or null
-// for a zero row), local weight row r from matrix row wrow(r) of (codes,
-// scales) with geometry g.
-struct SliceRegs {
-  static constexpr int kA = kTileTok * kSlice / 8 / kPfThreads;   // 16-byte activation units per thread
-  static constexpr int kW = kWRows * kSlice / 32 / kPfThreads;    // 16-byte code units (chunks) per thread
+constexpr int ilog2(int v) { return v <= 1 ? 0 : 1 + ilog2(v / 2); }
+
+// This thread's share of a slice: activation units (16 bytes of one row) and
+// weight chunks (16 bytes of codes, 32 columns of one row, with their scale
+// pair).  Unit u = tid + 256 i of the slice is row u / (SLICE / 8), 16-byte
+// column u % (SLICE / 8); chunk u is local weight row u / (SLICE / 32),
+// chunk u % (SLICE / 32).  The counts divide exactly for SLICE = 64, 128, 256.
+template <int SLICE>
+struct Stage {
+  static constexpr int kAsh = ilog2(SLICE / 8), kNsh = ilog2(SLICE / 32);
+  static constexpr int kA = kTileTok * SLICE / 8 / kPfThreads;
+  static constexpr int kW = kWRows * SLICE / 32 / kPfThreads;
+  static_assert(kA * kPfThreads == kTileTok * SLICE / 8 && kW * kPfThreads == kWRows * SLICE / 32, "whole units");
+  // fixed per workgroup
+  uint32_t aoff[kA];     // element offset of the unit's row start + column, from the activation base
+  uint32_t avalid;       // bit i: unit i's row holds a token (else it is staged as zeros)
+  uint32_t coff[kW];     // byte offset of the chunk's codes at slice 0
+  uint32_t soff[kW];     // byte offset of its scale word at slice 0
+  uint32_t shi;          // bit i: chunk i's pair is the word's upper half
+  // the slice in flight
   uint4 av[kA], wv[kW];
   uint32_t sv[kW];
-};
 
-// log2 of the slice's 16-byte activation units and chunks per row, and of
-// the geometry's rows per step (all powers of two): the staging splits a
-// thread's unit index with shifts, not divisions.
-struct SliceShape {
-  int ash, nsh, rsh;
-};
-__device__ __forceinline__ SliceShape slice_shape(int slice, const MatGeom& g) {
-  return SliceShape{__builtin_ctz((unsigned)slice / 8u), __builtin_ctz((unsigned)slice / 32u),
-                    __builtin_ctz((unsigned)g.rpw)};
-}
-
-template <class ActRow, class WRow>
-__device__ __forceinline__ void load_slice(SliceRegs& r, int k0, SliceShape sh, const MatGeom& g, const uint8_t* codes,
-                                           const uint8_t* scales, const uint16_t* any_row, ActRow&& act_row,
-                                           WRow&& wrow) {
-  const int c0 = k0 >> 5;
-  // every lane loads (a zero row reads any_row and drops it): no branch
-  // around the loads, so that they all issue back to back
+  template <class ActRow, class WRow>
+  __device__ __forceinline__ void setup(const MatGeom& g, int K, ActRow&& act_row, WRow&& wrow) {
+    const int rsh = __builtin_ctz((unsigned)g.rpw);
+    avalid = 0u;
 #pragma unroll
-  for (int i = 0; i < SliceRegs::kA; ++i) {
-    const int u = (int)threadIdx.x + kPfThreads * i, m = u >> sh.ash, q = u & ((1 << sh.ash) - 1);
-    const uint16_t* src = act_row(m < kTileTok ? m : 0);
-    const bool ok = m < kTileTok && src != nullptr;
-    const uint4 v = ld16((ok ? src : any_row) + k0 + q * 8);
-    r.av[i] = ok ? v : make_uint4(0u, 0u, 0u, 0u);
-  }
+    for (int i = 0; i < kA; ++i) {
+      const int u = (int)threadIdx.x + kPfThreads * i, m = u >> kAsh, q = u & ((1 << kAsh) - 1);
+      const int r = act_row(m);   // row of the activation matrix, or -1
+      aoff[i] = r >= 0 ? (uint32_t)r * (uint32_t)K + (uint32_t)(q * 8) : 0u;
+      avalid |= (r >= 0 ? 1u : 0u) << i;
+    }
+    shi = 0u;
 #pragma unroll
-  for (int i = 0; i < SliceRegs::kW; ++i) {
-    const int u = (int)threadIdx.x + kPfThreads * i, lr = u >> sh.nsh, q = u & ((1 << sh.nsh) - 1);
-    const int row = wrow(lr < kWRows ? lr : 0), cc = c0 + q;
-    const int t = row >> sh.rsh, ri = row & ((1 << sh.rsh) - 1);
-    r.wv[i] = ld16o(codes, (uint32_t)(row * g.cw + cc) * 16u);
-    r.sv[i] = ld32o(scales, (uint32_t)((t >> 1) * g.su + ri * g.cw + cc) * 4u) >> ((t & 1) << 4);
-  }
-}
-
-__device__ __forceinline__ void store_slice(GemmSmem& s, const SliceRegs& r, SliceShape sh) {
-#pragma unroll
-  for (int i = 0; i < SliceRegs::kA; ++i) {
-    const int u = (int)threadIdx.x + kPfThreads * i, m = u >> sh.ash, q = u & ((1 << sh.ash) - 1);
-    if (m < kTileTok) *reinterpret_cast<uint4*>(&s.act[m * kSlicePad + q * 8]) = r.av[i];
-  }
-#pragma unroll
-  for (int i = 0; i < SliceRegs::kW; ++i) {
-    const int u = (int)threadIdx.x + kPfThreads * i, lr = u >> sh.nsh, q = u & ((1 << sh.nsh) - 1);
-    if (lr < kWRows) {
-      *reinterpret_cast<uint4*>(&s.wc[lr * kWStride + q * 16]) = r.wv[i];
-      s.wsc[lr][q] = (uint16_t)r.sv[i];
+    for (int i = 0; i < kW; ++i) {
+      const int u = (int)threadIdx.x + kPfThreads * i, lr = u >> kNsh, q = u & ((1 << kNsh) - 1);
+      const int row = wrow(lr), t = row >> rsh, ri = row & ((1 << rsh) - 1);
+      coff[i] = (uint32_t)(row * g.cw + q) * 16u;
+      soff[i] = (uint32_t)((t >> 1) * g.su + ri * g.cw + q) * 4u;
+      shi |= (uint32_t)(t & 1) << i;
     }
   }
-}
+  // Every lane loads (a zero row reads the base row and drops it): no branch
+  // around the loads, so that they all issue back to back.
+  __device__ __forceinline__ void load(const uint16_t* act, const uint8_t* codes, const uint8_t* scales, int k0) {
+#pragma unroll
+    for (int i = 0; i < kA; ++i) {
+      const uint4 v = ld16(act + aoff[i] + k0);
+      av[i] = ((avalid >> i) & 1u) ? v : make_uint4(0u, 0u, 0u, 0u);
+    }
+    const uint32_t c0 = (uint32_t)(k0 >> 5);
+#pragma unroll
+    for (int i = 0; i < kW; ++i) {
+      wv[i] = ld16o(codes, coff[i] + c0 * 16u);
+      sv[i] = ld32o(scales, soff[i] + c0 * 4u) >> (((shi >> i) & 1u) << 4);
+    }
+  }
+  __device__ __forceinline__ void store(GemmSmem& s) const {
+#pragma unroll
+    for (int i = 0; i < kA; ++i) {
+      const int u = (int)threadIdx.x + kPfThreads * i, m = u >> kAsh, q = u & ((1 << kAsh) - 1);
+      *reinterpret_cast<uint4*>(&s.act[m * kSlicePad + q * 8]) = av[i];
+    }
+#pragma unroll
+    for (int i = 0; i < kW; ++i) {
+      const int u = (int)threadIdx.x + kPfThreads * i, lr = u >> kNsh, q = u & ((1 << kNsh) - 1);
+      *reinterpret_cast<uint4*>(&s.wc[lr * kWStride + q * 16]) = wv[i];
+      s.wsc[lr][q] = (uint16_t)sv[i];
+    }
+  }
+};
 
 // B operand of lane group kb (= lane / 16) from local weight row r, chunk q
 // of the staged slice: columns 8 kb .. 8 kb + 7, codes times their block's
@@ -399,14 +409,30 @@ __device__ __forceinline__ uint4 afrag(const GemmSmem& s, int mt, int q, int mi,
   return *reinterpret_cast<const uint4*>(&s.act[(16 * mt + mi) * kSlicePad + 32 * q + 8 * kb]);
 }
 
+// The group's weights (codes, scales) of matrix `which` (0: W13, 1: W2).
+struct GroupW {
+  const uint8_t *codes, *scales;
+  float ts;
+};
+__device__ __forceinline__ GroupW group_w(const PrefillArgs& a, int g, int which) {
+  const bool routed = g < a.E;
+  const int e = routed ? g : g - a.E;
+  GroupW w;
+  w.codes = (routed ? a.r_codes + (size_t)e * a.r_code_stride : a.s_codes + (size_t)e * a.s_code_stride) +
+            (which ? (routed ? a.r_w13_code : a.s_w13_code) : 0);
+  w.scales = (routed ? a.r_scales + (size_t)e * a.r_scale_stride : a.s_scales + (size_t)e * a.s_scale_stride) +
+             (which ? (routed ? a.r_w13_scale : a.s_w13_scale) : 0);
+  w.ts = (routed ? a.r_tscale : a.s_tscale)[2 * e + which];
+  return w;
+}
+
 // gate/up: workgroup (tile, y) takes intermediates [64 y, 64 y + 64): local
 // weight rows 0..63 are their gate rows, 64..127 their up rows; wave w's
-// lanes take intermediate 64 y + 16 w + lane % 16.
+// lanes take intermediate 64 y + 16 w + lane % 16.  K = H, a multiple of 256.
 __global__ __launch_bounds__(kPfThreads) void k_pf_gateup(PrefillArgs a) {
   __shared__ GemmSmem s;
-  int tile, yb;
-  tile_and_block(a.I / kGuCols, tile, yb);
-  const TileRows tr = tile_rows(a, s.toff, tile);
+  int yb;
+  const TileRows tr = tile_rows(a, s.toff, a.I / kGuCols, yb);
   if (tr.g < 0) return;
   const int wave = wave_id(), lane = (int)threadIdx.x & 63;
   const int mi = lane & 15, kb = lane >> 4;
@@ -415,36 +441,25 @@ __global__ __launch_bounds__(kPfThreads) void k_pf_gateup(PrefillArgs a) {
     const int r = (int)threadIdx.x;
     s.tok[r] = r >= tr.nrows ? -1 : routed ? a.perm[tr.row0 + r] / a.k : tr.r0 + r;
   }
-  const uint8_t* codes = routed ? a.r_codes + (size_t)tr.g * a.r_code_stride
-                                : a.s_codes + (size_t)(tr.g - a.E) * a.s_code_stride;
-  const uint8_t* scales = routed ? a.r_scales + (size_t)tr.g * a.r_scale_stride
-                                 : a.s_scales + (size_t)(tr.g - a.E) * a.s_scale_stride;
-  const float ts13 = routed ? a.r_tscale[2 * tr.g] : a.s_tscale[2 * (tr.g - a.E)];
+  const GroupW gw = group_w(a, tr.g, 0);
   const int j0 = yb * kGuCols, j = j0 + 16 * wave + mi;
   const uint16_t* xsrc = a.prenorm ? a.xhat : a.x;
   const int H = a.H, I = a.I;
   f32x4_t accg[4], accu[4];
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt) accg[mt] = accu[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  const int slice = min(kSlice, H);
-  const auto act_row = [&](int m) -> const uint16_t* {
-    const int t = s.tok[m];
-    return t >= 0 ? xsrc + (size_t)t * H : nullptr;
-  };
-  const auto wrow = [&](int r) { return r < kGuCols ? j0 + r : I + j0 + (r - kGuCols); };
-  const SliceShape shp = slice_shape(slice, a.g13);
   __syncthreads();   // the token list is written
-  SliceRegs sr;
-  load_slice(sr, 0, shp, a.g13, codes, scales, xsrc, act_row, wrow);
-  for (int k0 = 0; k0 < H; k0 += slice) {
+  Stage<kSlice> st;
+  st.setup(a.g13, H, [&](int m) { return s.tok[m]; },
+           [&](int r) { return r < kGuCols ? j0 + r : I + j0 + (r - kGuCols); });
+  st.load(xsrc, gw.codes, gw.scales, 0);
+  for (int k0 = 0; k0 < H; k0 += kSlice) {
     __syncthreads();   // the previous slice is consumed
-    store_slice(s, sr, shp);
+    st.store(s);
     __syncthreads();
-    if (k0 + slice < H) load_slice(sr, k0 + slice, shp, a.g13, codes, scales, xsrc, act_row, wrow);
-    const int nq = slice / 32;
+    if (k0 + kSlice < H) st.load(xsrc, gw.codes, gw.scales, k0 + kSlice);
 #pragma unroll
-    for (int q = 0; q < kChunks; ++q) {
-      if (q >= nq) break;
+    for (int q = 0; q < kSlice / 32; ++q) {
       const uint4 bg = wfrag(s, 16 * wave + mi, q, kb), bu = wfrag(s, kGuCols + 16 * wave + mi, q, kb);
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
@@ -460,48 +475,39 @@ __global__ __launch_bounds__(kPfThreads) void k_pf_gateup(PrefillArgs a) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int m = 16 * mt + 4 * kb + i;
-      if (m < tr.nrows) a.h[(size_t)(tr.row0 + m) * I + j] = (uint16_t)f2bf(silu_mul(accg[mt][i] * ts13, accu[mt][i] * ts13));
+      if (m < tr.nrows)
+        a.h[(size_t)(tr.row0 + m) * I + j] = (uint16_t)f2bf(silu_mul(accg[mt][i] * gw.ts, accu[mt][i] * gw.ts));
     }
 }
 
 // down: workgroup (tile, y) takes outputs [128 y, 128 y + 128) (W2 rows);
 // wave w's lanes take outputs 128 y + 32 w + 16 nt + lane % 16, nt = 0, 1.
+// K = I; SLICE = min(I, 256).
+template <int SLICE>
 __global__ __launch_bounds__(kPfThreads) void k_pf_down(PrefillArgs a) {
   __shared__ GemmSmem s;
-  int tile, yb;
-  tile_and_block(a.H / kDnCols, tile, yb);
-  const TileRows tr = tile_rows(a, s.toff, tile);
+  int yb;
+  const TileRows tr = tile_rows(a, s.toff, a.H / kDnCols, yb);
   if (tr.g < 0) return;
   const int wave = wave_id(), lane = (int)threadIdx.x & 63;
   const int mi = lane & 15, kb = lane >> 4;
-  const bool routed = tr.g < a.E;
-  const uint8_t* codes = routed ? a.r_codes + (size_t)tr.g * a.r_code_stride + a.r_w13_code
-                                : a.s_codes + (size_t)(tr.g - a.E) * a.s_code_stride + a.s_w13_code;
-  const uint8_t* scales = routed ? a.r_scales + (size_t)tr.g * a.r_scale_stride + a.r_w13_scale
-                                 : a.s_scales + (size_t)(tr.g - a.E) * a.s_scale_stride + a.s_w13_scale;
+  const GroupW gw = group_w(a, tr.g, 1);
   const int n0 = yb * kDnCols, H = a.H, I = a.I;
   f32x4_t acc[2][4];
 #pragma unroll
   for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) acc[nt][mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  const int slice = min(kSlice, I);
-  const auto act_row = [&](int m) -> const uint16_t* {
-    return m < tr.nrows ? a.h + (size_t)(tr.row0 + m) * I : nullptr;
-  };
-  const auto wrow = [&](int r) { return n0 + r; };
-  const SliceShape shp = slice_shape(slice, a.g2);
-  SliceRegs sr;
-  load_slice(sr, 0, shp, a.g2, codes, scales, a.h, act_row, wrow);
-  for (int k0 = 0; k0 < I; k0 += slice) {
+  Stage<SLICE> st;
+  st.setup(a.g2, I, [&](int m) { return m < tr.nrows ? tr.row0 + m : -1; }, [&](int r) { return n0 + r; });
+  st.load(a.h, gw.codes, gw.scales, 0);
+  for (int k0 = 0; k0 < I; k0 += SLICE) {
     __syncthreads();
-    store_slice(s, sr, shp);
+    st.store(s);
     __syncthreads();
-    if (k0 + slice < I) load_slice(sr, k0 + slice, shp, a.g2, codes, scales, a.h, act_row, wrow);
-    const int nq = slice / 32;
+    if (k0 + SLICE < I) st.load(a.h, gw.codes, gw.scales, k0 + SLICE);
 #pragma unroll
-    for (int q = 0; q < kChunks; ++q) {
-      if (q >= nq) break;
+    for (int q = 0; q < SLICE / 32; ++q) {
       const uint4 b0 = wfrag(s, 32 * wave + mi, q, kb), b1 = wfrag(s, 32 * wave + 16 + mi, q, kb);
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
@@ -584,7 +590,10 @@ int launch_prefill(const PrefillArgs& a, void* stream) {
   hipLaunchKernelGGL(k_pf_count, dim3(a.E), dim3(kPfThreads), 0, st, a);
   hipLaunchKernelGGL(k_pf_place, dim3(a.E), dim3(kPfThreads), 0, st, a);
   hipLaunchKernelGGL(k_pf_gateup, dim3(chunks * 8 * (a.I / kGuCols)), dim3(kPfThreads), 0, st, a);
-  hipLaunchKernelGGL(k_pf_down, dim3(chunks * 8 * (a.H / kDnCols)), dim3(kPfThreads), 0, st, a);
+  const dim3 dgrid(chunks * 8 * (a.H / kDnCols));
+  if (a.I == 64) hipLaunchKernelGGL(k_pf_down<64>, dgrid, dim3(kPfThreads), 0, st, a);
+  else if (a.I == 128) hipLaunchKernelGGL(k_pf_down<128>, dgrid, dim3(kPfThreads), 0, st, a);
+  else hipLaunchKernelGGL(k_pf_down<256>, dgrid, dim3(kPfThreads), 0, st, a);
   hipLaunchKernelGGL(k_pf_combine, dim3(a.T), dim3(kPfThreads), 0, st, a);
   return (int)hipGetLastError();
 }
