@@ -359,31 +359,31 @@ struct Stage {
     }
   }
   // Every lane loads (a zero row reads the base row and drops it): no branch
-  // around the loads, so that they all issue back to back.
+  // around the loads, so that they all issue back to back.  The loaded words
+  // are not touched until store(): a use right after the loads would make the
+  // wave wait for them before it multiplies the slice already staged.
   __device__ __forceinline__ void load(const uint16_t* act, const uint8_t* codes, const uint8_t* scales, int k0) {
 #pragma unroll
-    for (int i = 0; i < kA; ++i) {
-      const uint4 v = ld16(act + aoff[i] + k0);
-      av[i] = ((avalid >> i) & 1u) ? v : make_uint4(0u, 0u, 0u, 0u);
-    }
+    for (int i = 0; i < kA; ++i) av[i] = ld16(act + aoff[i] + k0);
     const uint32_t c0 = (uint32_t)(k0 >> 5);
 #pragma unroll
     for (int i = 0; i < kW; ++i) {
       wv[i] = ld16o(codes, coff[i] + c0 * 16u);
-      sv[i] = ld32o(scales, soff[i] + c0 * 4u) >> (((shi >> i) & 1u) << 4);
+      sv[i] = ld32o(scales, soff[i] + c0 * 4u);
     }
   }
   __device__ __forceinline__ void store(GemmSmem& s) const {
 #pragma unroll
     for (int i = 0; i < kA; ++i) {
       const int u = (int)threadIdx.x + kPfThreads * i, m = u >> kAsh, q = u & ((1 << kAsh) - 1);
-      *reinterpret_cast<uint4*>(&s.act[m * kSlicePad + q * 8]) = av[i];
+      *reinterpret_cast<uint4*>(&s.act[m * kSlicePad + q * 8]) =
+          ((avalid >> i) & 1u) ? av[i] : make_uint4(0u, 0u, 0u, 0u);
     }
 #pragma unroll
     for (int i = 0; i < kW; ++i) {
       const int u = (int)threadIdx.x + kPfThreads * i, lr = u >> kNsh, q = u & ((1 << kNsh) - 1);
       *reinterpret_cast<uint4*>(&s.wc[lr * kWStride + q * 16]) = wv[i];
-      s.wsc[lr][q] = (uint16_t)sv[i];
+      s.wsc[lr][q] = (uint16_t)(sv[i] >> (((shi >> i) & 1u) << 4));
     }
   }
 };
