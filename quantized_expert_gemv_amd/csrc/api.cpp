@@ -857,7 +857,7 @@ PfLayout pf_layout(const moe_layer_desc& d, int T) {
   w.logits = take((size_t)T * d.n_routed * 4);
   w.ids = take(Tk * 4);
   w.wts = take(Tk * 4);
-  w.counts = take((size_t)d.n_routed * 4);
+  w.counts = take((size_t)d.n_routed * 5 * 4);   // per expert: its pairs, then each counting wave's share
   w.offs = take(ng * 4);
   w.toff = take(ng * 4);
   w.perm = take(Tk * 4);

@@ -317,7 +317,7 @@ struct PrefillArgs {
   float* logits;    // fp32 [T][E]
   int* ids;         // [T][k] selection order
   float* wts;       // [T][k]
-  int* counts;      // [E] pairs per expert
+  int* counts;      // [5 E]: pairs per expert, then each counting wave's share [E][4]
   int* offs;        // [E + S + 1] first sorted row of each group
   int* tile_off;    // [E + S + 1] first tile of each group
   int* perm;        // [T k] sorted row -> token * k + slot

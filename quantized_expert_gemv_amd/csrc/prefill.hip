@@ -171,6 +171,43 @@ __global__ __launch_bounds__(kPfThreads) void k_pf_topk(PrefillArgs a) {
 }
 
 // ---------------------------------------------------------------- grouping
+// The selection list ids[T * k] (pair i = token i / k, slot i % k) is read in
+// groups of four pairs (16 bytes); wave w of a workgroup takes a contiguous
+// quarter of the groups, so the waves' pairs follow each other in list
+// order.  A partial last group reads -1 past the end.
+__device__ __forceinline__ int4 ids4(const int* ids, int g, int n) {
+  if (4 * g + 3 < n) return *reinterpret_cast<const int4*>(ids + 4 * g);
+  int4 v = make_int4(-1, -1, -1, -1);
+  if (4 * g < n) v.x = ids[4 * g];
+  if (4 * g + 1 < n) v.y = ids[4 * g + 1];
+  if (4 * g + 2 < n) v.z = ids[4 * g + 2];
+  return v;
+}
+__device__ __forceinline__ int matches4(const int4& v, int e) {
+  return (v.x == e) + (v.y == e) + (v.z == e) + (v.w == e);
+}
+// Groups [g0, g1) of wave `wave` (4 waves per workgroup).
+__device__ __forceinline__ void wave_groups(int n, int wave, int& g0, int& g1) {
+  const int ng = (n + 3) >> 2, per = (ng + 3) >> 2;
+  g0 = min(ng, wave * per);
+  g1 = min(ng, g0 + per);
+}
+// The wave's number of pairs that selected expert e.
+__device__ __forceinline__ int wave_count(const int* ids, int n, int e, int g0, int g1) {
+  const int lane = (int)threadIdx.x & 63;
+  int c = 0;
+  for (int g = g0 + lane; g < g1; g += 4 * 64) {
+    int4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v[u] = ids4(ids, min(g + 64 * u, g1 - 1), n);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) c += g + 64 * u < g1 ? matches4(v[u], e) : 0;
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) c += __shfl_xor(c, o);
+  return c;
+}
+
 __device__ __forceinline__ int block_sum_int(int v, int* red) {
   const int wave = wave_id(), lane = (int)threadIdx.x & 63;
 #pragma unroll
@@ -182,19 +219,25 @@ __device__ __forceinline__ int block_sum_int(int v, int* red) {
   return s;
 }
 
+// counts[e]: the pairs that selected expert e; counts[E + 4 e + w]: those
+// among wave w's quarter of the list.
 __global__ __launch_bounds__(kPfThreads) void k_pf_count(PrefillArgs a) {
   __shared__ int red[4];
-  const int e = blockIdx.x, n = a.T * a.k;
-  int c = 0;
-  for (int i = (int)threadIdx.x; i < n; i += kPfThreads) c += a.ids[i] == e;
-  c = block_sum_int(c, red);
-  if (threadIdx.x == 0) a.counts[e] = c;
+  const int e = blockIdx.x, n = a.T * a.k, wave = wave_id();
+  int g0, g1;
+  wave_groups(n, wave, g0, g1);
+  const int c = wave_count(a.ids, n, e, g0, g1);
+  if (((int)threadIdx.x & 63) == 0) {
+    red[wave] = c;
+    a.counts[a.E + 4 * e + wave] = c;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) a.counts[e] = red[0] + red[1] + red[2] + red[3];
 }
 
 __global__ __launch_bounds__(kPfThreads) void k_pf_place(PrefillArgs a) {
   __shared__ int red[4];
-  __shared__ int wsum[4];
-  __shared__ int tiles[kPfMaxE + MOE_MAX_SHARED + 1];
+  __shared__ int wsum[8];   // each wave's row and tile totals
   const int e = blockIdx.x, wave = wave_id(), lane = (int)threadIdx.x & 63;
   const int n = a.T * a.k;
   // the expert's first row: the pairs of every lower expert
@@ -202,18 +245,35 @@ __global__ __launch_bounds__(kPfThreads) void k_pf_place(PrefillArgs a) {
   for (int i = (int)threadIdx.x; i < e; i += kPfThreads) below += a.counts[i];
   const int off = block_sum_int(below, red);
   if (e == 0) {
-    // group offsets (rows) and tile offsets; the shared groups' rows follow
-    // the routed pairs, one group of T rows per shared expert
-    for (int i = (int)threadIdx.x; i < a.E; i += kPfThreads) tiles[i] = a.counts[i];
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      int rows = 0, tl = 0;
-      for (int g = 0; g < a.E; ++g) {
-        a.offs[g] = rows;
-        a.tile_off[g] = tl;
-        rows += tiles[g];
-        tl += (tiles[g] + kTileTok - 1) / kTileTok;
+    // group offsets (rows) and tile offsets: exclusive sums over the routed
+    // experts (thread t holds expert t), then the shared groups, T rows each
+    const int t = (int)threadIdx.x;
+    const int c = t < a.E ? a.counts[t] : 0, nt = (c + kTileTok - 1) / kTileTok;
+    int rc = c, rt = nt;   // inclusive sums within the wave
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int uc = __shfl_up(rc, o), ut = __shfl_up(rt, o);
+      if (lane >= o) {
+        rc += uc;
+        rt += ut;
       }
+    }
+    if (lane == 63) {
+      wsum[2 * wave] = rc;
+      wsum[2 * wave + 1] = rt;
+    }
+    __syncthreads();
+    int bc = 0, bt = 0;   // the waves before this one
+    for (int w = 0; w < wave; ++w) {
+      bc += wsum[2 * w];
+      bt += wsum[2 * w + 1];
+    }
+    if (t < a.E) {
+      a.offs[t] = bc + rc - c;
+      a.tile_off[t] = bt + rt - nt;
+    }
+    if (t == kPfThreads - 1) {   // the last thread's inclusive sums are the totals
+      int rows = bc + rc, tl = bt + rt;
       for (int s = 0; s < a.S; ++s) {
         a.offs[a.E + s] = rows;
         a.tile_off[a.E + s] = tl;
@@ -224,25 +284,34 @@ __global__ __launch_bounds__(kPfThreads) void k_pf_place(PrefillArgs a) {
       a.tile_off[a.E + a.S] = tl;
     }
   }
-  // the expert's pairs in token order: a block-wide stable compaction
-  int run = 0;
-  for (int base = 0; base < n; base += kPfThreads) {
-    const int i = base + (int)threadIdx.x;
-    const bool hit = i < n && a.ids[i] == e;
-    const unsigned long long b = __ballot(hit);
-    const int before_lane = __popcll(b & ((1ull << lane) - 1ull));
-    if (lane == 0) wsum[wave] = __popcll(b);
-    __syncthreads();
-    int before_wave = 0;
-    for (int w = 0; w < wave; ++w) before_wave += wsum[w];
-    const int total = wsum[0] + wsum[1] + wsum[2] + wsum[3];
-    if (hit) {
-      const int p = off + run + before_wave + before_lane;
-      a.perm[p] = i;
-      a.inv[i] = p;
+  // the expert's pairs in list order: each wave writes the pairs of its
+  // quarter after those of the waves before it (the quarters' counts are
+  // the counting kernel's)
+  int g0, g1;
+  wave_groups(n, wave, g0, g1);
+  int run = off;
+  for (int w = 0; w < wave; ++w) run += a.counts[a.E + 4 * e + w];
+  const unsigned long long lt = (1ull << lane) - 1ull;
+  for (int gb = g0; gb < g1; gb += 4 * 64) {
+    int4 v[4];   // four steps' loads in flight at once
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v[u] = ids4(a.ids, min(gb + 64 * u + lane, g1 - 1), n);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int g = gb + 64 * u + lane;
+      const bool in = g < g1;
+      const int m0 = in && v[u].x == e, m1 = in && v[u].y == e, m2 = in && v[u].z == e, m3 = in && v[u].w == e;
+      const int cl = m0 + m1 + m2 + m3;   // 0 .. 4
+      // matches in the lanes before this one: the three bits of cl, counted
+      const unsigned long long b0 = __ballot(cl & 1), b1 = __ballot(cl & 2), b2 = __ballot(cl & 4);
+      int p = run + __popcll(b0 & lt) + 2 * __popcll(b1 & lt) + 4 * __popcll(b2 & lt);
+      const int i0 = 4 * g;
+      if (m0) { a.perm[p] = i0; a.inv[i0] = p; ++p; }
+      if (m1) { a.perm[p] = i0 + 1; a.inv[i0 + 1] = p; ++p; }
+      if (m2) { a.perm[p] = i0 + 2; a.inv[i0 + 2] = p; ++p; }
+      if (m3) { a.perm[p] = i0 + 3; a.inv[i0 + 3] = p; }
+      run += __popcll(b0) + 2 * __popcll(b1) + 4 * __popcll(b2);
     }
-    run += total;
-    __syncthreads();
   }
 }
 
