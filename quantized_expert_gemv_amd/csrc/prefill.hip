@@ -49,8 +49,8 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 constexpr int kPfThreads = 256;   // four waves
 constexpr int kRouteTok = 16;     // tokens per routing workgroup (one MFMA row block)
 constexpr int kTileTok = 64;      // rows per gate/up and down tile (four MFMA row blocks)
-constexpr int kSlice = 256;       // K columns staged in shared memory at a time
-constexpr int kSlicePad = kSlice + 8;   // row stride in bf16: 16 B of padding spreads the rows over the banks
+constexpr int kGuSlice = 256;     // K columns staged in shared memory at a time: gate/up
+constexpr int kDnSlice = 256;     // down (at most; K = I may be shorter)
 constexpr int kGuCols = 64;       // intermediates per gate/up workgroup (16 per wave)
 constexpr int kDnCols = 128;      // outputs per down workgroup (32 per wave)
 
@@ -372,13 +372,13 @@ __device__ __forceinline__ TileRows tile_rows(const PrefillArgs& a, int* toff_s,
 // i.  Which rows and columns a thread moves does not change from slice to
 // slice: the offsets are worked out once, before the first slice.
 constexpr int kWRows = 128;                        // weight rows per workgroup
-constexpr int kWStride = kSlice / 2 + 16;          // bytes per staged weight row (+16 B: banks)
-constexpr int kChunks = kSlice / 32;               // 32-column chunks per slice at most
-
+template <int SLICE>
 struct __align__(16) GemmSmem {
-  uint16_t act[kTileTok * kSlicePad];              // activation rows, bf16
+  static constexpr int kPad = SLICE + 8;           // activation row stride in bf16 (+16 B: banks)
+  static constexpr int kWStride = SLICE / 2 + 16;  // bytes per staged weight row (+16 B: banks)
+  uint16_t act[kTileTok * kPad];                   // activation rows, bf16
   uint8_t wc[kWRows * kWStride];                   // weight codes
-  uint16_t wsc[kWRows][kChunks];                   // block scale pair (2 x e4m3) per row and chunk
+  uint16_t wsc[kWRows][SLICE / 32];                // block scale pair (2 x e4m3) per row and chunk
   int toff[kPfMaxE + MOE_MAX_SHARED + 1];
   int tok[kTileTok];
 };
@@ -441,11 +441,12 @@ struct Stage {
       sv[i] = ld32o(scales, soff[i] + c0 * 4u);
     }
   }
-  __device__ __forceinline__ void store(GemmSmem& s) const {
+  __device__ __forceinline__ void store(GemmSmem<SLICE>& s) const {
+    constexpr int kPad = GemmSmem<SLICE>::kPad, kWStride = GemmSmem<SLICE>::kWStride;
 #pragma unroll
     for (int i = 0; i < kA; ++i) {
       const int u = (int)threadIdx.x + kPfThreads * i, m = u >> kAsh, q = u & ((1 << kAsh) - 1);
-      *reinterpret_cast<uint4*>(&s.act[m * kSlicePad + q * 8]) =
+      *reinterpret_cast<uint4*>(&s.act[m * kPad + q * 8]) =
           ((avalid >> i) & 1u) ? av[i] : make_uint4(0u, 0u, 0u, 0u);
     }
 #pragma unroll
@@ -461,8 +462,9 @@ struct Stage {
 // of the staged slice: columns 8 kb .. 8 kb + 7, codes times their block's
 // e4m3 scale, as bf16.  Exact: an e2m1 value has at most 2 significant bits
 // and an e4m3 scale 4, so the product fits bf16's 8.
-__device__ __forceinline__ uint4 wfrag(const GemmSmem& s, int r, int q, int kb) {
-  const uint32_t d = *reinterpret_cast<const uint32_t*>(&s.wc[r * kWStride + q * 16 + 4 * kb]);
+template <int SLICE>
+__device__ __forceinline__ uint4 wfrag(const GemmSmem<SLICE>& s, int r, int q, int kb) {
+  const uint32_t d = *reinterpret_cast<const uint32_t*>(&s.wc[r * GemmSmem<SLICE>::kWStride + q * 16 + 4 * kb]);
   const float sc = e4m3f<0>((uint32_t)s.wsc[r][q] >> (kb & 2) * 4);   // block kb / 2 of the chunk
   typedef float f32x2_t __attribute__((ext_vector_type(2)));
   const f32x2_t v0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d, 1.0f, 0);
@@ -474,8 +476,40 @@ __device__ __forceinline__ uint4 wfrag(const GemmSmem& s, int r, int q, int kb) 
 }
 // A operand of lane (mi, kb) for row block mt, chunk q: activation row
 // 16 mt + mi, columns 32 q + 8 kb .. + 8.
-__device__ __forceinline__ uint4 afrag(const GemmSmem& s, int mt, int q, int mi, int kb) {
-  return *reinterpret_cast<const uint4*>(&s.act[(16 * mt + mi) * kSlicePad + 32 * q + 8 * kb]);
+template <int SLICE>
+__device__ __forceinline__ uint4 afrag(const GemmSmem<SLICE>& s, int mt, int q, int mi, int kb) {
+  return *reinterpret_cast<const uint4*>(&s.act[(16 * mt + mi) * GemmSmem<SLICE>::kPad + 32 * q + 8 * kb]);
+}
+
+// One wave's products over a staged slice of SLICE / 32 chunks: local weight rows
+// r0 + mi and r1 + mi (the B operands of lane group kb) against the tile's
+// four 16-row blocks, into acc0 and acc1.  Chunk q + 1's fragments are read
+// (and its weights decoded) before chunk q's products are issued, so the
+// shared-memory reads and the decoding overlap the matrix cores' work.
+template <int SLICE>
+__device__ __forceinline__ void mma_slice(const GemmSmem<SLICE>& s, int r0, int r1, int mi, int kb, f32x4_t (&acc0)[4],
+                                          f32x4_t (&acc1)[4]) {
+  constexpr int NQ = SLICE / 32;
+  uint4 av[2][4], bv[2][2];
+  bv[0][0] = wfrag(s, r0 + mi, 0, kb);
+  bv[0][1] = wfrag(s, r1 + mi, 0, kb);
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) av[0][mt] = afrag(s, mt, 0, mi, kb);
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) {
+    const int c = q & 1;
+    if (q + 1 < NQ) {
+      bv[c ^ 1][0] = wfrag(s, r0 + mi, q + 1, kb);
+      bv[c ^ 1][1] = wfrag(s, r1 + mi, q + 1, kb);
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) av[c ^ 1][mt] = afrag(s, mt, q + 1, mi, kb);
+    }
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      acc0[mt] = mfma32(av[c][mt], bv[c][0], acc0[mt]);
+      acc1[mt] = mfma32(av[c][mt], bv[c][1], acc1[mt]);
+    }
+  }
 }
 
 // The group's weights (codes, scales) of matrix `which` (0: W13, 1: W2).
@@ -499,7 +533,8 @@ __device__ __forceinline__ GroupW group_w(const PrefillArgs& a, int g, int which
 // weight rows 0..63 are their gate rows, 64..127 their up rows; wave w's
 // lanes take intermediate 64 y + 16 w + lane % 16.  K = H, a multiple of 256.
 __global__ __launch_bounds__(kPfThreads) void k_pf_gateup(PrefillArgs a) {
-  __shared__ GemmSmem s;
+  constexpr int SLICE = kGuSlice;
+  __shared__ GemmSmem<SLICE> s;
   int yb;
   const TileRows tr = tile_rows(a, s.toff, a.I / kGuCols, yb);
   if (tr.g < 0) return;
@@ -518,25 +553,16 @@ __global__ __launch_bounds__(kPfThreads) void k_pf_gateup(PrefillArgs a) {
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt) accg[mt] = accu[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   __syncthreads();   // the token list is written
-  Stage<kSlice> st;
+  Stage<SLICE> st;
   st.setup(a.g13, H, [&](int m) { return s.tok[m]; },
            [&](int r) { return r < kGuCols ? j0 + r : I + j0 + (r - kGuCols); });
   st.load(xsrc, gw.codes, gw.scales, 0);
-  for (int k0 = 0; k0 < H; k0 += kSlice) {
+  for (int k0 = 0; k0 < H; k0 += SLICE) {
     __syncthreads();   // the previous slice is consumed
     st.store(s);
     __syncthreads();
-    if (k0 + kSlice < H) st.load(xsrc, gw.codes, gw.scales, k0 + kSlice);
-#pragma unroll
-    for (int q = 0; q < kSlice / 32; ++q) {
-      const uint4 bg = wfrag(s, 16 * wave + mi, q, kb), bu = wfrag(s, kGuCols + 16 * wave + mi, q, kb);
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        const uint4 av = afrag(s, mt, q, mi, kb);
-        accg[mt] = mfma32(av, bg, accg[mt]);
-        accu[mt] = mfma32(av, bu, accu[mt]);
-      }
-    }
+    if (k0 + SLICE < H) st.load(xsrc, gw.codes, gw.scales, k0 + SLICE);
+    mma_slice(s, 16 * wave, kGuCols + 16 * wave, mi, kb, accg, accu);
   }
   // h = SiLU(g) * u at the tile's sorted rows; the lane holds rows 16 mt + 4 kb + i
 #pragma unroll
@@ -551,10 +577,10 @@ __global__ __launch_bounds__(kPfThreads) void k_pf_gateup(PrefillArgs a) {
 
 // down: workgroup (tile, y) takes outputs [128 y, 128 y + 128) (W2 rows);
 // wave w's lanes take outputs 128 y + 32 w + 16 nt + lane % 16, nt = 0, 1.
-// K = I; SLICE = min(I, 256).
+// K = I; SLICE = min(I, kDnSlice).
 template <int SLICE>
 __global__ __launch_bounds__(kPfThreads) void k_pf_down(PrefillArgs a) {
-  __shared__ GemmSmem s;
+  __shared__ GemmSmem<SLICE> s;
   int yb;
   const TileRows tr = tile_rows(a, s.toff, a.H / kDnCols, yb);
   if (tr.g < 0) return;
@@ -575,16 +601,7 @@ __global__ __launch_bounds__(kPfThreads) void k_pf_down(PrefillArgs a) {
     st.store(s);
     __syncthreads();
     if (k0 + SLICE < I) st.load(a.h, gw.codes, gw.scales, k0 + SLICE);
-#pragma unroll
-    for (int q = 0; q < SLICE / 32; ++q) {
-      const uint4 b0 = wfrag(s, 32 * wave + mi, q, kb), b1 = wfrag(s, 32 * wave + 16 + mi, q, kb);
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        const uint4 av = afrag(s, mt, q, mi, kb);
-        acc[0][mt] = mfma32(av, b0, acc[0][mt]);
-        acc[1][mt] = mfma32(av, b1, acc[1][mt]);
-      }
-    }
+    mma_slice(s, 32 * wave, 32 * wave + 16, mi, kb, acc[0], acc[1]);
   }
 #pragma unroll
   for (int nt = 0; nt < 2; ++nt)
@@ -660,8 +677,8 @@ int launch_prefill(const PrefillArgs& a, void* stream) {
   hipLaunchKernelGGL(k_pf_place, dim3(a.E), dim3(kPfThreads), 0, st, a);
   hipLaunchKernelGGL(k_pf_gateup, dim3(chunks * 8 * (a.I / kGuCols)), dim3(kPfThreads), 0, st, a);
   const dim3 dgrid(chunks * 8 * (a.H / kDnCols));
-  if (a.I == 64) hipLaunchKernelGGL(k_pf_down<64>, dgrid, dim3(kPfThreads), 0, st, a);
-  else if (a.I == 128) hipLaunchKernelGGL(k_pf_down<128>, dgrid, dim3(kPfThreads), 0, st, a);
+  if (a.I == 64 || kDnSlice == 64) hipLaunchKernelGGL(k_pf_down<64>, dgrid, dim3(kPfThreads), 0, st, a);
+  else if (a.I == 128 || kDnSlice == 128) hipLaunchKernelGGL(k_pf_down<128>, dgrid, dim3(kPfThreads), 0, st, a);
   else hipLaunchKernelGGL(k_pf_down<256>, dgrid, dim3(kPfThreads), 0, st, a);
   hipLaunchKernelGGL(k_pf_combine, dim3(a.T), dim3(kPfThreads), 0, st, a);
   return (int)hipGetLastError();
