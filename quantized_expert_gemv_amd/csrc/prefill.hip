@@ -64,7 +64,8 @@ __device__ __forceinline__ f32x4_t mfma32(const uint4& a, const uint4& b, f32x4_
 // wave w the 16 experts 64 y + 16 w.  The 16 rows (pre-normed if the layer
 // has a pre-norm; blocks of y = 0 write them to xhat) sit in shared memory;
 // lane (m = lane % 16, kb = lane / 16) feeds row m and columns 8 kb .. + 8 of
-// each 32-column step, router rows stream from memory 8 steps at a time.
+// each 32-column step, router rows stream from memory 8 steps at a time
+// (the next 8 in flight while these 8 multiply).
 constexpr int kLogitSteps = 8;
 
 __global__ __launch_bounds__(kPfThreads) void k_pf_logits(PrefillArgs a) {
@@ -72,9 +73,20 @@ __global__ __launch_bounds__(kPfThreads) void k_pf_logits(PrefillArgs a) {
   const int wave = wave_id(), lane = (int)threadIdx.x & 63;
   const int t0 = blockIdx.x * kRouteTok;
   const int H = a.H, upr = H / 8, ups = upr + 1;   // 16-byte units per row; row stride (+1: banks)
-  for (int u = (int)threadIdx.x; u < kRouteTok * upr; u += kPfThreads) {
-    const int m = u / upr, q = u - m * upr, t = t0 + m;
-    xs[m * ups + q] = t < a.T ? ld16(a.x + (size_t)t * H + q * 8) : make_uint4(0u, 0u, 0u, 0u);
+  {
+    // all of this thread's loads first, then the stores: one round trip
+    constexpr int kXU = kRouteTok * kPfMaxH / 8 / kPfThreads;
+    uint4 xv[kXU];
+#pragma unroll
+    for (int i = 0; i < kXU; ++i) {
+      const int u = (int)threadIdx.x + kPfThreads * i, m = u / upr, q = u - m * upr, t = t0 + m;
+      xv[i] = (u < kRouteTok * upr && t < a.T) ? ld16(a.x + (size_t)t * H + q * 8) : make_uint4(0u, 0u, 0u, 0u);
+    }
+#pragma unroll
+    for (int i = 0; i < kXU; ++i) {
+      const int u = (int)threadIdx.x + kPfThreads * i, m = u / upr, q = u - m * upr;
+      if (u < kRouteTok * upr) xs[m * ups + q] = xv[i];
+    }
   }
   __syncthreads();
   if (a.prenorm) {
@@ -107,12 +119,24 @@ __global__ __launch_bounds__(kPfThreads) void k_pf_logits(PrefillArgs a) {
   if (e0 >= a.E) return;
   const uint16_t* rrow = a.router_w + (size_t)(e0 + mi) * H + 8 * kb;
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-  for (int c = 0; c < H / 32; c += kLogitSteps) {
-    uint4 bv[kLogitSteps];
+  // two sets of router steps: one set's loads fly while the other's products run
+  const int nc = H / 32;
+  uint4 b0[kLogitSteps], b1[kLogitSteps];
+  const auto load = [&](uint4(&bv)[kLogitSteps], int c) {
 #pragma unroll
     for (int i = 0; i < kLogitSteps; ++i) bv[i] = ld16(rrow + 32 * (c + i));
+  };
+  const auto mma = [&](const uint4(&bv)[kLogitSteps], int c) {
 #pragma unroll
     for (int i = 0; i < kLogitSteps; ++i) acc = mfma32(xs[mi * ups + 4 * (c + i) + kb], bv[i], acc);
+  };
+  load(b0, 0);
+  for (int c = 0; c < nc; c += 2 * kLogitSteps) {
+    if (c + kLogitSteps < nc) load(b1, c + kLogitSteps);
+    mma(b0, c);
+    if (c + kLogitSteps >= nc) break;
+    if (c + 2 * kLogitSteps < nc) load(b0, c + 2 * kLogitSteps);
+    mma(b1, c + kLogitSteps);
   }
   const int e = e0 + mi;
   const float bias = a.bias ? a.bias[e] : 0.0f;
