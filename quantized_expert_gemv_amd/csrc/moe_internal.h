@@ -311,6 +311,7 @@ struct PrefillArgs {
   size_t r_code_stride, r_w13_code, r_scale_stride, r_w13_scale;
   size_t s_code_stride, s_w13_code, s_scale_stride, s_w13_scale;
   int T, H, I, E, k, S;
+  int tile_rows;     // rows per GEMM tile (64 or 128; chosen by launch_prefill)
   MatGeom g13, g2;
   // caller's workspace
   uint16_t* xhat;   // bf16 [T][H] (prenorm only)

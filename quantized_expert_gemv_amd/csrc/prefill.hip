@@ -48,9 +48,15 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kPfThreads = 256;   // four waves
 constexpr int kRouteTok = 16;     // tokens per routing workgroup (one MFMA row block)
-constexpr int kTileTok = 64;      // rows per gate/up and down tile (four MFMA row blocks)
-constexpr int kGuSlice = 256;     // K columns staged in shared memory at a time: gate/up
-constexpr int kDnSlice = 256;     // down (at most; K = I may be shorter)
+constexpr int kTileTok = 128;     // rows per gate/up and down tile at most
+// A call's tiles hold a.tile_rows rows (64, or 128 when the routed groups
+// average 128 rows or more); a tile of more than 64 rows runs as 8 MFMA row
+// blocks, a shorter one as 4.
+
+// Tiles of a group of c rows.
+__device__ __forceinline__ int group_tiles(int c, int rows) { return (c + rows - 1) / rows; }
+constexpr int kSliceShort = 256;  // K columns staged in shared memory at a time, tiles of <= 64 rows
+constexpr int kSliceLong = 128;   // and of more (at most: K = I may be shorter in the down GEMM)
 constexpr int kGuCols = 64;       // intermediates per gate/up workgroup (16 per wave)
 constexpr int kDnCols = 128;      // outputs per down workgroup (32 per wave)
 
@@ -272,7 +278,7 @@ __global__ __launch_bounds__(kPfThreads) void k_pf_place(PrefillArgs a) {
     // group offsets (rows) and tile offsets: exclusive sums over the routed
     // experts (thread t holds expert t), then the shared groups, T rows each
     const int t = (int)threadIdx.x;
-    const int c = t < a.E ? a.counts[t] : 0, nt = (c + kTileTok - 1) / kTileTok;
+    const int c = t < a.E ? a.counts[t] : 0, nt = group_tiles(c, a.tile_rows);
     int rc = c, rt = nt;   // inclusive sums within the wave
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
@@ -302,7 +308,7 @@ __global__ __launch_bounds__(kPfThreads) void k_pf_place(PrefillArgs a) {
         a.offs[a.E + s] = rows;
         a.tile_off[a.E + s] = tl;
         rows += a.T;
-        tl += (a.T + kTileTok - 1) / kTileTok;
+        tl += group_tiles(a.T, a.tile_rows);
       }
       a.offs[a.E + a.S] = rows;
       a.tile_off[a.E + a.S] = tl;
@@ -379,9 +385,9 @@ __device__ __forceinline__ TileRows tile_rows(const PrefillArgs& a, int* toff_s,
     return tr;
   }
   tr.g = group_of(toff_s, ng, tile);
-  tr.r0 = (tile - toff_s[tr.g]) * kTileTok;
   const int size = tr.g < a.E ? a.counts[tr.g] : a.T;
-  tr.nrows = min(kTileTok, size - tr.r0);
+  tr.r0 = (tile - toff_s[tr.g]) * a.tile_rows;
+  tr.nrows = min(a.tile_rows, size - tr.r0);
   tr.row0 = a.offs[tr.g] + tr.r0;
   return tr;
 }
@@ -396,13 +402,22 @@ __device__ __forceinline__ TileRows tile_rows(const PrefillArgs& a, int* toff_s,
 // i.  Which rows and columns a thread moves does not change from slice to
 // slice: the offsets are worked out once, before the first slice.
 constexpr int kWRows = 128;                        // weight rows per workgroup
-template <int SLICE>
+template <int SLICE, int ROWS>
 struct __align__(16) GemmSmem {
+  static constexpr int kSlice = SLICE, kRows = ROWS;
   static constexpr int kPad = SLICE + 8;           // activation row stride in bf16 (+16 B: banks)
   static constexpr int kWStride = SLICE / 2 + 16;  // bytes per staged weight row (+16 B: banks)
-  uint16_t act[kTileTok * kPad];                   // activation rows, bf16
+  uint16_t act[ROWS * kPad];                       // activation rows, bf16
   uint8_t wc[kWRows * kWStride];                   // weight codes
   uint16_t wsc[kWRows][SLICE / 32];                // block scale pair (2 x e4m3) per row and chunk
+};
+using SmemShort = GemmSmem<kSliceShort, 64>;
+template <int SLICE>
+using SmemLong = GemmSmem<SLICE, 128>;
+constexpr int kSmemBytes = sizeof(SmemShort) > sizeof(SmemLong<kSliceLong>) ? sizeof(SmemShort)
+                                                                            : sizeof(SmemLong<kSliceLong>);
+// The tile's bookkeeping, beside the staging buffers.
+struct TileSmem {
   int toff[kPfMaxE + MOE_MAX_SHARED + 1];
   int tok[kTileTok];
 };
@@ -414,12 +429,13 @@ constexpr int ilog2(int v) { return v <= 1 ? 0 : 1 + ilog2(v / 2); }
 // pair).  Unit u = tid + 256 i of the slice is row u / (SLICE / 8), 16-byte
 // column u % (SLICE / 8); chunk u is local weight row u / (SLICE / 32),
 // chunk u % (SLICE / 32).  The counts divide exactly for SLICE = 64, 128, 256.
-template <int SLICE>
+template <class SM>
 struct Stage {
+  static constexpr int SLICE = SM::kSlice, ROWS = SM::kRows;
   static constexpr int kAsh = ilog2(SLICE / 8), kNsh = ilog2(SLICE / 32);
-  static constexpr int kA = kTileTok * SLICE / 8 / kPfThreads;
+  static constexpr int kA = ROWS * SLICE / 8 / kPfThreads;
   static constexpr int kW = kWRows * SLICE / 32 / kPfThreads;
-  static_assert(kA * kPfThreads == kTileTok * SLICE / 8 && kW * kPfThreads == kWRows * SLICE / 32, "whole units");
+  static_assert(kA * kPfThreads == ROWS * SLICE / 8 && kW * kPfThreads == kWRows * SLICE / 32, "whole units");
   // fixed per workgroup
   uint32_t aoff[kA];     // element offset of the unit's row start + column, from the activation base
   uint32_t avalid;       // bit i: unit i's row holds a token (else it is staged as zeros)
@@ -465,8 +481,8 @@ struct Stage {
       sv[i] = ld32o(scales, soff[i] + c0 * 4u);
     }
   }
-  __device__ __forceinline__ void store(GemmSmem<SLICE>& s) const {
-    constexpr int kPad = GemmSmem<SLICE>::kPad, kWStride = GemmSmem<SLICE>::kWStride;
+  __device__ __forceinline__ void store(SM& s) const {
+    constexpr int kPad = SM::kPad, kWStride = SM::kWStride;
 #pragma unroll
     for (int i = 0; i < kA; ++i) {
       const int u = (int)threadIdx.x + kPfThreads * i, m = u >> kAsh, q = u & ((1 << kAsh) - 1);
@@ -486,9 +502,9 @@ struct Stage {
 // of the staged slice: columns 8 kb .. 8 kb + 7, codes times their block's
 // e4m3 scale, as bf16.  Exact: an e2m1 value has at most 2 significant bits
 // and an e4m3 scale 4, so the product fits bf16's 8.
-template <int SLICE>
-__device__ __forceinline__ uint4 wfrag(const GemmSmem<SLICE>& s, int r, int q, int kb) {
-  const uint32_t d = *reinterpret_cast<const uint32_t*>(&s.wc[r * GemmSmem<SLICE>::kWStride + q * 16 + 4 * kb]);
+template <class SM>
+__device__ __forceinline__ uint4 wfrag(const SM& s, int r, int q, int kb) {
+  const uint32_t d = *reinterpret_cast<const uint32_t*>(&s.wc[r * SM::kWStride + q * 16 + 4 * kb]);
   const float sc = e4m3f<0>((uint32_t)s.wsc[r][q] >> (kb & 2) * 4);   // block kb / 2 of the chunk
   typedef float f32x2_t __attribute__((ext_vector_type(2)));
   const f32x2_t v0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d, 1.0f, 0);
@@ -500,25 +516,25 @@ __device__ __forceinline__ uint4 wfrag(const GemmSmem<SLICE>& s, int r, int q, i
 }
 // A operand of lane (mi, kb) for row block mt, chunk q: activation row
 // 16 mt + mi, columns 32 q + 8 kb .. + 8.
-template <int SLICE>
-__device__ __forceinline__ uint4 afrag(const GemmSmem<SLICE>& s, int mt, int q, int mi, int kb) {
-  return *reinterpret_cast<const uint4*>(&s.act[(16 * mt + mi) * GemmSmem<SLICE>::kPad + 32 * q + 8 * kb]);
+template <class SM>
+__device__ __forceinline__ uint4 afrag(const SM& s, int mt, int q, int mi, int kb) {
+  return *reinterpret_cast<const uint4*>(&s.act[(16 * mt + mi) * SM::kPad + 32 * q + 8 * kb]);
 }
 
 // One wave's products over a staged slice of SLICE / 32 chunks: local weight rows
 // r0 + mi and r1 + mi (the B operands of lane group kb) against the tile's
-// four 16-row blocks, into acc0 and acc1.  Chunk q + 1's fragments are read
+// ROWS / 16 row blocks, into acc0 and acc1.  Chunk q + 1's fragments are read
 // (and its weights decoded) before chunk q's products are issued, so the
 // shared-memory reads and the decoding overlap the matrix cores' work.
-template <int SLICE>
-__device__ __forceinline__ void mma_slice(const GemmSmem<SLICE>& s, int r0, int r1, int mi, int kb, f32x4_t (&acc0)[4],
-                                          f32x4_t (&acc1)[4]) {
-  constexpr int NQ = SLICE / 32;
-  uint4 av[2][4], bv[2][2];
+template <class SM>
+__device__ __forceinline__ void mma_slice(const SM& s, int r0, int r1, int mi, int kb,
+                                          f32x4_t (&acc0)[SM::kRows / 16], f32x4_t (&acc1)[SM::kRows / 16]) {
+  constexpr int NQ = SM::kSlice / 32, kMT = SM::kRows / 16;
+  uint4 av[2][kMT], bv[2][2];
   bv[0][0] = wfrag(s, r0 + mi, 0, kb);
   bv[0][1] = wfrag(s, r1 + mi, 0, kb);
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt) av[0][mt] = afrag(s, mt, 0, mi, kb);
+  for (int mt = 0; mt < kMT; ++mt) av[0][mt] = afrag(s, mt, 0, mi, kb);
 #pragma unroll
   for (int q = 0; q < NQ; ++q) {
     const int c = q & 1;
@@ -526,10 +542,10 @@ __device__ __forceinline__ void mma_slice(const GemmSmem<SLICE>& s, int r0, int 
       bv[c ^ 1][0] = wfrag(s, r0 + mi, q + 1, kb);
       bv[c ^ 1][1] = wfrag(s, r1 + mi, q + 1, kb);
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) av[c ^ 1][mt] = afrag(s, mt, q + 1, mi, kb);
+      for (int mt = 0; mt < kMT; ++mt) av[c ^ 1][mt] = afrag(s, mt, q + 1, mi, kb);
     }
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
+    for (int mt = 0; mt < kMT; ++mt) {
       acc0[mt] = mfma32(av[c][mt], bv[c][0], acc0[mt]);
       acc1[mt] = mfma32(av[c][mt], bv[c][1], acc1[mt]);
     }
@@ -556,29 +572,21 @@ __device__ __forceinline__ GroupW group_w(const PrefillArgs& a, int g, int which
 // gate/up: workgroup (tile, y) takes intermediates [64 y, 64 y + 64): local
 // weight rows 0..63 are their gate rows, 64..127 their up rows; wave w's
 // lanes take intermediate 64 y + 16 w + lane % 16.  K = H, a multiple of 256.
-__global__ __launch_bounds__(kPfThreads) void k_pf_gateup(PrefillArgs a) {
-  constexpr int SLICE = kGuSlice;
-  __shared__ GemmSmem<SLICE> s;
-  int yb;
-  const TileRows tr = tile_rows(a, s.toff, a.I / kGuCols, yb);
-  if (tr.g < 0) return;
+template <class SM>
+__device__ __forceinline__ void gateup_tile(const PrefillArgs& a, const TileRows& tr, const TileSmem& ts, SM& s,
+                                            int yb) {
+  constexpr int kMT = SM::kRows / 16, SLICE = SM::kSlice;
   const int wave = wave_id(), lane = (int)threadIdx.x & 63;
   const int mi = lane & 15, kb = lane >> 4;
-  const bool routed = tr.g < a.E;
-  if (threadIdx.x < kTileTok) {
-    const int r = (int)threadIdx.x;
-    s.tok[r] = r >= tr.nrows ? -1 : routed ? a.perm[tr.row0 + r] / a.k : tr.r0 + r;
-  }
   const GroupW gw = group_w(a, tr.g, 0);
   const int j0 = yb * kGuCols, j = j0 + 16 * wave + mi;
   const uint16_t* xsrc = a.prenorm ? a.xhat : a.x;
   const int H = a.H, I = a.I;
-  f32x4_t accg[4], accu[4];
+  f32x4_t accg[kMT], accu[kMT];
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt) accg[mt] = accu[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  __syncthreads();   // the token list is written
-  Stage<SLICE> st;
-  st.setup(a.g13, H, [&](int m) { return s.tok[m]; },
+  for (int mt = 0; mt < kMT; ++mt) accg[mt] = accu[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  Stage<SM> st;
+  st.setup(a.g13, H, [&](int m) { return ts.tok[m]; },
            [&](int r) { return r < kGuCols ? j0 + r : I + j0 + (r - kGuCols); });
   st.load(xsrc, gw.codes, gw.scales, 0);
   for (int k0 = 0; k0 < H; k0 += SLICE) {
@@ -590,7 +598,7 @@ __global__ __launch_bounds__(kPfThreads) void k_pf_gateup(PrefillArgs a) {
   }
   // h = SiLU(g) * u at the tile's sorted rows; the lane holds rows 16 mt + 4 kb + i
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt)
+  for (int mt = 0; mt < kMT; ++mt)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int m = 16 * mt + 4 * kb + i;
@@ -599,25 +607,38 @@ __global__ __launch_bounds__(kPfThreads) void k_pf_gateup(PrefillArgs a) {
     }
 }
 
+template <bool LONG>
+__global__ __launch_bounds__(kPfThreads) void k_pf_gateup(PrefillArgs a) {
+  __shared__ TileSmem ts;
+  __shared__ __align__(16) uint8_t raw[kSmemBytes];
+  int yb;
+  const TileRows tr = tile_rows(a, ts.toff, a.I / kGuCols, yb);
+  if (tr.g < 0) return;
+  if (threadIdx.x < kTileTok) {
+    const int r = (int)threadIdx.x;
+    ts.tok[r] = r >= tr.nrows ? -1 : tr.g < a.E ? a.perm[tr.row0 + r] / a.k : tr.r0 + r;
+  }
+  __syncthreads();   // the token list is written
+  if (LONG && tr.nrows > 64) gateup_tile(a, tr, ts, *reinterpret_cast<SmemLong<kSliceLong>*>(raw), yb);
+  else gateup_tile(a, tr, ts, *reinterpret_cast<SmemShort*>(raw), yb);
+}
+
 // down: workgroup (tile, y) takes outputs [128 y, 128 y + 128) (W2 rows);
 // wave w's lanes take outputs 128 y + 32 w + 16 nt + lane % 16, nt = 0, 1.
-// K = I; SLICE = min(I, kDnSlice).
-template <int SLICE>
-__global__ __launch_bounds__(kPfThreads) void k_pf_down(PrefillArgs a) {
-  __shared__ GemmSmem<SLICE> s;
-  int yb;
-  const TileRows tr = tile_rows(a, s.toff, a.H / kDnCols, yb);
-  if (tr.g < 0) return;
+// K = I, staged in slices of SM::kSlice columns.
+template <class SM>
+__device__ __forceinline__ void down_tile(const PrefillArgs& a, const TileRows& tr, SM& s, int yb) {
+  constexpr int kMT = SM::kRows / 16, SLICE = SM::kSlice;
   const int wave = wave_id(), lane = (int)threadIdx.x & 63;
   const int mi = lane & 15, kb = lane >> 4;
   const GroupW gw = group_w(a, tr.g, 1);
   const int n0 = yb * kDnCols, H = a.H, I = a.I;
-  f32x4_t acc[2][4];
+  f32x4_t acc[2][kMT];
 #pragma unroll
   for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) acc[nt][mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  Stage<SLICE> st;
+    for (int mt = 0; mt < kMT; ++mt) acc[nt][mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  Stage<SM> st;
   st.setup(a.g2, I, [&](int m) { return m < tr.nrows ? tr.row0 + m : -1; }, [&](int r) { return n0 + r; });
   st.load(a.h, gw.codes, gw.scales, 0);
   for (int k0 = 0; k0 < I; k0 += SLICE) {
@@ -630,12 +651,26 @@ __global__ __launch_bounds__(kPfThreads) void k_pf_down(PrefillArgs a) {
 #pragma unroll
   for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+    for (int mt = 0; mt < kMT; ++mt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int m = 16 * mt + 4 * kb + i;
         if (m < tr.nrows) a.y[(size_t)(tr.row0 + m) * H + n0 + 32 * wave + 16 * nt + mi] = acc[nt][mt][i];
       }
+}
+
+// SHORT: the slice of tiles of <= 64 rows, min(I, 256); LS: of longer
+// tiles (if the call has any: LONG), min(I, 128).
+template <int SHORT, int LS, bool LONG>
+__global__ __launch_bounds__(kPfThreads) void k_pf_down(PrefillArgs a) {
+  __shared__ TileSmem ts;
+  __shared__ __align__(16) uint8_t raw[kSmemBytes];
+  static_assert(sizeof(GemmSmem<SHORT, 64>) <= kSmemBytes && sizeof(GemmSmem<LS, 128>) <= kSmemBytes, "fits");
+  int yb;
+  const TileRows tr = tile_rows(a, ts.toff, a.H / kDnCols, yb);
+  if (tr.g < 0) return;
+  if (LONG && tr.nrows > 64) down_tile(a, tr, *reinterpret_cast<GemmSmem<LS, 128>*>(raw), yb);
+  else down_tile(a, tr, *reinterpret_cast<GemmSmem<SHORT, 64>*>(raw), yb);
 }
 
 // ---------------------------------------------------------------- combine
@@ -688,22 +723,36 @@ __global__ __launch_bounds__(kPfThreads) void k_pf_combine(PrefillArgs a) {
 }  // namespace
 
 int prefill_max_tiles(int T, int k, int E, int S) {
-  return (T * k + kTileTok - 1) / kTileTok + E + S * ((T + kTileTok - 1) / kTileTok);
+  // at most ceil(c / 64) <= c / 64 + 1 tiles per group of c rows
+  return (T * k + 63) / 64 + E + S * ((T + 63) / 64);
 }
 
-int launch_prefill(const PrefillArgs& a, void* stream) {
+template <int SHORT, int LS>
+void launch_down(const PrefillArgs& a, bool lng, dim3 grid, hipStream_t st) {
+  if (lng) hipLaunchKernelGGL((k_pf_down<SHORT, LS, true>), grid, dim3(kPfThreads), 0, st, a);
+  else hipLaunchKernelGGL((k_pf_down<SHORT, LS, false>), grid, dim3(kPfThreads), 0, st, a);
+}
+
+int launch_prefill(const PrefillArgs& args, void* stream) {
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  PrefillArgs a = args;
+  // 128-row tiles once the routed groups average 128 rows: fewer decodes of
+  // each weight row per token; below that, more tiles in flight pay better
+  const bool lng = (long long)a.T * a.k >= 128LL * a.E;
+  a.tile_rows = lng ? 128 : 64;
   const int chunks = (prefill_max_tiles(a.T, a.k, a.E, a.S) + 7) / 8;   // of 8 tiles
   (void)hipGetLastError();
   hipLaunchKernelGGL(k_pf_logits, dim3((a.T + kRouteTok - 1) / kRouteTok, (a.E + 63) / 64), dim3(kPfThreads), 0, st, a);
   hipLaunchKernelGGL(k_pf_topk, dim3((a.T + kPfThreads / 64 - 1) / (kPfThreads / 64)), dim3(kPfThreads), 0, st, a);
   hipLaunchKernelGGL(k_pf_count, dim3(a.E), dim3(kPfThreads), 0, st, a);
   hipLaunchKernelGGL(k_pf_place, dim3(a.E), dim3(kPfThreads), 0, st, a);
-  hipLaunchKernelGGL(k_pf_gateup, dim3(chunks * 8 * (a.I / kGuCols)), dim3(kPfThreads), 0, st, a);
+  const dim3 ggrid(chunks * 8 * (a.I / kGuCols));
+  if (lng) hipLaunchKernelGGL(k_pf_gateup<true>, ggrid, dim3(kPfThreads), 0, st, a);
+  else hipLaunchKernelGGL(k_pf_gateup<false>, ggrid, dim3(kPfThreads), 0, st, a);
   const dim3 dgrid(chunks * 8 * (a.H / kDnCols));
-  if (a.I == 64 || kDnSlice == 64) hipLaunchKernelGGL(k_pf_down<64>, dgrid, dim3(kPfThreads), 0, st, a);
-  else if (a.I == 128 || kDnSlice == 128) hipLaunchKernelGGL(k_pf_down<128>, dgrid, dim3(kPfThreads), 0, st, a);
-  else hipLaunchKernelGGL(k_pf_down<256>, dgrid, dim3(kPfThreads), 0, st, a);
+  if (a.I == 64) launch_down<64, 64>(a, lng, dgrid, st);
+  else if (a.I == 128) launch_down<128, 128>(a, lng, dgrid, st);
+  else launch_down<kSliceShort, kSliceLong>(a, lng, dgrid, st);
   hipLaunchKernelGGL(k_pf_combine, dim3(a.T), dim3(kPfThreads), 0, st, a);
   return (int)hipGetLastError();
 }

@@ -9,9 +9,10 @@ definition, evaluated token by token.  Acceptance is the decode path's:
     with the GPU's selection forced);
   * routing weights within 1e-4 of the oracle's;
   * max |gpu - oracle| <= 1e-2 * max |oracle| over the compared rows.
-Cases: the tiny shape (every token compared, ragged T), the Flint shape at
-T = 64 (every token) and T = 1000 (sampled tokens, several tiles per
-expert), pre-norm + residual, distinct per-expert tensor scales, T = 1, and
+Cases: the tiny shape (every token compared, ragged T; T = 1500 with
+128-row tiles), the Flint shape at T = 64 (every token), T = 1000 and
+T = 8192 (sampled tokens, several tiles per expert; 128-row tiles at 8192),
+pre-norm + residual, distinct per-expert tensor scales, T = 1, and
 run-to-run / graph-replay bit equality.
 """
 
@@ -100,13 +101,29 @@ def test_prefill_flint_every_token():
 
 
 def test_prefill_flint_many_tokens_sampled():
-    """T = 1000: ~23 rows per expert on average, the busiest experts span
-    several 32-row tiles; the shared expert spans 32 tiles."""
+    """T = 1000: ~23 rows per expert on average, each routed group in one
+    64-row tile; the shared expert spans 16 tiles."""
     rng = np.random.default_rng(5)
     sample = [0, 1, 999] + rng.choice(1000, size=21, replace=False).tolist()
-    out, ids = check_prefill("flint_b1", 1000, step=4, sample=sample)
-    counts = np.bincount(ids.ravel(), minlength=256)
-    assert counts.max() > 32                      # some expert took more than one tile
+    check_prefill("flint_b1", 1000, step=4, sample=sample)
+
+
+def test_prefill_tiny_long_tiles_every_token():
+    """T = 1500 on the tiny shape (E = 16, top-2): the routed groups average
+    more than 128 rows, so the call runs 128-row tiles: full ones, partial
+    ones of 65..127 rows (8 row blocks) and remainders of <= 64 rows (4 row
+    blocks); the shared expert spans 12 tiles."""
+    out, ids = check_prefill("tiny", 1500, step=11)
+    counts = np.bincount(ids.ravel(), minlength=16)
+    assert counts.min() > 128 and np.any(counts % 128 > 64) and np.any((counts % 128 > 0) & (counts % 128 <= 64))
+
+
+def test_prefill_flint_long_tiles_sampled():
+    """T = 8192 at the Flint shape (the benchmarked size): ~192 rows per
+    routed expert, 128-row tiles; sampled tokens."""
+    rng = np.random.default_rng(9)
+    sample = [0, 8191] + rng.choice(8192, size=14, replace=False).tolist()
+    check_prefill("flint_b1", 8192, step=12, sample=sample)
 
 
 def test_prefill_prenorm_residual():
