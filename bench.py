@@ -59,7 +59,7 @@ def parse():
     p.add_argument("--steps", type=int, default=470)
     p.add_argument("--warmup", type=int, default=94)
     p.add_argument("--workload", default="flint_b1")
-    p.add_argument("--extra", default="flint_b8,flint_2bit_b1,flint_chain16_b1,dense_qkv_b1,dense_qkv_b8,flint_prefill_t1024,flint_prefill_t8192",
+    p.add_argument("--extra", default="flint_b8,flint_2bit_b1,flint_2bit_b8,flint_chain16_b1,dense_qkv_b1,dense_qkv_b8,flint_prefill_t1024,flint_prefill_t8192",
                    help="comma-separated extra workloads ('' for none)")
     p.add_argument("--all", action="store_true", help="also the BF16 and expert-sink workloads")
     p.add_argument("--slots", type=int, default=47)

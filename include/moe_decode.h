@@ -78,8 +78,9 @@ typedef enum {
  * experts at FP4 quality"): W = LEVEL[q] * e4m3 block-16 scale * fp32 tensor scale,
  * LEVEL = {-4, -1, 1, 4} for q = 0..3; canonical codes uint8 [rows][cols/4], element 4j+i
  * in bits 2i..2i+1 of byte j; scales and tensor scales as NVFP4.  Routed experts only,
- * on the Flint shape at batch 1 (max_batch 1, NVFP4 shared expert, sigmoid routing);
- * moe_requant_2bit makes the planes from NVFP4 experts.                                */
+ * on the Flint shape (batch 1 to 8, NVFP4 shared expert, sigmoid routing, a device with
+ * the 256 compute units the dedicated kernels take); moe_requant_2bit makes the planes
+ * from NVFP4 experts.                                                                  */
 typedef enum { MOE_W_NVFP4 = 0, MOE_W_BF16 = 1, MOE_W_2BIT = 2 } moe_wtype;
 
 /* The two expert sets of a layer.  The routed set lives in two buffers (moe_decode_layer's

@@ -67,11 +67,11 @@ int plan_shapes(const moe_layer_desc* d, Plan* p) {
   p->Er = Er;
   p->maxd = (d->max_batch * k < E) ? d->max_batch * k : E;
   p->G = 0;
-  // 2-bit routed experts run on the batch-1 kernel of the Flint shape only
+  // 2-bit routed experts run on the dedicated kernels of the Flint shape only
+  // (batch 1 and batch 2-8)
   if (d->routed_wtype == MOE_W_2BIT)
     return (H == moe::FlintShape::H && I == moe::FlintShape::I && E == moe::FlintShape::E && k == moe::FlintShape::k &&
-            S == moe::FlintShape::S && d->shared_wtype == MOE_W_NVFP4 && d->route == MOE_ROUTE_SIGMOID_TOPK &&
-            d->max_batch == 1)
+            S == moe::FlintShape::S && d->shared_wtype == MOE_W_NVFP4 && d->route == MOE_ROUTE_SIGMOID_TOPK)
                ? MOE_OK
                : MOE_ERR_UNSUPPORTED;
   // a kernel variant must exist for every batch bucket the layer may run
@@ -378,12 +378,13 @@ int plan_device(const moe_layer_desc* desc, Plan* pp, int device) {
   }
   const int rwt = desc->routed_wtype, swt = desc->shared_wtype;
   if (rwt == MOE_W_2BIT) {
-    // only the batch-1 kernel takes 2-bit routed experts
-    p.b8 = 0;
-    int occ1 = 0;
+    // only the dedicated kernels take 2-bit routed experts: batch 1 and, for
+    // a layer that may run more tokens, batch 2-8
+    int occ1 = 0, occ8 = 0;
     p.b1 = cus >= moe::kB1Workgroups && moe::b1_occupancy(&occ1) == 0 && occ1 >= 1;
+    p.b8 = cus >= moe::kB1Workgroups && moe::b8_occupancy(&occ8) == 0 && occ8 >= 1;
     (void)hipGetLastError();
-    if (!p.b1) return MOE_ERR_UNSUPPORTED;
+    if (!p.b1 || (desc->max_batch > 1 && !p.b8)) return MOE_ERR_UNSUPPORTED;
     plan_grid(desc, &p, moe::kB1Workgroups);
     return MOE_OK;
   }
@@ -760,7 +761,7 @@ int launch_layer(const moe_layer* L, const moe::FusedArgs& a, void* stream) {
       b.r2bit = L->d.routed_wtype == MOE_W_2BIT;
       return moe::launch_b1(b, stream);
     }
-    if (a.B >= 2 && L->p.b8) return moe::launch_b8(a, a.B, stream);
+    if (a.B >= 2 && L->p.b8) return moe::launch_b8(a, a.B, L->d.routed_wtype == MOE_W_2BIT, stream);
   }
   return moe::launch_fused(a, tb_of(a.B), L->d.routed_wtype, L->d.shared_wtype, stream);
 }

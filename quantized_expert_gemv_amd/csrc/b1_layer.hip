@@ -100,26 +100,6 @@ __device__ __forceinline__ uint32_t tag_at(uint32_t t0, int l) {
   return t;
 }
 
-// One 8-byte chunk of the 2-bit planes (32 codes, element k in bits 2k,
-// 2k+1) as the 16-byte e2m1 chunk of the same values: code q -> nibble
-// {-4, -1, 1, 4} = {0xE, 0xA, 0x2, 0x6}, i.e. 0b0010 with bit 3 = NOT q1 and
-// bit 2 = (q0 == q1).  The 2-bit fields are first spread to nibbles.
-__device__ __forceinline__ uint32_t widen_2bit_half(uint32_t h) {
-  uint32_t x = h & 0xFFFFu;
-  x = (x | (x << 8)) & 0x00FF00FFu;
-  x = (x | (x << 4)) & 0x0F0F0F0Fu;
-  x = (x | (x << 2)) & 0x33333333u;
-  const uint32_t b0 = x & 0x11111111u, b1 = (x >> 1) & 0x11111111u;
-  return 0x22222222u | ((b1 ^ 0x11111111u) << 3) | ((~(b0 ^ b1) & 0x11111111u) << 2);
-}
-__device__ __forceinline__ uint4 widen_2bit(const uint2& v) {
-  return make_uint4(widen_2bit_half(v.x), widen_2bit_half(v.x >> 16), widen_2bit_half(v.y), widen_2bit_half(v.y >> 16));
-}
-__device__ __forceinline__ uint2 ld8o(const uint8_t* base, uint32_t off) {
-  typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
-  const u32x2_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(base + off));
-  return make_uint2(v.x, v.y);
-}
 
 // Shared-memory position of 16-byte unit q of 64-byte chunk c: the units a
 // wave reads in one instruction (one per chunk, same q) fall in distinct banks.

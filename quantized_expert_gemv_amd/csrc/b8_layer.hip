@@ -142,13 +142,23 @@ __device__ __forceinline__ ItemRef item_ref(const KCommon& a, const SbSmem& s, i
 struct GuOffsets {
   uint32_t gate, up, sg, su;   // byte offsets of this lane's gate / up codes and scale words
 };
-__device__ __forceinline__ void gu_load(GuTile& t, const ItemRef& r, const GuOffsets& o, bool dm) {
+// two: the item's codes are 2-bit planes (same chunk order, 8 bytes a
+// chunk: every code offset halves); they stay narrow in t.c[].x, .y until
+// gu_item widens them, so that no instruction touches them before then.
+__device__ __forceinline__ void gu_load(GuTile& t, const ItemRef& r, const GuOffsets& o, bool dm, bool two) {
   const uint32_t m = dm ? 0u : ~0u;
   t.ts = *reinterpret_cast<const float2*>(r.ts);
-  t.c[0] = ld16o(r.cb, o.gate & m);
-  t.c[1] = ld16o(r.cb, (o.gate + kSbRow13) & m);
-  t.c[2] = ld16o(r.cb, o.up & m);
-  t.c[3] = ld16o(r.cb, (o.up + kSbRow13) & m);
+  const uint32_t off[4] = {o.gate & m, (o.gate + kSbRow13) & m, o.up & m, (o.up + kSbRow13) & m};
+  if (two) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint2 v = ld8o(r.cb, off[i] >> 1);
+      t.c[i] = make_uint4(v.x, v.y, 0u, 0u);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) t.c[i] = ld16o(r.cb, off[i]);
+  }
   t.sg = ld32o(r.sb, o.sg & m);
   t.su = ld32o(r.sb, o.su & m);
 }
@@ -176,10 +186,10 @@ __device__ __forceinline__ void wave_sum4(float (&v)[4]) {
 // SiLU(gate) * up of intermediates 2w, 2w + 1 for each token of item j, from
 // the item's gate/up share; published as the token's h word w of its pair.
 __device__ __forceinline__ void gu_item(const KCommon& a, SbSmem& s, const GuTile& t, int j, int B, int w, int lane,
-                                        uint32_t tag) {
+                                        uint32_t tag, bool two) {
   uint32_t wd[4][16];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) decode_chunk(t.c[r], wd[r]);
+  for (int r = 0; r < 4; ++r) decode_chunk(two ? widen_2bit(make_uint2(t.c[r].x, t.c[r].y)) : t.c[r], wd[r]);
   float sc0[4], sc1[4];
   sc0[0] = e4m3f<0>(t.sg);
   sc1[0] = e4m3f<1>(t.sg);
@@ -219,6 +229,8 @@ __device__ __forceinline__ void gu_item(const KCommon& a, SbSmem& s, const GuTil
   }
 }
 
+// R2: the routed experts are 2-bit planes (the shared expert stays NVFP4).
+template <bool R2>
 __global__ __launch_bounds__(kSbThreads) void k_b8_layer(KCommon a, int B) {
   __shared__ SbSmem s;
   const int tid = threadIdx.x, wave = wave_id(), lane = tid & 63;
@@ -298,7 +310,7 @@ __global__ __launch_bounds__(kSbThreads) void k_b8_layer(KCommon a, int B) {
   if (shared_wave) {
     // after x: issued at the start, these loads slowed the router rows
     sb_wait(&s.x_ready, B, deadline, a.err);
-    gu_load(g0, item_ref(a, s, 0), go, false);
+    gu_load(g0, item_ref(a, s, 0), go, false, false);
   }
 
   // ---- 2. logits of every expert and token; routing; the union of the selections ---------
@@ -428,8 +440,14 @@ __global__ __launch_bounds__(kSbThreads) void k_b8_layer(KCommon a, int B) {
       const ItemRef r = item_ref(a, s, j);
       const uint8_t* cb = dn_wave ? r.cb + r.w2c : dummy;
       const uint8_t* sb = dn_wave ? r.sb + r.w2s : dummy;
-      dn[p].c[0] = ld16o(cb, dn_wave ? dn_c : 0u);
-      dn[p].c[1] = ld16o(cb, dn_wave ? dn_c + kSbStep2 : 0u);
+      if (R2 && p < SK) {   // a routed pair's 2-bit rows: narrow until the down products
+        const uint2 v0 = ld8o(cb, dn_wave ? dn_c >> 1 : 0u), v1 = ld8o(cb, dn_wave ? (dn_c + kSbStep2) >> 1 : 0u);
+        dn[p].c[0] = make_uint4(v0.x, v0.y, 0u, 0u);
+        dn[p].c[1] = make_uint4(v1.x, v1.y, 0u, 0u);
+      } else {
+        dn[p].c[0] = ld16o(cb, dn_wave ? dn_c : 0u);
+        dn[p].c[1] = ld16o(cb, dn_wave ? dn_c + kSbStep2 : 0u);
+      }
       dn[p].sw = ld32o(sb, dn_wave ? dn_s : 0u);
     }
   }
@@ -450,17 +468,19 @@ __global__ __launch_bounds__(kSbThreads) void k_b8_layer(KCommon a, int B) {
   // a grab past the last slot loads a dummy; later grabs are past it too
   int ja = shared_wave ? 0 : grab();
   int jb = grab();
-  if (!shared_wave) gu_load(g0, item_ref(a, s, min(ja, nd)), go, ja > nd);
-  gu_load(g1, item_ref(a, s, min(jb, nd)), go, jb > nd);
+  // item j's codes are 2-bit planes when R2 and j is a routed slot; a dummy
+  // load past the last slot reads the last slot's region
+  if (!shared_wave) gu_load(g0, item_ref(a, s, min(ja, nd)), go, ja > nd, R2 && ja > 0);
+  gu_load(g1, item_ref(a, s, min(jb, nd)), go, jb > nd, R2);
   while (true) {
     if (ja > nd) break;
-    gu_item(a, s, g0, ja, B, w, lane, tag);
+    gu_item(a, s, g0, ja, B, w, lane, tag, R2 && ja > 0);
     ja = grab();
-    gu_load(g0, item_ref(a, s, min(ja, nd)), go, ja > nd);
+    gu_load(g0, item_ref(a, s, min(ja, nd)), go, ja > nd, R2);
     if (jb > nd) break;
-    gu_item(a, s, g1, jb, B, w, lane, tag);
+    gu_item(a, s, g1, jb, B, w, lane, tag, R2 && jb > 0);
     jb = grab();
-    gu_load(g1, item_ref(a, s, min(jb, nd)), go, jb > nd);
+    gu_load(g1, item_ref(a, s, min(jb, nd)), go, jb > nd, R2);
   }
   // ---- 4. down rows of token b: its pairs' 256 h words each, then the rows,
   // written straight to the output ---------------------------------------------------
@@ -514,8 +534,9 @@ __global__ __launch_bounds__(kSbThreads) void k_b8_layer(KCommon a, int B) {
 #pragma unroll
   for (int p = 0; p <= SK; ++p) {
     uint32_t wd[2][16], hk[16];
-    decode_chunk(dn[p].c[0], wd[0]);
-    decode_chunk(dn[p].c[1], wd[1]);
+    const bool two = R2 && p < SK;
+    decode_chunk(two ? widen_2bit(make_uint2(dn[p].c[0].x, dn[p].c[0].y)) : dn[p].c[0], wd[0]);
+    decode_chunk(two ? widen_2bit(make_uint2(dn[p].c[1].x, dn[p].c[1].y)) : dn[p].c[1], wd[1]);
 #pragma unroll
     for (int q = 0; q < 4; ++q)
       unpack4(reinterpret_cast<const uint4*>(&s.u.hs[b * (SK + 1) + p][0])[unit_pos(jj, q)], &hk[4 * q]);
@@ -547,16 +568,24 @@ __global__ __launch_bounds__(kSbThreads) void k_b8_layer(KCommon a, int B) {
 
 }  // namespace
 
-int launch_b8(const KCommon& a, int batch, void* stream) {
+int launch_b8(const KCommon& a, int batch, bool r2bit, void* stream) {
   if (batch < 2 || batch > kSbMaxB) return (int)hipErrorInvalidValue;
   (void)hipGetLastError();
-  hipLaunchKernelGGL(k_b8_layer, dim3(256), dim3(kSbThreads), 0, reinterpret_cast<hipStream_t>(stream), a, batch);
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (r2bit) hipLaunchKernelGGL(k_b8_layer<true>, dim3(256), dim3(kSbThreads), 0, st, a, batch);
+  else hipLaunchKernelGGL(k_b8_layer<false>, dim3(256), dim3(kSbThreads), 0, st, a, batch);
   return (int)hipGetLastError();
 }
 
 int b8_occupancy(int* blocks_per_cu) {
-  return (int)hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, reinterpret_cast<const void*>(&k_b8_layer),
+  int o0 = 0, o1 = 0;
+  int rc = (int)hipOccupancyMaxActiveBlocksPerMultiprocessor(
+      &o0, reinterpret_cast<const void*>(&k_b8_layer<false>), kSbThreads, 0);
+  if (rc == 0)
+    rc = (int)hipOccupancyMaxActiveBlocksPerMultiprocessor(&o1, reinterpret_cast<const void*>(&k_b8_layer<true>),
                                                            kSbThreads, 0);
+  *blocks_per_cu = o0 < o1 ? o0 : o1;
+  return rc;
 }
 
 }  // namespace moe

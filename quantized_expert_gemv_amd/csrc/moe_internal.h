@@ -346,7 +346,7 @@ int launch_dense(const DenseArgs& a, void* stream);
 int dense_grid(const MatGeom& g);
 
 // Batch 2-8 kernel of the same layers: 256 workgroups of 512 threads.
-int launch_b8(const KCommon& a, int batch, void* stream);
+int launch_b8(const KCommon& a, int batch, bool r2bit, void* stream);
 int b8_occupancy(int* blocks_per_cu);
 
 }  // namespace moe

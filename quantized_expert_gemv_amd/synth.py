@@ -79,6 +79,11 @@ WORKLOADS = {
     "flint_2bit_b1": Workload(10, "flint_2bit_b1", 2048, 512, 256, 6, 1, 1, routed_wtype="2bit",
                               description="Flint-shaped: H=2048 I=512 E=256 top-6, routed experts in 2-bit "
                                           "sign-symmetric planes, 1 NVFP4 shared, b1"),
+    "flint_2bit_b8": Workload(11, "flint_2bit_b8", 2048, 512, 256, 6, 1, 8, routed_wtype="2bit",
+                              router_std=None, bias_std=0.5,
+                              description="Flint-shaped: H=2048 I=512 E=256 top-6, routed experts in 2-bit "
+                                          "sign-symmetric planes, 1 NVFP4 shared, b8, router N(0,1/sqrt(H)) + "
+                                          "bias N(0,0.5)"),
     "sink_b4": Workload(4, "sink_b4", 7168, 2048, 256, 6, 2, 4,
                         route="sink", shared_wtype="bf16",
                         description="expert sink: H=7168 I=2048 E=256 NVFP4 top-6 + 2 BF16 shared in a 258-way softmax, b4"),

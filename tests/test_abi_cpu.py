@@ -315,11 +315,13 @@ def test_requant_argument_checks():
 
 
 def test_2bit_layer_validation_rules():
-    """2-bit routed experts: the Flint shape at batch 1 with an NVFP4 shared
-    expert and sigmoid routing; anything else is unsupported."""
+    """2-bit routed experts: the Flint shape at batch 1 to 8 with an NVFP4
+    shared expert and sigmoid routing; anything else is unsupported."""
     flint = dict(hidden=2048, inter=512, n_routed=256, top_k=6, n_shared=1, routed_wtype="2bit")
     assert B.moe_layer_validate(B.make_desc(max_batch=1, **flint)) == 0
-    assert B.moe_layer_validate(B.make_desc(max_batch=2, **flint)) == -2
+    assert B.moe_layer_validate(B.make_desc(max_batch=2, **flint)) == 0
+    assert B.moe_layer_validate(B.make_desc(max_batch=8, **flint)) == 0
+    assert B.moe_layer_validate(B.make_desc(max_batch=9, **flint)) == -2
     assert B.moe_layer_validate(B.make_desc(max_batch=1, shared_wtype="bf16", **flint)) == -2
     assert B.moe_layer_validate(B.make_desc(max_batch=1, route="sink", **flint)) == -2
     assert B.moe_layer_validate(B.make_desc(hidden=1024, inter=256, n_routed=64, top_k=4, n_shared=1, max_batch=1,

@@ -1,5 +1,6 @@
-"""GPU parity of the batch-1 layer with routed experts in the sign-symmetric
-2-bit planes (moe_decode_layer, through the C ABI) against the fp64 oracle.
+"""GPU parity of the layer with routed experts in the sign-symmetric 2-bit
+planes (moe_decode_layer, through the C ABI) against the fp64 oracle, at
+batch 1 and at batch 2-8.
 
 The layer is the Flint shape (H=2048, I=512, 256 routed experts, top-6, one
 NVFP4 shared expert); the routed experts' codes are uniform over the four
@@ -7,7 +8,10 @@ levels {-4, -1, 1, 4} with e4m3 block scales drawn as for NVFP4.  Acceptance
 is the decode path's: selection exact except near ties (gap < 1e-5), weights
 within 1e-4, max |gpu - oracle| <= 1e-2 max |oracle|; plus the per-pair h of
 the selected experts against the oracle's, distinct per-expert tensor scales,
-bitwise repetition and the handle-less entry point.
+bitwise repetition and the handle-less entry point.  At batch 2-8 the
+workload is the batch-8 one (router N(0, 1/sqrt(H)) + bias N(0, 0.5), so the
+tokens share some experts): batches 8, 3 and 2, distinct tensor scales, and
+bitwise repetition.
 """
 
 import sys
@@ -52,6 +56,45 @@ def dev_of(tscales=False):
             pytest.skip("2-bit experts run on the batch-1 kernel of the Flint shape (256 CUs)")
         _DEVS[tscales] = (layer, dev)
     return _DEVS[tscales]
+
+
+def dev_b8(tscales=False):
+    from quantized_expert_gemv_amd.device_layer import DeviceLayer
+    from quantized_expert_gemv_amd.synth import SynthLayer
+    key = ("b8", tscales)
+    if key not in _DEVS:
+        _note(f"[upload] flint_2bit_b8 tensor_scales={'distinct' if tscales else 'unit'}")
+        layer = SynthLayer("flint_2bit_b8", tscale_set=TS_SET if tscales else None)
+        dev = DeviceLayer(layer, 8)
+        if dev.set_path("auto") != "dedicated":
+            pytest.skip("2-bit experts run on the dedicated kernels of the Flint shape (256 CUs)")
+        _DEVS[key] = (layer, dev)
+    return _DEVS[key]
+
+
+@pytest.mark.parametrize("step,batch", [(0, 8), (1, 8), (2, 3), (3, 2)])
+def test_2bit_b8_meets_the_oracle(step, batch):
+    layer, dev = dev_b8()
+    r = compare_layer(dev, layer, layer.x(step, batch=batch))
+    _note(f"[2bit b{batch}] step {step}: rel_err={r['rel_err']:.3e} w_err={r['w_err']:.2e} "
+          f"mismatched={r['mismatched']} exempt={r['exempt']}")
+    assert not r["mismatched"] and r["rel_err"] <= 1e-2 and r["w_err"] <= 1e-4
+
+
+def test_2bit_b8_distinct_tensor_scales_and_repeats_bitwise():
+    from quantized_expert_gemv_amd.device_layer import bits_to_bf16_tensor
+    layer, dev = dev_b8(tscales=True)
+    x_bits = layer.x(4, batch=8)
+    r = compare_layer(dev, layer, x_bits)
+    _note(f"[2bit b8 ts] rel_err={r['rel_err']:.3e} mismatched={r['mismatched']}")
+    assert not r["mismatched"] and r["rel_err"] <= 1e-2 and r["w_err"] <= 1e-4
+    x = bits_to_bf16_tensor(x_bits, dev.device)
+    first = dev(x).clone()
+    for _ in range(3):
+        again = dev(x)
+        torch.cuda.synchronize()
+        assert torch.equal(again.view(torch.int16), first.view(torch.int16))
+    assert dev.error() == 0
 
 
 @pytest.mark.parametrize("step", [0, 1, 2, 3])
