@@ -31,6 +31,8 @@
 // has a fixed order: the result does not depend on scheduling.
 
 #include <hip/hip_runtime.h>
+
+#include <algorithm>
 #include <math.h>
 #include <stdint.h>
 
@@ -66,9 +68,11 @@ __device__ __forceinline__ f32x4_t mfma32(const uint4& a, const uint4& b, f32x4_
 }
 
 // ---------------------------------------------------------------- routing
-// Logits: workgroup (token block, expert block) takes 16 tokens x 64 experts;
-// wave w the 16 experts 64 y + 16 w.  The 16 rows (pre-normed if the layer
-// has a pre-norm; blocks of y = 0 write them to xhat) sit in shared memory;
+// Logits: workgroup (token block, y) takes 16 tokens and the blocks of 64
+// experts y, y + Y, ... (Y = gridDim.y: the fewer, the fewer times a token's
+// row is read; the host keeps >= ~1024 workgroups); wave w the 16 experts at
+// 16 w of each block.  The 16 rows (pre-normed if the layer has a pre-norm;
+// workgroups of y = 0 write them to xhat) sit in shared memory;
 // lane (m = lane % 16, kb = lane / 16) feeds row m and columns 8 kb .. + 8 of
 // each 32-column step, router rows stream from memory 8 steps at a time
 // (the next 8 in flight while these 8 multiply).
@@ -121,8 +125,7 @@ __global__ __launch_bounds__(kPfThreads) void k_pf_logits(PrefillArgs a) {
     __syncthreads();
   }
   const int mi = lane & 15, kb = lane >> 4;
-  const int e0 = blockIdx.y * 64 + 16 * wave;
-  if (e0 >= a.E) return;
+  for (int e0 = 64 * blockIdx.y + 16 * wave; e0 < a.E; e0 += 64 * gridDim.y) {   // the wave's 16-expert blocks
   const uint16_t* rrow = a.router_w + (size_t)(e0 + mi) * H + 8 * kb;
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
   // two sets of router steps: one set's loads fly while the other's products run
@@ -150,6 +153,7 @@ __global__ __launch_bounds__(kPfThreads) void k_pf_logits(PrefillArgs a) {
   for (int r = 0; r < 4; ++r) {
     const int t = t0 + 4 * kb + r;
     if (t < a.T) a.logits[(size_t)t * a.E + e] = acc[r] + bias;
+  }
   }
 }
 
@@ -742,7 +746,9 @@ int launch_prefill(const PrefillArgs& args, void* stream) {
   a.tile_rows = lng ? 128 : 64;
   const int chunks = (prefill_max_tiles(a.T, a.k, a.E, a.S) + 7) / 8;   // of 8 tiles
   (void)hipGetLastError();
-  hipLaunchKernelGGL(k_pf_logits, dim3((a.T + kRouteTok - 1) / kRouteTok, (a.E + 63) / 64), dim3(kPfThreads), 0, st, a);
+  const int tblocks = (a.T + kRouteTok - 1) / kRouteTok, eblocks = (a.E + 63) / 64;
+  const int ygroups = std::min(eblocks, std::max(1, (1024 + tblocks - 1) / tblocks));
+  hipLaunchKernelGGL(k_pf_logits, dim3(tblocks, ygroups), dim3(kPfThreads), 0, st, a);
   hipLaunchKernelGGL(k_pf_topk, dim3((a.T + kPfThreads / 64 - 1) / (kPfThreads / 64)), dim3(kPfThreads), 0, st, a);
   hipLaunchKernelGGL(k_pf_count, dim3(a.E), dim3(kPfThreads), 0, st, a);
   hipLaunchKernelGGL(k_pf_place, dim3(a.E), dim3(kPfThreads), 0, st, a);
