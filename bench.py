@@ -28,10 +28,11 @@ launch duration (the roofline figure uses it).  Also reported:
     the per-launch floor (an empty 256-workgroup kernel, 200 launches in a
     graph);
   * the fp64 oracle on the host's cores at 1 thread and at all threads.
-Other workloads (--extra, default flint_b8, a 16-layer chain in one launch,
-the dense QKV GEMV at batch 1 and 8, and the prefill of 1024 and 8192 tokens;
---all adds the BF16 and expert-sink workloads) are measured the same way and
-reported under "configs" in the same JSON line.
+Other workloads (--extra, default: Flint b8, the 2-bit planes at b1 and b8,
+BF16 experts at b1 and b8, the expert-sink layer at b4, a 16-layer chain in
+one launch, the dense QKV GEMV at batch 1 and 8, and the prefill of 1024 and
+8192 tokens) are measured the same way and reported under "configs" in the
+same JSON line.
 
 Prints one JSON line.
 """
@@ -59,9 +60,10 @@ def parse():
     p.add_argument("--steps", type=int, default=470)
     p.add_argument("--warmup", type=int, default=94)
     p.add_argument("--workload", default="flint_b1")
-    p.add_argument("--extra", default="flint_b8,flint_2bit_b1,flint_2bit_b8,flint_chain16_b1,dense_qkv_b1,dense_qkv_b8,flint_prefill_t1024,flint_prefill_t8192",
+    p.add_argument("--extra", default="flint_b8,flint_2bit_b1,flint_2bit_b8,flint_bf16_b1,flint_bf16_b8,sink_b4,"
+                                      "flint_chain16_b1,dense_qkv_b1,dense_qkv_b8,flint_prefill_t1024,flint_prefill_t8192",
                    help="comma-separated extra workloads ('' for none)")
-    p.add_argument("--all", action="store_true", help="also the BF16 and expert-sink workloads")
+    p.add_argument("--all", action="store_true", help="also the tiny workload")
     p.add_argument("--slots", type=int, default=47)
     p.add_argument("--replays", type=int, default=8)
     p.add_argument("--cpu-seconds", type=float, default=16.0, help="budget of the oracle CPU baseline")
@@ -612,7 +614,7 @@ def main():
     head, layer, xs_bits = measure(args.workload, K, W, SLOTS.get(args.workload, args.slots), args.replays, flush)
     extras = [n for n in args.extra.split(",") if n]
     if args.all:
-        extras += [n for n in ("flint_bf16_b1", "flint_bf16_b8", "sink_b4") if n not in extras]
+        extras += [n for n in ("tiny",) if n not in extras]
     configs = {}
     for n in extras:
         if n in DENSE:
