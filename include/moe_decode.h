@@ -408,11 +408,13 @@ int moe_prefill_layer(moe_layer_t layer, const void* x, const void* router_w,
                       int32_t* topk_ids, float* topk_w, void* stream);
 
 /* Test hook: which kernels run the handle's later calls.  MOE_PATH_AUTO (the default)
- * takes the kernels dedicated to the Flint shape where the layer has them (NVFP4 routed
- * and shared experts, sigmoid router, a device with at least 256 compute units): the
- * batch-1 kernel with a wavefront per expert, and the batch 2-8 kernel; every other
- * layer runs the general kernel.  MOE_PATH_GENERAL always takes the general kernel.
- * Both compute the same layer (their sums run in different orders).  Returns the path
+ * takes the kernels dedicated to the Flint shape where the layer has them (NVFP4 or
+ * 2-bit routed and NVFP4 shared experts, sigmoid router, a device with at least 256
+ * compute units): the batch-1 kernel with a wavefront per expert, and the batch 2-8
+ * kernel; every other layer runs the general kernel.  MOE_PATH_GENERAL always takes the
+ * general kernel, and is refused (MOE_ERR_UNSUPPORTED) for a 2-bit layer, which has no
+ * general kernel.  Both compute the same layer (their sums run in different orders).
+ * Returns the path
  * now in force through *active (may be NULL): MOE_PATH_DEDICATED or MOE_PATH_GENERAL.
  * Host-only; affects no call already made.                                           */
 enum moe_path { MOE_PATH_AUTO = 0, MOE_PATH_GENERAL = 1, MOE_PATH_DEDICATED = 2 };
