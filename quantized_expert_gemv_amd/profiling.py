@@ -6,8 +6,9 @@
 
 `traffic` turns the per-dispatch FETCH_SIZE / WRITE_SIZE counters (KiB) of
 each kernel into bytes per launch, each counter scaled by what it reads for
-a plain device copy of N bytes run in the same process (the largest
-copyBuffer dispatch), and records the digest of the kernel sources the
+a plain device copy of N bytes run in the same process (the benchmark runs it
+last: the process's last copyBuffer dispatch; weight uploads and slot copies
+come before it), and records the digest of the kernel sources the
 counters were taken with, so a later benchmark can tell whether they still
 describe the current kernels.
 """
@@ -58,10 +59,24 @@ def counter_means(path: str) -> dict:
     return agg
 
 
+def last_copy(path: str, counter: str) -> float:
+    """The counter of the last copyBuffer dispatch (highest dispatch id)."""
+    best = None
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if short_name(r["Kernel_Name"]) == "__amd_rocclr_copyBuffer" and r["Counter_Name"] == counter:
+                d = int(r["Dispatch_Id"])
+                if best is None or d > best[0]:
+                    best = (d, float(r["Counter_Value"]))
+    if best is None:
+        raise SystemExit(f"no copyBuffer dispatch in {path}")
+    return best[1]
+
+
 def traffic(fetch_csv: str, write_csv: str, copy_bytes: int) -> dict:
     fetch, write = counter_means(fetch_csv), counter_means(write_csv)
-    copy_f = max(fetch[("__amd_rocclr_copyBuffer", "FETCH_SIZE")])
-    copy_w = max(write[("__amd_rocclr_copyBuffer", "WRITE_SIZE")])
+    copy_f = last_copy(fetch_csv, "FETCH_SIZE")
+    copy_w = last_copy(write_csv, "WRITE_SIZE")
     kf = copy_bytes / (copy_f * 1024.0)
     kw = copy_bytes / (copy_w * 1024.0)
     out = {"copy_bytes": copy_bytes, "copy_fetch_kib": copy_f, "copy_write_kib": copy_w,
