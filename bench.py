@@ -31,8 +31,8 @@ launch duration (the roofline figure uses it).  Also reported:
 Other workloads (--extra, default: Flint b8, the 2-bit planes at b1 and b8,
 BF16 experts at b1 and b8, the expert-sink layer at b4, a 16-layer chain in
 one launch, the dense QKV GEMV at batch 1 and 8, and the prefill of 1024 and
-8192 tokens) are measured the same way and reported under "configs" in the
-same JSON line.
+8192 tokens with NVFP4 and with 2-bit routed experts) are measured the same
+way and reported under "configs" in the same JSON line.
 
 Prints one JSON line.
 """
@@ -61,7 +61,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=94)
     p.add_argument("--workload", default="flint_b1")
     p.add_argument("--extra", default="flint_b8,flint_2bit_b1,flint_2bit_b8,flint_bf16_b1,flint_bf16_b8,sink_b4,"
-                                      "flint_chain16_b1,dense_qkv_b1,dense_qkv_b8,flint_prefill_t1024,flint_prefill_t8192",
+                                      "flint_chain16_b1,dense_qkv_b1,dense_qkv_b8,flint_prefill_t1024,flint_prefill_t8192,"
+                                      "flint_2bit_prefill_t1024,flint_2bit_prefill_t8192",
                    help="comma-separated extra workloads ('' for none)")
     p.add_argument("--all", action="store_true", help="also the tiny workload")
     p.add_argument("--slots", type=int, default=47)
@@ -501,7 +502,8 @@ def measure_chain(name: str, K: int, W: int, L: int, R: int, flush) -> dict:
 
 # Prefill of T tokens through the Flint-shaped NVFP4 layer (moe_prefill_layer:
 # grouped GEMMs on the matrix cores).  name -> T
-PREFILL = {"flint_prefill_t1024": 1024, "flint_prefill_t8192": 8192}
+PREFILL = {"flint_prefill_t1024": ("flint_b1", 1024), "flint_prefill_t8192": ("flint_b1", 8192),
+           "flint_2bit_prefill_t1024": ("flint_2bit_b1", 1024), "flint_2bit_prefill_t8192": ("flint_2bit_b1", 8192)}
 MFMA_BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 matrix peak
 
 
@@ -514,8 +516,8 @@ def measure_prefill(name: str, K: int, W: int, R: int, flush) -> dict:
     from quantized_expert_gemv_amd.device_layer import DeviceLayer, bits_to_bf16_tensor
     from quantized_expert_gemv_amd.synth import WORKLOADS, SynthLayer
 
-    T = PREFILL[name]
-    wl = WORKLOADS["flint_b1"]
+    wname, T = PREFILL[name]
+    wl = WORKLOADS[wname]
     log(f"prefill of {T} tokens: {wl.description}")
     layer = SynthLayer(wl)
     dev = DeviceLayer(layer, max_batch=1)

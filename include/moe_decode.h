@@ -383,7 +383,8 @@ int moe_decode_chain(const moe_layer_t* layers, int n_layers, const void* x,
  *   down    y = W2 h in fp32 at the same sorted rows;
  *   combine out[t] = sum of the token's shared experts' y, then its routed slots' w * y in
  *           selection order (each times its W2 tensor scale), (+ x), one bf16 rounding.
- * Shapes it takes (else MOE_ERR_UNSUPPORTED): NVFP4 routed and shared experts, sigmoid
+ * Shapes it takes (else MOE_ERR_UNSUPPORTED): NVFP4 or 2-bit routed and NVFP4 shared
+ * experts (a 2-bit expert's chunks widen to e2m1 as they are staged), sigmoid
  * routing, H <= 2048 with H % 256 == 0, I = 64, 128 or a multiple of 256,
  * E <= 256 with E % 16 == 0.  1 <= tokens <= MOE_PREFILL_MAX_TOKENS and
  * tokens * (k + S) * I < 2^32 (else MOE_ERR_BATCH).                                   */

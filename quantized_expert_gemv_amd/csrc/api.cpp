@@ -825,7 +825,8 @@ bool prefill_supported(const moe_layer_desc& d, const Plan& p) {
   // the router GEMM takes 256 columns per pass, the expert GEMMs stage K in
   // slices of min(256, K) columns
   const auto slice_ok = [](int n) { return n % 256 == 0 || n == 64 || n == 128; };   // power-of-two slices
-  return d.routed_wtype == MOE_W_NVFP4 && (d.n_shared == 0 || d.shared_wtype == MOE_W_NVFP4) &&
+  return (d.routed_wtype == MOE_W_NVFP4 || d.routed_wtype == MOE_W_2BIT) &&
+         (d.n_shared == 0 || d.shared_wtype == MOE_W_NVFP4) &&
          d.route == MOE_ROUTE_SIGMOID_TOPK && d.hidden <= moe::kPfMaxH && d.hidden % 256 == 0 &&
          d.inter % 64 == 0 && slice_ok(d.hidden) && slice_ok(d.inter) && d.n_routed <= moe::kPfMaxE &&
          d.n_routed % 16 == 0 && p.g13.ns == 1 && p.g2.ns == 1;
@@ -931,6 +932,7 @@ int moe_prefill_layer(moe_layer_t L, const void* x, const void* router_w, const 
   a.S = d.n_shared;
   a.g13 = L->p.g13;
   a.g2 = L->p.g2;
+  a.r2bit = d.routed_wtype == MOE_W_2BIT;
   char* w = static_cast<char*>(workspace);
   a.xhat = reinterpret_cast<uint16_t*>(w + wl.xhat);
   a.logits = reinterpret_cast<float*>(w + wl.logits);

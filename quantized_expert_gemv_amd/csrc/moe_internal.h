@@ -312,6 +312,7 @@ struct PrefillArgs {
   size_t s_code_stride, s_w13_code, s_scale_stride, s_w13_scale;
   int T, H, I, E, k, S;
   int tile_rows;     // rows per GEMM tile (64 or 128; chosen by launch_prefill)
+  int r2bit;         // routed experts in the 2-bit planes (the shared ones are NVFP4)
   MatGeom g13, g2;
   // caller's workspace
   uint16_t* xhat;   // bf16 [T][H] (prenorm only)

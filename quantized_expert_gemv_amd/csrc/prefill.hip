@@ -446,13 +446,15 @@ struct Stage {
   uint32_t coff[kW];     // byte offset of the chunk's codes at slice 0
   uint32_t soff[kW];     // byte offset of its scale word at slice 0
   uint32_t shi;          // bit i: chunk i's pair is the word's upper half
+  bool two;              // the codes are 2-bit planes: 8-byte chunks at half the offsets
   // the slice in flight
   uint4 av[kA], wv[kW];
   uint32_t sv[kW];
 
   template <class ActRow, class WRow>
-  __device__ __forceinline__ void setup(const MatGeom& g, int K, ActRow&& act_row, WRow&& wrow) {
+  __device__ __forceinline__ void setup(const MatGeom& g, int K, bool two_bit, ActRow&& act_row, WRow&& wrow) {
     const int rsh = __builtin_ctz((unsigned)g.rpw);
+    two = two_bit;
     avalid = 0u;
 #pragma unroll
     for (int i = 0; i < kA; ++i) {
@@ -481,7 +483,15 @@ struct Stage {
     const uint32_t c0 = (uint32_t)(k0 >> 5);
 #pragma unroll
     for (int i = 0; i < kW; ++i) {
-      wv[i] = ld16o(codes, coff[i] + c0 * 16u);
+      if (two) {
+        // a slice takes half of each 128-byte line of 2-bit codes and the
+        // next slice the other half: a cached load, which the L2 may still
+        // hold for the next slice (nontemporal loads were no faster)
+        const uint2 v = *reinterpret_cast<const uint2*>(codes + ((coff[i] + c0 * 16u) >> 1));
+        wv[i] = make_uint4(v.x, v.y, 0u, 0u);
+      } else {
+        wv[i] = ld16o(codes, coff[i] + c0 * 16u);
+      }
       sv[i] = ld32o(scales, soff[i] + c0 * 4u);
     }
   }
@@ -496,7 +506,8 @@ struct Stage {
 #pragma unroll
     for (int i = 0; i < kW; ++i) {
       const int u = (int)threadIdx.x + kPfThreads * i, lr = u >> kNsh, q = u & ((1 << kNsh) - 1);
-      *reinterpret_cast<uint4*>(&s.wc[lr * kWStride + q * 16]) = wv[i];
+      // a 2-bit chunk widens to the e2m1 chunk of the same values here
+      *reinterpret_cast<uint4*>(&s.wc[lr * kWStride + q * 16]) = two ? widen_2bit(make_uint2(wv[i].x, wv[i].y)) : wv[i];
       s.wsc[lr][q] = (uint16_t)(sv[i] >> (((shi >> i) & 1u) << 4));
     }
   }
@@ -590,7 +601,7 @@ __device__ __forceinline__ void gateup_tile(const PrefillArgs& a, const TileRows
 #pragma unroll
   for (int mt = 0; mt < kMT; ++mt) accg[mt] = accu[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   Stage<SM> st;
-  st.setup(a.g13, H, [&](int m) { return ts.tok[m]; },
+  st.setup(a.g13, H, a.r2bit && tr.g < a.E, [&](int m) { return ts.tok[m]; },
            [&](int r) { return r < kGuCols ? j0 + r : I + j0 + (r - kGuCols); });
   st.load(xsrc, gw.codes, gw.scales, 0);
   for (int k0 = 0; k0 < H; k0 += SLICE) {
@@ -643,7 +654,8 @@ __device__ __forceinline__ void down_tile(const PrefillArgs& a, const TileRows& 
 #pragma unroll
     for (int mt = 0; mt < kMT; ++mt) acc[nt][mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   Stage<SM> st;
-  st.setup(a.g2, I, [&](int m) { return m < tr.nrows ? tr.row0 + m : -1; }, [&](int r) { return n0 + r; });
+  st.setup(a.g2, I, a.r2bit && tr.g < a.E, [&](int m) { return m < tr.nrows ? tr.row0 + m : -1; },
+           [&](int r) { return n0 + r; });
   st.load(a.h, gw.codes, gw.scales, 0);
   for (int k0 = 0; k0 < I; k0 += SLICE) {
     __syncthreads();

@@ -161,6 +161,4 @@ def test_2bit_layer_refuses_what_it_cannot_run():
         B.moe_decode_chain([dev.handle], x, [bufs["router_w"]], [bufs["expert_packed"]], [bufs["scales"]],
                            [bufs["shared_w"]], torch.empty_like(x), 1)
     assert e.value.status == -2
-    with pytest.raises(B.MoeError) as e:
-        B.moe_prefill_workspace_bytes(dev.handle, 4)
-    assert e.value.status == -2
+    assert B.moe_prefill_workspace_bytes(dev.handle, 4) > 0   # the prefill path takes 2-bit layers

@@ -12,8 +12,9 @@ definition, evaluated token by token.  Acceptance is the decode path's:
 Cases: the tiny shape (every token compared, ragged T; T = 1500 with
 128-row tiles), the Flint shape at T = 64 (every token), T = 1000 and
 T = 8192 (sampled tokens, several tiles per expert; 128-row tiles at 8192),
-pre-norm + residual, distinct per-expert tensor scales, T = 1, and
-run-to-run / graph-replay bit equality.
+pre-norm + residual, distinct per-expert tensor scales, routed experts in
+the 2-bit planes (T = 64 and T = 8192 sampled, and with distinct tensor
+scales), T = 1, and run-to-run / graph-replay bit equality.
 """
 
 import sys
@@ -124,6 +125,19 @@ def test_prefill_flint_long_tiles_sampled():
     rng = np.random.default_rng(9)
     sample = [0, 8191] + rng.choice(8192, size=14, replace=False).tolist()
     check_prefill("flint_b1", 8192, step=12, sample=sample)
+
+
+def test_prefill_2bit_every_token():
+    """Routed experts in the 2-bit planes (widened to e2m1 as they are
+    staged; the shared expert stays NVFP4), 64-row tiles."""
+    check_prefill("flint_2bit_b1", 64, step=13)
+
+
+def test_prefill_2bit_long_tiles_sampled_and_tensor_scales():
+    rng = np.random.default_rng(14)
+    sample = [0, 8191] + rng.choice(8192, size=10, replace=False).tolist()
+    check_prefill("flint_2bit_b1", 8192, step=14, sample=sample)
+    check_prefill("flint_2bit_b1", 100, step=15, tscales=True)
 
 
 def test_prefill_prenorm_residual():
