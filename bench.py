@@ -10,6 +10,9 @@ model) and step i uses slot i % L with its own input.  One cycle over the
 slots (~631 MB at batch 1) exceeds the 256 MB Infinity Cache plus the 32 MB
 of L2, and a 1 GiB read pass runs before the timed region.
 
+Before the first workload, 0.5 s of untimed read passes (--gpu-warmup-ms)
+let the GPU's clocks settle under load.
+
 Timed region: W eager warm-up steps and one untimed launch of each graph
 below (a graph's first launch also uploads it); then, after the read pass, one
 untimed replay of a graph of the L steps 0 .. L-1 and right behind it a HIP
@@ -66,6 +69,8 @@ def parse():
                    help="comma-separated extra workloads ('' for none)")
     p.add_argument("--all", action="store_true", help="also the tiny workload")
     p.add_argument("--slots", type=int, default=47)
+    p.add_argument("--gpu-warmup-ms", type=int, default=500,
+                   help="untimed read passes before the first measurement (0: none)")
     p.add_argument("--replays", type=int, default=8)
     p.add_argument("--cpu-seconds", type=float, default=16.0, help="budget of the oracle CPU baseline")
     p.add_argument("--no-cpu", action="store_true")
@@ -611,6 +616,15 @@ def main():
         # Infinity Cache and, unlike a write pass, leaves no dirty lines whose
         # write-back would run during the timed steps
         B.moe_bench_read_stream(flush_buf, flush_sink)
+
+    # the GPU's clocks settle under load: read passes for a while before the
+    # first measurement, so that it is taken at the same clocks as the later
+    # ones (untimed, like the warm-up steps)
+    if args.gpu_warmup_ms > 0:
+        t_end = time.perf_counter() + args.gpu_warmup_ms * 1e-3
+        while time.perf_counter() < t_end:
+            flush()
+            torch.cuda.synchronize()
 
     K, W = args.steps, args.warmup
     head, layer, xs_bits = measure(args.workload, K, W, SLOTS.get(args.workload, args.slots), args.replays, flush)
