@@ -1,26 +1,31 @@
 // Prefill / large-batch MoE layer for MI355X (gfx950): T tokens through the
-// same layer as the decode kernels (router GEMV, sigmoid top-k, NVFP4 gate/up
-// with SiLU*up, down, weighted combine), as grouped GEMMs on the matrix cores.
+// same layer as the decode kernels (router GEMV, sigmoid top-k, NVFP4 or
+// 2-bit gate/up with SiLU*up, down, weighted combine), as grouped GEMMs on the
+// matrix cores.
 //
 // The Flint page ("From 1,096 kernels to 346") counts the MoE kernel work as
 // the largest prefill gain; the SM120 page ("How it fits") replaces a
 // [tokens * top_k, hidden] fp32 scatter buffer and its weighted temporary by a
 // direct gather/reduce.  Here, in seven launches on one stream:
 //
-//   k_pf_logits   16 tokens x 64 experts per workgroup: the rows (pre-norm),
-//                 the router logits on MFMA (bf16 x bf16 -> fp32).
+//   k_pf_logits   16 tokens x one or more blocks of 64 experts per workgroup:
+//                 the rows (pre-norm), the router logits on MFMA (bf16 x bf16
+//                 -> fp32).
 //   k_pf_topk     one wave per token: the top-k and weights.
-//   k_pf_count    one workgroup per expert: its number of (token, slot) pairs.
+//   k_pf_count    one workgroup per expert: its number of (token, slot) pairs
+//                 (and each scanning wave's share).
 //   k_pf_place    one workgroup per expert: its pairs in token order, as the
 //                 expert's rows of the sorted list (perm) and the inverse map
 //                 (inv); workgroup 0 also writes the group and tile offsets.
-//   k_pf_gateup   one workgroup per (64-row tile of a group, 64 intermediates):
-//                 the group's tokens' xhat rows staged in shared memory, the
-//                 expert's gate and up rows decoded in registers; h = SiLU(g)*u
-//                 in bf16 at the tile's sorted rows.  A group is an expert's
-//                 sorted rows, or all T tokens for a shared expert.
-//   k_pf_down     one workgroup per (64-row tile, 128 outputs): y = W2 h in
-//                 fp32 at the same sorted rows.
+//   k_pf_gateup   one workgroup per (tile of a group's rows, 64 intermediates):
+//                 the tile's xhat rows and the expert's gate and up rows staged
+//                 slice by slice in shared memory (2-bit codes widened to e2m1
+//                 there); h = SiLU(g)*u in bf16 at the tile's sorted rows.  A
+//                 group is an expert's sorted rows, or all T tokens for a shared
+//                 expert; a tile is 64 rows, or 128 when the call's routed
+//                 groups average 128 rows or more.
+//   k_pf_down     one workgroup per (tile, 128 outputs): y = W2 h in fp32 at
+//                 the same sorted rows.
 //   k_pf_combine  one workgroup per token: out = sum over its shared then its
 //                 routed slots (selection order) of coef * tensor scale * y,
 //                 gathered through inv (+ residual), one bf16 rounding.

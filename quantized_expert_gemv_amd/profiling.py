@@ -21,16 +21,27 @@ import csv
 import hashlib
 import json
 import os
+import re
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 
 
+def _code_only(text: str) -> str:
+    """The source without its comments and blank lines (string literals in
+    these files hold no comment markers)."""
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    lines = [re.sub(r"//.*", "", ln).rstrip() for ln in text.splitlines()]
+    return "\n".join(ln for ln in lines if ln)
+
+
 def src_digest() -> str:
+    """Digest of the kernel and host sources as code: an edit of comments
+    alone leaves it unchanged."""
     h = hashlib.sha256()
     for f in ("layer.hip", "b1_layer.hip", "b8_layer.hip", "dense.hip", "prefill.hip", "kernel_common.h",
               "device_util.h", "api.cpp", "moe_internal.h"):
-        with open(os.path.join(_PKG, "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(_PKG, "csrc", f), encoding="utf-8") as fh:
+            h.update(_code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 
