@@ -598,8 +598,9 @@ def measure_prefill(name: str, K: int, W: int, R: int, flush) -> dict:
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the layer runs on one GPU "
-              "here; how it would shard over several is described in DESIGN.md)", file=sys.stderr)
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported: the layer runs on one GPU "
+              "(sharding it over several, tensor-parallel inside the experts with one all-reduce of the "
+              "output, is a design, not built)", file=sys.stderr)
         sys.exit(2)
     import torch
     from quantized_expert_gemv_amd import binding as B
